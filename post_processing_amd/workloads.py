@@ -1,0 +1,198 @@
+"""Seeded synthetic inputs for the frame pipeline (frames and score vectors).
+
+This module draws random numbers and nothing else: it holds none of the
+pipeline's arithmetic (no sampling, normalisation or selection), so both the
+CPU oracle's tests and the HIP path can take their inputs from it.
+
+Workload shapes follow the WarpStream TRT article (batch-1 interleaved RGB8
+producer frames, fixed-size FP32 classifier logits, Top-K with K <= 32) and the
+yolo.cu README (640x640 letterbox input, 8400 anchors x 80 classes):
+
+  C1  64x48 RGB8 -> 32x32 resize, K=5 over 1000 logits with 10 planted ties
+  C2  1920x1080 RGB8 (uniform + gradient) -> 224x224, K=5 over 1000 logits
+  C3  1280x720 RGB8 -> 640x640 letterbox (pad 114, /255 only),
+      K=32 over 8400x80 sigmoid scores
+  C4  3840x2160 RGB8 -> 384x384, K=32 over 21843 logits with 1% exact copies
+  C5L 8 lanes of C2-shaped frames read from mapped host memory, K=10
+  C5T 64 independent 1280x720 frames -> 224x224 (preprocess only)
+
+Every generator uses numpy.random.default_rng(seed) (PCG64) and draws in the
+order frame, scores, duplicate positions.  Widths are given first ("W x H"),
+so frame arrays have shape (H, W, 3).
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+IMAGENET_MEAN = (0.485, 0.456, 0.406)
+IMAGENET_STD = (0.229, 0.224, 0.225)
+
+RESIZE = 0
+LETTERBOX = 1
+
+
+@dataclass
+class Workload:
+    """One pipeline configuration plus its seeded inputs."""
+
+    name: str
+    src_w: int
+    src_h: int
+    dst_w: int
+    dst_h: int
+    mode: int                     # RESIZE or LETTERBOX
+    mean: tuple                   # unit range, per RGB channel
+    std: tuple
+    pad: float                    # letterbox pad value in byte units
+    k: int                        # 0 = no Top-K stage
+    frames: np.ndarray            # uint8 [B][H][W][3]
+    scores: np.ndarray | None     # float32 [N] or None
+    host_input: bool = False      # frame read from mapped pinned host memory
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.frames.shape[0])
+
+    @property
+    def num_scores(self) -> int:
+        return 0 if self.scores is None else int(self.scores.shape[0])
+
+
+def sha256(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def uniform_frame(rng: np.random.Generator, w: int, h: int) -> np.ndarray:
+    return rng.integers(0, 256, size=(h, w, 3), dtype=np.uint8)
+
+
+def gradient_frame(rng: np.random.Generator, w: int, h: int) -> np.ndarray:
+    """Uniform random bytes averaged with a smooth per-channel ramp.
+
+    Ramp: R rises along x, G along y, B along the diagonal; the blend is
+    (u + g) >> 1 in 16-bit integers.
+    """
+    u = uniform_frame(rng, w, h).astype(np.uint16)
+    xs = np.arange(w, dtype=np.int64)
+    ys = np.arange(h, dtype=np.int64)
+    g = np.empty((h, w, 3), dtype=np.uint16)
+    g[..., 0] = ((255 * xs) // max(w - 1, 1))[None, :]
+    g[..., 1] = ((255 * ys) // max(h - 1, 1))[:, None]
+    g[..., 2] = (255 * (xs[None, :] + ys[:, None])) // max(w + h - 2, 1)
+    return ((u + g) >> 1).astype(np.uint8)
+
+
+def plant_duplicates(rng: np.random.Generator, s: np.ndarray, sources: np.ndarray) -> np.ndarray:
+    """Copy s[sources[j]] onto distinct random positions that are not sources."""
+    s = s.copy()
+    mask = np.ones(s.shape[0], dtype=bool)
+    mask[sources] = False
+    free = np.flatnonzero(mask)
+    dst = rng.choice(free, size=sources.shape[0], replace=False)
+    s[dst] = s[sources]
+    return s
+
+
+def normal_logits(rng: np.random.Generator, n: int) -> np.ndarray:
+    return rng.standard_normal(n).astype(np.float32)
+
+
+def c1(seed: int = 0) -> Workload:
+    rng = np.random.default_rng(seed)
+    frame = uniform_frame(rng, 64, 48)
+    s = normal_logits(rng, 1000)
+    top10 = np.argsort(-s.astype(np.float64), kind="stable")[:10]
+    s = plant_duplicates(rng, s, top10)
+    return Workload("c1_64x48_to_32", 64, 48, 32, 32, RESIZE, IMAGENET_MEAN, IMAGENET_STD,
+                    114.0, 5, frame[None], s)
+
+
+def c2(seed: int = 1) -> Workload:
+    rng = np.random.default_rng(seed)
+    frame = gradient_frame(rng, 1920, 1080)
+    s = normal_logits(rng, 1000)
+    return Workload("c2_1920x1080_to_224", 1920, 1080, 224, 224, RESIZE, IMAGENET_MEAN,
+                    IMAGENET_STD, 114.0, 5, frame[None], s)
+
+
+def c3(seed: int = 2) -> Workload:
+    rng = np.random.default_rng(seed)
+    frame = uniform_frame(rng, 1280, 720)
+    x = rng.normal(-4.0, 2.0, 8400 * 80)
+    s = (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
+    return Workload("c3_1280x720_letterbox_640", 1280, 720, 640, 640, LETTERBOX,
+                    (0.0, 0.0, 0.0), (1.0, 1.0, 1.0), 114.0, 32, frame[None], s)
+
+
+def c4(seed: int = 3) -> Workload:
+    rng = np.random.default_rng(seed)
+    frame = uniform_frame(rng, 3840, 2160)
+    n = 21843
+    s = normal_logits(rng, n)
+    ndup = int(round(0.01 * n))
+    order = np.argsort(-s.astype(np.float64), kind="stable")
+    top = order[:32]
+    rest = rng.choice(order[32:], size=ndup - 32, replace=False)
+    s = plant_duplicates(rng, s, np.concatenate([top, rest]))
+    return Workload("c4_3840x2160_to_384", 3840, 2160, 384, 384, RESIZE, IMAGENET_MEAN,
+                    IMAGENET_STD, 114.0, 32, frame[None], s)
+
+
+def c5_lane(lane: int) -> Workload:
+    rng = np.random.default_rng(40 + lane)
+    frame = gradient_frame(rng, 1920, 1080)
+    s = normal_logits(rng, 1000)
+    return Workload(f"c5_lane{lane}_1920x1080_to_224", 1920, 1080, 224, 224, RESIZE,
+                    IMAGENET_MEAN, IMAGENET_STD, 114.0, 10, frame[None], s, host_input=True)
+
+
+def c5_throughput(frames: int = 64) -> Workload:
+    batch = np.empty((frames, 720, 1280, 3), dtype=np.uint8)
+    for i in range(frames):
+        batch[i] = uniform_frame(np.random.default_rng(1000 + i), 1280, 720)
+    return Workload(f"c5t_{frames}x1280x720_to_224", 1280, 720, 224, 224, RESIZE,
+                    IMAGENET_MEAN, IMAGENET_STD, 114.0, 0, batch, None)
+
+
+def random_small(seed: int, letterbox: bool = False, max_side: int = 67) -> Workload:
+    """Small random shapes (source and destination sides 1..max_side) for edge cases."""
+    rng = np.random.default_rng(10_000 + seed)
+    sw, sh, dw, dh = (int(v) for v in rng.integers(1, max_side + 1, size=4))
+    batch = int(rng.integers(1, 4))
+    frames = rng.integers(0, 256, size=(batch, sh, sw, 3), dtype=np.uint8)
+    mean = tuple(float(v) for v in rng.uniform(0.0, 1.0, 3))
+    std = tuple(float(v) for v in rng.uniform(0.1, 1.0, 3))
+    pad = float(rng.integers(0, 256))
+    return Workload(f"small{seed}_{sw}x{sh}_to_{dw}x{dh}{'_lb' if letterbox else ''}",
+                    sw, sh, dw, dh, LETTERBOX if letterbox else RESIZE, mean, std, pad, 0,
+                    frames, None)
+
+
+def scores_with_specials(seed: int, n: int, tie_frac: float = 0.1, nan_frac: float = 0.0,
+                         specials: bool = True) -> np.ndarray:
+    """N(0,1) scores with planted exact ties, NaNs, +-0, +-inf and subnormals."""
+    rng = np.random.default_rng(20_000 + seed)
+    s = rng.standard_normal(n).astype(np.float32)
+    if n == 0:
+        return s
+    nt = int(n * tie_frac)
+    if nt:
+        src = rng.integers(0, n, size=nt)
+        dst = rng.integers(0, n, size=nt)
+        s[dst] = s[src]
+    nn = int(n * nan_frac)
+    if nn:
+        s[rng.integers(0, n, size=nn)] = np.nan
+    if specials and n >= 8:
+        pos = rng.choice(n, size=8, replace=False)
+        vals = np.array([0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 1e-40, np.nan],
+                        dtype=np.float32)
+        s[pos] = vals
+    return s
+
+
+ALL_CONFIGS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4}

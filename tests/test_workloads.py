@@ -1,0 +1,51 @@
+"""Seeded input generators: determinism and the shapes/structure of each workload."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from post_processing_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "input_sha256.json")
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_config_hashes(name, golden):
+    w = wl.ALL_CONFIGS[name]()
+    assert wl.sha256(w.frames) == golden[name]["frames"]
+    assert wl.sha256(w.scores) == golden[name]["scores"]
+
+
+def test_lane_hashes(golden):
+    for lane in (0, 7):
+        w = wl.c5_lane(lane)
+        assert wl.sha256(w.frames) == golden[f"c5_lane{lane}"]["frames"]
+        assert w.host_input and w.k == 10
+
+
+def test_shapes():
+    assert wl.c1().frames.shape == (1, 48, 64, 3)
+    assert wl.c2().frames.shape == (1, 1080, 1920, 3)
+    w3 = wl.c3()
+    assert w3.frames.shape == (1, 720, 1280, 3) and w3.scores.shape == (672000,)
+    assert 0 < w3.scores.min() and w3.scores.max() < 1
+    w4 = wl.c4()
+    assert w4.scores.shape == (21843,)
+    # 218 planted copies: at least 218 values occur twice or more
+    _, counts = np.unique(w4.scores, return_counts=True)
+    assert (counts[counts > 1] - 1).sum() >= 218
+
+
+def test_c1_duplicates_of_top10():
+    w = wl.c1()
+    s = w.scores
+    top = np.sort(s)[::-1][:20]
+    vals, counts = np.unique(top, return_counts=True)
+    assert (counts == 2).sum() == 10

@@ -1,0 +1,346 @@
+"""Benchmark of the fixed-shape frame pipeline on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one replay of a lane's graph (fused preprocess, then exact Top-K)
+between the lane's two GPU events, driven by the native submit/wait loop; the
+inputs are resident (device memory, or the mapped host slot for the
+host-input lanes) before the timed region starts.  Prints ONE JSON line.
+
+Workloads (synthetic, seeded; shapes of the pages' classifier and detector
+inputs):
+  c2   1920x1080 RGB8 -> 224x224 ImageNet-normalised + Top-5 of 1000 (default)
+  c1   64x48 -> 32x32 + Top-5 of 1000 with planted ties
+  c3   1280x720 -> 640x640 letterbox (pad 114, /255) + Top-32 of 8400x80
+  c4   3840x2160 -> 384x384 + Top-32 of 21843 with 1% duplicates
+  c5l  8 lanes, one host thread each, 1920x1080 from mapped host memory, Top-10
+  c5t  64 frames 1280x720 -> 224x224 in one launch (preprocess only)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes (what the method must move at minimum, per frame).
+
+def touched_rows(src: int, dst: int) -> int:
+    rows = set()
+    for d in range(dst):
+        num = max((2 * d + 1) * src - dst, 0)
+        i0 = num // (2 * dst)
+        rows.add(i0)
+        rows.add(min(i0 + 1, src - 1))
+    return len(rows)
+
+
+def region(w) -> tuple[int, int]:
+    """(region_w, region_h) of the resampled area inside the tensor."""
+    if w.mode == 0:
+        return w.dst_w, w.dst_h
+    from fractions import Fraction
+    r = min(Fraction(w.dst_w, w.src_w), Fraction(w.dst_h, w.src_h))
+    rw = max(1, min(w.dst_w, int(w.src_w * r + Fraction(1, 2))))
+    rh = max(1, min(w.dst_h, int(w.src_h * r + Fraction(1, 2))))
+    return rw, rh
+
+
+def preprocess_bytes(w) -> dict:
+    """Source rows the taps touch (read whole) + the FP32 tensor, per launch."""
+    rw, rh = region(w)
+    src = touched_rows(w.src_h, rh) * 3 * w.src_w * w.batch
+    out = 3 * w.dst_w * w.dst_h * 4 * w.batch
+    return {"read": src, "write": out, "total": src + out}
+
+
+def topk_bytes(w) -> int:
+    return 0 if not w.k else 4 * w.num_scores + 8 * w.k
+
+
+# ---------------------------------------------------------------------------
+
+def pct(a, q):
+    return float(np.percentile(a, q))
+
+
+def lat_stats(ms: np.ndarray) -> dict:
+    us = ms.astype(np.float64) * 1e3
+    return {"p50_us": pct(us, 50), "p99_us": pct(us, 99), "mean_us": float(us.mean()),
+            "max_us": float(us.max()), "min_us": float(us.min()),
+            "p99_over_p50": pct(us, 99) / pct(us, 50)}
+
+
+def make_lane(w, torch, host_input=None, use_graph=True):
+    from post_processing_amd import ws
+    host = w.host_input if host_input is None else host_input
+    dev = torch.device("cuda:0")
+    keep = {}
+    keep["tensor"] = torch.empty((w.batch, 3, w.dst_h, w.dst_w), dtype=torch.float32, device=dev)
+    if w.k:
+        keep["scores"] = torch.from_numpy(w.scores).to(dev)
+    if not host:
+        keep["frames"] = torch.from_numpy(np.ascontiguousarray(w.frames)).to(dev)
+    torch.cuda.synchronize()
+    cfg = ws.make_config(src_w=w.src_w, src_h=w.src_h, dst_w=w.dst_w, dst_h=w.dst_h,
+                         batch=w.batch, letterbox=(w.mode == 1), pad=w.pad, mean=w.mean,
+                         std=w.std, num_scores=w.num_scores, k=w.k, host_input=host,
+                         use_graph=use_graph, input_dev=keep.get("frames"),
+                         scores_dev=keep.get("scores"), tensor_dev=keep["tensor"])
+    lane = ws.Lane(cfg)
+    if host:
+        lane.input_host_array()[...] = w.frames
+    lane._keep = keep
+    return lane
+
+
+def stage_roofline(lane, w, launches: int) -> dict:
+    """Per-kernel mean duration from back-to-back launches between HIP events
+    on the lane's stream, and the algorithmic bandwidth it implies."""
+    from post_processing_amd import ws
+    pb = preprocess_bytes(w)
+    out = {}
+    ms = lane.time_stage(ws.STAGE_PREPROCESS, launches)
+    out["preprocess"] = {"us": ms * 1e3, "bytes": pb["total"], "gbs": pb["total"] / (ms * 1e-3) / 1e9}
+    if w.k:
+        ms = lane.time_stage(ws.STAGE_TOPK, launches)
+        tb = topk_bytes(w)
+        out["topk"] = {"us": ms * 1e3, "bytes": tb, "gbs": tb / (ms * 1e-3) / 1e9}
+    return out
+
+
+def roofline_obj(stages: dict) -> dict:
+    name = max(stages, key=lambda s: stages[s]["us"])
+    st = stages[name]
+    return {"kernel": name, "bound": "hbm", "achieved": round(st["gbs"], 2),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(st["gbs"] / HBM_PEAK_GBS, 5),
+            "traffic": None, "bytes_per_launch": st["bytes"], "us_per_launch": round(st["us"], 3)}
+
+
+def run_single(w, torch, steps, warmup, use_graph=True):
+    lane = make_lane(w, torch, use_graph=use_graph)
+    lane.bench(warmup)
+    torch.cuda.synchronize()
+    ms, wall = lane.bench(steps)
+    torch.cuda.synchronize()
+    res = {"frames_per_s": steps * w.batch / wall, "wall_s": wall, **lat_stats(ms),
+           "plan": lane.plan()}
+    return lane, res
+
+
+def cold_replays(lane, torch, n: int, flush_bytes: int = 1 << 30) -> np.ndarray:
+    """Replays with a >= 1 GiB write between them, so no cache holds the frame."""
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    out = []
+    for i in range(n):
+        flush.fill_(float(i))
+        torch.cuda.synchronize()
+        out.append(lane.run())
+    del flush
+    return np.asarray(out, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, one thread, on the host of this run.
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+    from threadpoolctl import threadpool_limits
+
+    from oracle import preprocess_batch, topk
+    with threadpool_limits(1):
+        def one():
+            preprocess_batch(w.frames, w.dst_w, w.dst_h, w.mean, w.std,
+                             letterbox=(w.mode == 1), pad=w.pad)
+            if w.k:
+                topk(w.scores, w.k)
+        one()   # warm-up
+        times = []
+        t_end = time.perf_counter() + budget_s
+        while time.perf_counter() < t_end or len(times) < 3:
+            t0 = time.perf_counter()
+            one()
+            times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    return {"value": round(w.batch / med, 3), "unit": "frames/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} frames of {w.name} (float64 preprocess + stable-sort "
+                      f"Top-K), median {med * 1e3:.1f} ms/frame after 1 warm-up, 1 thread",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+# ---------------------------------------------------------------------------
+
+def versions() -> dict:
+    out = {"python": platform.python_version(), "numpy": np.__version__}
+    try:
+        import torch
+        out["torch"] = torch.__version__
+        out["hip"] = getattr(torch.version, "hip", None)
+    except Exception:
+        pass
+    try:
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
+                           timeout=30)
+        out["hipcc"] = r.stdout.splitlines()[0] if r.stdout else None
+    except Exception:
+        pass
+    return out
+
+
+def gpu_state() -> dict:
+    for cmd in (["amd-smi", "metric", "--json"], ["rocm-smi", "--showclocks", "--showtemp",
+                                                    "--showpower", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+            if r.returncode == 0 and r.stdout.strip():
+                return {"tool": cmd[0], "raw": r.stdout[:4000]}
+        except Exception:
+            continue
+    return {}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10000)
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5l", "c5t"])
+    ap.add_argument("--stage-launches", type=int, default=500)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
+    ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this pipeline runs on one GPU per process; --gpus {args.gpus} is not "
+              "supported (lanes and frames shard across GPUs with no exchange; see the design "
+              "notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    from post_processing_amd import workloads as wl
+    from post_processing_amd import ws
+    ws.load()
+
+    name = args.workload
+    t_gen = time.perf_counter()
+    if name == "c5l":
+        work = [wl.c5_lane(i) for i in range(8)]
+        w = work[0]
+    elif name == "c5t":
+        w = wl.c5_throughput(64)
+    else:
+        w = wl.ALL_CONFIGS[name]()
+    gen_s = time.perf_counter() - t_gen
+    print(f"[bench] inputs for {name} ready in {gen_s:.1f} s", file=sys.stderr, flush=True)
+
+    extra = {}
+    if name == "c5l":
+        lanes = [make_lane(x, torch) for x in work]
+        ws.bench_lanes(lanes, args.warmup)
+        torch.cuda.synchronize()
+        ms, wall = ws.bench_lanes(lanes, args.steps)
+        torch.cuda.synchronize()
+        frames = 8 * args.steps
+        res = {"frames_per_s": frames / wall, "wall_s": wall, **lat_stats(ms.ravel()),
+               "per_lane_p50_us": [pct(m * 1e3, 50) for m in ms],
+               "plan": lanes[0].plan()}
+        stages = stage_roofline(lanes[0], w, args.stage_launches)
+        pb = preprocess_bytes(w)
+        extra["mapped_host_read_gbs"] = pb["read"] / (stages["preprocess"]["us"] * 1e-6) / 1e9
+        lane = lanes[0]
+        steps_total = frames
+    else:
+        lane, res = run_single(w, torch, args.steps, args.warmup)
+        stages = stage_roofline(lane, w, args.stage_launches)
+        steps_total = args.steps
+        if name == "c5t":
+            cold = cold_replays(lane, torch, 20)
+            pb = preprocess_bytes(w)
+            extra["cold_replay_us_p50"] = float(np.median(cold) * 1e3)
+            extra["cold_hbm_gbs"] = pb["total"] / (np.median(cold) * 1e-3) / 1e9
+            extra["warm_replay_hbm_gbs"] = pb["total"] / (res["p50_us"] * 1e-6) / 1e9
+        if not args.no_direct and name != "c5t":
+            dl, dres = run_single(w, torch, min(args.steps, 2000), min(args.warmup, 200),
+                                  use_graph=False)
+            extra["direct_launch"] = {k: dres[k] for k in ("frames_per_s", "p50_us", "p99_us")}
+            dl.destroy()
+
+    roof = roofline_obj(stages)
+    pb = preprocess_bytes(w)
+    line = {
+        "metric": "frames/s and p50/p99 us per graph replay; preprocess HBM GB/s vs peak",
+        "value": round(res["frames_per_s"], 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": steps_total,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_s"] * 1e3 / steps_total, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name if name != "c5l" else "c5l_8lanes_1920x1080_to_224_mapped",
+                   "frames_per_step": w.batch, "src": [w.src_w, w.src_h],
+                   "dst": [w.dst_w, w.dst_h], "letterbox": w.mode == 1,
+                   "topk": {"n": w.num_scores, "k": w.k} if w.k else None,
+                   "input": "mapped_host" if (w.host_input or name == "c5l") else "device",
+                   "graph": True, "lanes": 8 if name == "c5l" else 1,
+                   "parallelism": "single_gpu"},
+        "p50_us": round(res["p50_us"], 3),
+        "p99_us": round(res["p99_us"], 3),
+        "p99_over_p50": round(res["p99_over_p50"], 4),
+        "preprocess_gbs": round(stages["preprocess"]["gbs"], 2),
+        "preprocess_frac_of_hbm_peak": round(stages["preprocess"]["gbs"] / HBM_PEAK_GBS, 5),
+        "kernels": {k: {"us": round(v["us"], 3), "gbs": round(v["gbs"], 2)}
+                    for k, v in stages.items()},
+        "plan": res["plan"],
+        "roofline": roof,
+    }
+    line.update({k: (round(v, 3) if isinstance(v, float) else v) for k, v in extra.items()})
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w)
+    else:
+        line["cpu_baseline"] = None
+    if args.report:
+        rep = dict(line)
+        rep["latency"] = {k: res[k] for k in res if k.endswith("_us") or k.startswith("p99")}
+        rep["versions"] = versions()
+        rep["gpu_state"] = gpu_state()
+        rep["input_sha256"] = {"frames": wl.sha256(w.frames),
+                               "scores": wl.sha256(w.scores) if w.k else None}
+        with open(args.report, "w") as f:
+            json.dump(rep, f, indent=1)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+/*
+ * ws.h -- C ABI of the fixed-shape batch-1 frame pipeline for MI355X (gfx950).
+ *
+ * A lane is one execution rail of the pipeline the WarpStream TRT article
+ * describes (its dataflow figure and its "lane" passage): the producer writes
+ * an interleaved RGB8 frame into a fixed input slot; a fused kernel resamples
+ * it (bilinear resize, or aspect-preserving letterbox as in the yolo.cu
+ * README), normalises it with a per-channel mean and standard deviation and
+ * writes the FP32 NCHW tensor; an exact Top-K kernel selects the K best
+ * entries of a fixed device-resident FP32 score vector and writes only the K
+ * score/index pairs into a mapped host result slot.  Both kernels are captured
+ * once into one hipGraph per lane and replayed per frame with no host decision
+ * point in between.  (In the article a network sits between the two stages;
+ * here the score vector is an independent input.)
+ *
+ * Everything is allocated, resolved and captured in ws_create_lane ("dynamism
+ * belongs at startup"); ws_submit and ws_wait allocate nothing and make no
+ * host decision on GPU data.
+ *
+ * Error convention: every call returns int, WS_OK (0) on success and a
+ * negative WS_E_* code otherwise.  Nothing throws across this boundary.  The
+ * last HIP error seen by a lane is kept and can be read with
+ * ws_lane_hip_error().
+ *
+ * Threading: at most one host thread may use a lane at a time.  Different
+ * lanes are independent and may be driven from different threads.
+ */
+#ifndef WS_H
+#define WS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define WS_OK              0
+#define WS_E_INVALID_ARG  (-1)  /* NULL pointer, size or value out of range  */
+#define WS_E_STATE        (-2)  /* submit while in flight, wait with nothing */
+#define WS_E_NO_MAP_HOST  (-3)  /* device cannot map pinned host memory      */
+#define WS_E_OOM          (-4)  /* a device or pinned allocation failed      */
+#define WS_E_CAPTURE      (-5)  /* graph capture / instantiation failed      */
+#define WS_E_HIP          (-6)  /* any other HIP runtime error               */
+#define WS_E_NO_DEVICE    (-7)  /* no such HIP device                        */
+
+/* ---- enumerations ------------------------------------------------------ */
+#define WS_RESIZE_BILINEAR   0  /* stretch the frame onto the whole tensor   */
+#define WS_RESIZE_LETTERBOX  1  /* keep aspect, centre, pad the rest         */
+
+#define WS_INPUT_MAPPED_HOST 0  /* producer writes pinned host memory the GPU
+                                   reads over the bus (zero-copy slot)        */
+#define WS_INPUT_DEVICE      1  /* frame already resides in device memory    */
+
+#define WS_WAIT_SPIN   0        /* ws_wait polls the completion event        */
+#define WS_WAIT_BLOCK  1        /* ws_wait blocks in the runtime             */
+
+/* Limits checked by ws_create_lane. */
+#define WS_MAX_K       32
+#define WS_MAX_BATCH   64
+#define WS_MAX_SIDE    16384
+
+/* One selected entry: the score (original bits; NaN reported as -inf) and its
+ * position in the score vector.  8 bytes, array of structs, rank order. */
+typedef struct ws_topk_entry {
+    float   score;
+    int32_t index;
+} ws_topk_entry;
+
+/* Lane construction parameters.  All fields are read once, by ws_create_lane.
+ * Zero-initialise the struct and set what you need. */
+typedef struct ws_lane_config {
+    int32_t device;        /* HIP device ordinal                              */
+    int32_t batch;         /* frames per submit, 1..WS_MAX_BATCH              */
+    int32_t src_w, src_h;  /* producer frame width and height, 1..WS_MAX_SIDE */
+    int32_t dst_w, dst_h;  /* tensor width and height, 1..WS_MAX_SIDE         */
+    int32_t resize_mode;   /* WS_RESIZE_*                                     */
+    int32_t input_mode;    /* WS_INPUT_*                                      */
+    double  pad_value;     /* letterbox fill in byte units, 0..255            */
+    double  mean[3];       /* per RGB channel, unit range (0.485 ...)         */
+    double  std[3];        /* per RGB channel, unit range, > 0                */
+    int32_t num_scores;    /* N; 0 = no Top-K stage                           */
+    int32_t k;             /* 1..min(WS_MAX_K, N) when N > 0                  */
+    int32_t use_graph;     /* 1 = replay the captured graph (the product);
+                              0 = launch the same kernels directly (for the
+                              graph vs direct-launch comparison only)        */
+    int32_t wait_mode;     /* WS_WAIT_*                                       */
+    /* Optional borrowed device buffers (NULL = the lane allocates its own).
+     * Each must be 16-byte aligned, large enough for its layout below,
+     * outlive the lane and never move: their addresses are baked into the
+     * graph. */
+    const uint8_t *input_dev;  /* WS_INPUT_DEVICE only                         */
+    const float   *scores_dev;
+    float         *tensor_dev;
+    /* Tuning knobs (0 = automatic choice); they change speed, never results. */
+    int32_t rows_per_group;    /* preprocess: output rows per workgroup        */
+    int32_t topk_chunk;        /* Top-K: scores per workgroup (multiple of 1024) */
+} ws_lane_config;
+
+/* Stable views of a lane's buffers, valid from ws_create_lane to ws_destroy.
+ *   input   uint8  [batch][src_h][src_w][3]   interleaved RGB, rows packed
+ *   tensor  float  [batch][3][dst_h][dst_w]   planar R, G, B
+ *   scores  float  [num_scores]
+ *   result  ws_topk_entry [k]                 mapped host memory, rank order
+ */
+typedef struct ws_lane_view {
+    uint8_t             *input_host;   /* producer's slot (mapped mode), else NULL */
+    const uint8_t       *input_dev;    /* address the preprocess kernel reads      */
+    float               *tensor_dev;
+    float               *scores_dev;   /* NULL when num_scores == 0                */
+    const ws_topk_entry *result_host;  /* NULL when num_scores == 0                */
+    size_t               input_bytes;
+    size_t               tensor_bytes;
+} ws_lane_view;
+
+typedef struct ws_lane ws_lane;
+
+/*
+ * ws_create_lane -- validate cfg, then allocate and bind everything the lane
+ * will ever use: input slot (hipHostMalloc mapped, coherent) or device input,
+ * tensor, scores, mapped result slot, exact sampling-tap tables, Top-K
+ * scratch, one non-blocking stream and two timing events.  Runs the kernels
+ * once outside capture (warm-up), captures them into one graph, instantiates
+ * and uploads it, and replays it once.  Source: the article's lane and
+ * initialisation passages (allocate once, bind once, capture once; map-host
+ * enabled before use, failing loudly when the device cannot map).
+ *
+ *   cfg   read only; not retained.
+ *   out   receives the lane handle (owned by the caller until ws_destroy).
+ *   view  optional (may be NULL); receives the stable buffer views.
+ * Returns WS_OK, WS_E_INVALID_ARG, WS_E_NO_DEVICE, WS_E_NO_MAP_HOST,
+ * WS_E_OOM, WS_E_CAPTURE or WS_E_HIP.  On failure nothing is leaked and *out
+ * is set to NULL.
+ */
+int ws_create_lane(const ws_lane_config *cfg, ws_lane **out, ws_lane_view *view);
+
+/*
+ * ws_submit -- READY -> IN_FLIGHT: record the start event, replay the lane's
+ * graph (preprocess, then Top-K, in stream order), record the done event.
+ * No allocation, no synchronisation, no host branch on GPU data.  The input
+ * slot and scores must hold the frame's data before this call and must not
+ * be modified until ws_wait returns.  Source: the article's submit passage.
+ * Returns WS_E_STATE if the lane is already in flight (a lane cannot be
+ * reused while busy; there is no queue), WS_E_INVALID_ARG for NULL, WS_E_HIP
+ * if a launch fails (the lane stays READY).
+ */
+int ws_submit(ws_lane *lane);
+
+/*
+ * ws_wait -- IN_FLIGHT -> READY: wait for the done event (spinning or
+ * blocking per cfg.wait_mode).  If gpu_ms is not NULL it receives the GPU
+ * time between the start and done events in milliseconds.  Afterwards the
+ * result slot and the tensor hold this frame's output until the next
+ * ws_submit.  Returns WS_E_STATE if nothing is in flight, WS_E_HIP on a
+ * runtime error.
+ */
+int ws_wait(ws_lane *lane, float *gpu_ms);
+
+/*
+ * ws_destroy -- release everything the lane owns (borrowed buffers are left
+ * alone).  Valid in any state: an in-flight lane is waited for first, so no
+ * memory the GPU may still touch is freed.  NULL is accepted (no-op).
+ */
+int ws_destroy(ws_lane *lane);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *ws_status_str(int status);
+
+/* Last hipError_t value the lane saw (0 if none); 0 for NULL. */
+int ws_lane_hip_error(const ws_lane *lane);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WS_H */

@@ -1,0 +1,72 @@
+/*
+ * ws_bench.h -- native latency harness around the lane ABI in ws.h.
+ *
+ * The WarpStream TRT article's benchmark passage times each replay with GPU
+ * events recorded just before the graph launch and just after Top-K, and
+ * measures throughput across one or more lanes with a host wall clock; the
+ * producer's write and the consumer's work are excluded.  These calls run
+ * that loop in native code so no interpreter overhead enters the wall clock.
+ * They are harness, not part of the per-frame product path.
+ */
+#ifndef WS_BENCH_H
+#define WS_BENCH_H
+
+#include "ws.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Launch geometry a lane chose at construction (for reports). */
+typedef struct ws_lane_plan {
+    int32_t pre_groups;       /* preprocess workgroups per launch            */
+    int32_t pre_block;        /* preprocess threads per workgroup            */
+    int32_t rows_per_group;   /* output rows per preprocess workgroup        */
+    int32_t pre_lds_bytes;    /* LDS per preprocess workgroup                */
+    int32_t topk_groups;      /* Top-K workgroups (0 = no Top-K stage)       */
+    int32_t topk_block;       /* Top-K threads per workgroup                 */
+    int32_t topk_chunk;       /* scores per Top-K workgroup                  */
+    int32_t graph_nodes;      /* kernel nodes in the captured graph          */
+} ws_lane_plan;
+
+/* Fill *plan for lane.  Returns WS_OK or WS_E_INVALID_ARG (NULL). */
+int ws_lane_describe(const ws_lane *lane, ws_lane_plan *plan);
+
+/*
+ * Run `replays` x (ws_submit, ws_wait) on one lane from the calling thread.
+ *   gpu_ms   optional, `replays` entries: start->done event time per replay.
+ *   wall_s   optional: host wall time from before the first submit to after
+ *            the last wait.
+ * Returns the first non-OK status of any call, else WS_OK.
+ */
+int ws_bench_replays(ws_lane *lane, int32_t replays, float *gpu_ms, double *wall_s);
+
+/*
+ * Drive `nlanes` lanes concurrently, one host thread per lane, each running
+ * `replays` x (ws_submit, ws_wait).  Threads start together after all are
+ * ready; wall_s spans from that release to the last thread's finish.
+ *   gpu_ms   optional, nlanes * replays entries, lane-major.
+ * Returns the first non-OK status seen, else WS_OK.
+ */
+int ws_bench_lanes(ws_lane **lanes, int32_t nlanes, int32_t replays, float *gpu_ms,
+                   double *wall_s);
+
+/* Stages of the per-frame launch sequence, for ws_bench_stage. */
+#define WS_STAGE_PREPROCESS 0
+#define WS_STAGE_TOPK       1
+
+/*
+ * Time one stage's kernel alone: `launches` back-to-back direct launches on
+ * the lane's stream between two events, then a synchronisation.  The lane
+ * must be READY and stays READY; its buffers receive that stage's output.
+ *   ms_per_launch  receives the elapsed event time divided by `launches`.
+ * Returns WS_OK, WS_E_STATE (in flight), WS_E_INVALID_ARG (NULL, bad stage,
+ * launches < 1, or a Top-K stage the lane does not have) or WS_E_HIP.
+ */
+int ws_bench_stage(ws_lane *lane, int32_t stage, int32_t launches, double *ms_per_launch);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WS_BENCH_H */

@@ -1,0 +1,67 @@
+"""Builds the lane library libws.so in-tree with hipcc for gfx950.
+
+    python -m post_processing_amd.build
+
+Also builds the host-only test driver of the planning code (g++, no HIP)
+when asked to (see tests/test_host_logic.py).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libws.so")
+SOURCES = ["ws_kernels.hip", "ws_runtime.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the lane library)")
+
+
+def lib_command(out: str) -> list[str]:
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-Wall", "-Wno-unused-command-line-argument",
+        # keep the compiler from forming packed FP32 instructions
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC,
+        "-o", out,
+    ] + [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build_lib(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = lib_command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def build_host_test(out: str) -> str:
+    """g++ build of the planning code's host-only test driver (no HIP)."""
+    src = os.path.join(ROOT, "tests", "host", "ws_plan_test.cpp")
+    cmd = ["g++", "-std=c++17", "-O1", "-Wall", "-Werror", "-I", INCLUDE, "-I", CSRC,
+           "-o", out, src]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("g++ failed:\n" + res.stdout + res.stderr)
+    return out
+
+
+if __name__ == "__main__":
+    print(build_lib(verbose=True))

@@ -1,0 +1,52 @@
+// ws_kernels.h -- launch parameters and launchers of the two pipeline kernels.
+// Internal to the library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ws {
+
+// Fused preprocess: RGB8 HWC frames -> resample -> normalise -> FP32 NCHW.
+struct PreParams {
+    const uint8_t* src;     // [batch][src_h][src_w][3], 16-byte aligned base
+    float* dst;             // [batch][3][dst_h][dst_w]
+    int64_t frame_bytes;    // 3 * src_w * src_h
+    int64_t total_bytes;    // batch * frame_bytes (bound of every staged load)
+    int32_t src_w, src_h;
+    int32_t dst_w, dst_h;
+    int32_t left, top;      // resampled region inside the tensor
+    int32_t reg_w, reg_h;
+    float inv_den_x;        // 1 / (2 reg_w)
+    float inv_den_y;        // 1 / (2 reg_h)
+    int32_t span_lo;        // first staged byte of a source row
+    int32_t slot_chunks;    // 16-byte chunks per staged row
+    int32_t quads_per_row;  // ceil(dst_w / 4)
+    int32_t rows_per_group;
+    int32_t groups_per_frame;
+    int32_t vec4;           // dst_w % 4 == 0: rows are 16-byte aligned
+    float a[3];             // 1 / (255 std[c])
+    float b[3];             // -mean[c] / std[c]
+    float padv[3];          // (pad / 255 - mean[c]) / std[c]
+};
+
+// Exact Top-K over FP32 scores; G workgroups each select their chunk's top K,
+// the last one to finish merges the G partial lists.
+struct TopkParams {
+    const float* scores;     // [n], 16-byte aligned
+    int64_t n;
+    int32_t k;
+    int32_t chunk;           // scores per workgroup, multiple of 1024
+    int32_t groups;
+    uint64_t* partials;      // [groups][k] order keys (groups > 1)
+    uint32_t* counter;       // arrival counter, zero between launches
+    uint2* result;           // [k] {score bits, index}, device view of the slot
+};
+
+hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_bytes,
+                             hipStream_t stream);
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+
+constexpr int kTopkThreads = 256;
+
+}  // namespace ws

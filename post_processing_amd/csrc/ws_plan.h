@@ -1,0 +1,257 @@
+// ws_plan.h -- host-side planning for a pipeline lane: configuration checks,
+// exact sampling taps, launch geometry and the lane state machine.
+//
+// Plain C++17 with no HIP dependency, so the same code the library runs can
+// be compiled and tested on a host without a GPU.
+//
+// Sampling rule (WarpStream TRT article, fused-preprocess passage: every
+// destination pixel takes a centre-aligned source coordinate and its four
+// bilinear neighbours; half-pixel centres, align_corners=false, edge clamp):
+//     src(d) = (d + 1/2) * S / R - 1/2 = ((2d + 1) S - R) / (2R)
+// clamped below at 0, i0 = floor(src), w = src - i0, i1 = min(i0 + 1, S - 1).
+// It is evaluated here in 64-bit integers, so the tap indices are exact and
+// each weight is the exact fraction rounded once to FP32.  (A float
+// evaluation of (d + 0.5) * scale - 0.5 is off by up to ~1e-4 px at
+// 1080 -> 224, which alone moves outputs by ~5e-4.)
+//
+// Letterbox (yolo.cu README: the raw frame is letterboxed on the GPU):
+// r = min(Dw/W, Dh/H) as a fraction; region Rw = floor(W r + 1/2),
+// Rh = floor(H r + 1/2), each at least 1; left = floor((Dw - Rw) / 2),
+// top = floor((Dh - Rh) / 2); the frame is resampled onto the region with the
+// rule above per axis and every other cell holds the pad byte value.
+#pragma once
+
+#include <cmath>
+#include <cstddef>
+#include <algorithm>
+#include <cstdint>
+
+#include "ws.h"
+
+namespace ws {
+
+// One sampling tap along an axis: the two source indices and the weight of
+// the second.
+struct Tap {
+    int32_t i0;
+    int32_t i1;
+    float w;
+};
+
+struct Region {
+    int32_t left, top, w, h;
+};
+
+// Exact tap for destination index d of an axis resampling S source samples
+// onto R destination samples.
+inline Tap axis_tap(int64_t S, int64_t R, int64_t d) {
+    int64_t num = (2 * d + 1) * S - R;
+    const int64_t den = 2 * R;
+    if (num < 0) num = 0;
+    const int64_t i0 = num / den;
+    const int64_t rem = num - i0 * den;
+    Tap t;
+    t.i0 = (int32_t)i0;
+    t.i1 = (int32_t)(i0 + 1 < S ? i0 + 1 : S - 1);
+    t.w = (float)((double)rem / (double)den);
+    return t;
+}
+
+inline Region letterbox_region(int64_t W, int64_t H, int64_t Dw, int64_t Dh) {
+    // r = min(Dw/W, Dh/H); compare Dw*H against Dh*W to pick the binding axis.
+    int64_t rn, rd;  // r = rn / rd
+    if (Dw * H <= Dh * W) { rn = Dw; rd = W; } else { rn = Dh; rd = H; }
+    // floor(X * rn / rd + 1/2) = floor((2 X rn + rd) / (2 rd))
+    int64_t rw = (2 * W * rn + rd) / (2 * rd);
+    int64_t rh = (2 * H * rn + rd) / (2 * rd);
+    if (rw < 1) rw = 1;
+    if (rh < 1) rh = 1;
+    if (rw > Dw) rw = Dw;
+    if (rh > Dh) rh = Dh;
+    Region g;
+    g.w = (int32_t)rw;
+    g.h = (int32_t)rh;
+    g.left = (int32_t)((Dw - rw) / 2);
+    g.top = (int32_t)((Dh - rh) / 2);
+    return g;
+}
+
+inline Region lane_region(const ws_lane_config& c) {
+    if (c.resize_mode == WS_RESIZE_LETTERBOX)
+        return letterbox_region(c.src_w, c.src_h, c.dst_w, c.dst_h);
+    Region g;
+    g.left = 0;
+    g.top = 0;
+    g.w = c.dst_w;
+    g.h = c.dst_h;
+    return g;
+}
+
+// ---------------------------------------------------------------------------
+// Configuration checks.
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int validate_config(const ws_lane_config* c) {
+    if (!c) return WS_E_INVALID_ARG;
+    if (c->device < 0) return WS_E_INVALID_ARG;
+    if (c->batch < 1 || c->batch > WS_MAX_BATCH) return WS_E_INVALID_ARG;
+    if (c->src_w < 1 || c->src_h < 1 || c->dst_w < 1 || c->dst_h < 1) return WS_E_INVALID_ARG;
+    if (c->src_w > WS_MAX_SIDE || c->src_h > WS_MAX_SIDE || c->dst_w > WS_MAX_SIDE ||
+        c->dst_h > WS_MAX_SIDE)
+        return WS_E_INVALID_ARG;
+    if (c->resize_mode != WS_RESIZE_BILINEAR && c->resize_mode != WS_RESIZE_LETTERBOX)
+        return WS_E_INVALID_ARG;
+    if (c->input_mode != WS_INPUT_MAPPED_HOST && c->input_mode != WS_INPUT_DEVICE)
+        return WS_E_INVALID_ARG;
+    if (!(c->pad_value >= 0.0 && c->pad_value <= 255.0)) return WS_E_INVALID_ARG;
+    for (int i = 0; i < 3; ++i) {
+        if (!std::isfinite(c->mean[i])) return WS_E_INVALID_ARG;
+        if (!(std::isfinite(c->std[i]) && c->std[i] > 0.0)) return WS_E_INVALID_ARG;
+    }
+    if (c->num_scores < 0) return WS_E_INVALID_ARG;
+    if (c->num_scores > 0) {
+        const int kmax = c->num_scores < WS_MAX_K ? c->num_scores : WS_MAX_K;
+        if (c->k < 1 || c->k > kmax) return WS_E_INVALID_ARG;
+    } else if (c->k != 0) {
+        return WS_E_INVALID_ARG;
+    }
+    if (c->use_graph != 0 && c->use_graph != 1) return WS_E_INVALID_ARG;
+    if (c->wait_mode != WS_WAIT_SPIN && c->wait_mode != WS_WAIT_BLOCK) return WS_E_INVALID_ARG;
+    if (c->input_dev && c->input_mode != WS_INPUT_DEVICE) return WS_E_INVALID_ARG;
+    if (!aligned16(c->input_dev) || !aligned16(c->scores_dev) || !aligned16(c->tensor_dev))
+        return WS_E_INVALID_ARG;
+    if (c->scores_dev && c->num_scores == 0) return WS_E_INVALID_ARG;
+    if (c->rows_per_group < 0 || c->rows_per_group > 64) return WS_E_INVALID_ARG;
+    if (c->topk_chunk < 0 || (c->topk_chunk % 1024) != 0) return WS_E_INVALID_ARG;
+    return WS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch geometry.
+
+constexpr int kMaxPreBlock = 512;          // preprocess threads per workgroup
+constexpr int kMaxLdsBytes = 156 * 1024;   // gfx950: 160 KiB LDS per workgroup, less static use
+constexpr int kTopkBlock = 256;            // four wave64s
+constexpr int kTopkAutoChunk = 4096;       // scores per Top-K workgroup (auto)
+
+struct Plan {
+    Region region;
+    // Source byte span [span_lo, span_lo + span) of each source row that the
+    // region's horizontal taps touch.
+    int64_t span_lo = 0, span = 0;
+    int32_t slot_bytes = 0;        // LDS bytes per staged source row (16-multiple)
+    int32_t quads_per_row = 0;     // ceil(dst_w / 4): each thread owns 4 columns
+    int32_t rows_per_group = 1;
+    int32_t pre_block = 64;
+    int32_t pre_groups = 0;
+    int32_t groups_per_frame = 0;
+    int32_t lds_bytes = 0;
+    // Top-K
+    int32_t topk_groups = 0;
+    int32_t topk_chunk = 0;
+    // Sizes
+    size_t frame_bytes = 0, input_bytes = 0, tensor_bytes = 0;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int32_t lds_for_rows(int32_t rows, int32_t slot_bytes) {
+    return 2 * rows * slot_bytes + 16;
+}
+
+// Returns WS_OK and fills *p, or WS_E_INVALID_ARG if the shape cannot be
+// staged (a source row span larger than LDS allows).
+inline int make_plan(const ws_lane_config& c, Plan* p) {
+    p->region = lane_region(c);
+    const Region& g = p->region;
+    const int64_t W = c.src_w, H = c.src_h, Dw = c.dst_w, Dh = c.dst_h;
+
+    // The byte span of a source row that the region's horizontal taps read.
+    const Tap first = axis_tap(W, g.w, 0);
+    const Tap last = axis_tap(W, g.w, g.w - 1);
+    p->span_lo = 3 * (int64_t)first.i0;
+    p->span = 3 * (int64_t)last.i1 + 3 - p->span_lo;
+    // A staged row starts at its 16-byte-aligned address below the span, so it
+    // needs up to 15 extra bytes in front.
+    p->slot_bytes = (int32_t)(ceil_div(p->span + 15, 16) * 16);
+    if (lds_for_rows(1, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
+
+    p->quads_per_row = (int32_t)ceil_div(Dw, 4);
+    const int32_t q = p->quads_per_row;
+
+    int32_t rows = c.rows_per_group;
+    if (rows == 0) {
+        // Prefer full lanes, but keep at least 512 workgroups (two per CU) when
+        // the tensor has that many rows, so small frames spread over the chip.
+        const int64_t total_rows = (int64_t)c.batch * Dh;
+        const int64_t min_groups = total_rows < 512 ? total_rows : 512;
+        double best_util = -1.0;
+        rows = 1;
+        for (int32_t r = 1; r <= 64; ++r) {
+            const int64_t threads = (int64_t)r * q;
+            if (r > 1 && threads > kMaxPreBlock) break;
+            if (r > Dh) break;
+            if (lds_for_rows(r, p->slot_bytes) > kMaxLdsBytes / 2 && r > 1) break;
+            const int64_t groups = (int64_t)c.batch * ceil_div(Dh, r);
+            if (groups < min_groups) break;
+            const int64_t blk = std::min<int64_t>(kMaxPreBlock, ceil_div(threads, 64) * 64);
+            const double util = (double)std::min<int64_t>(threads, blk) / (double)blk;
+            if (util > best_util + 1e-9) {
+                best_util = util;
+                rows = r;
+            }
+        }
+    }
+    if (rows > Dh) rows = (int32_t)Dh;
+    if (lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
+    p->rows_per_group = rows;
+    const int64_t threads = (int64_t)rows * q;
+    p->pre_block = (int32_t)std::min<int64_t>(kMaxPreBlock, ceil_div(threads, 64) * 64);
+    p->groups_per_frame = (int32_t)ceil_div(Dh, rows);
+    const int64_t groups = (int64_t)c.batch * p->groups_per_frame;
+    if (groups > 0x7fffffff) return WS_E_INVALID_ARG;
+    p->pre_groups = (int32_t)groups;
+    p->lds_bytes = lds_for_rows(rows, p->slot_bytes);
+
+    if (c.num_scores > 0) {
+        int64_t chunk = c.topk_chunk;
+        if (chunk == 0) {
+            chunk = c.num_scores <= kTopkAutoChunk ? ceil_div(c.num_scores, 1024) * 1024
+                                                   : kTopkAutoChunk;
+        }
+        p->topk_chunk = (int32_t)chunk;
+        p->topk_groups = (int32_t)ceil_div(c.num_scores, chunk);
+    }
+
+    p->frame_bytes = (size_t)W * (size_t)H * 3u;
+    p->input_bytes = p->frame_bytes * (size_t)c.batch;
+    p->tensor_bytes = (size_t)c.batch * 3u * (size_t)Dw * (size_t)Dh * sizeof(float);
+    return WS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Lane state machine: READY --submit--> IN_FLIGHT --wait--> READY.
+// A busy lane rejects a second submit (no hidden queue); a wait with nothing
+// in flight is an error.  Destroy is legal in both states.
+
+enum class LaneState : int { Ready = 0, InFlight = 1 };
+
+inline int begin_submit(LaneState s) { return s == LaneState::Ready ? WS_OK : WS_E_STATE; }
+inline int begin_wait(LaneState s) { return s == LaneState::InFlight ? WS_OK : WS_E_STATE; }
+
+inline const char* status_str(int s) {
+    switch (s) {
+        case WS_OK: return "WS_OK";
+        case WS_E_INVALID_ARG: return "WS_E_INVALID_ARG";
+        case WS_E_STATE: return "WS_E_STATE";
+        case WS_E_NO_MAP_HOST: return "WS_E_NO_MAP_HOST";
+        case WS_E_OOM: return "WS_E_OOM";
+        case WS_E_CAPTURE: return "WS_E_CAPTURE";
+        case WS_E_HIP: return "WS_E_HIP";
+        case WS_E_NO_DEVICE: return "WS_E_NO_DEVICE";
+        default: return "WS_E_UNKNOWN";
+    }
+}
+
+}  // namespace ws

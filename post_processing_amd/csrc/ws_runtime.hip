@@ -1,0 +1,414 @@
+// ws_runtime.hip -- lane runtime behind the C ABI in ws.h / ws_bench.h.
+//
+// WarpStream TRT article, lane and initialisation passages: each lane owns a
+// mapped input slot, a device tensor, device scores, a mapped result slot,
+// two timing events, a non-blocking stream and one instantiated graph; all of
+// it is created here once, and submit / wait only record events, replay the
+// graph and wait.  Map-host capability is checked before any mapped
+// allocation and its absence is reported, not ignored.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <chrono>
+#include <cstring>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "ws.h"
+#include "ws_bench.h"
+#include "ws_kernels.h"
+#include "ws_plan.h"
+
+namespace ws {
+hipError_t set_kernel_attributes();
+}
+
+struct ws_lane {
+    ws_lane_config cfg;
+    ws::Plan plan;
+    ws::LaneState state = ws::LaneState::Ready;
+    int device = 0;
+    hipStream_t stream = nullptr;
+    hipEvent_t ev_start = nullptr;
+    hipEvent_t ev_done = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    uint8_t* in_host = nullptr;        // mapped input slot (host view)
+    uint8_t* in_own = nullptr;         // lane-owned device input
+    const uint8_t* in_dev = nullptr;   // what the kernel reads
+    float* tensor = nullptr;
+    bool own_tensor = false;
+    float* scores = nullptr;
+    bool own_scores = false;
+    ws_topk_entry* res_host = nullptr;  // mapped result slot (host view)
+    uint2* res_dev = nullptr;           // its device view
+    uint64_t* partials = nullptr;
+    uint32_t* counter = nullptr;
+    ws::PreParams pre{};
+    ws::TopkParams tk{};
+    int nodes = 0;
+    int last_err = 0;
+};
+
+namespace {
+
+int fail(ws_lane* L, hipError_t e, int code) {
+    if (L) L->last_err = (int)e;
+    return code;
+}
+
+// The per-frame launch sequence: preprocess, then Top-K, in stream order.
+hipError_t launch_all(ws_lane* L) {
+    hipError_t e = ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
+                                         L->plan.lds_bytes, L->stream);
+    if (e != hipSuccess) return e;
+    if (L->cfg.num_scores > 0) e = ws::launch_topk(L->tk, L->stream);
+    return e;
+}
+
+void release(ws_lane* L) {
+    if (!L) return;
+    if (L->stream) hipStreamSynchronize(L->stream);
+    if (L->exec) hipGraphExecDestroy(L->exec);
+    if (L->graph) hipGraphDestroy(L->graph);
+    if (L->ev_start) hipEventDestroy(L->ev_start);
+    if (L->ev_done) hipEventDestroy(L->ev_done);
+    if (L->stream) hipStreamDestroy(L->stream);
+    if (L->in_host) hipHostFree(L->in_host);
+    if (L->in_own) hipFree(L->in_own);
+    if (L->own_tensor && L->tensor) hipFree(L->tensor);
+    if (L->own_scores && L->scores) hipFree(L->scores);
+    if (L->res_host) hipHostFree(L->res_host);
+    if (L->partials) hipFree(L->partials);
+    if (L->counter) hipFree(L->counter);
+    delete L;
+}
+
+int dev_alloc(ws_lane* L, void** p, size_t bytes) {
+    hipError_t e = hipMalloc(p, bytes < 16 ? 16 : bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return fail(L, e, WS_E_OOM);
+    }
+    return WS_OK;
+}
+
+// Pinned, mapped, coherent host memory and its device address.
+int mapped_alloc(ws_lane* L, void** host, void** dev, size_t bytes) {
+    hipError_t e = hipHostMalloc(host, bytes < 16 ? 16 : bytes,
+                                 hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess) {
+        *host = nullptr;
+        return fail(L, e, WS_E_OOM);
+    }
+    std::memset(*host, 0, bytes < 16 ? 16 : bytes);
+    e = hipHostGetDevicePointer(dev, *host, 0);
+    if (e != hipSuccess) return fail(L, e, WS_E_NO_MAP_HOST);
+    return WS_OK;
+}
+
+#define WS_TRY(expr)                 \
+    do {                             \
+        const int rc_ = (expr);      \
+        if (rc_ != WS_OK) return rc_; \
+    } while (0)
+
+#define WS_HIP(expr, code)                                 \
+    do {                                                   \
+        const hipError_t e_ = (expr);                      \
+        if (e_ != hipSuccess) return fail(L, e_, (code));  \
+    } while (0)
+
+int build(ws_lane* L) {
+    const ws_lane_config& c = L->cfg;
+    ws::Plan& P = L->plan;
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || c.device >= ndev) return WS_E_NO_DEVICE;
+    L->device = c.device;
+    WS_HIP(hipSetDevice(c.device), WS_E_HIP);
+    // Mapping must be enabled before use.  ROCm always allows it; the flag
+    // call fails harmlessly once the device is active, so the capability and
+    // the mapping itself are what decide.
+    (void)hipSetDeviceFlags(hipDeviceMapHost);
+    (void)hipGetLastError();
+    int can_map = 0;
+    WS_HIP(hipDeviceGetAttribute(&can_map, hipDeviceAttributeCanMapHostMemory, c.device),
+           WS_E_HIP);
+    if (!can_map) return WS_E_NO_MAP_HOST;
+
+    WS_TRY(ws::make_plan(c, &P));
+    // Raise the dynamic LDS limit for wide rows; only a plan that needs more
+    // than the default 64 KiB depends on it succeeding.
+    if (ws::set_kernel_attributes() != hipSuccess) {
+        const hipError_t e = hipGetLastError();
+        if (P.lds_bytes > 64 * 1024) return fail(L, e, WS_E_HIP);
+    }
+
+    // ---- buffers ---------------------------------------------------------
+    if (c.input_mode == WS_INPUT_MAPPED_HOST) {
+        void *h = nullptr, *d = nullptr;
+        WS_TRY(mapped_alloc(L, &h, &d, P.input_bytes));
+        L->in_host = static_cast<uint8_t*>(h);
+        L->in_dev = static_cast<const uint8_t*>(d);
+    } else if (c.input_dev) {
+        L->in_dev = c.input_dev;
+    } else {
+        void* d = nullptr;
+        WS_TRY(dev_alloc(L, &d, P.input_bytes));
+        L->in_own = static_cast<uint8_t*>(d);
+        L->in_dev = L->in_own;
+        WS_HIP(hipMemset(L->in_own, 0, P.input_bytes), WS_E_HIP);
+    }
+    if (c.tensor_dev) {
+        L->tensor = c.tensor_dev;
+    } else {
+        void* d = nullptr;
+        WS_TRY(dev_alloc(L, &d, P.tensor_bytes));
+        L->tensor = static_cast<float*>(d);
+        L->own_tensor = true;
+    }
+    if (c.num_scores > 0) {
+        if (c.scores_dev) {
+            L->scores = const_cast<float*>(c.scores_dev);
+        } else {
+            void* d = nullptr;
+            WS_TRY(dev_alloc(L, &d, (size_t)c.num_scores * sizeof(float)));
+            L->scores = static_cast<float*>(d);
+            L->own_scores = true;
+            WS_HIP(hipMemset(L->scores, 0, (size_t)c.num_scores * sizeof(float)), WS_E_HIP);
+        }
+        void *h = nullptr, *d = nullptr;
+        WS_TRY(mapped_alloc(L, &h, &d, (size_t)c.k * sizeof(ws_topk_entry)));
+        L->res_host = static_cast<ws_topk_entry*>(h);
+        L->res_dev = static_cast<uint2*>(d);
+        void* pp = nullptr;
+        WS_TRY(dev_alloc(L, &pp, (size_t)P.topk_groups * (size_t)c.k * sizeof(uint64_t)));
+        L->partials = static_cast<uint64_t*>(pp);
+        void* cn = nullptr;
+        WS_TRY(dev_alloc(L, &cn, sizeof(uint32_t)));
+        L->counter = static_cast<uint32_t*>(cn);
+        WS_HIP(hipMemset(L->counter, 0, sizeof(uint32_t)), WS_E_HIP);
+    }
+
+    // ---- kernel parameters (fixed for the lane's lifetime) ----------------
+    ws::PreParams& q = L->pre;
+    q.src = L->in_dev;
+    q.dst = L->tensor;
+    q.frame_bytes = (int64_t)P.frame_bytes;
+    q.total_bytes = (int64_t)P.input_bytes;
+    q.src_w = c.src_w;
+    q.src_h = c.src_h;
+    q.dst_w = c.dst_w;
+    q.dst_h = c.dst_h;
+    q.left = P.region.left;
+    q.top = P.region.top;
+    q.reg_w = P.region.w;
+    q.reg_h = P.region.h;
+    q.inv_den_x = (float)(1.0 / (2.0 * P.region.w));
+    q.inv_den_y = (float)(1.0 / (2.0 * P.region.h));
+    q.span_lo = (int32_t)P.span_lo;
+    q.slot_chunks = P.slot_bytes / 16;
+    q.quads_per_row = P.quads_per_row;
+    q.rows_per_group = P.rows_per_group;
+    q.groups_per_frame = P.groups_per_frame;
+    q.vec4 = (c.dst_w % 4) == 0;
+    for (int i = 0; i < 3; ++i) {
+        q.a[i] = (float)(1.0 / (255.0 * c.std[i]));
+        q.b[i] = (float)(-c.mean[i] / c.std[i]);
+        q.padv[i] = (float)((c.pad_value / 255.0 - c.mean[i]) / c.std[i]);
+    }
+    ws::TopkParams& t = L->tk;
+    t.scores = L->scores;
+    t.n = c.num_scores;
+    t.k = c.k;
+    t.chunk = P.topk_chunk;
+    t.groups = P.topk_groups;
+    t.partials = L->partials;
+    t.counter = L->counter;
+    t.result = L->res_dev;
+    L->nodes = 1 + (c.num_scores > 0 ? 1 : 0);
+
+    // ---- stream, events, warm-up, capture ---------------------------------
+    WS_HIP(hipStreamCreateWithFlags(&L->stream, hipStreamNonBlocking), WS_E_HIP);
+    WS_HIP(hipEventCreate(&L->ev_start), WS_E_HIP);
+    WS_HIP(hipEventCreate(&L->ev_done), WS_E_HIP);
+
+    // Warm-up outside capture: loads code objects and touches every buffer.
+    WS_HIP(launch_all(L), WS_E_HIP);
+    WS_HIP(hipStreamSynchronize(L->stream), WS_E_HIP);
+
+    if (c.use_graph) {
+        WS_HIP(hipStreamBeginCapture(L->stream, hipStreamCaptureModeThreadLocal), WS_E_CAPTURE);
+        const hipError_t le = launch_all(L);
+        const hipError_t ce = hipStreamEndCapture(L->stream, &L->graph);
+        if (le != hipSuccess) return fail(L, le, WS_E_CAPTURE);
+        if (ce != hipSuccess) return fail(L, ce, WS_E_CAPTURE);
+        WS_HIP(hipGraphInstantiate(&L->exec, L->graph, nullptr, nullptr, 0), WS_E_CAPTURE);
+        WS_HIP(hipGraphUpload(L->exec, L->stream), WS_E_CAPTURE);
+        WS_HIP(hipGraphLaunch(L->exec, L->stream), WS_E_HIP);
+        WS_HIP(hipStreamSynchronize(L->stream), WS_E_HIP);
+    }
+    return WS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ws_create_lane(const ws_lane_config* cfg, ws_lane** out, ws_lane_view* view) {
+    if (!out) return WS_E_INVALID_ARG;
+    *out = nullptr;
+    const int v = ws::validate_config(cfg);
+    if (v != WS_OK) return v;
+    ws_lane* L = new (std::nothrow) ws_lane();
+    if (!L) return WS_E_OOM;
+    L->cfg = *cfg;
+    const int rc = build(L);
+    if (rc != WS_OK) {
+        release(L);
+        return rc;
+    }
+    if (view) {
+        view->input_host = L->in_host;
+        view->input_dev = L->in_dev;
+        view->tensor_dev = L->tensor;
+        view->scores_dev = L->scores;
+        view->result_host = L->res_host;
+        view->input_bytes = L->plan.input_bytes;
+        view->tensor_bytes = L->plan.tensor_bytes;
+    }
+    *out = L;
+    return WS_OK;
+}
+
+int ws_submit(ws_lane* L) {
+    if (!L) return WS_E_INVALID_ARG;
+    if (ws::begin_submit(L->state) != WS_OK) return WS_E_STATE;
+    hipError_t e = hipEventRecord(L->ev_start, L->stream);
+    if (e != hipSuccess) return fail(L, e, WS_E_HIP);
+    e = L->cfg.use_graph ? hipGraphLaunch(L->exec, L->stream) : launch_all(L);
+    if (e == hipSuccess) e = hipEventRecord(L->ev_done, L->stream);
+    if (e != hipSuccess) {
+        // Whatever was enqueued finishes before the lane is usable again.
+        hipStreamSynchronize(L->stream);
+        return fail(L, e, WS_E_HIP);
+    }
+    L->state = ws::LaneState::InFlight;
+    return WS_OK;
+}
+
+int ws_wait(ws_lane* L, float* gpu_ms) {
+    if (!L) return WS_E_INVALID_ARG;
+    if (ws::begin_wait(L->state) != WS_OK) return WS_E_STATE;
+    hipError_t e;
+    if (L->cfg.wait_mode == WS_WAIT_SPIN) {
+        while ((e = hipEventQuery(L->ev_done)) == hipErrorNotReady) {
+        }
+    } else {
+        e = hipEventSynchronize(L->ev_done);
+    }
+    L->state = ws::LaneState::Ready;
+    if (e != hipSuccess) return fail(L, e, WS_E_HIP);
+    if (gpu_ms) {
+        e = hipEventElapsedTime(gpu_ms, L->ev_start, L->ev_done);
+        if (e != hipSuccess) return fail(L, e, WS_E_HIP);
+    }
+    return WS_OK;
+}
+
+int ws_destroy(ws_lane* L) {
+    if (!L) return WS_OK;
+    if (L->state == ws::LaneState::InFlight && L->ev_done) hipEventSynchronize(L->ev_done);
+    release(L);
+    return WS_OK;
+}
+
+const char* ws_status_str(int status) { return ws::status_str(status); }
+
+int ws_lane_hip_error(const ws_lane* L) { return L ? L->last_err : 0; }
+
+int ws_lane_describe(const ws_lane* L, ws_lane_plan* plan) {
+    if (!L || !plan) return WS_E_INVALID_ARG;
+    plan->pre_groups = L->plan.pre_groups;
+    plan->pre_block = L->plan.pre_block;
+    plan->rows_per_group = L->plan.rows_per_group;
+    plan->pre_lds_bytes = L->plan.lds_bytes;
+    plan->topk_groups = L->plan.topk_groups;
+    plan->topk_block = ws::kTopkThreads;
+    plan->topk_chunk = L->plan.topk_chunk;
+    plan->graph_nodes = L->nodes;
+    return WS_OK;
+}
+
+int ws_bench_replays(ws_lane* L, int32_t replays, float* gpu_ms, double* wall_s) {
+    if (!L || replays < 0) return WS_E_INVALID_ARG;
+    int rc = WS_OK;
+    const auto t0 = std::chrono::steady_clock::now();
+    for (int32_t i = 0; i < replays && rc == WS_OK; ++i) {
+        rc = ws_submit(L);
+        if (rc == WS_OK) rc = ws_wait(L, gpu_ms ? &gpu_ms[i] : nullptr);
+    }
+    const auto t1 = std::chrono::steady_clock::now();
+    if (wall_s) *wall_s = std::chrono::duration<double>(t1 - t0).count();
+    return rc;
+}
+
+int ws_bench_lanes(ws_lane** lanes, int32_t nlanes, int32_t replays, float* gpu_ms,
+                   double* wall_s) {
+    if (!lanes || nlanes < 1 || replays < 0) return WS_E_INVALID_ARG;
+    for (int32_t i = 0; i < nlanes; ++i)
+        if (!lanes[i]) return WS_E_INVALID_ARG;
+    std::atomic<int> ready{0};
+    std::atomic<bool> go{false};
+    std::vector<int> rcs((size_t)nlanes, WS_OK);
+    std::vector<std::thread> threads;
+    threads.reserve((size_t)nlanes);
+    for (int32_t i = 0; i < nlanes; ++i) {
+        threads.emplace_back([&, i]() {
+            hipSetDevice(lanes[i]->device);
+            ready.fetch_add(1);
+            while (!go.load(std::memory_order_acquire)) {
+            }
+            rcs[(size_t)i] = ws_bench_replays(lanes[i], replays,
+                                              gpu_ms ? gpu_ms + (size_t)i * replays : nullptr,
+                                              nullptr);
+        });
+    }
+    while (ready.load() < nlanes) {
+    }
+    const auto t0 = std::chrono::steady_clock::now();
+    go.store(true, std::memory_order_release);
+    for (auto& th : threads) th.join();
+    const auto t1 = std::chrono::steady_clock::now();
+    if (wall_s) *wall_s = std::chrono::duration<double>(t1 - t0).count();
+    for (int rc : rcs)
+        if (rc != WS_OK) return rc;
+    return WS_OK;
+}
+
+int ws_bench_stage(ws_lane* L, int32_t stage, int32_t launches, double* ms_per_launch) {
+    if (!L || !ms_per_launch || launches < 1) return WS_E_INVALID_ARG;
+    if (stage != WS_STAGE_PREPROCESS && stage != WS_STAGE_TOPK) return WS_E_INVALID_ARG;
+    if (stage == WS_STAGE_TOPK && L->cfg.num_scores == 0) return WS_E_INVALID_ARG;
+    if (ws::begin_submit(L->state) != WS_OK) return WS_E_STATE;
+    hipError_t e = hipEventRecord(L->ev_start, L->stream);
+    for (int32_t i = 0; i < launches && e == hipSuccess; ++i) {
+        e = stage == WS_STAGE_PREPROCESS
+                ? ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
+                                        L->plan.lds_bytes, L->stream)
+                : ws::launch_topk(L->tk, L->stream);
+    }
+    if (e == hipSuccess) e = hipEventRecord(L->ev_done, L->stream);
+    const hipError_t se = hipStreamSynchronize(L->stream);
+    if (e == hipSuccess) e = se;
+    if (e != hipSuccess) return fail(L, e, WS_E_HIP);
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, L->ev_start, L->ev_done);
+    if (e != hipSuccess) return fail(L, e, WS_E_HIP);
+    *ms_per_launch = (double)ms / (double)launches;
+    return WS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,276 @@
+"""Python binding of the lane C ABI (include/ws.h, include/ws_bench.h).
+
+Argument marshalling only: every step of the pipeline runs in the HIP
+library.  If the library is missing or cannot be loaded this module raises;
+there is no fallback implementation.
+
+Device buffers may be borrowed from any object exposing ``data_ptr()`` (a
+torch tensor) or given as integer addresses.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import (POINTER, Structure, byref, c_char_p, c_double, c_float, c_int, c_int32,
+                    c_size_t, c_uint8, c_void_p)
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libws.so")
+INCLUDE_DIR = os.path.join(os.path.dirname(_PKG), "include")
+
+WS_OK = 0
+WS_E_INVALID_ARG = -1
+WS_E_STATE = -2
+WS_E_NO_MAP_HOST = -3
+WS_E_OOM = -4
+WS_E_CAPTURE = -5
+WS_E_HIP = -6
+WS_E_NO_DEVICE = -7
+
+RESIZE_BILINEAR = 0
+RESIZE_LETTERBOX = 1
+INPUT_MAPPED_HOST = 0
+INPUT_DEVICE = 1
+WAIT_SPIN = 0
+WAIT_BLOCK = 1
+MAX_K = 32
+STAGE_PREPROCESS = 0
+STAGE_TOPK = 1
+
+
+class TopkEntry(Structure):
+    _fields_ = [("score", c_float), ("index", c_int32)]
+
+
+class LaneConfig(Structure):
+    _fields_ = [
+        ("device", c_int32), ("batch", c_int32),
+        ("src_w", c_int32), ("src_h", c_int32),
+        ("dst_w", c_int32), ("dst_h", c_int32),
+        ("resize_mode", c_int32), ("input_mode", c_int32),
+        ("pad_value", c_double), ("mean", c_double * 3), ("std", c_double * 3),
+        ("num_scores", c_int32), ("k", c_int32),
+        ("use_graph", c_int32), ("wait_mode", c_int32),
+        ("input_dev", c_void_p), ("scores_dev", c_void_p), ("tensor_dev", c_void_p),
+        ("rows_per_group", c_int32), ("topk_chunk", c_int32),
+    ]
+
+
+class LaneView(Structure):
+    _fields_ = [
+        ("input_host", POINTER(c_uint8)), ("input_dev", c_void_p),
+        ("tensor_dev", c_void_p), ("scores_dev", c_void_p),
+        ("result_host", POINTER(TopkEntry)),
+        ("input_bytes", c_size_t), ("tensor_bytes", c_size_t),
+    ]
+
+
+class LanePlan(Structure):
+    _fields_ = [
+        ("pre_groups", c_int32), ("pre_block", c_int32), ("rows_per_group", c_int32),
+        ("pre_lds_bytes", c_int32), ("topk_groups", c_int32), ("topk_block", c_int32),
+        ("topk_chunk", c_int32), ("graph_nodes", c_int32),
+    ]
+
+
+class WsError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        self.hip_error = hip_error
+        super().__init__(f"{what}: {status_str(status)} ({status}), hip error {hip_error}")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libws.so (built by post_processing_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m post_processing_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.ws_create_lane.argtypes = [POINTER(LaneConfig), POINTER(c_void_p), POINTER(LaneView)]
+    lib.ws_create_lane.restype = c_int
+    lib.ws_submit.argtypes = [c_void_p]
+    lib.ws_submit.restype = c_int
+    lib.ws_wait.argtypes = [c_void_p, POINTER(c_float)]
+    lib.ws_wait.restype = c_int
+    lib.ws_destroy.argtypes = [c_void_p]
+    lib.ws_destroy.restype = c_int
+    lib.ws_status_str.argtypes = [c_int]
+    lib.ws_status_str.restype = c_char_p
+    lib.ws_lane_hip_error.argtypes = [c_void_p]
+    lib.ws_lane_hip_error.restype = c_int
+    lib.ws_lane_describe.argtypes = [c_void_p, POINTER(LanePlan)]
+    lib.ws_lane_describe.restype = c_int
+    lib.ws_bench_replays.argtypes = [c_void_p, c_int32, POINTER(c_float), POINTER(c_double)]
+    lib.ws_bench_replays.restype = c_int
+    lib.ws_bench_lanes.argtypes = [POINTER(c_void_p), c_int32, c_int32, POINTER(c_float),
+                                   POINTER(c_double)]
+    lib.ws_bench_lanes.restype = c_int
+    lib.ws_bench_stage.argtypes = [c_void_p, c_int32, c_int32, POINTER(c_double)]
+    lib.ws_bench_stage.restype = c_int
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().ws_status_str(status).decode()
+
+
+def declared_functions() -> list[str]:
+    """Names of every function declared in include/*.h."""
+    names = []
+    for fn in sorted(os.listdir(INCLUDE_DIR)):
+        if fn.endswith(".h"):
+            with open(os.path.join(INCLUDE_DIR, fn)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w \t\*]*?\b(ws_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def _addr(x) -> int | None:
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x)
+
+
+def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114.0,
+                mean=(0.0, 0.0, 0.0), std=(1.0, 1.0, 1.0), num_scores=0, k=0,
+                host_input=False, use_graph=True, wait_mode=WAIT_SPIN, device=0,
+                input_dev=None, scores_dev=None, tensor_dev=None, rows_per_group=0,
+                topk_chunk=0) -> LaneConfig:
+    c = LaneConfig()
+    c.device = device
+    c.batch = batch
+    c.src_w, c.src_h, c.dst_w, c.dst_h = src_w, src_h, dst_w, dst_h
+    c.resize_mode = RESIZE_LETTERBOX if letterbox else RESIZE_BILINEAR
+    c.input_mode = INPUT_MAPPED_HOST if host_input else INPUT_DEVICE
+    c.pad_value = float(pad)
+    c.mean[:] = [float(v) for v in mean]
+    c.std[:] = [float(v) for v in std]
+    c.num_scores = num_scores
+    c.k = k
+    c.use_graph = 1 if use_graph else 0
+    c.wait_mode = wait_mode
+    c.input_dev = _addr(input_dev)
+    c.scores_dev = _addr(scores_dev)
+    c.tensor_dev = _addr(tensor_dev)
+    c.rows_per_group = rows_per_group
+    c.topk_chunk = topk_chunk
+    return c
+
+
+class Lane:
+    """One pipeline lane (ws_create_lane ... ws_destroy)."""
+
+    def __init__(self, cfg: LaneConfig):
+        self._lib = load()
+        self.cfg = cfg
+        self.view = LaneView()
+        h = c_void_p()
+        rc = self._lib.ws_create_lane(byref(cfg), byref(h), byref(self.view))
+        if rc != WS_OK:
+            raise WsError(rc, "ws_create_lane")
+        self.handle = h
+
+    # -- per-frame calls --------------------------------------------------
+    def submit(self) -> int:
+        return self._lib.ws_submit(self.handle)
+
+    def wait(self) -> tuple[int, float]:
+        ms = c_float(0.0)
+        rc = self._lib.ws_wait(self.handle, byref(ms))
+        return rc, ms.value
+
+    def run(self) -> float:
+        """submit + wait; returns the GPU event time in ms (raises on error)."""
+        rc = self.submit()
+        if rc != WS_OK:
+            raise WsError(rc, "ws_submit", self.hip_error())
+        rc, ms = self.wait()
+        if rc != WS_OK:
+            raise WsError(rc, "ws_wait", self.hip_error())
+        return ms
+
+    # -- buffers ----------------------------------------------------------
+    def input_host_array(self) -> np.ndarray:
+        """The mapped input slot as a writable uint8 [B][H][W][3] view."""
+        if not self.view.input_host:
+            raise RuntimeError("lane has no mapped input slot")
+        c = self.cfg
+        flat = np.ctypeslib.as_array(self.view.input_host, shape=(self.view.input_bytes,))
+        return flat.reshape(c.batch, c.src_h, c.src_w, 3)
+
+    def result(self) -> tuple[np.ndarray, np.ndarray]:
+        """Copy of the result slot: (float32 scores[k], int32 indices[k])."""
+        k = self.cfg.k
+        if k == 0 or not self.view.result_host:
+            raise RuntimeError("lane has no Top-K stage")
+        raw = np.ctypeslib.as_array(ctypes.cast(self.view.result_host, POINTER(ctypes.c_uint32)),
+                                    shape=(2 * k,)).copy()
+        return raw[0::2].view(np.float32), raw[1::2].view(np.int32)
+
+    def plan(self) -> dict:
+        p = LanePlan()
+        rc = self._lib.ws_lane_describe(self.handle, byref(p))
+        if rc != WS_OK:
+            raise WsError(rc, "ws_lane_describe")
+        return {name: getattr(p, name) for name, _ in LanePlan._fields_}
+
+    def hip_error(self) -> int:
+        return self._lib.ws_lane_hip_error(self.handle)
+
+    def bench(self, replays: int) -> tuple[np.ndarray, float]:
+        """Native submit/wait loop: (gpu_ms per replay, wall seconds)."""
+        ms = (c_float * replays)()
+        wall = c_double(0.0)
+        rc = self._lib.ws_bench_replays(self.handle, replays, ms, byref(wall))
+        if rc != WS_OK:
+            raise WsError(rc, "ws_bench_replays", self.hip_error())
+        return np.ctypeslib.as_array(ms).copy(), wall.value
+
+    def time_stage(self, stage: int, launches: int) -> float:
+        """Mean ms per direct launch of one stage's kernel (native loop)."""
+        ms = c_double(0.0)
+        rc = self._lib.ws_bench_stage(self.handle, stage, launches, byref(ms))
+        if rc != WS_OK:
+            raise WsError(rc, "ws_bench_stage", self.hip_error())
+        return ms.value
+
+    def destroy(self) -> None:
+        if self.handle:
+            self._lib.ws_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.destroy()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def bench_lanes(lanes: list[Lane], replays: int) -> tuple[np.ndarray, float]:
+    """Drive several lanes from one native thread each: (gpu_ms [L][R], wall s)."""
+    lib = load()
+    n = len(lanes)
+    handles = (c_void_p * n)(*[ln.handle for ln in lanes])
+    ms = (c_float * (n * replays))()
+    wall = c_double(0.0)
+    rc = lib.ws_bench_lanes(handles, n, replays, ms, byref(wall))
+    if rc != WS_OK:
+        raise WsError(rc, "ws_bench_lanes")
+    return np.ctypeslib.as_array(ms).copy().reshape(n, replays), wall.value

@@ -1,0 +1,147 @@
+// Host-only driver for the lane planning code (ws_plan.h): compiled with g++
+// and no HIP by tests/test_host_logic.py.
+//   ws_plan_test taps S R           -> "i0 i1 w" per destination index
+//   ws_plan_test letterbox W H Dw Dh -> "left top w h"
+//   ws_plan_test plan <cfg fields>   -> launch geometry
+//   ws_plan_test selftest            -> config validation + state machine checks
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "ws_plan.h"
+
+static int failures = 0;
+#define CHECK(cond)                                                    \
+    do {                                                               \
+        if (!(cond)) {                                                 \
+            std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #cond); \
+            ++failures;                                                \
+        }                                                              \
+    } while (0)
+
+static ws_lane_config good() {
+    ws_lane_config c;
+    std::memset(&c, 0, sizeof c);
+    c.batch = 1;
+    c.src_w = 1920;
+    c.src_h = 1080;
+    c.dst_w = 224;
+    c.dst_h = 224;
+    c.resize_mode = WS_RESIZE_BILINEAR;
+    c.input_mode = WS_INPUT_DEVICE;
+    c.pad_value = 114;
+    for (int i = 0; i < 3; ++i) {
+        c.mean[i] = 0.5;
+        c.std[i] = 0.25;
+    }
+    c.num_scores = 1000;
+    c.k = 5;
+    c.use_graph = 1;
+    return c;
+}
+
+static int selftest() {
+    ws_lane_config c = good();
+    CHECK(ws::validate_config(&c) == WS_OK);
+    CHECK(ws::validate_config(nullptr) == WS_E_INVALID_ARG);
+#define BAD(field, value)                                     \
+    do {                                                      \
+        ws_lane_config b = good();                            \
+        b.field = value;                                      \
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);   \
+    } while (0)
+    BAD(batch, 0);
+    BAD(batch, WS_MAX_BATCH + 1);
+    BAD(src_w, 0);
+    BAD(dst_h, -3);
+    BAD(src_h, WS_MAX_SIDE + 1);
+    BAD(resize_mode, 2);
+    BAD(input_mode, 7);
+    BAD(pad_value, -1.0);
+    BAD(pad_value, 256.0);
+    BAD(k, 0);
+    BAD(k, WS_MAX_K + 1);
+    BAD(num_scores, -1);
+    BAD(use_graph, 2);
+    BAD(wait_mode, 9);
+    BAD(rows_per_group, 65);
+    BAD(topk_chunk, 1000);
+    {
+        ws_lane_config b = good();
+        b.std[1] = 0.0;
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);
+        b = good();
+        b.mean[2] = 1.0 / 0.0;
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);
+        b = good();
+        b.num_scores = 3;
+        b.k = 4;  // K > N
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);
+        b.k = 3;
+        CHECK(ws::validate_config(&b) == WS_OK);
+        b = good();
+        b.num_scores = 0;
+        b.k = 0;  // no Top-K stage
+        CHECK(ws::validate_config(&b) == WS_OK);
+        b.k = 1;
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);
+        b = good();
+        b.input_dev = reinterpret_cast<const uint8_t*>(uintptr_t(0x1008));  // misaligned
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);
+        b.input_dev = reinterpret_cast<const uint8_t*>(uintptr_t(0x1000));
+        CHECK(ws::validate_config(&b) == WS_OK);
+        b.input_mode = WS_INPUT_MAPPED_HOST;  // a device input in mapped mode
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);
+    }
+    // State machine: submit only when READY, wait only when IN_FLIGHT.
+    CHECK(ws::begin_submit(ws::LaneState::Ready) == WS_OK);
+    CHECK(ws::begin_submit(ws::LaneState::InFlight) == WS_E_STATE);
+    CHECK(ws::begin_wait(ws::LaneState::InFlight) == WS_OK);
+    CHECK(ws::begin_wait(ws::LaneState::Ready) == WS_E_STATE);
+    CHECK(std::strcmp(ws::status_str(WS_E_STATE), "WS_E_STATE") == 0);
+    CHECK(std::strcmp(ws::status_str(12345), "WS_E_UNKNOWN") == 0);
+    // Plans: every lane shape the workloads use is feasible.
+    ws::Plan p;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(p.pre_groups == 224 && p.quads_per_row == 56);
+    CHECK(p.span_lo == 3 * 3);  // first tap of 1920 -> 224: (1920 - 224) / 448 -> column 3
+    c.batch = 64;
+    c.src_w = 1280;
+    c.src_h = 720;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(p.rows_per_group * p.quads_per_row <= p.pre_block);
+    CHECK(p.lds_bytes <= ws::kMaxLdsBytes);
+    c = good();
+    c.src_w = WS_MAX_SIDE;
+    c.dst_w = WS_MAX_SIDE;
+    CHECK(ws::make_plan(c, &p) == WS_OK);  // widest rows still stage
+    CHECK(p.lds_bytes <= ws::kMaxLdsBytes);
+    c = good();
+    c.num_scores = 672000;
+    c.k = 32;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(p.topk_groups * (int64_t)p.topk_chunk >= 672000);
+    CHECK(p.topk_chunk % 1024 == 0);
+    std::printf("%d failures\n", failures);
+    return failures == 0 ? 0 : 1;
+}
+
+int main(int argc, char** argv) {
+    if (argc >= 2 && !std::strcmp(argv[1], "selftest")) return selftest();
+    if (argc == 4 && !std::strcmp(argv[1], "taps")) {
+        const long S = std::atol(argv[2]), R = std::atol(argv[3]);
+        for (long d = 0; d < R; ++d) {
+            const ws::Tap t = ws::axis_tap(S, R, d);
+            std::printf("%d %d %.9g\n", t.i0, t.i1, (double)t.w);
+        }
+        return 0;
+    }
+    if (argc == 6 && !std::strcmp(argv[1], "letterbox")) {
+        const ws::Region g = ws::letterbox_region(std::atol(argv[2]), std::atol(argv[3]),
+                                                  std::atol(argv[4]), std::atol(argv[5]));
+        std::printf("%d %d %d %d\n", g.left, g.top, g.w, g.h);
+        return 0;
+    }
+    std::fprintf(stderr, "usage: ws_plan_test selftest | taps S R | letterbox W H Dw Dh\n");
+    return 2;
+}

@@ -1,0 +1,269 @@
+"""GPU parity of the lane pipeline against the CPU oracle, through the C ABI.
+
+Bar: the FP32 tensor within 1e-5 absolute of the float64 oracle everywhere;
+Top-K indices and value bits identical.  Every workload is run in the launch
+configuration the benchmark uses (captured graph, automatic geometry).
+"""
+import numpy as np
+import pytest
+
+from oracle import preprocess_batch, topk
+from post_processing_amd import workloads as wl
+from post_processing_amd import ws
+
+from gpu_util import Run, assert_tensor_close, assert_topk_exact, oracle_outputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_config_parity_device_input(gpu_lib, name):
+    w = wl.ALL_CONFIGS[name]()
+    ref, rtk = oracle_outputs(w)
+    r = Run(w, host_input=False)
+    try:
+        r.run()
+        t, tk = r.outputs()
+        err = assert_tensor_close(t, ref)
+        assert_topk_exact(tk, rtk)
+        print(f"{name}: max|err| {err:.2e}, plan {r.lane.plan()}")
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_config_parity_mapped_host_input(gpu_lib, name):
+    w = wl.ALL_CONFIGS[name]()
+    ref, rtk = oracle_outputs(w)
+    r = Run(w, host_input=True)
+    try:
+        r.run()
+        t, tk = r.outputs()
+        assert_tensor_close(t, ref)
+        assert_topk_exact(tk, rtk)
+    finally:
+        r.close()
+
+
+def test_throughput_batch_parity(gpu_lib):
+    w = wl.c5_throughput(64)
+    ref, _ = oracle_outputs(w)
+    r = Run(w, host_input=False)
+    try:
+        r.run()
+        t, _ = r.outputs()
+        assert_tensor_close(t, ref)
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("letterbox", [False, True])
+def test_random_small_shapes(gpu_lib, seed, letterbox):
+    w = wl.random_small(seed, letterbox=letterbox)
+    ref, _ = oracle_outputs(w)
+    r = Run(w, host_input=bool(seed % 2))
+    try:
+        r.run()
+        t, _ = r.outputs()
+        assert_tensor_close(t, ref)
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("name,rows", [("c4", 1), ("c4", 2), ("c4", 3), ("c4", 6), ("c1", 5),
+                                       ("c1", 32), ("c2", 9), ("c3", 4)])
+def test_rows_per_group_does_not_change_results(gpu_lib, name, rows):
+    w = wl.ALL_CONFIGS[name]()
+    ref, _ = oracle_outputs(w)
+    r = Run(w, host_input=False, rows_per_group=rows)
+    try:
+        assert r.lane.plan()["rows_per_group"] == rows
+        r.run()
+        t, _ = r.outputs()
+        assert_tensor_close(t, ref)
+    finally:
+        r.close()
+
+
+def test_rows_per_group_beyond_lds_rejected(gpu_lib):
+    # 7 staged row pairs of 3840-pixel rows need ~161 KB of LDS: more than a
+    # workgroup may hold, so the lane refuses the plan instead of launching it.
+    with pytest.raises(ws.WsError) as ei:
+        Run(wl.c4(), host_input=False, rows_per_group=7)
+    assert ei.value.status == ws.WS_E_INVALID_ARG
+
+
+def _topk_workload(n, k, seed):
+    s = wl.scores_with_specials(seed, n, tie_frac=0.2, nan_frac=0.02)
+    frame = np.zeros((1, 4, 4, 3), dtype=np.uint8)
+    return wl.Workload(f"topk_{n}_{k}", 4, 4, 4, 4, wl.RESIZE, (0, 0, 0), (1, 1, 1), 114.0, k,
+                       frame, s)
+
+
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 1000, 4097, 65537, 672000])
+@pytest.mark.parametrize("k", [1, 5, 10, 31, 32])
+def test_topk_edge_sizes(gpu_lib, n, k):
+    if k > n:
+        pytest.skip("K > N is rejected at create")
+    w = _topk_workload(n, k, seed=n * 37 + k)
+    rtk = topk(w.scores, k)
+    r = Run(w, host_input=False)
+    try:
+        r.run()
+        _, tk = r.outputs()
+        assert_topk_exact(tk, rtk)
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("chunk", [1024, 2048, 8192, 65536, 688128])
+def test_topk_chunking_does_not_change_results(gpu_lib, chunk):
+    w = wl.c3()
+    rtk = topk(w.scores, w.k)
+    r = Run(w, host_input=False, topk_chunk=chunk)
+    try:
+        r.run()
+        _, tk = r.outputs()
+        assert_topk_exact(tk, rtk)
+    finally:
+        r.close()
+
+
+def test_topk_all_equal_and_all_nan(gpu_lib):
+    for vals in (np.full(3000, 0.5, np.float32), np.full(3000, np.nan, np.float32),
+                 np.where(np.arange(3000) % 2 == 0, 0.0, -0.0).astype(np.float32)):
+        frame = np.zeros((1, 4, 4, 3), dtype=np.uint8)
+        w = wl.Workload("same", 4, 4, 4, 4, wl.RESIZE, (0, 0, 0), (1, 1, 1), 114.0, 32, frame,
+                        vals)
+        r = Run(w, host_input=False)
+        try:
+            r.run()
+            _, tk = r.outputs()
+            assert_topk_exact(tk, topk(vals, 32))
+        finally:
+            r.close()
+
+
+def test_replays_are_bitwise_stable(gpu_lib):
+    w = wl.c2()
+    r = Run(w, host_input=False)
+    try:
+        r.run()
+        t0, tk0 = r.outputs()
+        ms, wall = r.lane.bench(2000)
+        assert (ms > 0).all()
+        t1, tk1 = r.outputs()
+        np.testing.assert_array_equal(t0.view(np.uint32), t1.view(np.uint32))
+        assert_topk_exact(tk1, tk0)
+    finally:
+        r.close()
+
+
+def test_graph_and_direct_launch_agree(gpu_lib):
+    w = wl.c3()
+    a = Run(w, host_input=False, use_graph=True)
+    b = Run(w, host_input=False, use_graph=False)
+    try:
+        a.run()
+        b.run()
+        ta, ka = a.outputs()
+        tb, kb = b.outputs()
+        np.testing.assert_array_equal(ta.view(np.uint32), tb.view(np.uint32))
+        assert_topk_exact(ka, kb)
+    finally:
+        a.close()
+        b.close()
+
+
+def test_mapped_and_device_input_agree(gpu_lib):
+    w = wl.c2()
+    a = Run(w, host_input=True)
+    b = Run(w, host_input=False)
+    try:
+        a.run()
+        b.run()
+        np.testing.assert_array_equal(a.outputs()[0].view(np.uint32),
+                                      b.outputs()[0].view(np.uint32))
+    finally:
+        a.close()
+        b.close()
+
+
+def test_mapped_slot_sees_each_new_frame(gpu_lib):
+    # The producer rewrites the slot between frames; every replay must read
+    # the new bytes (no stale cached copy of the previous frame).
+    w = wl.c1()
+    r = Run(w, host_input=True)
+    try:
+        slot = r.lane.input_host_array()
+        for i in range(4):
+            frame = np.random.default_rng(500 + i).integers(0, 256, size=w.frames.shape,
+                                                            dtype=np.uint8)
+            slot[...] = frame
+            r.run()
+            ref = preprocess_batch(frame, w.dst_w, w.dst_h, w.mean, w.std)
+            assert_tensor_close(r.outputs()[0], ref)
+    finally:
+        r.close()
+
+
+def test_scores_rewritten_between_frames(gpu_lib):
+    import torch
+    w = wl.c1()
+    r = Run(w, host_input=False)
+    try:
+        for i in range(3):
+            s = wl.scores_with_specials(900 + i, w.num_scores, tie_frac=0.3)
+            r.scores.copy_(torch.from_numpy(s))
+            torch.cuda.synchronize()
+            r.run()
+            assert_topk_exact(r.outputs()[1], topk(s, w.k))
+    finally:
+        r.close()
+
+
+def test_state_machine_misuse(gpu_lib):
+    w = wl.c1()
+    r = Run(w, host_input=False)
+    lane = r.lane
+    try:
+        rc, _ = lane.wait()
+        assert rc == ws.WS_E_STATE                   # nothing in flight
+        assert lane.submit() == ws.WS_OK
+        assert lane.submit() == ws.WS_E_STATE        # busy lane: no hidden queue
+        rc, ms = lane.wait()
+        assert rc == ws.WS_OK and ms > 0
+        rc, _ = lane.wait()
+        assert rc == ws.WS_E_STATE
+        assert lane.submit() == ws.WS_OK             # destroy while in flight waits first
+    finally:
+        r.close()
+
+
+def test_invalid_configs_rejected(gpu_lib):
+    bad = [dict(k=33, num_scores=1000), dict(k=6, num_scores=5), dict(batch=0),
+           dict(batch=65), dict(std=(0.2, 0.0, 0.2)), dict(pad=300.0), dict(src_w=0)]
+    for b in bad:
+        args = dict(src_w=64, src_h=48, dst_w=32, dst_h=32, mean=(0.4, 0.4, 0.4),
+                    std=(0.2, 0.2, 0.2), num_scores=0, k=0)
+        args.update(b)
+        with pytest.raises(ws.WsError) as ei:
+            ws.Lane(ws.make_config(**args))
+        assert ei.value.status == ws.WS_E_INVALID_ARG
+
+
+def test_eight_lanes_concurrently(gpu_lib):
+    lanes = [wl.c5_lane(i) for i in range(8)]
+    runs = [Run(w) for w in lanes]
+    try:
+        ms, wall = ws.bench_lanes([r.lane for r in runs], 50)
+        assert ms.shape == (8, 50) and (ms > 0).all()
+        for w, r in zip(lanes, runs):
+            ref, rtk = oracle_outputs(w)
+            t, tk = r.outputs()
+            assert_tensor_close(t, ref)
+            assert_topk_exact(tk, rtk)
+    finally:
+        for r in runs:
+            r.close()

@@ -83,6 +83,9 @@ def lat_stats(ms: np.ndarray) -> dict:
             "p99_over_p50": pct(us, 99) / pct(us, 50)}
 
 
+KNOBS = {}
+
+
 def make_lane(w, torch, host_input=None, use_graph=True):
     from post_processing_amd import ws
     host = w.host_input if host_input is None else host_input
@@ -98,7 +101,7 @@ def make_lane(w, torch, host_input=None, use_graph=True):
                          batch=w.batch, letterbox=(w.mode == 1), pad=w.pad, mean=w.mean,
                          std=w.std, num_scores=w.num_scores, k=w.k, host_input=host,
                          use_graph=use_graph, input_dev=keep.get("frames"),
-                         scores_dev=keep.get("scores"), tensor_dev=keep["tensor"])
+                         scores_dev=keep.get("scores"), tensor_dev=keep["tensor"], **KNOBS)
     lane = ws.Lane(cfg)
     if host:
         lane.input_host_array()[...] = w.frames
@@ -221,13 +224,38 @@ def gpu_state() -> dict:
     return {}
 
 
+def copy_calibration(torch, args) -> int:
+    """A plain device-to-device copy of known size, the reference for scaling
+    the profiler's byte counters (FETCH_SIZE / WRITE_SIZE) to real bytes."""
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup if args.warmup < 10 else 3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"metric": "device copy bandwidth (calibration)", "value": 2 * n / dt / 1e9,
+                      "unit": "GB/s", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "steps": args.steps}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5l", "c5t"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c1", "c2", "c3", "c4", "c5l", "c5t", "copy"])
+    ap.add_argument("--copy-mib", type=int, default=256,
+                    help="copy workload: bytes per device-to-device copy (MiB)")
     ap.add_argument("--stage-launches", type=int, default=500)
+    ap.add_argument("--rows-per-group", type=int, default=0, help="preprocess tuning knob (0 = auto)")
+    ap.add_argument("--topk-chunk", type=int, default=0, help="Top-K tuning knob (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
     ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
@@ -247,7 +275,10 @@ def main(argv=None) -> int:
     from post_processing_amd import ws
     ws.load()
 
+    KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk)
     name = args.workload
+    if name == "copy":
+        return copy_calibration(torch, args)
     t_gen = time.perf_counter()
     if name == "c5l":
         work = [wl.c5_lane(i) for i in range(8)]

@@ -256,6 +256,8 @@ def main(argv=None) -> int:
     ap.add_argument("--stage-launches", type=int, default=500)
     ap.add_argument("--rows-per-group", type=int, default=0, help="preprocess tuning knob (0 = auto)")
     ap.add_argument("--topk-chunk", type=int, default=0, help="Top-K tuning knob (0 = auto)")
+    ap.add_argument("--pixels-per-thread", type=int, default=0,
+                    help="preprocess tuning knob: 1, 2 or 4 (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
     ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
@@ -275,7 +277,8 @@ def main(argv=None) -> int:
     from post_processing_amd import ws
     ws.load()
 
-    KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk)
+    KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
+                 pixels_per_thread=args.pixels_per_thread)
     name = args.workload
     if name == "copy":
         return copy_calibration(torch, args)

@@ -60,6 +60,7 @@ extern "C" {
 #define WS_MAX_K       32
 #define WS_MAX_BATCH   64
 #define WS_MAX_SIDE    16384
+#define WS_MAX_SCORES  (1 << 30)
 
 /* One selected entry: the score (original bits; NaN reported as -inf) and its
  * position in the score vector.  8 bytes, array of structs, rank order. */
@@ -80,7 +81,7 @@ typedef struct ws_lane_config {
     double  pad_value;     /* letterbox fill in byte units, 0..255            */
     double  mean[3];       /* per RGB channel, unit range (0.485 ...)         */
     double  std[3];        /* per RGB channel, unit range, > 0                */
-    int32_t num_scores;    /* N; 0 = no Top-K stage                           */
+    int32_t num_scores;    /* N, 0..WS_MAX_SCORES; 0 = no Top-K stage        */
     int32_t k;             /* 1..min(WS_MAX_K, N) when N > 0                  */
     int32_t use_graph;     /* 1 = replay the captured graph (the product);
                               0 = launch the same kernels directly (for the
@@ -96,6 +97,7 @@ typedef struct ws_lane_config {
     /* Tuning knobs (0 = automatic choice); they change speed, never results. */
     int32_t rows_per_group;    /* preprocess: output rows per workgroup        */
     int32_t topk_chunk;        /* Top-K: scores per workgroup (multiple of 1024) */
+    int32_t pixels_per_thread; /* preprocess: output columns per thread: 1, 2, 4 */
 } ws_lane_config;
 
 /* Stable views of a lane's buffers, valid from ws_create_lane to ws_destroy.
@@ -119,8 +121,8 @@ typedef struct ws_lane ws_lane;
 /*
  * ws_create_lane -- validate cfg, then allocate and bind everything the lane
  * will ever use: input slot (hipHostMalloc mapped, coherent) or device input,
- * tensor, scores, mapped result slot, exact sampling-tap tables, Top-K
- * scratch, one non-blocking stream and two timing events.  Runs the kernels
+ * tensor, scores, mapped result slot, Top-K scratch, one non-blocking
+ * stream and two timing events, and fixes the launch geometry.  Runs the kernels
  * once outside capture (warm-up), captures them into one graph, instantiates
  * and uploads it, and replays it once.  Source: the article's lane and
  * initialisation passages (allocate once, bind once, capture once; map-host

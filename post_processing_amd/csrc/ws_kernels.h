@@ -21,10 +21,11 @@ struct PreParams {
     float inv_den_y;        // 1 / (2 reg_h)
     int32_t span_lo;        // first staged byte of a source row
     int32_t slot_chunks;    // 16-byte chunks per staged row
-    int32_t quads_per_row;  // ceil(dst_w / 4)
+    int32_t pixels_per_thread;  // PX: 1, 2 or 4 adjacent output columns
+    int32_t threads_per_row;    // ceil(dst_w / PX)
     int32_t rows_per_group;
     int32_t groups_per_frame;
-    int32_t vec4;           // dst_w % 4 == 0: rows are 16-byte aligned
+    int32_t vec;            // dst_w % PX == 0: each thread's columns form an aligned vector
     float a[3];             // 1 / (255 std[c])
     float b[3];             // -mean[c] / std[c]
     float padv[3];          // (pad / 255 - mean[c]) / std[c]
@@ -38,6 +39,7 @@ struct TopkParams {
     int32_t k;
     int32_t chunk;           // scores per workgroup, multiple of 1024
     int32_t groups;
+    int32_t waves;           // wave64s per workgroup, 1..4
     uint64_t* partials;      // [groups][k] order keys (groups > 1)
     uint32_t* counter;       // arrival counter, zero between launches
     uint2* result;           // [k] {score bits, index}, device view of the slot
@@ -47,6 +49,6 @@ hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_
                              hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 
-constexpr int kTopkThreads = 256;
+constexpr int kTopkMaxThreads = 256;   // 4 wave64s: one per SIMD
 
 }  // namespace ws

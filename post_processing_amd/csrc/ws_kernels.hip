@@ -24,10 +24,12 @@ namespace {
 //  1. For each output row it stages the two source rows its vertical taps
 //     read (only the byte span the horizontal taps touch) into LDS with
 //     16-byte global loads, all issued before any LDS write.
-//  2. Each thread owns 4 adjacent output columns of one row: it computes the
-//     exact taps, fetches each RGB triple from LDS as one aligned dword pair
-//     funnel-shifted into place, interpolates and normalises in FP32, and
-//     writes one 16-byte vector per channel plane.
+//  2. Each thread owns PX (1, 2 or 4) adjacent output columns of one row: it
+//     computes the exact taps, fetches each RGB triple from LDS as one aligned
+//     dword pair funnel-shifted into place, interpolates and normalises in
+//     FP32, and writes one PX-wide vector per channel plane.  Small frames
+//     take PX = 1 (more waves per row, shorter per-thread chains); large
+//     batches PX = 4 (fewer, wider stores).
 // Taps are exact integers: src = ((2d + 1) S - R) / (2R), clamped at 0;
 // i0 = floor, the weight is the remainder times 1/(2R) in FP32.
 
@@ -64,6 +66,7 @@ __device__ __forceinline__ float chan(uint32_t rgb, int c) {
     return (float)((rgb >> (8 * c)) & 0xffu);
 }
 
+template <int PX>
 __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
     extern __shared__ uint4 lds_dyn[];
     __shared__ int64_t slot_addr[kMaxSlots];   // unaligned start of a staged row, -1 = none
@@ -131,13 +134,13 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
     __syncthreads();
 
     // 2. Resample, normalise, store planar.
-    const int q = p.quads_per_row;
+    const int q = p.threads_per_row;
     const int work = nrows * q;
     const int64_t plane = (int64_t)p.dst_h * p.dst_w;
     float* const frame_out = p.dst + (int64_t)f * 3 * plane;
     for (int wi = tid; wi < work; wi += nthr) {
         const int r = wi / q;
-        const int x_first = 4 * (wi - r * q);
+        const int x_first = PX * (wi - r * q);
         const int y = y_base + r;
         const int dy = y - p.top;
         const bool row_in = dy >= 0 && dy < p.reg_h;
@@ -148,9 +151,9 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
             base0 = (uint32_t)(2 * r) * slot_bytes + (uint32_t)(slot_addr[2 * r] & 15);
             base1 = (uint32_t)(2 * r + 1) * slot_bytes + (uint32_t)(slot_addr[2 * r + 1] & 15);
         }
-        float out[3][4];
+        float out[3][PX];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < PX; ++i) {
             const int dx = x_first + i - p.left;
             if (row_in && dx >= 0 && dx < p.reg_w) {
                 const AxisTap tx = exact_tap(dx, p.src_w, p.reg_w, p.inv_den_x);
@@ -175,16 +178,22 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
             }
         }
         float* const row_out = frame_out + (int64_t)y * p.dst_w + x_first;
-        if (p.vec4) {
+        if (p.vec) {   // dst_w % PX == 0: the PX columns are one aligned vector
 #pragma unroll
-            for (int c = 0; c < 3; ++c)
-                *reinterpret_cast<float4*>(row_out + c * plane) =
-                    make_float4(out[c][0], out[c][1], out[c][2], out[c][3]);
+            for (int c = 0; c < 3; ++c) {
+                if constexpr (PX == 4)
+                    *reinterpret_cast<float4*>(row_out + c * plane) =
+                        make_float4(out[c][0], out[c][1], out[c][2], out[c][3]);
+                else if constexpr (PX == 2)
+                    *reinterpret_cast<float2*>(row_out + c * plane) = make_float2(out[c][0], out[c][1]);
+                else
+                    row_out[c * plane] = out[c][0];
+            }
         } else {
 #pragma unroll
             for (int c = 0; c < 3; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < PX; ++i)
                     if (x_first + i < p.dst_w) row_out[c * plane + i] = out[c][i];
         }
     }
@@ -200,29 +209,67 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
 // unique and needs no tie logic.  Key 0 is below every real key (sentinel).
 //
 // Each wave64 keeps a sorted list of its 64 best keys, one per lane (lane 0
-// best).  Scores stream past in tiles of 64 (one per lane); a tile is skipped
-// unless some lane beats the current K-th best.  A tile with many winners is
-// bitonic-sorted across lanes and merged (elementwise max against the list,
-// then a bitonic clean-up); a few winners are inserted one at a time.
+// best).  Scores arrive in batches of 1024 (16 keys per lane).  Only keys
+// above the running K-th best can matter; when more than 64 do, the K-th
+// largest of the 64 lane maxima is also a lower bound (K distinct keys of the
+// batch reach it), which prunes the rest; it is found on the 32-bit value
+// image alone, bit by bit with ballots.  Survivors are compacted through the
+// wave's LDS scratch.  A few are inserted one by one; up to 64 - K are merged
+// by counting ranks; more go in tiles of 64, each bitonic-sorted across lanes
+// and merged into the list (elementwise max against the reversed tile, then
+// a bitonic clean-up).  All lane exchanges run on the VALU: DPP for lane
+// distances 1, 2, 4, 8 and the permlane swaps for 16 and 32.  Waves of a
+// workgroup merge pairwise through LDS; workgroups publish their K best and
+// the last one to arrive merges those lists the same way.
 
-__device__ __forceinline__ uint64_t order_key(float v, uint32_t idx) {
+// Order-preserving unsigned image of an FP32 value: NaN -> -inf and -0 -> +0
+// first; then negative values have all bits flipped, others the sign bit set.
+__device__ __forceinline__ uint32_t order_image(float v) {
     uint32_t b = __float_as_uint(v);
-    if ((b & 0x7fffffffu) > 0x7f800000u) b = 0xff800000u;   // NaN -> -inf
-    if (b == 0x80000000u) b = 0u;                             // -0 -> +0
-    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint64_t)(~idx);
+    b = (b & 0x7fffffffu) > 0x7f800000u ? 0xff800000u : b;   // NaN -> -inf
+    b = b == 0x80000000u ? 0u : b;                            // -0 -> +0
+    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int mask) {
-    const int lo = __shfl_xor((int)(uint32_t)v, mask);
-    const int hi = __shfl_xor((int)(uint32_t)(v >> 32), mask);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+// Value held by lane (lane ^ J).  Every source lane is inside the wave, so
+// the DPP forms need no "old" operand (bound_ctrl).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int lane) {
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);   // quad_perm 1,0,3,2
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);   // quad_perm 2,3,0,1
+    } else if constexpr (J == 4) {
+        const uint32_t fwd = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, true);  // row_ror:12 -> lane+4
+        const uint32_t bwd = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true);  // row_ror:4  -> lane-4
+        return (lane & 4) ? bwd : fwd;
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);  // row_ror:8
+    } else if constexpr (J == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? s[0] : s[1];
+    } else {
+        static_assert(J == 32, "lane distance must be a power of two below 64");
+        const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? s[0] : s[1];
+    }
 }
 
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane32<J>((uint32_t)v, lane);
+    const uint32_t hi = xor_lane32<J>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Value held by lane - 1 (lane 0 keeps its own): DPP wave_shr:1.
 __device__ __forceinline__ uint64_t prev_lane64(uint64_t v) {
-    const int lo = __shfl_up((int)(uint32_t)v, 1);
-    const int hi = __shfl_up((int)(uint32_t)(v >> 32), 1);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v,
+                                                              0x138, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32),
+                                                              (int)(uint32_t)(v >> 32), 0x138, 0xF,
+                                                              0xF, false);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
@@ -234,29 +281,67 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a < b ? b : a; }
 
-// Bitonic sort of one key per lane into ascending lane order.
-__device__ __forceinline__ uint64_t wave_sort_asc(uint64_t x, int lane) {
-#pragma unroll
-    for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            const uint64_t y = xor_lane64(x, j);
-            const bool up = (lane & k) == 0;
-            const bool lower = (lane & j) == 0;
-            x = (lower == up) ? umin64(x, y) : umax64(x, y);
-        }
-    }
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Orders LDS traffic between lanes of one wave (in-order per wave on CDNA).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic network stages for block size B with distances J, J/2, ..., 1.
+// Lanes in a block whose bit B is clear run ascending, the others descending;
+// DESC flips the whole network.  B = 64 with J = 32 is the final merge.  One
+// compare per stage: a lane keeps its own key when "mine is larger" agrees
+// with the side of the pair it must end on.
+template <int B, int J, bool DESC, typename T>
+__device__ __forceinline__ T bitonic_stages(T x, int lane) {
+    T y;
+    if constexpr (sizeof(T) == 8) y = xor_lane64<J>(x, lane);
+    else y = xor_lane32<J>(x, lane);
+    const bool lower = (lane & J) == 0;
+    const bool ascending_block = (lane & B) == 0;
+    const bool keep_large = (lower != ascending_block) != DESC;
+    x = ((x > y) == keep_large) ? x : y;
+    if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC>(x, lane);
     return x;
+}
+
+// Sort one key per lane across the wave.
+template <bool DESC, typename T>
+__device__ __forceinline__ T wave_sort(T x, int lane) {
+    x = bitonic_stages<2, 1, DESC>(x, lane);
+    x = bitonic_stages<4, 2, DESC>(x, lane);
+    x = bitonic_stages<8, 4, DESC>(x, lane);
+    x = bitonic_stages<16, 8, DESC>(x, lane);
+    x = bitonic_stages<32, 16, DESC>(x, lane);
+    return bitonic_stages<64, 32, DESC>(x, lane);
 }
 
 // Sort a bitonic sequence (one key per lane) into descending lane order.
 __device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
+    return bitonic_stages<64, 32, true>(x, lane);
+}
+
+constexpr int kKeysPerLane = 16;                    // one batch = 1024 keys per wave
+constexpr int kBatch = 64 * kKeysPerLane;
+constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
+
+// K-th largest of one 32-bit value per lane, with multiplicity (0 when fewer
+// than K lanes hold a non-zero value): the answer's bits are fixed from the
+// top, each by one ballot count, so there is no long cross-lane chain.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k) {
+    uint32_t prefix = 0;
 #pragma unroll
-    for (int j = 32; j > 0; j >>= 1) {
-        const uint64_t y = xor_lane64(x, j);
-        x = (lane & j) == 0 ? umax64(x, y) : umin64(x, y);
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = prefix | (1u << b);
+        if (__popcll(__ballot(m >= cand)) >= k) prefix = cand;
     }
-    return x;
+    return prefix;
 }
 
 struct WaveTopK {
@@ -272,44 +357,94 @@ struct WaveTopK {
         lane = lane_;
     }
 
-    // Merge a full sorted-descending list held one key per lane.
-    __device__ __forceinline__ void merge_sorted_desc_list(uint64_t other_asc) {
-        best = wave_clean_desc(umax64(best, other_asc), lane);
+    // Merge a list sorted ascending across lanes (e.g. a reversed list).
+    __device__ __forceinline__ void merge_ascending(uint64_t asc) {
+        best = wave_clean_desc(umax64(best, asc), lane);
         thr = readlane64(best, k - 1);
     }
 
-    // Offer one tile: every lane contributes `key` (0 = nothing).
-    __device__ __forceinline__ void offer(uint64_t key) {
-        uint64_t m = __ballot(key > thr);
-        if (m == 0) return;
-        if (__popcll(m) > 4) {
-            const uint64_t t = wave_sort_asc(key > thr ? key : 0, lane);
-            best = wave_clean_desc(umax64(best, t), lane);
-            thr = readlane64(best, k - 1);
-            return;
-        }
-        while (m) {
-            const int src = __ffsll((long long)m) - 1;
-            m &= m - 1;
-            const uint64_t c = readlane64(key, src);
-            if (c > thr) {
-                const int pos = __popcll(__ballot(best > c));
-                const uint64_t shifted = prev_lane64(best);
-                best = lane < pos ? best : (lane == pos ? c : shifted);
-                thr = readlane64(best, k - 1);
+    __device__ __forceinline__ void insert(uint64_t c) {
+        if (c <= thr) return;
+        const int pos = __popcll(__ballot(best > c));
+        const uint64_t shifted = prev_lane64(best);
+        best = lane < pos ? best : (lane == pos ? c : shifted);
+        thr = readlane64(best, k - 1);
+    }
+
+    // Merge survivors scratch[0..c) when k + c <= 64: every lane holds one of
+    // the k list keys or one survivor, counts how many of them beat its key
+    // (independent compares, no sorting network) and writes it at that rank.
+    __device__ __forceinline__ void rank_merge(uint64_t* scratch, int c) {
+        const int m = k + c;
+        const uint64_t v = lane < k ? best : (lane < m ? scratch[lane - k] : 0);
+        int rank = 0;
+#pragma unroll 4
+        for (int j = 0; j < m; ++j) rank += readlane64(v, j) > v ? 1 : 0;
+        wave_lds_sync();   // every survivor is read before the area is reused
+        if (lane < k) scratch[lane] = 0;
+        wave_lds_sync();
+        if (rank < k && v != 0) scratch[rank] = v;
+        wave_lds_sync();
+        best = lane < k ? scratch[lane] : 0;
+        thr = readlane64(best, k - 1);
+    }
+
+    // Offer one batch: kKeysPerLane keys per lane (0 = nothing).  `scratch`
+    // is this wave's private LDS area of kBatch keys.
+    __device__ __forceinline__ void offer(const uint64_t (&key)[kKeysPerLane], uint64_t* scratch) {
+        uint64_t cut = thr;
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerLane; ++j) cnt += __popcll(__ballot(key[j] > cut));
+        if (cnt == 0) return;
+        if (cnt > 64) {
+            // K lanes hold a key whose value image is at least the K-th largest
+            // lane maximum t, so every key of the K best has value image >= t.
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < kKeysPerLane; ++j) m = max(m, (uint32_t)(key[j] >> 32));
+            const uint32_t t = wave_kth_largest(m, k);
+            const uint64_t tcut = ((uint64_t)t << 32) - 1;   // key > tcut <=> value image >= t
+            if (t != 0 && tcut > cut) {
+                cut = tcut;
+                cnt = 0;
+#pragma unroll
+                for (int j = 0; j < kKeysPerLane; ++j) cnt += __popcll(__ballot(key[j] > cut));
             }
         }
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerLane; ++j) {
+            const bool take = key[j] > cut;
+            const uint64_t b = __ballot(take);
+            if (take) scratch[base + lanes_below(b)] = key[j];
+            base += __popcll(b);
+        }
+        wave_lds_sync();
+        if (cnt <= kInsertMax) {
+            const uint64_t cand = lane < cnt ? scratch[lane] : 0;
+            for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
+        } else if (k + cnt <= 64) {
+            rank_merge(scratch, cnt);
+        } else {
+            for (int t = 0; t < cnt; t += 64) {
+                const uint64_t tile = t + lane < cnt ? scratch[t + lane] : 0;
+                best = wave_clean_desc(umax64(best, wave_sort<false>(tile, lane)), lane);
+            }
+            thr = readlane64(best, k - 1);
+        }
+        wave_lds_sync();
     }
 };
 
-// Merge the four waves' lists of one workgroup into wave 0.
-__device__ __forceinline__ void block_merge(WaveTopK& st, uint64_t (*s_best)[64], int wave,
-                                            int lane) {
-    s_best[wave][lane] = st.best;
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int w = 1; w < kTopkThreads / 64; ++w) st.merge_sorted_desc_list(s_best[w][63 - lane]);
+// Pairwise tree merge of the waves' lists into wave 0.
+__device__ __forceinline__ void block_merge(WaveTopK& st, uint64_t (*s_list)[64], int wave,
+                                            int waves) {
+    for (int stride = 1; stride < waves; stride <<= 1) {
+        if ((wave & (2 * stride - 1)) == stride) s_list[wave][st.lane] = st.best;
+        __syncthreads();
+        if ((wave & (2 * stride - 1)) == 0 && wave + stride < waves)
+            st.merge_ascending(s_list[wave + stride][63 - st.lane]);
     }
 }
 
@@ -322,55 +457,75 @@ __device__ __forceinline__ void write_result(const TopkParams& p, uint64_t key, 
     p.result[lane] = make_uint2(bits, idx);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-    __shared__ uint64_t s_best[kTopkThreads / 64][64];
+// One wave's batch: 16 scores per lane as four float4 loads, lane-interleaved
+// so each load instruction covers 1 KiB of consecutive scores.  Score
+// positions fit in 31 bits (the vector length is an int32).
+__device__ __forceinline__ void load_batch(const float* __restrict__ scores, int32_t wb, int32_t g1,
+                                           int lane, float4 (&v)[kKeysPerLane / 4]) {
+#pragma unroll
+    for (int u = 0; u < kKeysPerLane / 4; ++u) {
+        const int32_t e = wb + 4 * (lane + 64 * u);
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e + 4 <= g1) {
+            v[u] = *reinterpret_cast<const float4*>(scores + e);
+        } else {
+            if (e + 0 < g1) v[u].x = scores[e + 0];
+            if (e + 1 < g1) v[u].y = scores[e + 1];
+            if (e + 2 < g1) v[u].z = scores[e + 2];
+        }
+    }
+}
+
+// Order keys of a loaded batch; positions at or past g1 become the sentinel.
+__device__ __forceinline__ void batch_keys(const float4 (&v)[kKeysPerLane / 4], int32_t wb,
+                                           int32_t g1, int lane, uint64_t (&key)[kKeysPerLane]) {
+#pragma unroll
+    for (int u = 0; u < kKeysPerLane / 4; ++u) {
+        const int32_t e = wb + 4 * (lane + 64 * u);
+        const int32_t rem = g1 - e;
+        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint64_t k = ((uint64_t)order_image(f[j]) << 32) | (uint32_t)~(uint32_t)(e + j);
+            key[4 * u + j] = k & (0ull - (uint64_t)(j < rem));
+        }
+    }
+}
+
+__global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
+    __shared__ uint64_t s_scratch[kTopkMaxThreads / 64][kBatch];
+    __shared__ uint64_t s_list[kTopkMaxThreads / 64][64];
     __shared__ int s_last;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int waves = p.waves;
 
     WaveTopK st;
     st.init(p.k, lane);
 
-    const int64_t g0 = (int64_t)blockIdx.x * p.chunk;
-    const int64_t g1 = min(p.n, g0 + (int64_t)p.chunk);
-    const int iters = (int)((g1 - g0 + 1023) / 1024);
-    for (int it0 = 0; it0 < iters; it0 += 4) {
-        float4 v[4];
-        int64_t base[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            base[u] = g0 + (int64_t)(it0 + u) * 1024 + 4 * tid;
-            v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (it0 + u < iters) {
-                if (base[u] + 4 <= g1) {
-                    v[u] = *reinterpret_cast<const float4*>(p.scores + base[u]);
-                } else {
-                    if (base[u] + 0 < g1) v[u].x = p.scores[base[u] + 0];
-                    if (base[u] + 1 < g1) v[u].y = p.scores[base[u] + 1];
-                    if (base[u] + 2 < g1) v[u].z = p.scores[base[u] + 2];
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (it0 + u >= iters) break;
-            const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t i = base[u] + j;
-                st.offer(i < g1 ? order_key(e[j], (uint32_t)i) : 0);
-            }
-        }
+    // 1. This workgroup's chunk, one 1024-score batch per wave per round; the
+    //    next round's scores are loaded while the current batch is offered.
+    const int32_t g0 = (int32_t)blockIdx.x * p.chunk;
+    const int32_t g1 = (int32_t)min(p.n, (int64_t)g0 + p.chunk);
+    const int32_t round = waves * kBatch;
+    float4 v[kKeysPerLane / 4];
+    load_batch(p.scores, g0 + wave * kBatch, g1, lane, v);
+    for (int32_t rb = g0; rb < g1; rb += round) {
+        const int32_t wb = rb + wave * kBatch;
+        uint64_t key[kKeysPerLane];
+        batch_keys(v, wb, g1, lane, key);
+        if (rb + round < g1) load_batch(p.scores, wb + round, g1, lane, v);
+        st.offer(key, s_scratch[wave]);
     }
-    block_merge(st, s_best, wave, lane);
+    block_merge(st, s_list, wave, waves);
 
     if (p.groups == 1) {
         if (wave == 0 && lane < p.k) write_result(p, st.best, lane);
         return;
     }
 
-    // Publish this workgroup's K best; the last workgroup to arrive merges all.
+    // 2. Publish this workgroup's K best; the last workgroup to arrive merges all.
     if (wave == 0 && lane < p.k) p.partials[(int64_t)blockIdx.x * p.k + lane] = st.best;
     __threadfence();
     __syncthreads();
@@ -381,20 +536,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
 
     WaveTopK mt;
     mt.init(p.k, lane);
-    const int total = p.groups * p.k;
-    constexpr int kMergeUnroll = 8;
-    for (int i0 = 0; i0 < total; i0 += kTopkThreads * kMergeUnroll) {
-        uint64_t key[kMergeUnroll];
+    const int64_t total = (int64_t)p.groups * p.k;
+    for (int64_t rb = 0; rb < total; rb += (int64_t)waves * kBatch) {
+        const int64_t wb = rb + (int64_t)wave * kBatch;
+        uint64_t key[kKeysPerLane];
 #pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-            const int i = i0 + u * kTopkThreads + tid;
+        for (int u = 0; u < kKeysPerLane; ++u) {
+            const int64_t i = wb + lane + 64 * u;
             key[u] = i < total ? p.partials[i] : 0;
         }
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) mt.offer(key[u]);
+        mt.offer(key, s_scratch[wave]);
     }
-    __syncthreads();   // every wave is done reading s_best from the first merge
-    block_merge(mt, s_best, wave, lane);
+    block_merge(mt, s_list, wave, waves);
     if (wave == 0) {
         if (lane < p.k) write_result(p, mt.best, lane);
         if (lane == 0) *p.counter = 0u;   // ready for the next launch
@@ -405,19 +558,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
 
 hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_bytes,
                              hipStream_t stream) {
-    hipLaunchKernelGGL(preprocess_kernel, dim3((unsigned)groups), dim3((unsigned)block),
-                       (unsigned)lds_bytes, stream, p);
+    const dim3 g((unsigned)groups), b((unsigned)block);
+    switch (p.pixels_per_thread) {
+        case 1: hipLaunchKernelGGL(preprocess_kernel<1>, g, b, (unsigned)lds_bytes, stream, p); break;
+        case 2: hipLaunchKernelGGL(preprocess_kernel<2>, g, b, (unsigned)lds_bytes, stream, p); break;
+        case 4: hipLaunchKernelGGL(preprocess_kernel<4>, g, b, (unsigned)lds_bytes, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)p.groups), dim3(kTopkThreads), 0, stream, p);
+    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)p.groups), dim3((unsigned)(64 * p.waves)), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
 hipError_t set_kernel_attributes() {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(preprocess_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+    const void* fns[3] = {reinterpret_cast<const void*>(preprocess_kernel<1>),
+                          reinterpret_cast<const void*>(preprocess_kernel<2>),
+                          reinterpret_cast<const void*>(preprocess_kernel<4>)};
+    for (const void* f : fns) {
+        const hipError_t e =
+            hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace ws

@@ -124,6 +124,10 @@ inline int validate_config(const ws_lane_config* c) {
     if (c->scores_dev && c->num_scores == 0) return WS_E_INVALID_ARG;
     if (c->rows_per_group < 0 || c->rows_per_group > 64) return WS_E_INVALID_ARG;
     if (c->topk_chunk < 0 || (c->topk_chunk % 1024) != 0) return WS_E_INVALID_ARG;
+    if (c->num_scores > WS_MAX_SCORES) return WS_E_INVALID_ARG;
+    if (c->pixels_per_thread != 0 && c->pixels_per_thread != 1 && c->pixels_per_thread != 2 &&
+        c->pixels_per_thread != 4)
+        return WS_E_INVALID_ARG;
     return WS_OK;
 }
 
@@ -132,8 +136,10 @@ inline int validate_config(const ws_lane_config* c) {
 
 constexpr int kMaxPreBlock = 512;          // preprocess threads per workgroup
 constexpr int kMaxLdsBytes = 156 * 1024;   // gfx950: 160 KiB LDS per workgroup, less static use
-constexpr int kTopkBlock = 256;            // four wave64s
-constexpr int kTopkAutoChunk = 4096;       // scores per Top-K workgroup (auto)
+constexpr int kTopkBatch = 1024;           // scores one wave takes per round
+constexpr int kTopkMaxWaves = 4;           // one wave per SIMD of a CU
+constexpr int kTopkSingleGroupMax = 65536; // up to here one workgroup, no hand-off
+constexpr int kTopkAutoChunk = 16384;      // beyond: scores per workgroup
 
 struct Plan {
     Region region;
@@ -141,7 +147,8 @@ struct Plan {
     // region's horizontal taps touch.
     int64_t span_lo = 0, span = 0;
     int32_t slot_bytes = 0;        // LDS bytes per staged source row (16-multiple)
-    int32_t quads_per_row = 0;     // ceil(dst_w / 4): each thread owns 4 columns
+    int32_t pixels_per_thread = 1; // adjacent output columns per thread (1, 2, 4)
+    int32_t threads_per_row = 0;   // ceil(dst_w / pixels_per_thread)
     int32_t rows_per_group = 1;
     int32_t pre_block = 64;
     int32_t pre_groups = 0;
@@ -150,6 +157,7 @@ struct Plan {
     // Top-K
     int32_t topk_groups = 0;
     int32_t topk_chunk = 0;
+    int32_t topk_waves = 0;        // wave64s per Top-K workgroup
     // Sizes
     size_t frame_bytes = 0, input_bytes = 0, tensor_bytes = 0;
 };
@@ -177,8 +185,17 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
     p->slot_bytes = (int32_t)(ceil_div(p->span + 15, 16) * 16);
     if (lds_for_rows(1, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
 
-    p->quads_per_row = (int32_t)ceil_div(Dw, 4);
-    const int32_t q = p->quads_per_row;
+    // Pixels per thread: large batches are bandwidth work and take 4 (fewer,
+    // wider stores); single frames are latency work and take 1 so that more
+    // waves share each row (2 when a row would need more than 512 threads).
+    int32_t px = c.pixels_per_thread;
+    if (px == 0) {
+        const int64_t total_px = (int64_t)c.batch * Dw * Dh;
+        px = total_px >= (int64_t)1 << 20 ? 4 : (Dw <= kMaxPreBlock ? 1 : (Dw <= 2 * kMaxPreBlock ? 2 : 4));
+    }
+    p->pixels_per_thread = px;
+    p->threads_per_row = (int32_t)ceil_div(Dw, px);
+    const int32_t q = p->threads_per_row;
 
     int32_t rows = c.rows_per_group;
     if (rows == 0) {
@@ -215,12 +232,18 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
     p->lds_bytes = lds_for_rows(rows, p->slot_bytes);
 
     if (c.num_scores > 0) {
+        // Up to 64 Ki scores one workgroup does everything (its waves take
+        // 1024-score batches in rounds), so no hand-off between workgroups is
+        // needed; beyond that, workgroups take 16 Ki scores each and the last
+        // to finish merges their lists.
         int64_t chunk = c.topk_chunk;
         if (chunk == 0) {
-            chunk = c.num_scores <= kTopkAutoChunk ? ceil_div(c.num_scores, 1024) * 1024
-                                                   : kTopkAutoChunk;
+            chunk = c.num_scores <= kTopkSingleGroupMax
+                        ? ceil_div(c.num_scores, kTopkBatch) * kTopkBatch
+                        : kTopkAutoChunk;
         }
         p->topk_chunk = (int32_t)chunk;
+        p->topk_waves = (int32_t)std::min<int64_t>(kTopkMaxWaves, chunk / kTopkBatch);
         p->topk_groups = (int32_t)ceil_div(c.num_scores, chunk);
     }
 

@@ -210,10 +210,11 @@ int build(ws_lane* L) {
     q.inv_den_y = (float)(1.0 / (2.0 * P.region.h));
     q.span_lo = (int32_t)P.span_lo;
     q.slot_chunks = P.slot_bytes / 16;
-    q.quads_per_row = P.quads_per_row;
+    q.pixels_per_thread = P.pixels_per_thread;
+    q.threads_per_row = P.threads_per_row;
     q.rows_per_group = P.rows_per_group;
     q.groups_per_frame = P.groups_per_frame;
-    q.vec4 = (c.dst_w % 4) == 0;
+    q.vec = (c.dst_w % P.pixels_per_thread) == 0;
     for (int i = 0; i < 3; ++i) {
         q.a[i] = (float)(1.0 / (255.0 * c.std[i]));
         q.b[i] = (float)(-c.mean[i] / c.std[i]);
@@ -225,6 +226,7 @@ int build(ws_lane* L) {
     t.k = c.k;
     t.chunk = P.topk_chunk;
     t.groups = P.topk_groups;
+    t.waves = P.topk_waves;
     t.partials = L->partials;
     t.counter = L->counter;
     t.result = L->res_dev;
@@ -336,7 +338,7 @@ int ws_lane_describe(const ws_lane* L, ws_lane_plan* plan) {
     plan->rows_per_group = L->plan.rows_per_group;
     plan->pre_lds_bytes = L->plan.lds_bytes;
     plan->topk_groups = L->plan.topk_groups;
-    plan->topk_block = ws::kTopkThreads;
+    plan->topk_block = 64 * L->plan.topk_waves;
     plan->topk_chunk = L->plan.topk_chunk;
     plan->graph_nodes = L->nodes;
     return WS_OK;

@@ -56,6 +56,7 @@ class LaneConfig(Structure):
         ("use_graph", c_int32), ("wait_mode", c_int32),
         ("input_dev", c_void_p), ("scores_dev", c_void_p), ("tensor_dev", c_void_p),
         ("rows_per_group", c_int32), ("topk_chunk", c_int32),
+        ("pixels_per_thread", c_int32),
     ]
 
 
@@ -146,7 +147,7 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
                 mean=(0.0, 0.0, 0.0), std=(1.0, 1.0, 1.0), num_scores=0, k=0,
                 host_input=False, use_graph=True, wait_mode=WAIT_SPIN, device=0,
                 input_dev=None, scores_dev=None, tensor_dev=None, rows_per_group=0,
-                topk_chunk=0) -> LaneConfig:
+                topk_chunk=0, pixels_per_thread=0) -> LaneConfig:
     c = LaneConfig()
     c.device = device
     c.batch = batch
@@ -165,6 +166,7 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
     c.tensor_dev = _addr(tensor_dev)
     c.rows_per_group = rows_per_group
     c.topk_chunk = topk_chunk
+    c.pixels_per_thread = pixels_per_thread
     return c
 
 

@@ -66,6 +66,8 @@ static int selftest() {
     BAD(wait_mode, 9);
     BAD(rows_per_group, 65);
     BAD(topk_chunk, 1000);
+    BAD(pixels_per_thread, 3);
+    BAD(num_scores, WS_MAX_SCORES + 1);
     {
         ws_lane_config b = good();
         b.std[1] = 0.0;
@@ -103,13 +105,14 @@ static int selftest() {
     // Plans: every lane shape the workloads use is feasible.
     ws::Plan p;
     CHECK(ws::make_plan(c, &p) == WS_OK);
-    CHECK(p.pre_groups == 224 && p.quads_per_row == 56);
+    CHECK(p.pre_groups == 224 && p.pixels_per_thread == 1 && p.threads_per_row == 224);
     CHECK(p.span_lo == 3 * 3);  // first tap of 1920 -> 224: (1920 - 224) / 448 -> column 3
     c.batch = 64;
     c.src_w = 1280;
     c.src_h = 720;
     CHECK(ws::make_plan(c, &p) == WS_OK);
-    CHECK(p.rows_per_group * p.quads_per_row <= p.pre_block);
+    CHECK(p.pixels_per_thread == 4);
+    CHECK(p.rows_per_group * p.threads_per_row <= p.pre_block);
     CHECK(p.lds_bytes <= ws::kMaxLdsBytes);
     c = good();
     c.src_w = WS_MAX_SIDE;

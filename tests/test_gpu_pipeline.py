@@ -62,7 +62,7 @@ def test_throughput_batch_parity(gpu_lib):
 def test_random_small_shapes(gpu_lib, seed, letterbox):
     w = wl.random_small(seed, letterbox=letterbox)
     ref, _ = oracle_outputs(w)
-    r = Run(w, host_input=bool(seed % 2))
+    r = Run(w, host_input=bool(seed % 2), pixels_per_thread=(1, 2, 4)[seed % 3])
     try:
         r.run()
         t, _ = r.outputs()
@@ -71,12 +71,13 @@ def test_random_small_shapes(gpu_lib, seed, letterbox):
         r.close()
 
 
-@pytest.mark.parametrize("name,rows", [("c4", 1), ("c4", 2), ("c4", 3), ("c4", 6), ("c1", 5),
-                                       ("c1", 32), ("c2", 9), ("c3", 4)])
-def test_rows_per_group_does_not_change_results(gpu_lib, name, rows):
+@pytest.mark.parametrize("name,rows,px", [("c4", 1, 4), ("c4", 2, 1), ("c4", 3, 2), ("c4", 6, 4),
+                                          ("c1", 5, 1), ("c1", 32, 2), ("c2", 9, 4), ("c2", 1, 2),
+                                          ("c3", 4, 4), ("c3", 1, 1), ("c3", 2, 2)])
+def test_launch_geometry_does_not_change_results(gpu_lib, name, rows, px):
     w = wl.ALL_CONFIGS[name]()
     ref, _ = oracle_outputs(w)
-    r = Run(w, host_input=False, rows_per_group=rows)
+    r = Run(w, host_input=False, rows_per_group=rows, pixels_per_thread=px)
     try:
         assert r.lane.plan()["rows_per_group"] == rows
         r.run()

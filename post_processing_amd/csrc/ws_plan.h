@@ -199,26 +199,13 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
 
     int32_t rows = c.rows_per_group;
     if (rows == 0) {
-        // Prefer full lanes, but keep at least 512 workgroups (two per CU) when
-        // the tensor has that many rows, so small frames spread over the chip.
-        const int64_t total_rows = (int64_t)c.batch * Dh;
-        const int64_t min_groups = total_rows < 512 ? total_rows : 512;
-        double best_util = -1.0;
-        rows = 1;
-        for (int32_t r = 1; r <= 64; ++r) {
-            const int64_t threads = (int64_t)r * q;
-            if (r > 1 && threads > kMaxPreBlock) break;
-            if (r > Dh) break;
-            if (lds_for_rows(r, p->slot_bytes) > kMaxLdsBytes / 2 && r > 1) break;
-            const int64_t groups = (int64_t)c.batch * ceil_div(Dh, r);
-            if (groups < min_groups) break;
-            const int64_t blk = std::min<int64_t>(kMaxPreBlock, ceil_div(threads, 64) * 64);
-            const double util = (double)std::min<int64_t>(threads, blk) / (double)blk;
-            if (util > best_util + 1e-9) {
-                best_util = util;
-                rows = r;
-            }
-        }
+        // Measured on MI355X: batches (bandwidth work) run best with one row
+        // per workgroup, the most workgroups in flight; single frames with one
+        // row, or two once the tensor has 320+ rows (fewer, fuller groups).
+        // Tiny rows are packed so a workgroup holds at least one full wave.
+        rows = (px == 4 || Dh < 320) ? 1 : 2;
+        while (rows < Dh && (int64_t)(rows + 1) * q <= 64) ++rows;
+        while (rows > 1 && lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes / 2) --rows;
     }
     if (rows > Dh) rows = (int32_t)Dh;
     if (lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;

@@ -111,9 +111,16 @@ def lat_stats(ms: np.ndarray) -> dict:
 KNOBS = {}
 
 
+INPUT_OVERRIDE = {}
+
+
 def make_lane(w, torch, host_input=None, use_graph=True):
     from post_processing_amd import ws
     host = w.host_input if host_input is None else host_input
+    mode = INPUT_OVERRIDE.get("mode")
+    if mode is None:
+        mode = ws.INPUT_MAPPED_HOST if host else ws.INPUT_DEVICE
+    host = mode != ws.INPUT_DEVICE
     dev = torch.device("cuda:0")
     keep = {}
     keep["tensor"] = torch.empty((w.batch, 3, w.dst_h, w.dst_w), dtype=torch.float32, device=dev)
@@ -124,7 +131,7 @@ def make_lane(w, torch, host_input=None, use_graph=True):
     torch.cuda.synchronize()
     cfg = ws.make_config(src_w=w.src_w, src_h=w.src_h, dst_w=w.dst_w, dst_h=w.dst_h,
                          batch=w.batch, letterbox=(w.mode == 1), pad=w.pad, mean=w.mean,
-                         std=w.std, num_scores=w.num_scores, k=w.k, host_input=host,
+                         std=w.std, num_scores=w.num_scores, k=w.k, input_mode=mode,
                          use_graph=use_graph, input_dev=keep.get("frames"),
                          scores_dev=keep.get("scores"), tensor_dev=keep["tensor"], **KNOBS)
     lane = ws.Lane(cfg)
@@ -285,6 +292,8 @@ def main(argv=None) -> int:
     ap.add_argument("--stage-launches", type=int, default=500)
     ap.add_argument("--rows-per-group", type=int, default=0, help="preprocess tuning knob (0 = auto)")
     ap.add_argument("--topk-chunk", type=int, default=0, help="Top-K tuning knob (0 = auto)")
+    ap.add_argument("--input", default=None, choices=["device", "mapped", "copy"],
+                    help="override the workload's input mode")
     ap.add_argument("--pixels-per-thread", type=int, default=0,
                     help="preprocess tuning knob: 1, 2 or 4 (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -308,6 +317,9 @@ def main(argv=None) -> int:
 
     KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
                  pixels_per_thread=args.pixels_per_thread)
+    if args.input:
+        INPUT_OVERRIDE["mode"] = {"device": ws.INPUT_DEVICE, "mapped": ws.INPUT_MAPPED_HOST,
+                                  "copy": ws.INPUT_COPY}[args.input]
     name = args.workload
     if name == "copy":
         return copy_calibration(torch, args)
@@ -373,7 +385,7 @@ def main(argv=None) -> int:
                    "frames_per_step": w.batch, "src": [w.src_w, w.src_h],
                    "dst": [w.dst_w, w.dst_h], "letterbox": w.mode == 1,
                    "topk": {"n": w.num_scores, "k": w.k} if w.k else None,
-                   "input": "mapped_host" if (w.host_input or name == "c5l") else "device",
+                   "input": args.input or ("mapped" if (w.host_input or name == "c5l") else "device"),
                    "graph": True, "lanes": 8 if name == "c5l" else 1,
                    "parallelism": "single_gpu"},
         "p50_us": round(res["p50_us"], 3),

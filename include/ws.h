@@ -52,6 +52,10 @@ extern "C" {
 #define WS_INPUT_MAPPED_HOST 0  /* producer writes pinned host memory the GPU
                                    reads over the bus (zero-copy slot)        */
 #define WS_INPUT_DEVICE      1  /* frame already resides in device memory    */
+#define WS_INPUT_COPY        2  /* producer writes pinned host memory; each
+                                   replay first copies the whole frame into a
+                                   fixed device buffer (a DMA memcpy node of
+                                   the graph), then preprocess reads HBM     */
 
 #define WS_WAIT_SPIN   0        /* ws_wait polls the completion event        */
 #define WS_WAIT_BLOCK  1        /* ws_wait blocks in the runtime             */
@@ -107,7 +111,7 @@ typedef struct ws_lane_config {
  *   result  ws_topk_entry [k]                 mapped host memory, rank order
  */
 typedef struct ws_lane_view {
-    uint8_t             *input_host;   /* producer's slot (mapped mode), else NULL */
+    uint8_t             *input_host;   /* producer's slot (mapped / copy mode), else NULL */
     const uint8_t       *input_dev;    /* address the preprocess kernel reads      */
     float               *tensor_dev;
     float               *scores_dev;   /* NULL when num_scores == 0                */
@@ -120,7 +124,8 @@ typedef struct ws_lane ws_lane;
 
 /*
  * ws_create_lane -- validate cfg, then allocate and bind everything the lane
- * will ever use: input slot (hipHostMalloc mapped, coherent) or device input,
+ * will ever use: input slot (hipHostMalloc mapped, coherent; for the copy mode
+ * pinned host memory plus a device copy) or device input,
  * tensor, scores, mapped result slot, Top-K scratch, one non-blocking
  * stream and two timing events, and fixes the launch geometry.  Runs the kernels
  * once outside capture (warm-up), captures them into one graph, instantiates

@@ -102,7 +102,8 @@ inline int validate_config(const ws_lane_config* c) {
         return WS_E_INVALID_ARG;
     if (c->resize_mode != WS_RESIZE_BILINEAR && c->resize_mode != WS_RESIZE_LETTERBOX)
         return WS_E_INVALID_ARG;
-    if (c->input_mode != WS_INPUT_MAPPED_HOST && c->input_mode != WS_INPUT_DEVICE)
+    if (c->input_mode != WS_INPUT_MAPPED_HOST && c->input_mode != WS_INPUT_DEVICE &&
+        c->input_mode != WS_INPUT_COPY)
         return WS_E_INVALID_ARG;
     if (!(c->pad_value >= 0.0 && c->pad_value <= 255.0)) return WS_E_INVALID_ARG;
     for (int i = 0; i < 3; ++i) {

@@ -58,10 +58,16 @@ int fail(ws_lane* L, hipError_t e, int code) {
     return code;
 }
 
-// The per-frame launch sequence: preprocess, then Top-K, in stream order.
+// The per-frame launch sequence, in stream order: (copy mode) the frame's
+// host-to-device copy, preprocess, Top-K.
 hipError_t launch_all(ws_lane* L) {
-    hipError_t e = ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
-                                         L->plan.lds_bytes, L->stream);
+    hipError_t e = hipSuccess;
+    if (L->cfg.input_mode == WS_INPUT_COPY)
+        e = hipMemcpyAsync(L->in_own, L->in_host, L->plan.input_bytes, hipMemcpyHostToDevice,
+                           L->stream);
+    if (e != hipSuccess) return e;
+    e = ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block, L->plan.lds_bytes,
+                              L->stream);
     if (e != hipSuccess) return e;
     if (L->cfg.num_scores > 0) e = ws::launch_topk(L->tk, L->stream);
     return e;
@@ -152,6 +158,19 @@ int build(ws_lane* L) {
         WS_TRY(mapped_alloc(L, &h, &d, P.input_bytes));
         L->in_host = static_cast<uint8_t*>(h);
         L->in_dev = static_cast<const uint8_t*>(d);
+    } else if (c.input_mode == WS_INPUT_COPY) {
+        // Pinned host slot for the producer (the DMA engine reads it) and the
+        // fixed device buffer the copy lands in.
+        void* h = nullptr;
+        const size_t hb = P.input_bytes < 16 ? 16 : P.input_bytes;
+        hipError_t e = hipHostMalloc(&h, hb, hipHostMallocDefault);
+        if (e != hipSuccess) return fail(L, e, WS_E_OOM);
+        std::memset(h, 0, hb);
+        L->in_host = static_cast<uint8_t*>(h);
+        void* d = nullptr;
+        WS_TRY(dev_alloc(L, &d, P.input_bytes));
+        L->in_own = static_cast<uint8_t*>(d);
+        L->in_dev = L->in_own;
     } else if (c.input_dev) {
         L->in_dev = c.input_dev;
     } else {
@@ -230,7 +249,7 @@ int build(ws_lane* L) {
     t.partials = L->partials;
     t.counter = L->counter;
     t.result = L->res_dev;
-    L->nodes = 1 + (c.num_scores > 0 ? 1 : 0);
+    L->nodes = 1 + (c.num_scores > 0 ? 1 : 0) + (c.input_mode == WS_INPUT_COPY ? 1 : 0);
 
     // ---- stream, events, warm-up, capture ---------------------------------
     WS_HIP(hipStreamCreateWithFlags(&L->stream, hipStreamNonBlocking), WS_E_HIP);

@@ -34,6 +34,7 @@ RESIZE_BILINEAR = 0
 RESIZE_LETTERBOX = 1
 INPUT_MAPPED_HOST = 0
 INPUT_DEVICE = 1
+INPUT_COPY = 2
 WAIT_SPIN = 0
 WAIT_BLOCK = 1
 MAX_K = 32
@@ -147,13 +148,15 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
                 mean=(0.0, 0.0, 0.0), std=(1.0, 1.0, 1.0), num_scores=0, k=0,
                 host_input=False, use_graph=True, wait_mode=WAIT_SPIN, device=0,
                 input_dev=None, scores_dev=None, tensor_dev=None, rows_per_group=0,
-                topk_chunk=0, pixels_per_thread=0) -> LaneConfig:
+                topk_chunk=0, pixels_per_thread=0, input_mode=None) -> LaneConfig:
     c = LaneConfig()
     c.device = device
     c.batch = batch
     c.src_w, c.src_h, c.dst_w, c.dst_h = src_w, src_h, dst_w, dst_h
     c.resize_mode = RESIZE_LETTERBOX if letterbox else RESIZE_BILINEAR
-    c.input_mode = INPUT_MAPPED_HOST if host_input else INPUT_DEVICE
+    if input_mode is None:
+        input_mode = INPUT_MAPPED_HOST if host_input else INPUT_DEVICE
+    c.input_mode = input_mode
     c.pad_value = float(pad)
     c.mean[:] = [float(v) for v in mean]
     c.std[:] = [float(v) for v in std]
@@ -204,9 +207,10 @@ class Lane:
 
     # -- buffers ----------------------------------------------------------
     def input_host_array(self) -> np.ndarray:
-        """The mapped input slot as a writable uint8 [B][H][W][3] view."""
+        """The producer's host input slot (mapped or copy mode) as a writable
+        uint8 [B][H][W][3] view."""
         if not self.view.input_host:
-            raise RuntimeError("lane has no mapped input slot")
+            raise RuntimeError("lane has no host input slot")
         c = self.cfg
         flat = np.ctypeslib.as_array(self.view.input_host, shape=(self.view.input_bytes,))
         return flat.reshape(c.batch, c.src_h, c.src_w, 3)

@@ -19,10 +19,13 @@ def oracle_outputs(w: wl.Workload):
 class Run:
     """A lane built for a workload, with borrowed torch buffers kept alive."""
 
-    def __init__(self, w: wl.Workload, host_input=None, use_graph=True, **knobs):
+    def __init__(self, w: wl.Workload, host_input=None, use_graph=True, input_mode=None, **knobs):
         import torch
         self.w = w
         self.host_input = w.host_input if host_input is None else host_input
+        if input_mode is None:
+            input_mode = ws.INPUT_MAPPED_HOST if self.host_input else ws.INPUT_DEVICE
+        self.host_input = input_mode != ws.INPUT_DEVICE
         dev = torch.device("cuda:0")
         self.tensor = torch.empty((w.batch, 3, w.dst_h, w.dst_w), dtype=torch.float32, device=dev)
         self.tensor.fill_(float("nan"))
@@ -36,7 +39,7 @@ class Run:
         cfg = ws.make_config(src_w=w.src_w, src_h=w.src_h, dst_w=w.dst_w, dst_h=w.dst_h,
                              batch=w.batch, letterbox=(w.mode == wl.LETTERBOX), pad=w.pad,
                              mean=w.mean, std=w.std, num_scores=w.num_scores, k=w.k,
-                             host_input=self.host_input, use_graph=use_graph,
+                             input_mode=input_mode, use_graph=use_graph,
                              input_dev=self.frames, scores_dev=self.scores,
                              tensor_dev=self.tensor, **knobs)
         self.lane = ws.Lane(cfg)

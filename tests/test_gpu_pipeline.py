@@ -45,6 +45,37 @@ def test_config_parity_mapped_host_input(gpu_lib, name):
         r.close()
 
 
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_config_parity_copy_input(gpu_lib, name):
+    w = wl.ALL_CONFIGS[name]()
+    ref, rtk = oracle_outputs(w)
+    r = Run(w, input_mode=ws.INPUT_COPY)
+    try:
+        assert r.lane.plan()["graph_nodes"] == 3
+        r.run()
+        t, tk = r.outputs()
+        assert_tensor_close(t, ref)
+        assert_topk_exact(tk, rtk)
+    finally:
+        r.close()
+
+
+def test_input_modes_agree_bitwise(gpu_lib):
+    w = wl.c2()
+    runs = [Run(w, input_mode=m) for m in (ws.INPUT_DEVICE, ws.INPUT_MAPPED_HOST, ws.INPUT_COPY)]
+    try:
+        outs = []
+        for r in runs:
+            r.run()
+            outs.append(r.outputs())
+        for t, tk in outs[1:]:
+            np.testing.assert_array_equal(t.view(np.uint32), outs[0][0].view(np.uint32))
+            assert_topk_exact(tk, outs[0][1])
+    finally:
+        for r in runs:
+            r.close()
+
+
 def test_throughput_batch_parity(gpu_lib):
     w = wl.c5_throughput(64)
     ref, _ = oracle_outputs(w)
@@ -191,11 +222,12 @@ def test_mapped_and_device_input_agree(gpu_lib):
         b.close()
 
 
-def test_mapped_slot_sees_each_new_frame(gpu_lib):
+@pytest.mark.parametrize("mode", ["mapped", "copy"])
+def test_host_slot_sees_each_new_frame(gpu_lib, mode):
     # The producer rewrites the slot between frames; every replay must read
     # the new bytes (no stale cached copy of the previous frame).
     w = wl.c1()
-    r = Run(w, host_input=True)
+    r = Run(w, input_mode=ws.INPUT_MAPPED_HOST if mode == "mapped" else ws.INPUT_COPY)
     try:
         slot = r.lane.input_host_array()
         for i in range(4):

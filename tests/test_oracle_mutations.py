@@ -1,0 +1,185 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one bug in a copy of the oracle's source (on the CPU): a
+dropped term, a wrong sign or index, a transposed operand, a wrong tie rule.
+The pins below (closed forms, hand-derived taps, torch's float64 bilinear,
+brute-force selection) must reject every mutant while accepting the oracle
+itself.  This shows the pins constrain the oracle rather than restate it.
+"""
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+
+def load_variant(filename: str, old: str = None, new: str = None) -> types.ModuleType:
+    with open(os.path.join(ORACLE_DIR, filename)) as f:
+        src = f.read()
+    if old is not None:
+        assert old in src, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new, 1)
+    mod = types.ModuleType("oracle_variant")
+    exec(compile(src, filename, "exec"), mod.__dict__)
+    return mod
+
+
+MEAN = (0.485, 0.456, 0.406)
+STD = (0.229, 0.224, 0.225)
+
+
+def preprocess_pins(m) -> list[str]:
+    """Run the preprocess pins against module m; return the names that fail."""
+    failed = []
+    norm = lambda v, c: (np.asarray(v, float) / 255.0 - MEAN[c]) / STD[c]
+
+    def check(name, fn):
+        try:
+            if not fn():
+                failed.append(name)
+        except Exception:
+            failed.append(name)
+
+    rng = np.random.default_rng(7)
+    f = rng.integers(0, 256, size=(5, 7, 3), dtype=np.uint8)
+    check("identity", lambda: all(np.allclose(m.preprocess(f, 7, 5, MEAN, STD)[c], norm(f[..., c], c),
+                                              atol=1e-12, rtol=0) for c in range(3)))
+    const = np.empty((9, 4, 3), dtype=np.uint8)
+    const[..., 0], const[..., 1], const[..., 2] = 10, 128, 251
+    check("constant", lambda: all(np.allclose(m.preprocess(const, 13, 6, MEAN, STD)[c],
+                                              norm(v, c), atol=1e-12, rtol=0)
+                                  for c, v in enumerate((10, 128, 251))))
+    vals = np.array([17, 200, 3], dtype=np.uint8)
+    row = np.zeros((1, 3, 3), dtype=np.uint8)
+    row[0, :, 0] = vals
+    want32 = norm(np.array([[0.75, 0.25, 0], [0, 0.25, 0.75]]) @ vals.astype(float), 0)
+    check("taps_3_to_2_x", lambda: np.allclose(m.preprocess(row, 2, 1, MEAN, STD)[0, 0], want32,
+                                               atol=1e-12, rtol=0))
+    col = np.zeros((3, 1, 3), dtype=np.uint8)
+    col[:, 0, 1] = vals
+    want32y = norm(np.array([[0.75, 0.25, 0], [0, 0.25, 0.75]]) @ vals.astype(float), 1)
+    check("taps_3_to_2_y", lambda: np.allclose(m.preprocess(col, 1, 2, MEAN, STD)[1, :, 0], want32y,
+                                               atol=1e-12, rtol=0))
+    up = np.zeros((1, 2, 3), dtype=np.uint8)
+    up[0, :, 0] = [40, 200]
+    want24 = norm(np.array([40, 80, 160, 200], float), 0)
+    check("taps_2_to_4", lambda: np.allclose(m.preprocess(up, 4, 1, MEAN, STD)[0, 0], want24,
+                                             atol=1e-12, rtol=0))
+    g = rng.integers(0, 256, size=(8, 6, 3), dtype=np.uint8)
+    blk = g.astype(float).reshape(4, 2, 3, 2, 3).mean(axis=(1, 3))
+    check("block_mean", lambda: all(np.allclose(m.preprocess(g, 3, 4, MEAN, STD)[c],
+                                                norm(blk[..., c], c), atol=1e-12, rtol=0)
+                                    for c in range(3)))
+
+    def torch_pin():
+        torch = pytest.importorskip("torch")
+        F = torch.nn.functional
+        h = rng.integers(0, 256, size=(11, 17, 3), dtype=np.uint8)
+        out = m.preprocess(h, 7, 13, (0, 0, 0), (1 / 255, 1 / 255, 1 / 255))
+        t = torch.from_numpy(h.astype(np.float64)).permute(2, 0, 1)[None]
+        ref = F.interpolate(t, size=(13, 7), mode="bilinear", align_corners=False)[0].numpy()
+        return np.allclose(out, ref, atol=1e-9, rtol=0)
+    check("torch_bilinear", torch_pin)
+
+    def letterbox_pin():
+        fr = rng.integers(0, 256, size=(720 // 40, 1280 // 40, 3), dtype=np.uint8)   # 32x18
+        out = m.preprocess(fr, 16, 16, (0, 0, 0), (1, 1, 1), letterbox=True, pad=114.0)
+        if m.letterbox_region(32, 18, 16, 16) != (0, 3, 16, 9):
+            return False
+        blk2 = fr.astype(float).reshape(9, 2, 16, 2, 3).mean(axis=(1, 3))
+        return (np.allclose(out[:, :3], 114 / 255, atol=1e-15) and
+                np.allclose(out[:, 12:], 114 / 255, atol=1e-15) and
+                np.allclose(out[:, 3:12], np.moveaxis(blk2, 2, 0) / 255, atol=1e-12))
+    check("letterbox", letterbox_pin)
+    check("letterbox_boxes", lambda: m.letterbox_region(3, 1, 8, 8) == (0, 2, 8, 3) and
+          m.letterbox_region(20, 40, 30, 30) == (7, 0, 15, 30))
+    return failed
+
+
+def naive_topk(s, k):
+    key = [(-math.inf if math.isnan(v) else float(v)) for v in s]
+    chosen = []
+    for _ in range(k):
+        best = None
+        for i in range(len(s)):
+            if i in chosen:
+                continue
+            if best is None or key[i] > key[best] or (key[i] == key[best] and i < best):
+                best = i
+        chosen.append(best)
+    return chosen
+
+
+def topk_pins(m) -> list[str]:
+    failed = []
+    cases = [
+        np.array([0.5, 2.0, 2.0, -1.0, np.nan, 3.0, -0.0, 0.0], dtype=np.float32),
+        np.array([np.nan, -np.inf, 1.0, 1.0, np.nan], dtype=np.float32),
+        np.random.default_rng(3).standard_normal(200).astype(np.float32),
+    ]
+    for ci, s in enumerate(cases):
+        for k in (1, 3, min(5, len(s))):
+            try:
+                vals, idx = m.topk(s, k)
+                want = naive_topk(s, k)
+                bits = s.view(np.uint32)[want].copy()
+                bits[np.isnan(s[want])] = 0xFF800000
+                if idx.tolist() != want or vals.view(np.uint32).tolist() != bits.tolist():
+                    failed.append(f"case{ci}_k{k}")
+            except Exception:
+                failed.append(f"case{ci}_k{k}")
+    return failed
+
+
+def test_unmodified_oracle_passes_all_pins():
+    assert preprocess_pins(load_variant("preprocess.py")) == []
+    assert topk_pins(load_variant("topk.py")) == []
+
+
+PREPROCESS_MUTANTS = [
+    ("centre offset sign", "pos = Fraction((2 * d + 1) * src - dst, 2 * dst)",
+     "pos = Fraction((2 * d + 1) * src + dst, 2 * dst)"),
+    ("no half-pixel centre", "pos = Fraction((2 * d + 1) * src - dst, 2 * dst)",
+     "pos = Fraction(2 * d * src, 2 * dst)"),
+    ("no left clamp", "        if pos < 0:\n            pos = Fraction(0)\n", ""),
+    ("right tap unclamped", "i1[d] = min(lo + 1, src - 1)", "i1[d] = min(lo + 1, src)"),
+    ("right tap equals left", "i1[d] = min(lo + 1, src - 1)", "i1[d] = lo"),
+    ("weight complement swapped", "top_row = (1.0 - ax) * p00 + ax * p01",
+     "top_row = ax * p00 + (1.0 - ax) * p01"),
+    ("bottom row dropped", "val = (1.0 - ay) * top_row + ay * bot_row", "val = top_row"),
+    ("x/y taps transposed", "    p01 = p[y0][:, x1]\n    p10 = p[y1][:, x0]\n",
+     "    p01 = p[y1][:, x0]\n    p10 = p[y0][:, x1]\n"),
+    ("axes swapped", "    x0, x1, wx = axis_taps(w, rw)\n    y0, y1, wy = axis_taps(h, rh)",
+     "    x0, x1, wx = axis_taps(w, rh)\n    y0, y1, wy = axis_taps(h, rw)"),
+    ("mean sign", "(val[:, :, c] / 255.0 - mean[c]) / std[c]", "(val[:, :, c] / 255.0 + mean[c]) / std[c]"),
+    ("no byte scaling", "(val[:, :, c] / 255.0 - mean[c]) / std[c]", "(val[:, :, c] - mean[c]) / std[c]"),
+    ("channel order reversed", "out[c, top:top + rh, left:left + rw] = (val[:, :, c]",
+     "out[c, top:top + rh, left:left + rw] = (val[:, :, 2 - c]"),
+    ("letterbox rounds down", "rh = int((src_h * r + half) // 1)", "rh = int((src_h * r) // 1)"),
+    ("letterbox top at zero", "return (dst_w - rw) // 2, (dst_h - rh) // 2, rw, rh",
+     "return (dst_w - rw) // 2, 0, rw, rh"),
+]
+
+
+@pytest.mark.parametrize("label,old,new", PREPROCESS_MUTANTS, ids=[m[0] for m in PREPROCESS_MUTANTS])
+def test_preprocess_mutant_is_caught(label, old, new):
+    failed = preprocess_pins(load_variant("preprocess.py", old, new))
+    assert failed, f"no pin caught the mutant: {label}"
+
+
+TOPK_MUTANTS = [
+    ("ascending order", "key=lambda i: (-keys[i], i)", "key=lambda i: (keys[i], i)"),
+    ("ties to the higher index", "key=lambda i: (-keys[i], i)", "key=lambda i: (-keys[i], -i)"),
+    ("NaN ranked as +inf", "(-math.inf if math.isnan(v) else v)", "(math.inf if math.isnan(v) else v)"),
+    ("NaN reported as NaN", "    bits[nan] = NEG_INF_BITS\n", ""),
+    ("off by one in k", "order = topk_keys_order(s)[:k]", "order = topk_keys_order(s)[1:k + 1]"),
+]
+
+
+@pytest.mark.parametrize("label,old,new", TOPK_MUTANTS, ids=[m[0] for m in TOPK_MUTANTS])
+def test_topk_mutant_is_caught(label, old, new):
+    failed = topk_pins(load_variant("topk.py", old, new))
+    assert failed, f"no pin caught the mutant: {label}"

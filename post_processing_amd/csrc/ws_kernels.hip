@@ -331,17 +331,19 @@ constexpr int kKeysPerLane = 16;                    // one batch = 1024 keys per
 constexpr int kBatch = 64 * kKeysPerLane;
 constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
 
-// K-th largest of one 32-bit value per lane, with multiplicity (0 when fewer
-// than K lanes hold a non-zero value): the answer's bits are fixed from the
-// top, each by one ballot count, so there is no long cross-lane chain.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k) {
-    uint32_t prefix = 0;
-#pragma unroll
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = prefix | (1u << b);
-        if (__popcll(__ballot(m >= cand)) >= k) prefix = cand;
-    }
-    return prefix;
+// K-th largest of one 32-bit value per lane, with multiplicity: a descending
+// bitonic sort across the wave (DPP / permlane exchanges), then lane K - 1.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(m, lane), k - 1);
+}
+
+// Raw-bit screen for scores against a strictly positive FP32 threshold value
+// whose bits are `cut_bits` (> 0 as a signed integer): for every non-NaN x,
+// int(bits(x)) >= cut_bits  <=>  x >= threshold (negative values and -0 have
+// negative integer images).  Positive NaNs pass too; the exact order key
+// (NaN -> -inf) then rejects them.
+__device__ __forceinline__ bool raw_at_least(float x, int32_t cut_bits) {
+    return (int32_t)__float_as_uint(x) >= cut_bits;
 }
 
 struct WaveTopK {
@@ -371,27 +373,58 @@ struct WaveTopK {
         thr = readlane64(best, k - 1);
     }
 
-    // Merge survivors scratch[0..c) when k + c <= 64: every lane holds one of
-    // the k list keys or one survivor, counts how many of them beat its key
-    // (independent compares, no sorting network) and writes it at that rank.
-    __device__ __forceinline__ void rank_merge(uint64_t* scratch, int c) {
+    // Merge survivors src[0..c) when k + c <= 64: every lane holds one of the
+    // k list keys or one survivor and counts how many of them beat its key,
+    // reading all of them back through LDS broadcasts (16 bytes at a time,
+    // independent loads, no cross-lane chain); then it writes its key at that
+    // rank.  `stage` is this wave's 64-key LDS row; `out` receives the new
+    // list and may overlap src[0..k) (already consumed).
+    __device__ __forceinline__ void rank_merge(const uint64_t* src, int c, uint64_t* stage,
+                                               uint64_t* out) {
         const int m = k + c;
-        const uint64_t v = lane < k ? best : (lane < m ? scratch[lane - k] : 0);
+        const uint64_t v = lane < k ? best : (lane < m ? src[lane - k] : 0);
+        stage[lane] = v;
+        wave_lds_sync();
         int rank = 0;
+        const ulonglong2* pairs = reinterpret_cast<const ulonglong2*>(stage);
 #pragma unroll 4
-        for (int j = 0; j < m; ++j) rank += readlane64(v, j) > v ? 1 : 0;
-        wave_lds_sync();   // every survivor is read before the area is reused
-        if (lane < k) scratch[lane] = 0;
+        for (int j = 0; j < m; j += 2) {
+            const ulonglong2 q = pairs[j >> 1];
+            rank += (q.x > v ? 1 : 0) + (q.y > v ? 1 : 0);
+        }
+        if (lane < k) out[lane] = 0;
         wave_lds_sync();
-        if (rank < k && v != 0) scratch[rank] = v;
+        if (rank < k && v != 0) out[rank] = v;
         wave_lds_sync();
-        best = lane < k ? scratch[lane] : 0;
+        best = lane < k ? out[lane] : 0;
         thr = readlane64(best, k - 1);
+        wave_lds_sync();   // both rows are free again
     }
 
-    // Offer one batch: kKeysPerLane keys per lane (0 = nothing).  `scratch`
-    // is this wave's private LDS area of kBatch keys.
-    __device__ __forceinline__ void offer(const uint64_t (&key)[kKeysPerLane], uint64_t* scratch) {
+    // Merge `cnt` compacted survivors scratch[0..cnt) into the list.
+    __device__ __forceinline__ void merge_survivors(uint64_t* scratch, int cnt, uint64_t* ranks) {
+        const int room = 64 - k;
+        if (cnt <= kInsertMax) {
+            const uint64_t cand = lane < cnt ? scratch[lane] : 0;
+            for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
+        } else if (cnt <= 2 * room) {
+            // Pass p reads scratch[p room ..), then writes the list to
+            // scratch[0, k): k <= room, so only pass-0 survivors are overwritten.
+            for (int off = 0; off < cnt; off += room)
+                rank_merge(scratch + off, min(room, cnt - off), ranks, scratch);
+        } else {
+            for (int t = 0; t < cnt; t += 64) {
+                const uint64_t tile = t + lane < cnt ? scratch[t + lane] : 0;
+                best = wave_clean_desc(umax64(best, wave_sort<false>(tile, lane)), lane);
+            }
+            thr = readlane64(best, k - 1);
+        }
+    }
+
+    // Offer one batch of order keys, kKeysPerLane per lane (0 = nothing).
+    // `scratch` is this wave's LDS area of kBatch keys, `ranks` its 64-key row.
+    __device__ __forceinline__ void offer(const uint64_t (&key)[kKeysPerLane], uint64_t* scratch,
+                                          uint64_t* ranks) {
         uint64_t cut = thr;
         int cnt = 0;
 #pragma unroll
@@ -403,7 +436,7 @@ struct WaveTopK {
             uint32_t m = 0;
 #pragma unroll
             for (int j = 0; j < kKeysPerLane; ++j) m = max(m, (uint32_t)(key[j] >> 32));
-            const uint32_t t = wave_kth_largest(m, k);
+            const uint32_t t = wave_kth_largest(m, k, lane);
             const uint64_t tcut = ((uint64_t)t << 32) - 1;   // key > tcut <=> value image >= t
             if (t != 0 && tcut > cut) {
                 cut = tcut;
@@ -421,18 +454,57 @@ struct WaveTopK {
             base += __popcll(b);
         }
         wave_lds_sync();
-        if (cnt <= kInsertMax) {
-            const uint64_t cand = lane < cnt ? scratch[lane] : 0;
-            for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
-        } else if (k + cnt <= 64) {
-            rank_merge(scratch, cnt);
-        } else {
-            for (int t = 0; t < cnt; t += 64) {
-                const uint64_t tile = t + lane < cnt ? scratch[t + lane] : 0;
-                best = wave_clean_desc(umax64(best, wave_sort<false>(tile, lane)), lane);
-            }
-            thr = readlane64(best, k - 1);
+        merge_survivors(scratch, cnt, ranks);
+        wave_lds_sync();
+    }
+
+    // Offer one batch of raw scores: f[4u + j] sits at position
+    // wb + 4 (lane + 64 u) + j; positions at or past the end hold -inf.
+    // Once the cut is a positive value, scores are screened on their raw bits
+    // and only survivors get exact order keys; otherwise every score does.
+    __device__ __forceinline__ void offer_scores(const float (&f)[kKeysPerLane], int32_t wb,
+                                                 int32_t g1, uint64_t* scratch, uint64_t* ranks) {
+        uint32_t cut_ord = (uint32_t)(thr >> 32);          // value image of the K-th best
+        if (cut_ord <= 0x80000000u) {
+            // No positive cut yet: the K-th largest lane maximum bounds the
+            // batch's K best from below.
+            float m = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < kKeysPerLane; ++j) m = fmaxf(m, f[j]);
+            const uint32_t t = wave_kth_largest(order_image(m), k, lane);
+            cut_ord = max(cut_ord, t);
         }
+        if (cut_ord <= 0x80000000u) {   // cut at or below +0: exact keys for all
+            uint64_t key[kKeysPerLane];
+#pragma unroll
+            for (int u = 0; u < kKeysPerLane / 4; ++u) {
+                const int32_t e = wb + 4 * (lane + 64 * u);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint64_t kk = ((uint64_t)order_image(f[4 * u + j]) << 32) |
+                                        (uint32_t)~(uint32_t)(e + j);
+                    key[4 * u + j] = kk & (0ull - (uint64_t)(e + j < g1));
+                }
+            }
+            offer(key, scratch, ranks);
+            return;
+        }
+        const int32_t cut_bits = (int32_t)(cut_ord & 0x7fffffffu);
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysPerLane; ++j) {
+            const bool pass = raw_at_least(f[j], cut_bits);
+            if (__ballot(pass) == 0) continue;   // wave-uniform skip
+            const int32_t e = wb + 4 * (lane + 64 * (j >> 2)) + (j & 3);
+            const uint64_t kk = ((uint64_t)order_image(f[j]) << 32) | (uint32_t)~(uint32_t)e;
+            const bool take = pass && kk > thr;
+            const uint64_t b = __ballot(take);
+            if (take) scratch[base + lanes_below(b)] = kk;
+            base += __popcll(b);
+        }
+        if (base == 0) return;
+        wave_lds_sync();
+        merge_survivors(scratch, base, ranks);
         wave_lds_sync();
     }
 };
@@ -465,29 +537,14 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ scores, int
 #pragma unroll
     for (int u = 0; u < kKeysPerLane / 4; ++u) {
         const int32_t e = wb + 4 * (lane + 64 * u);
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float ninf = -__builtin_inff();
+        v[u] = make_float4(ninf, ninf, ninf, ninf);
         if (e + 4 <= g1) {
             v[u] = *reinterpret_cast<const float4*>(scores + e);
         } else {
             if (e + 0 < g1) v[u].x = scores[e + 0];
             if (e + 1 < g1) v[u].y = scores[e + 1];
             if (e + 2 < g1) v[u].z = scores[e + 2];
-        }
-    }
-}
-
-// Order keys of a loaded batch; positions at or past g1 become the sentinel.
-__device__ __forceinline__ void batch_keys(const float4 (&v)[kKeysPerLane / 4], int32_t wb,
-                                           int32_t g1, int lane, uint64_t (&key)[kKeysPerLane]) {
-#pragma unroll
-    for (int u = 0; u < kKeysPerLane / 4; ++u) {
-        const int32_t e = wb + 4 * (lane + 64 * u);
-        const int32_t rem = g1 - e;
-        const float f[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint64_t k = ((uint64_t)order_image(f[j]) << 32) | (uint32_t)~(uint32_t)(e + j);
-            key[4 * u + j] = k & (0ull - (uint64_t)(j < rem));
         }
     }
 }
@@ -513,10 +570,16 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
     load_batch(p.scores, g0 + wave * kBatch, g1, lane, v);
     for (int32_t rb = g0; rb < g1; rb += round) {
         const int32_t wb = rb + wave * kBatch;
-        uint64_t key[kKeysPerLane];
-        batch_keys(v, wb, g1, lane, key);
+        float f[kKeysPerLane];
+#pragma unroll
+        for (int u = 0; u < kKeysPerLane / 4; ++u) {
+            f[4 * u + 0] = v[u].x;
+            f[4 * u + 1] = v[u].y;
+            f[4 * u + 2] = v[u].z;
+            f[4 * u + 3] = v[u].w;
+        }
         if (rb + round < g1) load_batch(p.scores, wb + round, g1, lane, v);
-        st.offer(key, s_scratch[wave]);
+        st.offer_scores(f, wb, g1, s_scratch[wave], s_list[wave]);
     }
     block_merge(st, s_list, wave, waves);
 
@@ -526,8 +589,10 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
     }
 
     // 2. Publish this workgroup's K best; the last workgroup to arrive merges all.
-    if (wave == 0 && lane < p.k) p.partials[(int64_t)blockIdx.x * p.k + lane] = st.best;
-    __threadfence();
+    if (wave == 0) {
+        if (lane < p.k) p.partials[(int64_t)blockIdx.x * p.k + lane] = st.best;
+        __threadfence();   // release by the only wave that published anything
+    }
     __syncthreads();
     if (tid == 0) s_last = atomicAdd(p.counter, 1u) == (uint32_t)(p.groups - 1);
     __syncthreads();
@@ -545,7 +610,7 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
             const int64_t i = wb + lane + 64 * u;
             key[u] = i < total ? p.partials[i] : 0;
         }
-        mt.offer(key, s_scratch[wave]);
+        mt.offer(key, s_scratch[wave], s_list[wave]);
     }
     block_merge(mt, s_list, wave, waves);
     if (wave == 0) {

@@ -178,13 +178,16 @@ def run_single(w, torch, steps, warmup, use_graph=True):
 
 def cold_launches(lane, torch, n: int, flush_bytes: int = 1 << 30) -> np.ndarray:
     """Single preprocess launches (HIP events around one direct launch), each
-    after a >= 1 GiB write, so no cache level holds the frame or the tensor;
-    returns microseconds per launch (dispatch overhead included)."""
+    after reading a >= 1 GiB buffer, so no cache level holds the frame or the
+    tensor.  The evicting pass only reads (the buffer is written once, before
+    the loop), so no dirty lines are left behind for the timed launch to write
+    back.  Returns microseconds per launch (dispatch overhead included)."""
     from post_processing_amd import ws
-    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    flush = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
     out = []
-    for i in range(n):
-        flush.fill_(float(i))
+    for _ in range(n):
+        flush.sum()
         torch.cuda.synchronize()
         out.append(lane.time_stage(ws.STAGE_PREPROCESS, 1) * 1e3)
     del flush

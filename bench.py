@@ -83,11 +83,15 @@ def region(w) -> tuple[int, int]:
     return rw, rh
 
 
+TENSOR = {"dtype": "f32"}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
 def preprocess_bytes(w) -> dict:
-    """Source rows the taps touch (read whole) + the FP32 tensor, per launch."""
+    """Source rows the taps touch (read whole) + the tensor, per launch."""
     rw, rh = region(w)
     src = touched_rows(w.src_h, rh) * 3 * w.src_w * w.batch
-    out = 3 * w.dst_w * w.dst_h * 4 * w.batch
+    out = 3 * w.dst_w * w.dst_h * ELEM_BYTES[TENSOR["dtype"]] * w.batch
     return {"read": src, "write": out, "total": src + out}
 
 
@@ -123,7 +127,8 @@ def make_lane(w, torch, host_input=None, use_graph=True):
     host = mode != ws.INPUT_DEVICE
     dev = torch.device("cuda:0")
     keep = {}
-    keep["tensor"] = torch.empty((w.batch, 3, w.dst_h, w.dst_w), dtype=torch.float32, device=dev)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[TENSOR["dtype"]]
+    keep["tensor"] = torch.empty((w.batch, 3, w.dst_h, w.dst_w), dtype=tdt, device=dev)
     if w.k:
         keep["scores"] = torch.from_numpy(w.scores).to(dev)
     if not host:
@@ -133,7 +138,9 @@ def make_lane(w, torch, host_input=None, use_graph=True):
                          batch=w.batch, letterbox=(w.mode == 1), pad=w.pad, mean=w.mean,
                          std=w.std, num_scores=w.num_scores, k=w.k, input_mode=mode,
                          use_graph=use_graph, input_dev=keep.get("frames"),
-                         scores_dev=keep.get("scores"), tensor_dev=keep["tensor"], **KNOBS)
+                         scores_dev=keep.get("scores"), tensor_dev=keep["tensor"],
+                         tensor_dtype={"f32": ws.DTYPE_F32, "f16": ws.DTYPE_F16,
+                                       "bf16": ws.DTYPE_BF16}[TENSOR["dtype"]], **KNOBS)
     lane = ws.Lane(cfg)
     if host:
         lane.input_host_array()[...] = w.frames
@@ -295,6 +302,8 @@ def main(argv=None) -> int:
     ap.add_argument("--stage-launches", type=int, default=500)
     ap.add_argument("--rows-per-group", type=int, default=0, help="preprocess tuning knob (0 = auto)")
     ap.add_argument("--topk-chunk", type=int, default=0, help="Top-K tuning knob (0 = auto)")
+    ap.add_argument("--dtype", default="f32", choices=["f32", "f16", "bf16"],
+                    help="tensor element type (arithmetic stays FP32)")
     ap.add_argument("--input", default=None, choices=["device", "mapped", "copy"],
                     help="override the workload's input mode")
     ap.add_argument("--pixels-per-thread", type=int, default=0,
@@ -320,6 +329,7 @@ def main(argv=None) -> int:
 
     KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
                  pixels_per_thread=args.pixels_per_thread)
+    TENSOR["dtype"] = args.dtype
     if args.input:
         INPUT_OVERRIDE["mode"] = {"device": ws.INPUT_DEVICE, "mapped": ws.INPUT_MAPPED_HOST,
                                   "copy": ws.INPUT_COPY}[args.input]
@@ -382,7 +392,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if args.dtype == "f32" else f"f32->{args.dtype}",
         "data": "synthetic",
         "config": {"workload": w.name if name != "c5l" else "c5l_8lanes_1920x1080_to_224_mapped",
                    "frames_per_step": w.batch, "src": [w.src_w, w.src_h],

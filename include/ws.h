@@ -57,6 +57,13 @@ extern "C" {
                                    fixed device buffer (a DMA memcpy node of
                                    the graph), then preprocess reads HBM     */
 
+#define WS_DTYPE_F32   0        /* tensor element: IEEE single               */
+#define WS_DTYPE_F16   1        /* IEEE half, rounded to nearest even        */
+#define WS_DTYPE_BF16  2        /* bfloat16, rounded to nearest even         */
+
+#define WS_CHANNELS_RGB 0       /* producer bytes per pixel: R, G, B         */
+#define WS_CHANNELS_BGR 1       /* producer bytes per pixel: B, G, R         */
+
 #define WS_WAIT_SPIN   0        /* ws_wait polls the completion event        */
 #define WS_WAIT_BLOCK  1        /* ws_wait blocks in the runtime             */
 
@@ -83,7 +90,7 @@ typedef struct ws_lane_config {
     int32_t resize_mode;   /* WS_RESIZE_*                                     */
     int32_t input_mode;    /* WS_INPUT_*                                      */
     double  pad_value;     /* letterbox fill in byte units, 0..255            */
-    double  mean[3];       /* per RGB channel, unit range (0.485 ...)         */
+    double  mean[3];       /* per output channel R, G, B, unit range          */
     double  std[3];        /* per RGB channel, unit range, > 0                */
     int32_t num_scores;    /* N, 0..WS_MAX_SCORES; 0 = no Top-K stage        */
     int32_t k;             /* 1..min(WS_MAX_K, N) when N > 0                  */
@@ -97,23 +104,28 @@ typedef struct ws_lane_config {
      * graph. */
     const uint8_t *input_dev;  /* WS_INPUT_DEVICE only                         */
     const float   *scores_dev;
-    float         *tensor_dev;
+    void          *tensor_dev;   /* element type per tensor_dtype              */
     /* Tuning knobs (0 = automatic choice); they change speed, never results. */
     int32_t rows_per_group;    /* preprocess: output rows per workgroup        */
     int32_t topk_chunk;        /* Top-K: scores per workgroup (multiple of 1024) */
     int32_t pixels_per_thread; /* preprocess: output columns per thread: 1, 2, 4 */
+    /* Formats (0 = FP32 tensor from RGB bytes). */
+    int32_t tensor_dtype;      /* WS_DTYPE_*                                    */
+    int32_t channel_order;     /* WS_CHANNELS_*; the tensor planes are always
+                                  R, G, B                                       */
 } ws_lane_config;
 
 /* Stable views of a lane's buffers, valid from ws_create_lane to ws_destroy.
  *   input   uint8  [batch][src_h][src_w][3]   interleaved RGB, rows packed
- *   tensor  float  [batch][3][dst_h][dst_w]   planar R, G, B
+ *   tensor  [batch][3][dst_h][dst_w]          planar R, G, B; FP32, FP16
+ *                                             or BF16 per tensor_dtype
  *   scores  float  [num_scores]
  *   result  ws_topk_entry [k]                 mapped host memory, rank order
  */
 typedef struct ws_lane_view {
     uint8_t             *input_host;   /* producer's slot (mapped / copy mode), else NULL */
     const uint8_t       *input_dev;    /* address the preprocess kernel reads      */
-    float               *tensor_dev;
+    void                *tensor_dev;
     float               *scores_dev;   /* NULL when num_scores == 0                */
     const ws_topk_entry *result_host;  /* NULL when num_scores == 0                */
     size_t               input_bytes;

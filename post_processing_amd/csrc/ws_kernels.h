@@ -5,12 +5,16 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "ws.h"
+
 namespace ws {
 
 // Fused preprocess: RGB8 HWC frames -> resample -> normalise -> FP32 NCHW.
 struct PreParams {
     const uint8_t* src;     // [batch][src_h][src_w][3], 16-byte aligned base
-    float* dst;             // [batch][3][dst_h][dst_w]
+    void* dst;              // [batch][3][dst_h][dst_w] of FP32 / FP16 / BF16
+    int32_t dtype;          // WS_DTYPE_*
+    uint32_t shift[3];      // bit offset of output channel c's byte in a pixel
     int64_t frame_bytes;    // 3 * src_w * src_h
     int64_t total_bytes;    // batch * frame_bytes (bound of every staged load)
     int32_t src_w, src_h;

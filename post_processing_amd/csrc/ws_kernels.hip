@@ -2,14 +2,19 @@
 // (CDNA4, wave64).
 //
 // preprocess_kernel: WarpStream TRT article, fused-preprocess passage and its
-//   dataflow figure -- one pass from interleaved RGB8 to the planar FP32
-//   tensor: centre-aligned bilinear sample, x 1/255, (v - mean) / std, store
-//   into the destination channel plane; no intermediate image.  Letterbox
-//   placement per the yolo.cu README.
+//   dataflow figure -- one pass from interleaved 8-bit RGB (or BGR, the
+//   yolo.cu README's producer order) to the planar tensor: centre-aligned
+//   bilinear sample, x 1/255, (v - mean) / std, store into the destination
+//   channel plane; no intermediate image.  Letterbox placement per the
+//   yolo.cu README.  The tensor is FP32, or FP16 / BF16 (the article's
+//   precision-specialised preprocessing next step), computed in FP32 and
+//   rounded once to nearest even.
 // topk_kernel: the article's Top-K passage -- exact K best of FP32 scores,
 //   ties to the lower index, NaN as -inf, only K pairs leave the GPU; the
 //   large-label-space advice (hierarchical selection) gives the partial +
 //   merge split across workgroups.
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include "ws_kernels.h"
@@ -62,12 +67,40 @@ __device__ __forceinline__ uint32_t lds_rgb(const uint32_t* lds32, uint32_t byte
     return __builtin_amdgcn_alignbyte(hi, lo, byte & 3u);
 }
 
-__device__ __forceinline__ float chan(uint32_t rgb, int c) {
-    return (float)((rgb >> (8 * c)) & 0xffu);
+// Byte `shift / 8` of a pixel's 3-byte group as a float (v_cvt_f32_ubyteN).
+__device__ __forceinline__ float chan(uint32_t px, uint32_t shift) {
+    return (float)((px >> shift) & 0xffu);
 }
 
-template <int PX>
+// Output element types: FP32, or FP16 / BF16 rounded to nearest even.
+template <typename T> struct OutFormat;
+template <> struct OutFormat<float> {
+    using Pack2 = float2;
+    using Pack4 = float4;
+    __device__ static float cvt(float x) { return x; }
+    __device__ static float2 pack2(const float* v) { return make_float2(v[0], v[1]); }
+    __device__ static float4 pack4(const float* v) { return make_float4(v[0], v[1], v[2], v[3]); }
+};
+template <> struct OutFormat<__half> {
+    using Pack2 = uint32_t;
+    using Pack4 = uint2;
+    __device__ static uint16_t bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
+    __device__ static __half cvt(float x) { return __float2half_rn(x); }
+    __device__ static uint32_t pack2(const float* v) { return bits(v[0]) | ((uint32_t)bits(v[1]) << 16); }
+    __device__ static uint2 pack4(const float* v) { return make_uint2(pack2(v), pack2(v + 2)); }
+};
+template <> struct OutFormat<__hip_bfloat16> {
+    using Pack2 = uint32_t;
+    using Pack4 = uint2;
+    __device__ static uint16_t bits(float x) { return __bfloat16_as_ushort(__float2bfloat16(x)); }
+    __device__ static __hip_bfloat16 cvt(float x) { return __float2bfloat16(x); }
+    __device__ static uint32_t pack2(const float* v) { return bits(v[0]) | ((uint32_t)bits(v[1]) << 16); }
+    __device__ static uint2 pack4(const float* v) { return make_uint2(pack2(v), pack2(v + 2)); }
+};
+
+template <int PX, typename OutT>
 __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
+    using Fmt = OutFormat<OutT>;
     extern __shared__ uint4 lds_dyn[];
     __shared__ int64_t slot_addr[kMaxSlots];   // unaligned start of a staged row, -1 = none
 
@@ -137,7 +170,7 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
     const int q = p.threads_per_row;
     const int work = nrows * q;
     const int64_t plane = (int64_t)p.dst_h * p.dst_w;
-    float* const frame_out = p.dst + (int64_t)f * 3 * plane;
+    OutT* const frame_out = reinterpret_cast<OutT*>(p.dst) + (int64_t)f * 3 * plane;
     for (int wi = tid; wi < work; wi += nthr) {
         const int r = wi / q;
         const int x_first = PX * (wi - r * q);
@@ -165,8 +198,9 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
                 const uint32_t t11 = lds_rgb(lds32, base1 + o1);
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
-                    const float p00 = chan(t00, c), p01 = chan(t01, c);
-                    const float p10 = chan(t10, c), p11 = chan(t11, c);
+                    const uint32_t sh = p.shift[c];   // byte of output channel c
+                    const float p00 = chan(t00, sh), p01 = chan(t01, sh);
+                    const float p10 = chan(t10, sh), p11 = chan(t11, sh);
                     const float h0 = fmaf(tx.w, p01 - p00, p00);
                     const float h1 = fmaf(tx.w, p11 - p10, p10);
                     const float v = fmaf(wy, h1 - h0, h0);
@@ -177,24 +211,23 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
                 for (int c = 0; c < 3; ++c) out[c][i] = p.padv[c];
             }
         }
-        float* const row_out = frame_out + (int64_t)y * p.dst_w + x_first;
+        OutT* const row_out = frame_out + (int64_t)y * p.dst_w + x_first;
         if (p.vec) {   // dst_w % PX == 0: the PX columns are one aligned vector
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
                 if constexpr (PX == 4)
-                    *reinterpret_cast<float4*>(row_out + c * plane) =
-                        make_float4(out[c][0], out[c][1], out[c][2], out[c][3]);
+                    *reinterpret_cast<typename Fmt::Pack4*>(row_out + c * plane) = Fmt::pack4(out[c]);
                 else if constexpr (PX == 2)
-                    *reinterpret_cast<float2*>(row_out + c * plane) = make_float2(out[c][0], out[c][1]);
+                    *reinterpret_cast<typename Fmt::Pack2*>(row_out + c * plane) = Fmt::pack2(out[c]);
                 else
-                    row_out[c * plane] = out[c][0];
+                    row_out[c * plane] = Fmt::cvt(out[c][0]);
             }
         } else {
 #pragma unroll
             for (int c = 0; c < 3; ++c)
 #pragma unroll
                 for (int i = 0; i < PX; ++i)
-                    if (x_first + i < p.dst_w) row_out[c * plane + i] = out[c][i];
+                    if (x_first + i < p.dst_w) row_out[c * plane + i] = Fmt::cvt(out[c][i]);
         }
     }
 }
@@ -621,16 +654,45 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
 
 }  // namespace
 
-hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_bytes,
-                             hipStream_t stream) {
-    const dim3 g((unsigned)groups), b((unsigned)block);
+namespace {
+
+template <typename OutT>
+hipError_t launch_preprocess_as(const PreParams& p, dim3 g, dim3 b, unsigned lds,
+                                hipStream_t stream) {
     switch (p.pixels_per_thread) {
-        case 1: hipLaunchKernelGGL(preprocess_kernel<1>, g, b, (unsigned)lds_bytes, stream, p); break;
-        case 2: hipLaunchKernelGGL(preprocess_kernel<2>, g, b, (unsigned)lds_bytes, stream, p); break;
-        case 4: hipLaunchKernelGGL(preprocess_kernel<4>, g, b, (unsigned)lds_bytes, stream, p); break;
+        case 1: hipLaunchKernelGGL((preprocess_kernel<1, OutT>), g, b, lds, stream, p); break;
+        case 2: hipLaunchKernelGGL((preprocess_kernel<2, OutT>), g, b, lds, stream, p); break;
+        case 4: hipLaunchKernelGGL((preprocess_kernel<4, OutT>), g, b, lds, stream, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <typename OutT>
+hipError_t raise_lds_limit() {
+    const void* fns[3] = {reinterpret_cast<const void*>(preprocess_kernel<1, OutT>),
+                          reinterpret_cast<const void*>(preprocess_kernel<2, OutT>),
+                          reinterpret_cast<const void*>(preprocess_kernel<4, OutT>)};
+    for (const void* f : fns) {
+        const hipError_t e =
+            hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_bytes,
+                             hipStream_t stream) {
+    const dim3 g((unsigned)groups), b((unsigned)block);
+    switch (p.dtype) {
+        case WS_DTYPE_F32: return launch_preprocess_as<float>(p, g, b, (unsigned)lds_bytes, stream);
+        case WS_DTYPE_F16: return launch_preprocess_as<__half>(p, g, b, (unsigned)lds_bytes, stream);
+        case WS_DTYPE_BF16:
+            return launch_preprocess_as<__hip_bfloat16>(p, g, b, (unsigned)lds_bytes, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
@@ -640,15 +702,10 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
 }
 
 hipError_t set_kernel_attributes() {
-    const void* fns[3] = {reinterpret_cast<const void*>(preprocess_kernel<1>),
-                          reinterpret_cast<const void*>(preprocess_kernel<2>),
-                          reinterpret_cast<const void*>(preprocess_kernel<4>)};
-    for (const void* f : fns) {
-        const hipError_t e =
-            hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 1024);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    hipError_t e = raise_lds_limit<float>();
+    if (e == hipSuccess) e = raise_lds_limit<__half>();
+    if (e == hipSuccess) e = raise_lds_limit<__hip_bfloat16>();
+    return e;
 }
 
 }  // namespace ws

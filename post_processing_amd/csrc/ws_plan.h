@@ -129,6 +129,11 @@ inline int validate_config(const ws_lane_config* c) {
     if (c->pixels_per_thread != 0 && c->pixels_per_thread != 1 && c->pixels_per_thread != 2 &&
         c->pixels_per_thread != 4)
         return WS_E_INVALID_ARG;
+    if (c->tensor_dtype != WS_DTYPE_F32 && c->tensor_dtype != WS_DTYPE_F16 &&
+        c->tensor_dtype != WS_DTYPE_BF16)
+        return WS_E_INVALID_ARG;
+    if (c->channel_order != WS_CHANNELS_RGB && c->channel_order != WS_CHANNELS_BGR)
+        return WS_E_INVALID_ARG;
     return WS_OK;
 }
 
@@ -241,7 +246,8 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
 
     p->frame_bytes = (size_t)W * (size_t)H * 3u;
     p->input_bytes = p->frame_bytes * (size_t)c.batch;
-    p->tensor_bytes = (size_t)c.batch * 3u * (size_t)Dw * (size_t)Dh * sizeof(float);
+    p->tensor_bytes = (size_t)c.batch * 3u * (size_t)Dw * (size_t)Dh *
+                      (c.tensor_dtype == WS_DTYPE_F32 ? 4u : 2u);
     return WS_OK;
 }
 

@@ -37,7 +37,7 @@ struct ws_lane {
     uint8_t* in_host = nullptr;        // mapped input slot (host view)
     uint8_t* in_own = nullptr;         // lane-owned device input
     const uint8_t* in_dev = nullptr;   // what the kernel reads
-    float* tensor = nullptr;
+    void* tensor = nullptr;
     bool own_tensor = false;
     float* scores = nullptr;
     bool own_scores = false;
@@ -185,7 +185,7 @@ int build(ws_lane* L) {
     } else {
         void* d = nullptr;
         WS_TRY(dev_alloc(L, &d, P.tensor_bytes));
-        L->tensor = static_cast<float*>(d);
+        L->tensor = d;
         L->own_tensor = true;
     }
     if (c.num_scores > 0) {
@@ -234,6 +234,9 @@ int build(ws_lane* L) {
     q.rows_per_group = P.rows_per_group;
     q.groups_per_frame = P.groups_per_frame;
     q.vec = (c.dst_w % P.pixels_per_thread) == 0;
+    q.dtype = c.tensor_dtype;
+    for (int i = 0; i < 3; ++i)   // output plane i reads byte i (RGB) or byte 2 - i (BGR)
+        q.shift[i] = 8u * (uint32_t)(c.channel_order == WS_CHANNELS_BGR ? 2 - i : i);
     for (int i = 0; i < 3; ++i) {
         q.a[i] = (float)(1.0 / (255.0 * c.std[i]));
         q.b[i] = (float)(-c.mean[i] / c.std[i]);

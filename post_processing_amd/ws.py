@@ -35,6 +35,11 @@ RESIZE_LETTERBOX = 1
 INPUT_MAPPED_HOST = 0
 INPUT_DEVICE = 1
 INPUT_COPY = 2
+DTYPE_F32 = 0
+DTYPE_F16 = 1
+DTYPE_BF16 = 2
+CHANNELS_RGB = 0
+CHANNELS_BGR = 1
 WAIT_SPIN = 0
 WAIT_BLOCK = 1
 MAX_K = 32
@@ -58,6 +63,7 @@ class LaneConfig(Structure):
         ("input_dev", c_void_p), ("scores_dev", c_void_p), ("tensor_dev", c_void_p),
         ("rows_per_group", c_int32), ("topk_chunk", c_int32),
         ("pixels_per_thread", c_int32),
+        ("tensor_dtype", c_int32), ("channel_order", c_int32),
     ]
 
 
@@ -148,7 +154,8 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
                 mean=(0.0, 0.0, 0.0), std=(1.0, 1.0, 1.0), num_scores=0, k=0,
                 host_input=False, use_graph=True, wait_mode=WAIT_SPIN, device=0,
                 input_dev=None, scores_dev=None, tensor_dev=None, rows_per_group=0,
-                topk_chunk=0, pixels_per_thread=0, input_mode=None) -> LaneConfig:
+                topk_chunk=0, pixels_per_thread=0, input_mode=None, tensor_dtype=DTYPE_F32,
+                channel_order=CHANNELS_RGB) -> LaneConfig:
     c = LaneConfig()
     c.device = device
     c.batch = batch
@@ -170,6 +177,8 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
     c.rows_per_group = rows_per_group
     c.topk_chunk = topk_chunk
     c.pixels_per_thread = pixels_per_thread
+    c.tensor_dtype = tensor_dtype
+    c.channel_order = channel_order
     return c
 
 

@@ -19,7 +19,8 @@ def oracle_outputs(w: wl.Workload):
 class Run:
     """A lane built for a workload, with borrowed torch buffers kept alive."""
 
-    def __init__(self, w: wl.Workload, host_input=None, use_graph=True, input_mode=None, **knobs):
+    def __init__(self, w: wl.Workload, host_input=None, use_graph=True, input_mode=None,
+                 tensor_dtype=ws.DTYPE_F32, **knobs):
         import torch
         self.w = w
         self.host_input = w.host_input if host_input is None else host_input
@@ -27,7 +28,9 @@ class Run:
             input_mode = ws.INPUT_MAPPED_HOST if self.host_input else ws.INPUT_DEVICE
         self.host_input = input_mode != ws.INPUT_DEVICE
         dev = torch.device("cuda:0")
-        self.tensor = torch.empty((w.batch, 3, w.dst_h, w.dst_w), dtype=torch.float32, device=dev)
+        tdt = {ws.DTYPE_F32: torch.float32, ws.DTYPE_F16: torch.float16,
+               ws.DTYPE_BF16: torch.bfloat16}[tensor_dtype]
+        self.tensor = torch.empty((w.batch, 3, w.dst_h, w.dst_w), dtype=tdt, device=dev)
         self.tensor.fill_(float("nan"))
         self.scores = None
         if w.k:
@@ -39,7 +42,7 @@ class Run:
         cfg = ws.make_config(src_w=w.src_w, src_h=w.src_h, dst_w=w.dst_w, dst_h=w.dst_h,
                              batch=w.batch, letterbox=(w.mode == wl.LETTERBOX), pad=w.pad,
                              mean=w.mean, std=w.std, num_scores=w.num_scores, k=w.k,
-                             input_mode=input_mode, use_graph=use_graph,
+                             input_mode=input_mode, use_graph=use_graph, tensor_dtype=tensor_dtype,
                              input_dev=self.frames, scores_dev=self.scores,
                              tensor_dev=self.tensor, **knobs)
         self.lane = ws.Lane(cfg)
@@ -51,7 +54,7 @@ class Run:
         return ms
 
     def outputs(self):
-        t = self.tensor.cpu().numpy()
+        t = self.tensor.float().cpu().numpy()
         tk = self.lane.result() if self.w.k else None
         return t, tk
 
@@ -66,6 +69,23 @@ def assert_tensor_close(got, ref, tol=TOL):
     worst = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= tol, f"max |err| {err.max():.3e} at {worst}"
     return float(err.max())
+
+
+MANTISSA_BITS = {"f16": 10, "bf16": 7}
+
+
+def assert_rounded_close(got, ref, fmt, slack=2e-6):
+    """A 16-bit tensor: every element within half an ulp of the output format
+    (at the exact value) plus the FP32 arithmetic's slack of the exact value,
+    i.e. the correctly rounded value or, at a near-tie, its neighbour."""
+    assert got.shape == ref.shape
+    assert np.isfinite(got).all(), "non-finite values in the tensor"
+    mag = np.maximum(np.abs(ref), 2.0 ** -14)
+    ulp = 2.0 ** (np.floor(np.log2(mag)) - MANTISSA_BITS[fmt])
+    err = np.abs(got.astype(np.float64) - ref)
+    bad = err > 0.5 * ulp + slack
+    assert not bad.any(), f"{int(bad.sum())} elements off; worst {err[bad].max():.3e}"
+    return float((err / ulp).max())
 
 
 def assert_topk_exact(got, ref):

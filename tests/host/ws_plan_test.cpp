@@ -67,6 +67,8 @@ static int selftest() {
     BAD(rows_per_group, 65);
     BAD(topk_chunk, 1000);
     BAD(pixels_per_thread, 3);
+    BAD(tensor_dtype, 3);
+    BAD(channel_order, 2);
     BAD(num_scores, WS_MAX_SCORES + 1);
     {
         ws_lane_config b = good();

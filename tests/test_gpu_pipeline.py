@@ -11,7 +11,8 @@ from oracle import preprocess_batch, topk
 from post_processing_amd import workloads as wl
 from post_processing_amd import ws
 
-from gpu_util import Run, assert_tensor_close, assert_topk_exact, oracle_outputs
+from gpu_util import (Run, assert_rounded_close, assert_tensor_close, assert_topk_exact,
+                      oracle_outputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +75,60 @@ def test_input_modes_agree_bitwise(gpu_lib):
     finally:
         for r in runs:
             r.close()
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_reduced_precision_tensor(gpu_lib, name, fmt):
+    w = wl.ALL_CONFIGS[name]()
+    ref, rtk = oracle_outputs(w)
+    dt = ws.DTYPE_F16 if fmt == "f16" else ws.DTYPE_BF16
+    r = Run(w, host_input=False, tensor_dtype=dt)
+    try:
+        r.run()
+        t, tk = r.outputs()
+        worst = assert_rounded_close(t, ref, fmt)
+        assert_topk_exact(tk, rtk)
+        print(f"{name} {fmt}: worst error {worst:.3f} ulp")
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_reduced_precision_small_shapes(gpu_lib, seed, fmt):
+    w = wl.random_small(100 + seed, letterbox=bool(seed % 2))
+    ref, _ = oracle_outputs(w)
+    r = Run(w, host_input=False, tensor_dtype=ws.DTYPE_F16 if fmt == "f16" else ws.DTYPE_BF16,
+            pixels_per_thread=(1, 2, 4)[seed % 3])
+    try:
+        r.run()
+        assert_rounded_close(r.outputs()[0], ref, fmt)
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_bgr_input(gpu_lib, name):
+    # A BGR producer's frame is the RGB frame with its channel axis reversed;
+    # the BGR lane must give the RGB lane's tensor bit for bit, and the oracle's.
+    w = wl.ALL_CONFIGS[name]()
+    ref, rtk = oracle_outputs(w)
+    bgr = wl.Workload(w.name + "_bgr", w.src_w, w.src_h, w.dst_w, w.dst_h, w.mode, w.mean, w.std,
+                      w.pad, w.k, np.ascontiguousarray(w.frames[..., ::-1]), w.scores)
+    a = Run(w, host_input=False)
+    b = Run(bgr, host_input=False, channel_order=ws.CHANNELS_BGR)
+    try:
+        a.run()
+        b.run()
+        ta, _ = a.outputs()
+        tb, tk = b.outputs()
+        np.testing.assert_array_equal(ta.view(np.uint32), tb.view(np.uint32))
+        assert_tensor_close(tb, ref)
+        assert_topk_exact(tk, rtk)
+    finally:
+        a.close()
+        b.close()
 
 
 def test_throughput_batch_parity(gpu_lib):

@@ -70,7 +70,7 @@ def test_config_struct_layout():
     # pointers after the int32 fields, 136 bytes total.
     import ctypes
     from post_processing_amd import ws
-    assert ctypes.sizeof(ws.LaneConfig) == 144
+    assert ctypes.sizeof(ws.LaneConfig) == 152
     assert ws.LaneConfig.pad_value.offset == 32
     assert ws.LaneConfig.input_dev.offset == 104
     assert ctypes.sizeof(ws.TopkEntry) == 8

@@ -308,6 +308,8 @@ def main(argv=None) -> int:
                     help="override the workload's input mode")
     ap.add_argument("--pixels-per-thread", type=int, default=0,
                     help="preprocess tuning knob: 1, 2 or 4 (0 = auto)")
+    ap.add_argument("--autotune", action="store_true",
+                    help="let each lane time candidate launch geometries at create")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
     ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
@@ -328,7 +330,7 @@ def main(argv=None) -> int:
     ws.load()
 
     KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
-                 pixels_per_thread=args.pixels_per_thread)
+                 pixels_per_thread=args.pixels_per_thread, autotune=args.autotune)
     TENSOR["dtype"] = args.dtype
     if args.input:
         INPUT_OVERRIDE["mode"] = {"device": ws.INPUT_DEVICE, "mapped": ws.INPUT_MAPPED_HOST,

@@ -113,6 +113,9 @@ typedef struct ws_lane_config {
     int32_t tensor_dtype;      /* WS_DTYPE_*                                    */
     int32_t channel_order;     /* WS_CHANNELS_*; the tensor planes are always
                                   R, G, B                                       */
+    int32_t autotune;          /* 1 = time candidate launch geometries on the
+                                  lane's buffers at create and keep the fastest
+                                  (knobs above then only seed the search)       */
 } ws_lane_config;
 
 /* Stable views of a lane's buffers, valid from ws_create_lane to ws_destroy.

@@ -27,6 +27,7 @@ typedef struct ws_lane_plan {
     int32_t topk_block;       /* Top-K threads per workgroup                 */
     int32_t topk_chunk;       /* scores per Top-K workgroup                  */
     int32_t graph_nodes;      /* kernel nodes in the captured graph          */
+    int32_t pixels_per_thread;/* output pixels per preprocess thread         */
 } ws_lane_plan;
 
 /* Fill *plan for lane.  Returns WS_OK or WS_E_INVALID_ARG (NULL). */

@@ -134,6 +134,7 @@ inline int validate_config(const ws_lane_config* c) {
         return WS_E_INVALID_ARG;
     if (c->channel_order != WS_CHANNELS_RGB && c->channel_order != WS_CHANNELS_BGR)
         return WS_E_INVALID_ARG;
+    if (c->autotune != 0 && c->autotune != 1) return WS_E_INVALID_ARG;
     return WS_OK;
 }
 

@@ -8,6 +8,7 @@
 // allocation and its absence is reported, not ignored.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cstring>
@@ -126,6 +127,136 @@ int mapped_alloc(ws_lane* L, void** host, void** dev, size_t bytes) {
         if (e_ != hipSuccess) return fail(L, e_, (code));  \
     } while (0)
 
+// Kernel parameters from the lane's config and current plan (fixed for the
+// lane's lifetime once construction ends).
+void fill_params(ws_lane* L) {
+    const ws_lane_config& c = L->cfg;
+    const ws::Plan& P = L->plan;
+    ws::PreParams& q = L->pre;
+    q.src = L->in_dev;
+    q.dst = L->tensor;
+    q.frame_bytes = (int64_t)P.frame_bytes;
+    q.total_bytes = (int64_t)P.input_bytes;
+    q.src_w = c.src_w;
+    q.src_h = c.src_h;
+    q.dst_w = c.dst_w;
+    q.dst_h = c.dst_h;
+    q.left = P.region.left;
+    q.top = P.region.top;
+    q.reg_w = P.region.w;
+    q.reg_h = P.region.h;
+    q.inv_den_x = (float)(1.0 / (2.0 * P.region.w));
+    q.inv_den_y = (float)(1.0 / (2.0 * P.region.h));
+    q.span_lo = (int32_t)P.span_lo;
+    q.slot_chunks = P.slot_bytes / 16;
+    q.pixels_per_thread = P.pixels_per_thread;
+    q.threads_per_row = P.threads_per_row;
+    q.rows_per_group = P.rows_per_group;
+    q.groups_per_frame = P.groups_per_frame;
+    q.vec = (c.dst_w % P.pixels_per_thread) == 0;
+    q.dtype = c.tensor_dtype;
+    for (int i = 0; i < 3; ++i)   // output plane i reads byte i (RGB) or byte 2 - i (BGR)
+        q.shift[i] = 8u * (uint32_t)(c.channel_order == WS_CHANNELS_BGR ? 2 - i : i);
+    for (int i = 0; i < 3; ++i) {
+        q.a[i] = (float)(1.0 / (255.0 * c.std[i]));
+        q.b[i] = (float)(-c.mean[i] / c.std[i]);
+        q.padv[i] = (float)((c.pad_value / 255.0 - c.mean[i]) / c.std[i]);
+    }
+    ws::TopkParams& t = L->tk;
+    t.scores = L->scores;
+    t.n = c.num_scores;
+    t.k = c.k;
+    t.chunk = P.topk_chunk;
+    t.groups = P.topk_groups;
+    t.waves = P.topk_waves;
+    t.partials = L->partials;
+    t.counter = L->counter;
+    t.result = L->res_dev;
+}
+
+// Microseconds per launch of one stage on the lane's stream: the best of
+// three timed runs of `reps` back-to-back launches (after two untimed
+// launches), or a huge value on error.
+double time_stage_us(ws_lane* L, int stage, int reps) {
+    hipError_t e = hipSuccess;
+    auto launch = [&]() {
+        return stage == WS_STAGE_PREPROCESS
+                   ? ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
+                                           L->plan.lds_bytes, L->stream)
+                   : ws::launch_topk(L->tk, L->stream);
+    };
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = launch();
+    double best = 1e30;
+    for (int trial = 0; trial < 3 && e == hipSuccess; ++trial) {
+        e = hipEventRecord(L->ev_start, L->stream);
+        for (int i = 0; i < reps && e == hipSuccess; ++i) e = launch();
+        if (e == hipSuccess) e = hipEventRecord(L->ev_done, L->stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(L->stream);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, L->ev_start, L->ev_done);
+        if (e == hipSuccess) best = std::min(best, 1e3 * (double)ms / reps);
+    }
+    return e == hipSuccess ? best : 1e30;
+}
+
+// Construction-time autotune: time a few launch geometries on this lane's own
+// buffers and keep the fastest (yolo.cu times its tile choices once at
+// startup).  Geometry changes speed only, never results.  A candidate must
+// beat the current choice by 2% to replace it, so timing noise does not move
+// the lane off the heuristic plan.
+int autotune(ws_lane* L) {
+    const ws_lane_config base = L->cfg;
+    const int kReps = 10;
+    ws::Plan best = L->plan;
+    double best_us = time_stage_us(L, WS_STAGE_PREPROCESS, kReps);
+    for (int px : {1, 2, 4}) {
+        for (int rows : {1, 2, 4}) {
+            ws_lane_config c = base;
+            c.pixels_per_thread = px;
+            c.rows_per_group = rows;
+            ws::Plan p;
+            if (ws::make_plan(c, &p) != WS_OK) continue;
+            L->plan.pixels_per_thread = p.pixels_per_thread;
+            L->plan.threads_per_row = p.threads_per_row;
+            L->plan.rows_per_group = p.rows_per_group;
+            L->plan.pre_block = p.pre_block;
+            L->plan.pre_groups = p.pre_groups;
+            L->plan.groups_per_frame = p.groups_per_frame;
+            L->plan.lds_bytes = p.lds_bytes;
+            fill_params(L);
+            const double us = time_stage_us(L, WS_STAGE_PREPROCESS, kReps);
+            if (us < 0.98 * best_us) {
+                best_us = us;
+                best = L->plan;
+            }
+        }
+    }
+    L->plan = best;
+    fill_params(L);
+    if (base.num_scores > ws::kTopkSingleGroupMax) {
+        double best_tk = time_stage_us(L, WS_STAGE_TOPK, kReps);
+        for (int chunk : {1024, 2048, 4096, 8192, 16384}) {
+            ws_lane_config c = base;
+            c.topk_chunk = chunk;
+            ws::Plan p;
+            if (ws::make_plan(c, &p) != WS_OK) continue;
+            L->plan.topk_chunk = p.topk_chunk;
+            L->plan.topk_waves = p.topk_waves;
+            L->plan.topk_groups = p.topk_groups;
+            fill_params(L);
+            const double us = time_stage_us(L, WS_STAGE_TOPK, kReps);
+            if (us < 0.98 * best_tk) {
+                best_tk = us;
+                best = L->plan;
+            }
+        }
+        L->plan = best;
+        fill_params(L);
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? WS_OK : fail(L, e, WS_E_HIP);
+}
+
 int build(ws_lane* L) {
     const ws_lane_config& c = L->cfg;
     ws::Plan& P = L->plan;
@@ -203,7 +334,9 @@ int build(ws_lane* L) {
         L->res_host = static_cast<ws_topk_entry*>(h);
         L->res_dev = static_cast<uint2*>(d);
         void* pp = nullptr;
-        WS_TRY(dev_alloc(L, &pp, (size_t)P.topk_groups * (size_t)c.k * sizeof(uint64_t)));
+        // Room for the most workgroups any geometry can use (1024-score chunks).
+        const size_t max_groups = ((size_t)c.num_scores + 1023) / 1024;
+        WS_TRY(dev_alloc(L, &pp, max_groups * (size_t)c.k * sizeof(uint64_t)));
         L->partials = static_cast<uint64_t*>(pp);
         void* cn = nullptr;
         WS_TRY(dev_alloc(L, &cn, sizeof(uint32_t)));
@@ -211,53 +344,15 @@ int build(ws_lane* L) {
         WS_HIP(hipMemset(L->counter, 0, sizeof(uint32_t)), WS_E_HIP);
     }
 
-    // ---- kernel parameters (fixed for the lane's lifetime) ----------------
-    ws::PreParams& q = L->pre;
-    q.src = L->in_dev;
-    q.dst = L->tensor;
-    q.frame_bytes = (int64_t)P.frame_bytes;
-    q.total_bytes = (int64_t)P.input_bytes;
-    q.src_w = c.src_w;
-    q.src_h = c.src_h;
-    q.dst_w = c.dst_w;
-    q.dst_h = c.dst_h;
-    q.left = P.region.left;
-    q.top = P.region.top;
-    q.reg_w = P.region.w;
-    q.reg_h = P.region.h;
-    q.inv_den_x = (float)(1.0 / (2.0 * P.region.w));
-    q.inv_den_y = (float)(1.0 / (2.0 * P.region.h));
-    q.span_lo = (int32_t)P.span_lo;
-    q.slot_chunks = P.slot_bytes / 16;
-    q.pixels_per_thread = P.pixels_per_thread;
-    q.threads_per_row = P.threads_per_row;
-    q.rows_per_group = P.rows_per_group;
-    q.groups_per_frame = P.groups_per_frame;
-    q.vec = (c.dst_w % P.pixels_per_thread) == 0;
-    q.dtype = c.tensor_dtype;
-    for (int i = 0; i < 3; ++i)   // output plane i reads byte i (RGB) or byte 2 - i (BGR)
-        q.shift[i] = 8u * (uint32_t)(c.channel_order == WS_CHANNELS_BGR ? 2 - i : i);
-    for (int i = 0; i < 3; ++i) {
-        q.a[i] = (float)(1.0 / (255.0 * c.std[i]));
-        q.b[i] = (float)(-c.mean[i] / c.std[i]);
-        q.padv[i] = (float)((c.pad_value / 255.0 - c.mean[i]) / c.std[i]);
-    }
-    ws::TopkParams& t = L->tk;
-    t.scores = L->scores;
-    t.n = c.num_scores;
-    t.k = c.k;
-    t.chunk = P.topk_chunk;
-    t.groups = P.topk_groups;
-    t.waves = P.topk_waves;
-    t.partials = L->partials;
-    t.counter = L->counter;
-    t.result = L->res_dev;
+    fill_params(L);
     L->nodes = 1 + (c.num_scores > 0 ? 1 : 0) + (c.input_mode == WS_INPUT_COPY ? 1 : 0);
 
     // ---- stream, events, warm-up, capture ---------------------------------
     WS_HIP(hipStreamCreateWithFlags(&L->stream, hipStreamNonBlocking), WS_E_HIP);
     WS_HIP(hipEventCreate(&L->ev_start), WS_E_HIP);
     WS_HIP(hipEventCreate(&L->ev_done), WS_E_HIP);
+
+    if (c.autotune) WS_TRY(autotune(L));
 
     // Warm-up outside capture: loads code objects and touches every buffer.
     WS_HIP(launch_all(L), WS_E_HIP);
@@ -363,6 +458,7 @@ int ws_lane_describe(const ws_lane* L, ws_lane_plan* plan) {
     plan->topk_block = 64 * L->plan.topk_waves;
     plan->topk_chunk = L->plan.topk_chunk;
     plan->graph_nodes = L->nodes;
+    plan->pixels_per_thread = L->plan.pixels_per_thread;
     return WS_OK;
 }
 

@@ -63,7 +63,7 @@ class LaneConfig(Structure):
         ("input_dev", c_void_p), ("scores_dev", c_void_p), ("tensor_dev", c_void_p),
         ("rows_per_group", c_int32), ("topk_chunk", c_int32),
         ("pixels_per_thread", c_int32),
-        ("tensor_dtype", c_int32), ("channel_order", c_int32),
+        ("tensor_dtype", c_int32), ("channel_order", c_int32), ("autotune", c_int32),
     ]
 
 
@@ -80,7 +80,7 @@ class LanePlan(Structure):
     _fields_ = [
         ("pre_groups", c_int32), ("pre_block", c_int32), ("rows_per_group", c_int32),
         ("pre_lds_bytes", c_int32), ("topk_groups", c_int32), ("topk_block", c_int32),
-        ("topk_chunk", c_int32), ("graph_nodes", c_int32),
+        ("topk_chunk", c_int32), ("graph_nodes", c_int32), ("pixels_per_thread", c_int32),
     ]
 
 
@@ -155,7 +155,7 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
                 host_input=False, use_graph=True, wait_mode=WAIT_SPIN, device=0,
                 input_dev=None, scores_dev=None, tensor_dev=None, rows_per_group=0,
                 topk_chunk=0, pixels_per_thread=0, input_mode=None, tensor_dtype=DTYPE_F32,
-                channel_order=CHANNELS_RGB) -> LaneConfig:
+                channel_order=CHANNELS_RGB, autotune=False) -> LaneConfig:
     c = LaneConfig()
     c.device = device
     c.batch = batch
@@ -179,6 +179,7 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
     c.pixels_per_thread = pixels_per_thread
     c.tensor_dtype = tensor_dtype
     c.channel_order = channel_order
+    c.autotune = 1 if autotune else 0
     return c
 
 

@@ -4,10 +4,13 @@
 //   ws_plan_test letterbox W H Dw Dh -> "left top w h"
 //   ws_plan_test plan <cfg fields>   -> launch geometry
 //   ws_plan_test selftest            -> config validation + state machine checks
+//   ws_plan_test layout              -> "struct field offset" for the ABI structs
+#include <cstddef>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
+#include "ws_bench.h"
 #include "ws_plan.h"
 
 static int failures = 0;
@@ -69,6 +72,7 @@ static int selftest() {
     BAD(pixels_per_thread, 3);
     BAD(tensor_dtype, 3);
     BAD(channel_order, 2);
+    BAD(autotune, 2);
     BAD(num_scores, WS_MAX_SCORES + 1);
     {
         ws_lane_config b = good();
@@ -131,7 +135,58 @@ static int selftest() {
     return failures == 0 ? 0 : 1;
 }
 
+static int layout() {
+    std::printf("ws_lane_config sizeof %zu\n", sizeof(ws_lane_config));
+    std::printf("ws_lane_config device %zu\n", offsetof(ws_lane_config, device));
+    std::printf("ws_lane_config batch %zu\n", offsetof(ws_lane_config, batch));
+    std::printf("ws_lane_config src_w %zu\n", offsetof(ws_lane_config, src_w));
+    std::printf("ws_lane_config src_h %zu\n", offsetof(ws_lane_config, src_h));
+    std::printf("ws_lane_config dst_w %zu\n", offsetof(ws_lane_config, dst_w));
+    std::printf("ws_lane_config dst_h %zu\n", offsetof(ws_lane_config, dst_h));
+    std::printf("ws_lane_config resize_mode %zu\n", offsetof(ws_lane_config, resize_mode));
+    std::printf("ws_lane_config input_mode %zu\n", offsetof(ws_lane_config, input_mode));
+    std::printf("ws_lane_config pad_value %zu\n", offsetof(ws_lane_config, pad_value));
+    std::printf("ws_lane_config mean %zu\n", offsetof(ws_lane_config, mean));
+    std::printf("ws_lane_config std %zu\n", offsetof(ws_lane_config, std));
+    std::printf("ws_lane_config num_scores %zu\n", offsetof(ws_lane_config, num_scores));
+    std::printf("ws_lane_config k %zu\n", offsetof(ws_lane_config, k));
+    std::printf("ws_lane_config use_graph %zu\n", offsetof(ws_lane_config, use_graph));
+    std::printf("ws_lane_config wait_mode %zu\n", offsetof(ws_lane_config, wait_mode));
+    std::printf("ws_lane_config input_dev %zu\n", offsetof(ws_lane_config, input_dev));
+    std::printf("ws_lane_config scores_dev %zu\n", offsetof(ws_lane_config, scores_dev));
+    std::printf("ws_lane_config tensor_dev %zu\n", offsetof(ws_lane_config, tensor_dev));
+    std::printf("ws_lane_config rows_per_group %zu\n", offsetof(ws_lane_config, rows_per_group));
+    std::printf("ws_lane_config topk_chunk %zu\n", offsetof(ws_lane_config, topk_chunk));
+    std::printf("ws_lane_config pixels_per_thread %zu\n", offsetof(ws_lane_config, pixels_per_thread));
+    std::printf("ws_lane_config tensor_dtype %zu\n", offsetof(ws_lane_config, tensor_dtype));
+    std::printf("ws_lane_config channel_order %zu\n", offsetof(ws_lane_config, channel_order));
+    std::printf("ws_lane_config autotune %zu\n", offsetof(ws_lane_config, autotune));
+    std::printf("ws_lane_view sizeof %zu\n", sizeof(ws_lane_view));
+    std::printf("ws_lane_view input_host %zu\n", offsetof(ws_lane_view, input_host));
+    std::printf("ws_lane_view input_dev %zu\n", offsetof(ws_lane_view, input_dev));
+    std::printf("ws_lane_view tensor_dev %zu\n", offsetof(ws_lane_view, tensor_dev));
+    std::printf("ws_lane_view scores_dev %zu\n", offsetof(ws_lane_view, scores_dev));
+    std::printf("ws_lane_view result_host %zu\n", offsetof(ws_lane_view, result_host));
+    std::printf("ws_lane_view input_bytes %zu\n", offsetof(ws_lane_view, input_bytes));
+    std::printf("ws_lane_view tensor_bytes %zu\n", offsetof(ws_lane_view, tensor_bytes));
+    std::printf("ws_topk_entry sizeof %zu\n", sizeof(ws_topk_entry));
+    std::printf("ws_topk_entry score %zu\n", offsetof(ws_topk_entry, score));
+    std::printf("ws_topk_entry index %zu\n", offsetof(ws_topk_entry, index));
+    std::printf("ws_lane_plan sizeof %zu\n", sizeof(ws_lane_plan));
+    std::printf("ws_lane_plan pre_groups %zu\n", offsetof(ws_lane_plan, pre_groups));
+    std::printf("ws_lane_plan pre_block %zu\n", offsetof(ws_lane_plan, pre_block));
+    std::printf("ws_lane_plan rows_per_group %zu\n", offsetof(ws_lane_plan, rows_per_group));
+    std::printf("ws_lane_plan pre_lds_bytes %zu\n", offsetof(ws_lane_plan, pre_lds_bytes));
+    std::printf("ws_lane_plan topk_groups %zu\n", offsetof(ws_lane_plan, topk_groups));
+    std::printf("ws_lane_plan topk_block %zu\n", offsetof(ws_lane_plan, topk_block));
+    std::printf("ws_lane_plan topk_chunk %zu\n", offsetof(ws_lane_plan, topk_chunk));
+    std::printf("ws_lane_plan graph_nodes %zu\n", offsetof(ws_lane_plan, graph_nodes));
+    std::printf("ws_lane_plan pixels_per_thread %zu\n", offsetof(ws_lane_plan, pixels_per_thread));
+    return 0;
+}
+
 int main(int argc, char** argv) {
+    if (argc == 2 && !std::strcmp(argv[1], "layout")) return layout();
     if (argc >= 2 && !std::strcmp(argv[1], "selftest")) return selftest();
     if (argc == 4 && !std::strcmp(argv[1], "taps")) {
         const long S = std::atol(argv[2]), R = std::atol(argv[3]);

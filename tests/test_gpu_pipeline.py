@@ -173,6 +173,33 @@ def test_launch_geometry_does_not_change_results(gpu_lib, name, rows, px):
         r.close()
 
 
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_autotuned_lane_matches_default_lane(gpu_lib, name):
+    # The autotuner only picks launch geometry: its lane must reproduce the
+    # default lane bit for bit, and the oracle to the usual bound.
+    w = wl.ALL_CONFIGS[name]()
+    ref, rtk = oracle_outputs(w)
+    a = Run(w, host_input=False)
+    b = Run(w, host_input=False, autotune=True)
+    try:
+        plan = b.lane.plan()
+        assert plan["pixels_per_thread"] in (1, 2, 4)
+        assert plan["rows_per_group"] in (1, 2, 4)
+        for _ in range(2):
+            a.run()
+            b.run()
+            ta, tka = a.outputs()
+            tb, tkb = b.outputs()
+            np.testing.assert_array_equal(ta.view(np.uint32), tb.view(np.uint32))
+            assert_tensor_close(tb, ref)
+            if w.k:
+                assert_topk_exact(tkb, rtk)
+                assert_topk_exact(tka, rtk)
+    finally:
+        a.close()
+        b.close()
+
+
 def test_rows_per_group_beyond_lds_rejected(gpu_lib):
     # 7 staged row pairs of 3840-pixel rows need ~161 KB of LDS: more than a
     # workgroup may hold, so the lane refuses the plan instead of launching it.

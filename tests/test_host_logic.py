@@ -65,13 +65,21 @@ def test_library_exports_declared_symbols():
     assert not missing, missing
 
 
-def test_config_struct_layout():
-    # LaneConfig must match the C layout (x86-64 SysV): doubles 8-aligned,
-    # pointers after the int32 fields, 136 bytes total.
+def test_abi_struct_layout(driver):
+    # The ctypes mirrors must match the C compiler's layout of include/ws.h
+    # field by field (x86-64 SysV: doubles and pointers 8-aligned).
     import ctypes
     from post_processing_amd import ws
-    assert ctypes.sizeof(ws.LaneConfig) == 152
-    assert ws.LaneConfig.pad_value.offset == 32
-    assert ws.LaneConfig.input_dev.offset == 104
-    assert ctypes.sizeof(ws.TopkEntry) == 8
-    assert ctypes.sizeof(ws.LaneView) == 56
+    mirrors = {"ws_lane_config": ws.LaneConfig, "ws_lane_view": ws.LaneView,
+               "ws_topk_entry": ws.TopkEntry, "ws_lane_plan": ws.LanePlan}
+    seen = {name: set() for name in mirrors}
+    for line in run(driver, "layout").splitlines():
+        struct, field, value = line.split()
+        mirror = mirrors[struct]
+        if field == "sizeof":
+            assert ctypes.sizeof(mirror) == int(value), struct
+        else:
+            assert getattr(mirror, field).offset == int(value), (struct, field)
+            seen[struct].add(field)
+    for name, mirror in mirrors.items():
+        assert seen[name] == {f[0] for f in mirror._fields_}, name

@@ -3,7 +3,9 @@
 A plain, slow, obviously-correct restatement of what the pipeline computes,
 written from the WarpStream TRT article (fused-preprocess passage and its
 dataflow figure; the Top-K passage) and the yolo.cu README (letterboxed
-input), in float64 with exact rational sampling coordinates.
+input; DFL decode and greedy NMS), in float64 with exact rational sampling
+coordinates.  Detection decisions are taken in binary32 with a fixed
+operation order (oracle/detect.py says why).
 
 Only the test-suite, the package's smoke entry point and the benchmark's CPU
 baseline leg may import this package.  The HIP library never does, and this
@@ -17,6 +19,7 @@ workload exercises.
 """
 from .preprocess import axis_taps, letterbox_region, preprocess, preprocess_batch, pad_value
 from .topk import topk, topk_keys_order
+from . import detect
 
 __all__ = ["axis_taps", "letterbox_region", "preprocess", "preprocess_batch", "pad_value",
-           "topk", "topk_keys_order"]
+           "topk", "topk_keys_order", "detect"]

@@ -15,6 +15,8 @@ yolo.cu README (640x640 letterbox input, 8400 anchors x 80 classes):
   C4  3840x2160 RGB8 -> 384x384, K=32 over 21843 logits with 1% exact copies
   C5L 8 lanes of C2-shaped frames read from mapped host memory, K=10
   C5T 64 independent 1280x720 frames -> 224x224 (preprocess only)
+  C3D C3's frame geometry plus a YOLO-style detection head (4x16 DFL logits
+      + 80 class probabilities per anchor, 8400 anchors) with planted objects
 
 Every generator uses numpy.random.default_rng(seed) (PCG64) and draws in the
 order frame, scores, duplicate positions.  Widths are given first ("W x H"),
@@ -52,6 +54,8 @@ class Workload:
     scores: np.ndarray | None     # float32 [N] or None
     host_input: bool = False      # frame read from mapped pinned host memory
     meta: dict = field(default_factory=dict)
+    head: np.ndarray | None = None  # float32 [64 + nc][A] detection head, or None
+    det: dict = field(default_factory=dict)   # nc, conf, iou, max_det, agnostic, planted
 
     @property
     def batch(self) -> int:
@@ -193,6 +197,111 @@ def scores_with_specials(seed: int, n: int, tie_frac: float = 0.1, nan_frac: flo
                         dtype=np.float32)
         s[pos] = vals
     return s
+
+
+HEAD_BINS = 16            # DFL bins per box side
+HEAD_STRIDES = (8, 16, 32)
+
+
+def head_anchor_grid(net_w: int, net_h: int):
+    """Anchor cell centres (cx, cy) in cells and strides, in head order:
+    stride-8 grid, then 16, then 32, row-major within a grid."""
+    cx, cy, st = [], [], []
+    for s in HEAD_STRIDES:
+        gy, gx = np.meshgrid(np.arange(net_h // s), np.arange(net_w // s), indexing="ij")
+        cx.append(gx.ravel() + 0.5)
+        cy.append(gy.ravel() + 0.5)
+        st.append(np.full(gx.size, s, dtype=np.float64))
+    return np.concatenate(cx), np.concatenate(cy), np.concatenate(st)
+
+
+def detection_head(rng: np.random.Generator, net_w: int, net_h: int, nc: int, region,
+                   objects: int, bg_mean: float = -7.0, bg_std: float = 1.5):
+    """A synthetic head: background anchors with low class probabilities
+    (sigmoid of N(bg_mean, bg_std)) and N(0, 1.5) box logits; each planted
+    object lights up the anchors whose centre lies in the middle half of its
+    box, on the grids where its larger side spans 3..20 cells, with a
+    probability sigmoid(N(2, 1)) for its class and box logits peaked (a
+    Gaussian bump of width 0.7 bins plus N(0, 0.2) noise) at the distances
+    to the object's edges jittered by N(0, 0.15) cells.  Objects are boxes
+    inside `region` = (left, top, w, h) with sides 12..45% of the region.
+    Returns (head float32 [64 + nc][A], planted [(class, x1, y1, x2, y2)])."""
+    cx, cy, st = head_anchor_grid(net_w, net_h)
+    A = cx.size
+    head = np.empty((4 * HEAD_BINS + nc, A), dtype=np.float32)
+    head[:4 * HEAD_BINS] = rng.normal(0.0, 1.5, (4 * HEAD_BINS, A))
+    head[4 * HEAD_BINS:] = 1.0 / (1.0 + np.exp(-rng.normal(bg_mean, bg_std, (nc, A))))
+    left, top, rw, rh = region
+    bins = np.arange(HEAD_BINS, dtype=np.float64)[:, None]
+    planted = []
+    for _ in range(objects):
+        cls = int(rng.integers(0, nc))
+        w = rw * rng.uniform(0.12, 0.45)
+        h = rh * rng.uniform(0.12, 0.45)
+        x1 = left + rng.uniform(0, rw - w)
+        y1 = top + rng.uniform(0, rh - h)
+        x2, y2 = x1 + w, y1 + h
+        planted.append((cls, x1, y1, x2, y2))
+        span = max(w, h) / st
+        px, py = cx * st, cy * st
+        hit = ((span >= 3) & (span <= 20) &
+               (np.abs(px - (x1 + x2) / 2) <= w / 4) & (np.abs(py - (y1 + y2) / 2) <= h / 4))
+        idx = np.flatnonzero(hit)
+        if idx.size == 0:
+            continue
+        p = 1.0 / (1.0 + np.exp(-rng.normal(2.0, 1.0, idx.size)))
+        head[4 * HEAD_BINS + cls, idx] = p
+        dist = np.stack([cx[idx] - x1 / st[idx], cy[idx] - y1 / st[idx],
+                         x2 / st[idx] - cx[idx], y2 / st[idx] - cy[idx]])
+        dist = np.clip(dist + rng.normal(0.0, 0.15, dist.shape), 0.0, HEAD_BINS - 1)
+        for side in range(4):
+            bump = -((bins - dist[side][None, :]) ** 2) / (2 * 0.7 ** 2)
+            head[side * HEAD_BINS:(side + 1) * HEAD_BINS, idx] = (
+                bump + rng.normal(0.0, 0.2, bump.shape))
+    return head, planted
+
+
+def c3d(seed: int = 5, objects: int = 24) -> Workload:
+    """C3's geometry with a detection head: 1280x720 -> 640x640 letterbox,
+    8400 anchors x 80 classes, conf > 0.25, IoU > 0.45, at most 300 boxes.
+    The Top-K stage ranks the head's class block (the same 8400x80 scores)."""
+    rng = np.random.default_rng(seed)
+    frame = uniform_frame(rng, 1280, 720)
+    region = (0, 140, 640, 360)       # where a 1280x720 frame lands in 640x640
+    head, planted = detection_head(rng, 640, 640, 80, region, objects)
+    return Workload("c3d_1280x720_letterbox_640_detect", 1280, 720, 640, 640, LETTERBOX,
+                    (0.0, 0.0, 0.0), (1.0, 1.0, 1.0), 114.0, 32, frame[None],
+                    head[4 * HEAD_BINS:].ravel().copy(), head=head,
+                    det=dict(nc=80, conf=0.25, iou=0.45, max_det=300, agnostic=False,
+                             planted=planted))
+
+
+def detect_small(seed: int) -> Workload:
+    """Small random detection cases: network sides 32..256 (multiples of 32),
+    1..120 classes, 0..12 objects, random thresholds, letterbox or resize,
+    sometimes class-agnostic, sometimes a small max_det."""
+    rng = np.random.default_rng(30_000 + seed)
+    nw, nh = (int(v) * 32 for v in rng.integers(1, 9, size=2))
+    sw, sh = (int(v) for v in rng.integers(8, 400, size=2))
+    letterbox = bool(rng.integers(0, 2))
+    nc = int(rng.integers(1, 121))
+    if letterbox:
+        r = min(nw / sw, nh / sh)
+        rw = min(max(int(np.floor(sw * r + 0.5)), 1), nw)
+        rh = min(max(int(np.floor(sh * r + 0.5)), 1), nh)
+        region = ((nw - rw) // 2, (nh - rh) // 2, rw, rh)
+    else:
+        region = (0, 0, nw, nh)
+    head, planted = detection_head(rng, nw, nh, nc, region, int(rng.integers(0, 13)),
+                                   bg_mean=float(rng.uniform(-7.0, -1.0)))
+    frames = rng.integers(0, 256, size=(1, sh, sw, 3), dtype=np.uint8)
+    det = dict(nc=nc, conf=float(np.float32(rng.uniform(0.05, 0.6))),
+               iou=float(np.float32(rng.uniform(0.2, 0.9))),
+               max_det=int(rng.choice([1, 3, 10, 300])), agnostic=bool(rng.integers(0, 2)),
+               planted=planted)
+    return Workload(f"detect_small{seed}_{sw}x{sh}_to_{nw}x{nh}", sw, sh, nw, nh,
+                    LETTERBOX if letterbox else RESIZE, (0.0, 0.0, 0.0), (1.0, 1.0, 1.0),
+                    114.0, 0, frames, None, head=head, det=det)
 
 
 ALL_CONFIGS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4}

@@ -25,6 +25,8 @@ def hashes():
         out[f"c5_lane{lane}"] = {"frames": wl.sha256(w.frames), "scores": wl.sha256(w.scores)}
     w = wl.c5_throughput(64)
     out["c5t"] = {"frames": wl.sha256(w.frames)}
+    w = wl.c3d()
+    out["c3d"] = {"frames": wl.sha256(w.frames), "head": wl.sha256(w.head)}
     return out
 
 

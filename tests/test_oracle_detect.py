@@ -1,0 +1,276 @@
+"""Pins for the detection oracle (oracle/detect.py).
+
+Each check ties the oracle to something other than itself: math.exp, a
+float64 softmax from torch, closed forms of the DFL expectation, exact
+rational IoU, a hand-worked suppression example (tests/golden/), the
+defining properties of greedy suppression, and recovery of the objects the
+input generator planted.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import detect as D
+from oracle import letterbox_region
+from post_processing_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "nms_worked_example.json")
+F32 = np.float32
+
+
+# ---------------------------------------------------------------- exp32
+def test_exp32_within_two_ulp_of_math_exp():
+    x = np.linspace(-80.0, 0.0, 400_001).astype(F32)
+    got = D.exp32(x).astype(np.float64)
+    ref = np.array([math.exp(float(v)) for v in x[::7]])
+    ulp = np.spacing(ref.astype(F32)).astype(np.float64)
+    assert (np.abs(got[::7] - ref) / ulp).max() <= 2.0
+
+
+def test_exp32_special_values():
+    assert D.exp32(F32(0.0)) == F32(1.0)
+    # ln 2 multiples land on powers of two, up to the polynomial's error and
+    # the rounding of the argument itself to binary32
+    for k in range(0, 100, 7):
+        x = F32(-k * math.log(2))
+        v = float(D.exp32(x))
+        dx = abs(float(x) + k * math.log(2))
+        assert abs(v / 2.0 ** -k - 1) < dx * 1.01 + 2.5e-7
+    # below the floor the result is e^-80, not a subnormal or zero
+    assert D.exp32(F32(-200.0)) == D.exp32(F32(-80.0)) > 0
+
+
+# ---------------------------------------------------------------- DFL
+def test_dfl_uniform_logits_give_mean_bin():
+    z = np.zeros((16, 3), F32) + F32([0.0, -3.5, 12.25])
+    assert D.dfl32(z).tolist() == [7.5, 7.5, 7.5]
+    assert D.dfl_exact(np.zeros(16)) == 7.5
+
+
+@pytest.mark.parametrize("b", [0, 1, 7, 15])
+def test_dfl_peaked_logits_give_their_bin(b):
+    # one logit D above the rest: E = (b e^D + sum_{i != b} i) / (e^D + 15)
+    for gap in (5.0, 20.0):
+        l = np.zeros(16)
+        l[b] = gap
+        want = (b * math.exp(gap) + (120 - b)) / (math.exp(gap) + 15)
+        assert abs(D.dfl_exact(l) - want) < 1e-12
+        assert abs(float(D.dfl32(l.astype(F32)[:, None])[0]) - want) < 2e-6
+
+
+def test_dfl_two_equal_peaks_give_their_midpoint():
+    l = np.full(16, -60.0, F32)
+    l[3] = l[11] = 2.0
+    assert abs(float(D.dfl32(l[:, None])[0]) - 7.0) < 1e-6
+
+
+def test_dfl_matches_float64_softmax_expectation():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    l = rng.normal(0, 3, (16, 3000)).astype(F32)
+    p = torch.softmax(torch.from_numpy(l.astype(np.float64)), dim=0).numpy()
+    want = (np.arange(16)[:, None] * p).sum(0)
+    got = D.dfl32(l).astype(np.float64)
+    # 16 exponentials within 2 ulp and 31 roundings of sums/products in
+    # [0, 16): the error stays well under 16 * 2^-23 * 16
+    assert np.abs(got - want).max() < 3e-5
+    assert np.abs(np.array([D.dfl_exact(l[:, j]) for j in range(0, 3000, 97)])
+                  - want[::97]).max() < 1e-12
+
+
+# ---------------------------------------------------------------- anchors
+def test_anchor_grid_layout():
+    a = D.anchors(640, 640)
+    assert D.num_anchors(640, 640) == len(a) == 80 * 80 + 40 * 40 + 20 * 20 == 8400
+    assert a[0] == (0.5, 0.5, 8)
+    assert a[81] == (1.5, 1.5, 8)           # row-major: 80 cells per row
+    assert a[6400] == (0.5, 0.5, 16)        # second grid starts after 80 * 80
+    assert a[8000] == (0.5, 0.5, 32)
+    assert a[-1] == (19.5, 19.5, 32)
+    assert D.num_anchors(96, 32) == 12 * 4 + 6 * 2 + 3 * 1
+
+
+def _one_hot_head(nc, A, dists, a, cls, conf):
+    head = np.full((64 + nc, A), -30.0, F32)
+    head[64:] = 0.0
+    for side, d in enumerate(dists):
+        head[side * 16 + d, a] = 30.0
+    head[64 + cls, a] = conf
+    return head
+
+
+def test_box_decode_closed_form():
+    # bin-peaked logits decode to integer distances: box = (c - l, c - t, c + r, c + b) * stride
+    nw, nh = 96, 64
+    anc = D.anchors(nw, nh)
+    for a, dists in [(0, (0, 0, 1, 1)), (13, (2, 3, 4, 5)), (len(anc) - 1, (1, 0, 0, 1)),
+                     (12 * 8 + 5, (6, 1, 2, 9))]:
+        head = _one_hot_head(3, len(anc), dists, a, 2, 0.9)
+        (c,) = D.decode_candidates(head, nw, nh, 3, 0.5)
+        cx, cy, s = anc[a]
+        want = [(cx - dists[0]) * s, (cy - dists[1]) * s, (cx + dists[2]) * s, (cy + dists[3]) * s]
+        assert c[0] == a and c[1] == 2 and c[2] == F32(0.9)
+        assert np.allclose(c[3], want, atol=1e-4 * s)
+        assert np.allclose(D.box_exact(head, a, nw, nh), want, atol=1e-9 * s)
+
+
+def test_decode_float32_within_bound_of_definition():
+    w = wl.detect_small(3)
+    nc = w.det["nc"]
+    for c in D.decode_candidates(w.head, w.dst_w, w.dst_h, nc, w.det["conf"])[:50]:
+        exact = D.box_exact(w.head, c[0], w.dst_w, w.dst_h)
+        assert np.abs(c[3].astype(np.float64) - exact).max() < 32 * 3e-5 + 1e-4
+
+
+def test_best_class_ties_nan_and_threshold():
+    probs = np.array([[0.3, np.nan, 0.5, np.nan, 0.25],
+                      [0.7, 0.2, 0.5, np.nan, 0.25],
+                      [0.7, 0.1, 0.1, np.nan, 0.1]], F32)
+    cls, conf = D.best_class(probs)
+    assert cls.tolist() == [1, 1, 0, 0, 0]               # first maximum wins ties
+    assert conf[:3].tolist() == [F32(0.7), F32(0.2), F32(0.5)]
+    assert conf[3] == -np.inf                              # all NaN: never a candidate
+    # strictly above the threshold: conf == thr is not a candidate
+    A = D.num_anchors(32, 32)
+    head = np.zeros((64 + 2, A), F32)
+    head[64, :5] = [0.25, 0.2500001, 0.9, 0.9, 0.24999999]
+    got = D.decode_candidates(head, 32, 32, 2, 0.25)
+    assert [c[0] for c in got] == [2, 3, 1]               # equal conf -> lower anchor first
+
+
+# ---------------------------------------------------------------- IoU
+def test_iou_exact_cases():
+    b = lambda *v: np.array(v, F32)
+    assert D.iou32(b(0, 0, 10, 10), b(0, 0, 10, 10)) == 1
+    assert D.iou32(b(0, 0, 10, 10), b(20, 0, 30, 10)) == 0
+    assert D.iou32(b(0, 0, 10, 10), b(10, 0, 20, 10)) == 0            # touching edges
+    assert D.iou32(b(0, 0, 2, 1), b(1, 0, 3, 1)) == F32(1) / F32(3)
+    assert math.isnan(D.iou32(b(1, 1, 1, 1), b(1, 1, 1, 1)))          # 0/0 never suppresses
+    assert D.iou_exact(b(0, 0, 10, 10), b(1, 1, 11, 11)) == Fraction(81, 119)
+
+
+def test_iou32_matches_exact_rational():
+    rng = np.random.default_rng(11)
+    for _ in range(2000):
+        p = rng.uniform(0, 100, 4)
+        q = p + rng.normal(0, 8, 4)
+        a = np.array([min(p[0], p[2]), min(p[1], p[3]), max(p[0], p[2]), max(p[1], p[3])], F32)
+        c = np.array([min(q[0], q[2]), min(q[1], q[3]), max(q[0], q[2]), max(q[1], q[3])], F32)
+        assert abs(float(D.iou32(a, c)) - float(D.iou_exact(a, c))) < 2e-6
+
+
+# ---------------------------------------------------------------- NMS
+def _golden_cands():
+    g = json.load(open(GOLDEN))
+    names = sorted(g["boxes"], key=lambda n: -g["scores"][n])
+    return g, [(i, g["classes"][n], F32(g["scores"][n]), np.array(g["boxes"][n], F32), n)
+               for i, n in enumerate(names)]
+
+
+def test_nms_hand_worked_example():
+    g, cands = _golden_cands()
+    for case in g["cases"]:
+        kept = D.nms([c[:4] for c in cands], case["iou"], case["max_det"], case["agnostic"])
+        names = [cands[k[0]][4] for k in kept]
+        assert names == case["kept"], case["why"]
+
+
+def _random_cands(rng, n, nc):
+    cands = []
+    for i in range(n):
+        x, y = rng.uniform(0, 60, 2)
+        w, h = rng.uniform(4, 30, 2)
+        cands.append((i, int(rng.integers(0, nc)), F32(rng.uniform(0.3, 1.0)),
+                      np.array([x, y, x + w, y + h], F32)))
+    cands.sort(key=lambda c: (-float(c[2]), c[0]))
+    return cands
+
+
+@pytest.mark.parametrize("agnostic", [False, True])
+def test_nms_result_is_the_greedy_fixed_point(agnostic):
+    # Greedy suppression is the unique kept list (taken in rank order) such
+    # that no kept box overlaps an earlier kept box of its class above the
+    # threshold, and every dropped candidate before the max_det cut does.
+    rng = np.random.default_rng(12 if agnostic else 13)
+    for trial in range(150):
+        cands = _random_cands(rng, int(rng.integers(0, 40)), int(rng.integers(1, 4)))
+        thr = F32(rng.uniform(0.1, 0.8))
+        max_det = int(rng.choice([1, 2, 5, 300]))
+        kept = D.nms(cands, thr, max_det, agnostic)
+        ids = [k[0] for k in kept]
+        pos = [next(j for j, c in enumerate(cands) if c[0] == i) for i in ids]
+        assert pos == sorted(pos) and len(kept) <= max_det
+        same = lambda p, q: agnostic or p[1] == q[1]
+        exact = lambda p, q: D.iou_exact(p[3], q[3])
+        for a in range(len(kept)):
+            for b in range(a):
+                if same(kept[a], kept[b]):
+                    assert not float(exact(kept[a], kept[b])) > float(thr) + 2e-6
+        cut = pos[-1] if len(kept) == max_det else len(cands) - 1
+        for j, c in enumerate(cands[:cut + 1]):
+            if c[0] in ids:
+                continue
+            assert any(same(k, c) and float(exact(k, c)) > float(thr) - 2e-6
+                       for k, p in zip(kept, pos) if p < j)
+
+
+# ---------------------------------------------------------------- mapping
+def test_map_to_source_round_trip():
+    # the image region of the network input maps onto the whole source frame
+    for (sw, sh, nw, nh) in [(1280, 720, 640, 640), (300, 200, 96, 96), (50, 400, 64, 32)]:
+        left, top, rw, rh = letterbox_region(sw, sh, nw, nh)
+        sx, sy = F32(sw / rw), F32(sh / rh)
+        box = np.array([left, top, left + rw, top + rh], F32)
+        m = D.map_to_source(box, left, top, sx, sy, sw, sh)
+        assert m[0] == 0 and m[1] == 0
+        assert abs(float(m[2]) - sw) <= float(np.spacing(F32(sw))) and m[2] <= sw
+        assert abs(float(m[3]) - sh) <= float(np.spacing(F32(sh))) and m[3] <= sh
+        # a box wholly inside the pad clips to a zero-area box on the border
+        pad = np.array([0, 0, max(left, 1) * 0.5, max(top, 1) * 0.5], F32)
+        mp = D.map_to_source(pad, left, top, sx, sy, sw, sh)
+        assert (mp[2] - mp[0]) * (mp[3] - mp[1]) == 0 or (left == 0 and top == 0)
+
+
+def test_detect_maps_a_known_box_to_the_frame():
+    # 300x100 frame letterboxed into 64x64: region (0, 21, 64, 21).  Distances
+    # (1, 1, 1, 1) on stride-8 cell (3, 4) give (20, 28, 36, 44) network
+    # pixels, i.e. x * 300/64 and (y - 21) * 100/21 in the frame, clipped.
+    assert letterbox_region(300, 100, 64, 64) == (0, 21, 64, 21)
+    head = np.full((65, D.num_anchors(64, 64)), -30.0, F32)
+    a = 4 * 8 + 3
+    for side in range(4):
+        head[side * 16 + 1, a] = 30.0
+    head[64] = 0.0
+    head[64, a] = 0.8
+    boxes, scores, classes, n = D.detect(head, 300, 100, 64, 64, (0, 21, 64, 21), 1, 0.5, 0.5, 10)
+    assert n == 1 and classes.tolist() == [0] and scores[0] == F32(0.8)
+    np.testing.assert_allclose(boxes[0], [93.75, 100 / 3, 168.75, 100.0], rtol=1e-5)
+
+
+# ---------------------------------------------------------------- end to end
+def test_planted_objects_are_recovered():
+    w = wl.c3d()
+    region = letterbox_region(w.src_w, w.src_h, w.dst_w, w.dst_h)
+    assert region == (0, 140, 640, 360)
+    cands = D.decode_candidates(w.head, w.dst_w, w.dst_h, 80, w.det["conf"])
+    kept = D.nms(cands, w.det["iou"], w.det["max_det"])
+    # recall: every planted object whose anchors fired has a kept box of its
+    # class within IoU 0.75 of it, in network-input pixels
+    anc_x, anc_y, st = wl.head_anchor_grid(w.dst_w, w.dst_h)
+    found = 0
+    for cls, x1, y1, x2, y2 in w.det["planted"]:
+        box = np.array([x1, y1, x2, y2])
+        best = max((float(D.iou_exact(k[3], box)) for k in kept if k[1] == cls), default=0.0)
+        found += best > 0.75
+    assert found >= len(w.det["planted"]) - 2
+    # the mapped boxes lie in the source frame
+    boxes, scores, classes, n = D.detect(w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, region,
+                                         80, w.det["conf"], w.det["iou"], w.det["max_det"])
+    assert n == len(cands) and len(scores) == len(kept)
+    assert (boxes >= 0).all() and (boxes[:, [0, 2]] <= w.src_w).all()
+    assert (boxes[:, [1, 3]] <= w.src_h).all()
+    assert np.all(np.diff(scores.astype(np.float64)) <= 0)

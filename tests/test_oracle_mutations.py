@@ -183,3 +183,164 @@ TOPK_MUTANTS = [
 def test_topk_mutant_is_caught(label, old, new):
     failed = topk_pins(load_variant("topk.py", old, new))
     assert failed, f"no pin caught the mutant: {label}"
+
+
+def detect_pins(m) -> list[str]:
+    """The detection pins of tests/test_oracle_detect.py, run against module m."""
+    import json
+    from oracle import letterbox_region
+    from post_processing_amd import workloads as wl
+    F32 = np.float32
+    failed = []
+
+    def check(name, fn):
+        try:
+            if not fn():
+                failed.append(name)
+        except Exception:
+            failed.append(name)
+
+    def exp_pin():
+        x = np.linspace(-80.0, 0.0, 20_001).astype(F32)
+        ref = np.exp(x.astype(np.float64))
+        ulp = np.spacing(ref.astype(F32)).astype(np.float64)
+        return (np.abs(m.exp32(x).astype(np.float64) - ref) / ulp).max() <= 2.0
+    check("exp", exp_pin)
+
+    def dfl_pin():
+        ok = m.dfl32(np.zeros((16, 1), F32)).tolist() == [7.5]
+        for b in (0, 7, 15):
+            l = np.zeros(16)
+            l[b] = 5.0
+            want = (b * math.exp(5.0) + (120 - b)) / (math.exp(5.0) + 15)
+            ok &= abs(float(m.dfl32(l.astype(F32)[:, None])[0]) - want) < 2e-6
+        return ok
+    check("dfl", dfl_pin)
+
+    def anchors_pin():
+        a = m.anchors(640, 640)
+        return (len(a) == 8400 and a[0] == (0.5, 0.5, 8) and a[81] == (1.5, 1.5, 8)
+                and a[6400] == (0.5, 0.5, 16) and a[-1] == (19.5, 19.5, 32))
+    check("anchors", anchors_pin)
+
+    def box_pin():
+        nw, nh = 96, 64
+        anc = m.anchors(nw, nh)
+        # anchor 13: stride-8 grid (12 x 8 cells), cell (1, 1); anchor 101:
+        # stride-16 grid (6 x 4 cells) starts at 96, cell (5, 0)
+        for a, d, (cx, cy, s) in [(13, (2, 3, 4, 5), (1.5, 1.5, 8)),
+                                  (101, (6, 1, 2, 9), (5.5, 0.5, 16))]:
+            head = np.full((67, len(anc)), -30.0, F32)
+            head[64:] = 0.0
+            for side, v in enumerate(d):
+                head[side * 16 + v, a] = 30.0
+            head[66, a] = 0.9
+            (c,) = m.decode_candidates(head, nw, nh, 3, 0.5)
+            want = [(cx - d[0]) * s, (cy - d[1]) * s, (cx + d[2]) * s, (cy + d[3]) * s]
+            if not (c[0] == a and c[1] == 2 and np.allclose(c[3], want, atol=1e-3)):
+                return False
+        return True
+    check("box", box_pin)
+
+    def class_pin():
+        probs = np.array([[0.3, np.nan, 0.5], [0.7, 0.2, 0.5], [0.7, 0.1, 0.1]], F32)
+        cls, conf = m.best_class(probs)
+        head = np.zeros((66, m.num_anchors(32, 32)), F32)
+        head[64, :5] = [0.25, 0.2500001, 0.9, 0.9, 0.24999999]
+        got = [c[0] for c in m.decode_candidates(head, 32, 32, 2, 0.25)]
+        return cls.tolist() == [1, 1, 0] and got == [2, 3, 1]
+    check("class", class_pin)
+
+    def iou_pin():
+        b = lambda *v: np.array(v, F32)
+        return (m.iou32(b(0, 0, 10, 10), b(0, 0, 10, 10)) == 1
+                and m.iou32(b(0, 0, 2, 1), b(1, 0, 3, 1)) == F32(1) / F32(3)
+                and abs(float(m.iou32(b(0, 0, 10, 10), b(1, 1, 11, 11))) - 81 / 119) < 1e-6)
+    check("iou", iou_pin)
+
+    def golden_pin():
+        g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                        "nms_worked_example.json")))
+        names = sorted(g["boxes"], key=lambda n: -g["scores"][n])
+        cands = [(i, g["classes"][n], F32(g["scores"][n]), np.array(g["boxes"][n], F32))
+                 for i, n in enumerate(names)]
+        for case in g["cases"]:
+            kept = m.nms(cands, case["iou"], case["max_det"], case["agnostic"])
+            if [names[k[0]] for k in kept] != case["kept"]:
+                return False
+        return True
+    check("golden_nms", golden_pin)
+
+    def map_pin():
+        for (sw, sh, nw, nh) in [(1280, 720, 640, 640), (50, 400, 64, 32)]:
+            left, top, rw, rh = letterbox_region(sw, sh, nw, nh)
+            box = np.array([left, top, left + rw, top + rh], F32)
+            mm = m.map_to_source(box, left, top, F32(sw / rw), F32(sh / rh), sw, sh)
+            if not (mm[0] == 0 and mm[1] == 0 and abs(float(mm[2]) - sw) < 1e-3
+                    and abs(float(mm[3]) - sh) < 1e-3):
+                return False
+        return True
+    check("map", map_pin)
+
+    def detect_pin():
+        # 300x100 frame letterboxed into 64x64: region (0, 21, 64, 21); a box
+        # of distances (1, 1, 1, 1) on stride-8 cell (3, 4) spans (20, 28, 36, 44)
+        # network pixels, i.e. x * 300/64 and (y - 21) * 100/21 in the frame
+        head = np.full((65, m.num_anchors(64, 64)), -30.0, F32)
+        a = 4 * 8 + 3
+        for side in range(4):
+            head[side * 16 + 1, a] = 30.0
+        head[64] = 0.0
+        head[64, a] = 0.8
+        boxes, scores, classes, n = m.detect(head, 300, 100, 64, 64, (0, 21, 64, 21), 1,
+                                             0.5, 0.5, 10)
+        want = [20 * 300 / 64, 7 * 100 / 21, 36 * 300 / 64, 100.0]
+        return n == 1 and np.allclose(boxes[0], want, rtol=1e-5) and scores[0] == F32(0.8)
+    check("detect", detect_pin)
+
+    def planted_pin():
+        w = wl.c3d()
+        kept = m.nms(m.decode_candidates(w.head, 640, 640, 80, 0.25), 0.45, 300)
+        found = 0
+        for cls, x1, y1, x2, y2 in w.det["planted"]:
+            best = max((float(m.iou_exact(k[3], (x1, y1, x2, y2))) for k in kept if k[1] == cls),
+                       default=0.0)
+            found += best > 0.75
+        return found >= len(w.det["planted"]) - 2
+    check("planted", planted_pin)
+    return failed
+
+
+def test_unmodified_detect_oracle_passes_all_pins():
+    assert detect_pins(load_variant("detect.py")) == []
+
+
+DETECT_MUTANTS = [
+    ("anchor at cell corner", "out.append((gx + 0.5, gy + 0.5, s))", "out.append((gx, gy, s))"),
+    ("grids in reverse order", "STRIDES = (8, 16, 32)", "STRIDES = (32, 16, 8)"),
+    ("left and right distances swapped", "    x1 = (cx - d[0]) * st\n", "    x1 = (cx - d[2]) * st\n"),
+    ("top uses the left distance", "    y1 = (cy - d[1]) * st\n", "    y1 = (cy - d[0]) * st\n"),
+    ("expectation from bin 1", "num = num + F32(b) * e[b]", "num = num + F32(b + 1) * e[b]"),
+    ("polynomial truncated", "for k in range(6, -1, -1):", "for k in range(4, -1, -1):"),
+    ("reduction drops the low part", "r = (x - n * LN2_HI) - n * LN2_LO", "r = x - n * LN2_HI"),
+    ("argmax ties to the last class", "better = probs[c] > best", "better = probs[c] >= best"),
+    ("threshold inclusive", "cand = np.nonzero(conf > F32(conf_thr))[0]",
+     "cand = np.nonzero(conf >= F32(conf_thr))[0]"),
+    ("ascending score order", "out.sort(key=lambda c: (-float(c[2]), c[0]))",
+     "out.sort(key=lambda c: (float(c[2]), c[0]))"),
+    ("equal scores to the higher anchor", "out.sort(key=lambda c: (-float(c[2]), c[0]))",
+     "out.sort(key=lambda c: (-float(c[2]), -c[0]))"),
+    ("union keeps the intersection", "    union = (area_a + area_b) - inter\n",
+     "    union = area_a + area_b\n"),
+    ("suppression at equality", "iou32(k[3], c[3]) > t", "iou32(k[3], c[3]) >= t"),
+    ("classes ignored", "(agnostic or k[1] == c[1])", "(True)"),
+    ("one box too many", "if len(kept) == max_det:", "if len(kept) == max_det + 1:"),
+    ("map ignores the top offset", "(box[1] - F32(top)) * sy", "(box[1] - F32(left)) * sy"),
+    ("y scale from the region width", "sy = F32(src_h / rh)", "sy = F32(src_h / rw)"),
+]
+
+
+@pytest.mark.parametrize("label,old,new", DETECT_MUTANTS, ids=[m[0] for m in DETECT_MUTANTS])
+def test_detect_mutant_is_caught(label, old, new):
+    failed = detect_pins(load_variant("detect.py", old, new))
+    assert failed, f"no pin caught the mutant: {label}"

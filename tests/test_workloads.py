@@ -30,6 +30,20 @@ def test_lane_hashes(golden):
         assert w.host_input and w.k == 10
 
 
+def test_detection_head_hash_and_structure(golden):
+    w = wl.c3d()
+    assert wl.sha256(w.head) == golden["c3d"]["head"]
+    assert wl.sha256(w.frames) == golden["c3d"]["frames"]
+    assert w.head.shape == (64 + 80, 8400) and w.head.dtype == np.float32
+    probs = w.head[64:]
+    assert 0 < probs.min() and probs.max() < 1
+    # the Top-K stage ranks the head's class block
+    assert np.array_equal(w.scores, probs.ravel())
+    # background stays low; planted anchors light up
+    assert (probs.max(axis=0) > 0.25).sum() > 300
+    assert len(w.det["planted"]) == 24
+
+
 def test_shapes():
     assert wl.c1().frames.shape == (1, 48, 64, 3)
     assert wl.c2().frames.shape == (1, 1080, 1920, 3)

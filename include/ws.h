@@ -35,6 +35,62 @@
 extern "C" {
 #endif
 
+/* ---- optional detection stage --------------------------------------------
+ * Decode + greedy NMS of a YOLO-style detection head, as in the yolo.cu
+ * README (its end-to-end pipeline passage: DFL decode and NMS inside the one
+ * graph; the GPU-resident NMS highlight: greedy suppression over the live
+ * candidates in score order, only the final boxes cross to pinned memory;
+ * the embedding example: up to 300 boxes in source-image coordinates).
+ *
+ * Head layout, float32 [4 * WS_DET_REG_MAX + nc][A], channel-major:
+ *   channels 16*s .. 16*s+15  logits of the distance distribution of box
+ *                             side s (0 left, 1 top, 2 right, 3 bottom), in
+ *                             cells of the anchor's grid;
+ *   channels 64 .. 64+nc-1    class probabilities (already through the
+ *                             head's sigmoid).
+ * Anchors: the cells of the stride-8, -16 and -32 grids over the dst_w x
+ * dst_h network input, grid by grid, row-major within a grid, each at its
+ * cell centre.  A = sum over s of (dst_w/s) * (dst_h/s).
+ *
+ * Per frame:
+ *   1. each anchor's best class is the first maximum of its probabilities
+ *      (NaN never wins); the anchor is a candidate when that probability
+ *      > det_conf;
+ *   2. a candidate's distances are softmax expectations of bin index, and
+ *      its box is (cx - l, cy - t, cx + r, cy + b) * stride;
+ *   3. candidates are taken by probability descending, then anchor
+ *      ascending; each is kept unless an already kept box of the same class
+ *      (any class when det_agnostic) has IoU > det_iou with it; at most
+ *      det_max_det are kept;
+ *   4. kept boxes are mapped back through the letterbox (or plain resize)
+ *      to source pixels and clipped to the frame.
+ * All of it runs in binary32 with a fixed operation order and no fused
+ * multiply-add, with the exponential computed by Cody and Waite's reduction
+ * plus a degree-7 Taylor polynomial, so the result is reproducible bit for
+ * bit.  Box logits must be finite.
+ */
+#define WS_DET_REG_MAX      16     /* DFL bins per box side                  */
+#define WS_DET_MAX_DET      1024   /* upper bound of det_max_det             */
+#define WS_DET_MAX_ANCHORS  16384  /* upper bound of A                       */
+#define WS_DET_MAX_CLASSES  4096
+
+/* One kept box: source-frame pixels (x right, y down), its class
+ * probability and class.  24 bytes. */
+typedef struct ws_det {
+    float   x1, y1, x2, y2;
+    float   score;
+    int32_t class_id;
+} ws_det;
+
+/* Detection result slot (mapped host memory, written by the GPU in-graph):
+ * `count` kept boxes in keep order (score descending), and the number of
+ * candidates that passed det_conf. */
+typedef struct ws_det_result {
+    int32_t count;
+    int32_t candidates;
+    ws_det  det[WS_DET_MAX_DET];
+} ws_det_result;
+
 /* ---- status codes ---------------------------------------------------- */
 #define WS_OK              0
 #define WS_E_INVALID_ARG  (-1)  /* NULL pointer, size or value out of range  */
@@ -116,6 +172,16 @@ typedef struct ws_lane_config {
     int32_t autotune;          /* 1 = time candidate launch geometries on the
                                   lane's buffers at create and keep the fastest
                                   (knobs above then only seed the search)       */
+    /* Detection stage (see above); det_classes = 0 leaves it out. */
+    int32_t det_classes;       /* nc, 0..WS_DET_MAX_CLASSES; needs dst_w and
+                                  dst_h multiples of 32 and A <= 16384          */
+    int32_t det_max_det;       /* 1..WS_DET_MAX_DET                             */
+    float   det_conf;          /* candidate threshold, 0 <= det_conf < 1        */
+    float   det_iou;           /* suppression threshold, 0 <= det_iou <= 1      */
+    int32_t det_agnostic;      /* 1 = boxes of any class suppress each other    */
+    int32_t det_reserved;      /* must be 0                                     */
+    const float *det_head_dev; /* borrowed head, or NULL: the lane owns one,
+                                  zero-filled at create                         */
 } ws_lane_config;
 
 /* Stable views of a lane's buffers, valid from ws_create_lane to ws_destroy.
@@ -133,6 +199,8 @@ typedef struct ws_lane_view {
     const ws_topk_entry *result_host;  /* NULL when num_scores == 0                */
     size_t               input_bytes;
     size_t               tensor_bytes;
+    float               *det_head_dev;     /* NULL without a detection stage   */
+    const ws_det_result *det_result_host;  /* NULL without a detection stage   */
 } ws_lane_view;
 
 typedef struct ws_lane ws_lane;
@@ -159,9 +227,11 @@ int ws_create_lane(const ws_lane_config *cfg, ws_lane **out, ws_lane_view *view)
 
 /*
  * ws_submit -- READY -> IN_FLIGHT: record the start event, replay the lane's
- * graph (preprocess, then Top-K, in stream order), record the done event.
+ * graph (preprocess, then Top-K, then detection decode and NMS, in stream
+ * order, each stage present when configured), record the done event.
  * No allocation, no synchronisation, no host branch on GPU data.  The input
- * slot and scores must hold the frame's data before this call and must not
+ * slot, scores and detection head must hold the frame's data before this
+ * call and must not
  * be modified until ws_wait returns.  Source: the article's submit passage.
  * Returns WS_E_STATE if the lane is already in flight (a lane cannot be
  * reused while busy; there is no queue), WS_E_INVALID_ARG for NULL, WS_E_HIP

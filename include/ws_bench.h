@@ -28,6 +28,8 @@ typedef struct ws_lane_plan {
     int32_t topk_chunk;       /* scores per Top-K workgroup                  */
     int32_t graph_nodes;      /* kernel nodes in the captured graph          */
     int32_t pixels_per_thread;/* output pixels per preprocess thread         */
+    int32_t det_anchors;      /* detection anchors (0 = no detection stage)  */
+    int32_t det_decode_groups;/* decode workgroups (one thread per anchor)   */
 } ws_lane_plan;
 
 /* Fill *plan for lane.  Returns WS_OK or WS_E_INVALID_ARG (NULL). */
@@ -55,6 +57,7 @@ int ws_bench_lanes(ws_lane **lanes, int32_t nlanes, int32_t replays, float *gpu_
 /* Stages of the per-frame launch sequence, for ws_bench_stage. */
 #define WS_STAGE_PREPROCESS 0
 #define WS_STAGE_TOPK       1
+#define WS_STAGE_DETECT     2   /* decode + NMS: two kernels per launch     */
 
 /*
  * Time one stage's kernel alone: `launches` back-to-back direct launches on
@@ -62,7 +65,8 @@ int ws_bench_lanes(ws_lane **lanes, int32_t nlanes, int32_t replays, float *gpu_
  * must be READY and stays READY; its buffers receive that stage's output.
  *   ms_per_launch  receives the elapsed event time divided by `launches`.
  * Returns WS_OK, WS_E_STATE (in flight), WS_E_INVALID_ARG (NULL, bad stage,
- * launches < 1, or a Top-K stage the lane does not have) or WS_E_HIP.
+ * launches < 1, or a Top-K or detection stage the lane does not have) or
+ * WS_E_HIP.
  */
 int ws_bench_stage(ws_lane *lane, int32_t stage, int32_t launches, double *ms_per_launch);
 

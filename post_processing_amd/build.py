@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libws.so")
-SOURCES = ["ws_kernels.hip", "ws_runtime.hip"]
+SOURCES = ["ws_kernels.hip", "ws_detect.hip", "ws_runtime.hip"]
 ARCH = "gfx950"
 
 
@@ -34,6 +34,8 @@ def lib_command(out: str) -> list[str]:
         "-Wall", "-Wno-unused-command-line-argument",
         # keep the compiler from forming packed FP32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # IEEE binary32 division and square root (detection decisions rely on it)
+        "-fhip-fp32-correctly-rounded-divide-sqrt",
         "-I", INCLUDE, "-I", CSRC,
         "-o", out,
     ] + [os.path.join(CSRC, s) for s in SOURCES]

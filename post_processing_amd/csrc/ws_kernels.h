@@ -49,9 +49,31 @@ struct TopkParams {
     uint2* result;           // [k] {score bits, index}, device view of the slot
 };
 
+// Detection decode + greedy NMS over a YOLO-style head (layout in ws.h).
+struct DetParams {
+    const float* head;       // [4 * 16 + nc][anchors], 16-byte aligned
+    int32_t anchors;         // A <= WS_DET_MAX_ANCHORS
+    int32_t nc;
+    int32_t level_end[3];    // anchor index where the stride-8/16/32 grids end
+    int32_t grid_w[3];       // cells per row of each grid
+    float conf;              // candidate: best probability > conf
+    float iou;               // suppression: IoU > iou
+    int32_t max_det;
+    int32_t agnostic;
+    float4* boxes;           // [anchors] network-input xyxy, written for candidates
+    uint64_t* keys;          // [anchors] compact candidate keys
+    uint32_t* counter;       // candidates appended; zero between replays
+    float left, top;         // image region origin in the network input
+    float sx, sy;            // source pixels per network pixel (binary32 of W/rw, H/rh)
+    float src_w, src_h;      // clip bounds
+    ws_det_result* out;      // device view of the mapped result slot
+};
+
 hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_bytes,
                              hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+// Decode (one thread per anchor) then NMS (one workgroup), in stream order.
+hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream);
 
 constexpr int kTopkMaxThreads = 256;   // 4 wave64s: one per SIMD
 

@@ -1,0 +1,65 @@
+// ws_lanes.h -- cross-lane primitives of a wave64 on CDNA (gfx950), shared
+// by the library's kernels.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ws {
+
+// Value held by lane (lane ^ J).  Every source lane is inside the wave, so
+// the DPP forms need no "old" operand (bound_ctrl).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane32(uint32_t v, int lane) {
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);   // quad_perm 1,0,3,2
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);   // quad_perm 2,3,0,1
+    } else if constexpr (J == 4) {
+        const uint32_t fwd = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12C, 0xF, 0xF, true);  // row_ror:12 -> lane+4
+        const uint32_t bwd = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, true);  // row_ror:4  -> lane-4
+        return (lane & 4) ? bwd : fwd;
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);  // row_ror:8
+    } else if constexpr (J == 16) {
+        const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (lane & 16) ? s[0] : s[1];
+    } else {
+        static_assert(J == 32, "lane distance must be a power of two below 64");
+        const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (lane & 32) ? s[0] : s[1];
+    }
+}
+
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
+    const uint32_t lo = xor_lane32<J>((uint32_t)v, lane);
+    const uint32_t hi = xor_lane32<J>((uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Value held by lane - 1 (lane 0 keeps its own): DPP wave_shr:1.
+__device__ __forceinline__ uint64_t prev_lane64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v,
+                                                              0x138, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32),
+                                                              (int)(uint32_t)(v >> 32), 0x138, 0xF,
+                                                              0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a < b ? b : a; }
+
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+}  // namespace ws

@@ -92,6 +92,31 @@ inline Region lane_region(const ws_lane_config& c) {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Detection anchors: cells of the stride-8, -16 and -32 grids over the
+// network input (its sides must be multiples of 32).
+constexpr int kDetStrides[3] = {8, 16, 32};
+
+inline int64_t det_anchor_count(int64_t net_w, int64_t net_h) {
+    int64_t a = 0;
+    for (int s : kDetStrides) a += (net_w / s) * (net_h / s);
+    return a;
+}
+
+inline int validate_detection(const ws_lane_config* c) {
+    if (c->det_classes == 0) return c->det_head_dev ? WS_E_INVALID_ARG : WS_OK;
+    if (c->det_classes < 0 || c->det_classes > WS_DET_MAX_CLASSES) return WS_E_INVALID_ARG;
+    if (c->batch != 1) return WS_E_INVALID_ARG;          // one head per frame, batch-1 lanes
+    if (c->dst_w % 32 != 0 || c->dst_h % 32 != 0) return WS_E_INVALID_ARG;
+    if (det_anchor_count(c->dst_w, c->dst_h) > WS_DET_MAX_ANCHORS) return WS_E_INVALID_ARG;
+    if (c->det_max_det < 1 || c->det_max_det > WS_DET_MAX_DET) return WS_E_INVALID_ARG;
+    if (!(c->det_conf >= 0.0f && c->det_conf < 1.0f)) return WS_E_INVALID_ARG;
+    if (!(c->det_iou >= 0.0f && c->det_iou <= 1.0f)) return WS_E_INVALID_ARG;
+    if (c->det_agnostic != 0 && c->det_agnostic != 1) return WS_E_INVALID_ARG;
+    if (c->det_reserved != 0) return WS_E_INVALID_ARG;
+    if (!aligned16(c->det_head_dev)) return WS_E_INVALID_ARG;
+    return WS_OK;
+}
+
 inline int validate_config(const ws_lane_config* c) {
     if (!c) return WS_E_INVALID_ARG;
     if (c->device < 0) return WS_E_INVALID_ARG;
@@ -135,7 +160,7 @@ inline int validate_config(const ws_lane_config* c) {
     if (c->channel_order != WS_CHANNELS_RGB && c->channel_order != WS_CHANNELS_BGR)
         return WS_E_INVALID_ARG;
     if (c->autotune != 0 && c->autotune != 1) return WS_E_INVALID_ARG;
-    return WS_OK;
+    return validate_detection(c);
 }
 
 // ---------------------------------------------------------------------------
@@ -147,6 +172,8 @@ constexpr int kTopkBatch = 1024;           // scores one wave takes per round
 constexpr int kTopkMaxWaves = 4;           // one wave per SIMD of a CU
 constexpr int kTopkSingleGroupMax = 4096;  // up to here one workgroup, no hand-off
 constexpr int kTopkLargeN = 262144;        // beyond: 8 Ki scores per workgroup
+constexpr int kDetDecodeBlock = 256;       // detection decode: one thread per anchor
+constexpr int kDetNmsBlock = 1024;         // detection NMS: one workgroup
 
 struct Plan {
     Region region;
@@ -167,6 +194,12 @@ struct Plan {
     int32_t topk_waves = 0;        // wave64s per Top-K workgroup
     // Sizes
     size_t frame_bytes = 0, input_bytes = 0, tensor_bytes = 0;
+    // Detection (det_anchors == 0: no detection stage)
+    int32_t det_anchors = 0;
+    int32_t det_level_end[3] = {0, 0, 0};  // anchor index where each grid ends
+    int32_t det_grid_w[3] = {0, 0, 0};     // cells per row of each grid
+    int32_t det_decode_groups = 0;         // 256-thread workgroups, one thread per anchor
+    size_t det_head_bytes = 0;
 };
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -243,6 +276,19 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
         p->topk_chunk = (int32_t)chunk;
         p->topk_waves = (int32_t)std::min<int64_t>(kTopkMaxWaves, chunk / kTopkBatch);
         p->topk_groups = (int32_t)ceil_div(c.num_scores, chunk);
+    }
+
+    if (c.det_classes > 0) {
+        int32_t end = 0;
+        for (int l = 0; l < 3; ++l) {
+            const int s = kDetStrides[l];
+            p->det_grid_w[l] = (int32_t)(Dw / s);
+            end += (int32_t)((Dw / s) * (Dh / s));
+            p->det_level_end[l] = end;
+        }
+        p->det_anchors = end;
+        p->det_decode_groups = (int32_t)ceil_div(end, kDetDecodeBlock);
+        p->det_head_bytes = (size_t)(4 * WS_DET_REG_MAX + c.det_classes) * (size_t)end * 4u;
     }
 
     p->frame_bytes = (size_t)W * (size_t)H * 3u;

@@ -46,8 +46,16 @@ struct ws_lane {
     uint2* res_dev = nullptr;           // its device view
     uint64_t* partials = nullptr;
     uint32_t* counter = nullptr;
+    float* det_head = nullptr;
+    bool own_det_head = false;
+    float4* det_boxes = nullptr;
+    uint64_t* det_keys = nullptr;
+    uint32_t* det_counter = nullptr;
+    ws_det_result* det_host = nullptr;  // mapped detection result slot
+    ws_det_result* det_dev = nullptr;   // its device view
     ws::PreParams pre{};
     ws::TopkParams tk{};
+    ws::DetParams det{};
     int nodes = 0;
     int last_err = 0;
 };
@@ -60,7 +68,7 @@ int fail(ws_lane* L, hipError_t e, int code) {
 }
 
 // The per-frame launch sequence, in stream order: (copy mode) the frame's
-// host-to-device copy, preprocess, Top-K.
+// host-to-device copy, preprocess, Top-K, detection decode + NMS.
 hipError_t launch_all(ws_lane* L) {
     hipError_t e = hipSuccess;
     if (L->cfg.input_mode == WS_INPUT_COPY)
@@ -71,6 +79,8 @@ hipError_t launch_all(ws_lane* L) {
                               L->stream);
     if (e != hipSuccess) return e;
     if (L->cfg.num_scores > 0) e = ws::launch_topk(L->tk, L->stream);
+    if (e != hipSuccess) return e;
+    if (L->plan.det_anchors > 0) e = ws::launch_detect(L->det, L->plan.det_decode_groups, L->stream);
     return e;
 }
 
@@ -89,6 +99,11 @@ void release(ws_lane* L) {
     if (L->res_host) hipHostFree(L->res_host);
     if (L->partials) hipFree(L->partials);
     if (L->counter) hipFree(L->counter);
+    if (L->own_det_head && L->det_head) hipFree(L->det_head);
+    if (L->det_boxes) hipFree(L->det_boxes);
+    if (L->det_keys) hipFree(L->det_keys);
+    if (L->det_counter) hipFree(L->det_counter);
+    if (L->det_host) hipHostFree(L->det_host);
     delete L;
 }
 
@@ -172,6 +187,30 @@ void fill_params(ws_lane* L) {
     t.partials = L->partials;
     t.counter = L->counter;
     t.result = L->res_dev;
+    ws::DetParams& d = L->det;
+    d.head = L->det_head;
+    d.anchors = P.det_anchors;
+    d.nc = c.det_classes;
+    for (int i = 0; i < 3; ++i) {
+        d.level_end[i] = P.det_level_end[i];
+        d.grid_w[i] = P.det_grid_w[i];
+    }
+    d.conf = c.det_conf;
+    d.iou = c.det_iou;
+    d.max_det = c.det_max_det;
+    d.agnostic = c.det_agnostic;
+    d.boxes = L->det_boxes;
+    d.keys = L->det_keys;
+    d.counter = L->det_counter;
+    d.left = (float)P.region.left;
+    d.top = (float)P.region.top;
+    // Source pixels per network pixel inside the image region: the binary32
+    // value of the float64 quotient.
+    d.sx = (float)((double)c.src_w / (double)P.region.w);
+    d.sy = (float)((double)c.src_h / (double)P.region.h);
+    d.src_w = (float)c.src_w;
+    d.src_h = (float)c.src_h;
+    d.out = L->det_dev;
 }
 
 // Microseconds per launch of one stage on the lane's stream: the best of
@@ -344,8 +383,34 @@ int build(ws_lane* L) {
         WS_HIP(hipMemset(L->counter, 0, sizeof(uint32_t)), WS_E_HIP);
     }
 
+    if (P.det_anchors > 0) {
+        const size_t A = (size_t)P.det_anchors;
+        if (c.det_head_dev) {
+            L->det_head = const_cast<float*>(c.det_head_dev);
+        } else {
+            void* d = nullptr;
+            WS_TRY(dev_alloc(L, &d, P.det_head_bytes));
+            L->det_head = static_cast<float*>(d);
+            L->own_det_head = true;
+            WS_HIP(hipMemset(L->det_head, 0, P.det_head_bytes), WS_E_HIP);
+        }
+        void *bx = nullptr, *ky = nullptr, *cn = nullptr;
+        WS_TRY(dev_alloc(L, &bx, A * sizeof(float4)));
+        L->det_boxes = static_cast<float4*>(bx);
+        WS_TRY(dev_alloc(L, &ky, A * sizeof(uint64_t)));
+        L->det_keys = static_cast<uint64_t*>(ky);
+        WS_TRY(dev_alloc(L, &cn, sizeof(uint32_t)));
+        L->det_counter = static_cast<uint32_t*>(cn);
+        WS_HIP(hipMemset(L->det_counter, 0, sizeof(uint32_t)), WS_E_HIP);
+        void *h = nullptr, *d = nullptr;
+        WS_TRY(mapped_alloc(L, &h, &d, sizeof(ws_det_result)));
+        L->det_host = static_cast<ws_det_result*>(h);
+        L->det_dev = static_cast<ws_det_result*>(d);
+    }
+
     fill_params(L);
-    L->nodes = 1 + (c.num_scores > 0 ? 1 : 0) + (c.input_mode == WS_INPUT_COPY ? 1 : 0);
+    L->nodes = 1 + (c.num_scores > 0 ? 1 : 0) + (c.input_mode == WS_INPUT_COPY ? 1 : 0) +
+               (P.det_anchors > 0 ? 2 : 0);
 
     // ---- stream, events, warm-up, capture ---------------------------------
     WS_HIP(hipStreamCreateWithFlags(&L->stream, hipStreamNonBlocking), WS_E_HIP);
@@ -397,6 +462,8 @@ int ws_create_lane(const ws_lane_config* cfg, ws_lane** out, ws_lane_view* view)
         view->result_host = L->res_host;
         view->input_bytes = L->plan.input_bytes;
         view->tensor_bytes = L->plan.tensor_bytes;
+        view->det_head_dev = L->det_head;
+        view->det_result_host = L->det_host;
     }
     *out = L;
     return WS_OK;
@@ -459,6 +526,8 @@ int ws_lane_describe(const ws_lane* L, ws_lane_plan* plan) {
     plan->topk_chunk = L->plan.topk_chunk;
     plan->graph_nodes = L->nodes;
     plan->pixels_per_thread = L->plan.pixels_per_thread;
+    plan->det_anchors = L->plan.det_anchors;
+    plan->det_decode_groups = L->plan.det_decode_groups;
     return WS_OK;
 }
 
@@ -510,15 +579,20 @@ int ws_bench_lanes(ws_lane** lanes, int32_t nlanes, int32_t replays, float* gpu_
 
 int ws_bench_stage(ws_lane* L, int32_t stage, int32_t launches, double* ms_per_launch) {
     if (!L || !ms_per_launch || launches < 1) return WS_E_INVALID_ARG;
-    if (stage != WS_STAGE_PREPROCESS && stage != WS_STAGE_TOPK) return WS_E_INVALID_ARG;
+    if (stage != WS_STAGE_PREPROCESS && stage != WS_STAGE_TOPK && stage != WS_STAGE_DETECT)
+        return WS_E_INVALID_ARG;
     if (stage == WS_STAGE_TOPK && L->cfg.num_scores == 0) return WS_E_INVALID_ARG;
+    if (stage == WS_STAGE_DETECT && L->plan.det_anchors == 0) return WS_E_INVALID_ARG;
     if (ws::begin_submit(L->state) != WS_OK) return WS_E_STATE;
     hipError_t e = hipEventRecord(L->ev_start, L->stream);
     for (int32_t i = 0; i < launches && e == hipSuccess; ++i) {
-        e = stage == WS_STAGE_PREPROCESS
-                ? ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
-                                        L->plan.lds_bytes, L->stream)
-                : ws::launch_topk(L->tk, L->stream);
+        if (stage == WS_STAGE_PREPROCESS)
+            e = ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
+                                      L->plan.lds_bytes, L->stream);
+        else if (stage == WS_STAGE_TOPK)
+            e = ws::launch_topk(L->tk, L->stream);
+        else
+            e = ws::launch_detect(L->det, L->plan.det_decode_groups, L->stream);
     }
     if (e == hipSuccess) e = hipEventRecord(L->ev_done, L->stream);
     const hipError_t se = hipStreamSynchronize(L->stream);

@@ -45,10 +45,21 @@ WAIT_BLOCK = 1
 MAX_K = 32
 STAGE_PREPROCESS = 0
 STAGE_TOPK = 1
+STAGE_DETECT = 2
+DET_MAX_DET = 1024
 
 
 class TopkEntry(Structure):
     _fields_ = [("score", c_float), ("index", c_int32)]
+
+
+class Det(Structure):
+    _fields_ = [("x1", c_float), ("y1", c_float), ("x2", c_float), ("y2", c_float),
+                ("score", c_float), ("class_id", c_int32)]
+
+
+class DetResult(Structure):
+    _fields_ = [("count", c_int32), ("candidates", c_int32), ("det", Det * DET_MAX_DET)]
 
 
 class LaneConfig(Structure):
@@ -64,6 +75,9 @@ class LaneConfig(Structure):
         ("rows_per_group", c_int32), ("topk_chunk", c_int32),
         ("pixels_per_thread", c_int32),
         ("tensor_dtype", c_int32), ("channel_order", c_int32), ("autotune", c_int32),
+        ("det_classes", c_int32), ("det_max_det", c_int32),
+        ("det_conf", c_float), ("det_iou", c_float),
+        ("det_agnostic", c_int32), ("det_reserved", c_int32), ("det_head_dev", c_void_p),
     ]
 
 
@@ -73,6 +87,7 @@ class LaneView(Structure):
         ("tensor_dev", c_void_p), ("scores_dev", c_void_p),
         ("result_host", POINTER(TopkEntry)),
         ("input_bytes", c_size_t), ("tensor_bytes", c_size_t),
+        ("det_head_dev", c_void_p), ("det_result_host", POINTER(DetResult)),
     ]
 
 
@@ -81,6 +96,7 @@ class LanePlan(Structure):
         ("pre_groups", c_int32), ("pre_block", c_int32), ("rows_per_group", c_int32),
         ("pre_lds_bytes", c_int32), ("topk_groups", c_int32), ("topk_block", c_int32),
         ("topk_chunk", c_int32), ("graph_nodes", c_int32), ("pixels_per_thread", c_int32),
+        ("det_anchors", c_int32), ("det_decode_groups", c_int32),
     ]
 
 
@@ -155,7 +171,9 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
                 host_input=False, use_graph=True, wait_mode=WAIT_SPIN, device=0,
                 input_dev=None, scores_dev=None, tensor_dev=None, rows_per_group=0,
                 topk_chunk=0, pixels_per_thread=0, input_mode=None, tensor_dtype=DTYPE_F32,
-                channel_order=CHANNELS_RGB, autotune=False) -> LaneConfig:
+                channel_order=CHANNELS_RGB, autotune=False, det_classes=0, det_max_det=300,
+                det_conf=0.25, det_iou=0.45, det_agnostic=False,
+                det_head_dev=None) -> LaneConfig:
     c = LaneConfig()
     c.device = device
     c.batch = batch
@@ -180,6 +198,13 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
     c.tensor_dtype = tensor_dtype
     c.channel_order = channel_order
     c.autotune = 1 if autotune else 0
+    c.det_classes = det_classes
+    if det_classes:
+        c.det_max_det = det_max_det
+        c.det_conf = det_conf
+        c.det_iou = det_iou
+        c.det_agnostic = 1 if det_agnostic else 0
+        c.det_head_dev = _addr(det_head_dev)
     return c
 
 
@@ -233,6 +258,18 @@ class Lane:
         raw = np.ctypeslib.as_array(ctypes.cast(self.view.result_host, POINTER(ctypes.c_uint32)),
                                     shape=(2 * k,)).copy()
         return raw[0::2].view(np.float32), raw[1::2].view(np.int32)
+
+    def detections(self) -> tuple[np.ndarray, np.ndarray, np.ndarray, int]:
+        """Copy of the detection slot: (float32 boxes[n][4], float32 scores[n],
+        int32 classes[n], number of candidates)."""
+        if not self.view.det_result_host:
+            raise RuntimeError("lane has no detection stage")
+        r = self.view.det_result_host.contents
+        n = r.count
+        raw = np.ctypeslib.as_array(ctypes.cast(ctypes.addressof(r.det), POINTER(ctypes.c_uint32)),
+                                    shape=(6 * n,)).copy().reshape(n, 6)
+        return (raw[:, :4].view(np.float32).copy(), raw[:, 4].view(np.float32).copy(),
+                raw[:, 5].view(np.int32).copy(), int(r.candidates))
 
     def plan(self) -> dict:
         p = LanePlan()

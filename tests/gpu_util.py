@@ -2,7 +2,8 @@
 compute the oracle's answer for it."""
 import numpy as np
 
-from oracle import preprocess_batch, topk
+from oracle import letterbox_region, preprocess_batch, topk
+from oracle import detect as odet
 from post_processing_amd import workloads as wl
 from post_processing_amd import ws
 
@@ -14,6 +15,23 @@ def oracle_outputs(w: wl.Workload):
                            letterbox=(w.mode == wl.LETTERBOX), pad=w.pad)
     tk = topk(w.scores, w.k) if w.k else None
     return ref, tk
+
+
+def workload_region(w: wl.Workload):
+    """(left, top, width, height) of the image inside the network input."""
+    if w.mode == wl.LETTERBOX:
+        return letterbox_region(w.src_w, w.src_h, w.dst_w, w.dst_h)
+    return (0, 0, w.dst_w, w.dst_h)
+
+
+def oracle_detections(w: wl.Workload, head=None, **override):
+    """The oracle's decode + NMS for a workload's head (or `head`), with
+    optional threshold overrides."""
+    d = dict(w.det)
+    d.update(override)
+    return odet.detect(w.head if head is None else head, w.src_w, w.src_h, w.dst_w, w.dst_h,
+                       workload_region(w), d["nc"], d["conf"], d["iou"], d["max_det"],
+                       d["agnostic"])
 
 
 class Run:
@@ -35,6 +53,14 @@ class Run:
         self.scores = None
         if w.k:
             self.scores = torch.from_numpy(w.scores).to(dev)
+        self.head = None
+        det = {}
+        if w.head is not None:
+            self.head = torch.from_numpy(np.ascontiguousarray(w.head)).to(dev)
+            det = dict(det_classes=w.det["nc"], det_max_det=w.det["max_det"],
+                       det_conf=w.det["conf"], det_iou=w.det["iou"],
+                       det_agnostic=w.det["agnostic"], det_head_dev=self.head)
+            det.update({k: knobs.pop(k) for k in list(knobs) if k.startswith("det_")})
         self.frames = None
         if not self.host_input:
             self.frames = torch.from_numpy(np.ascontiguousarray(w.frames)).to(dev)
@@ -44,7 +70,7 @@ class Run:
                              mean=w.mean, std=w.std, num_scores=w.num_scores, k=w.k,
                              input_mode=input_mode, use_graph=use_graph, tensor_dtype=tensor_dtype,
                              input_dev=self.frames, scores_dev=self.scores,
-                             tensor_dev=self.tensor, **knobs)
+                             tensor_dev=self.tensor, **det, **knobs)
         self.lane = ws.Lane(cfg)
         if self.host_input:
             self.lane.input_host_array()[...] = w.frames
@@ -57,6 +83,9 @@ class Run:
         t = self.tensor.float().cpu().numpy()
         tk = self.lane.result() if self.w.k else None
         return t, tk
+
+    def detections(self):
+        return self.lane.detections()
 
     def close(self):
         self.lane.destroy()
@@ -93,3 +122,15 @@ def assert_topk_exact(got, ref):
     rv, ri = ref
     np.testing.assert_array_equal(gi, ri)
     np.testing.assert_array_equal(gv.view(np.uint32), rv.view(np.uint32))
+
+
+def assert_detections_exact(got, ref):
+    """Kept boxes, scores and classes identical bit for bit, in keep order,
+    and the same number of candidates."""
+    gb, gs, gc, gn = got
+    rb, rs, rc, rn = ref
+    assert gn == rn, f"candidates: gpu {gn}, oracle {rn}"
+    assert len(gs) == len(rs), f"kept: gpu {len(gs)}, oracle {len(rs)}"
+    np.testing.assert_array_equal(gc, rc)
+    np.testing.assert_array_equal(gs.view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(gb.view(np.uint32), rb.astype(np.float32).view(np.uint32))

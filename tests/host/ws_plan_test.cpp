@@ -73,6 +73,47 @@ static int selftest() {
     BAD(tensor_dtype, 3);
     BAD(channel_order, 2);
     BAD(autotune, 2);
+    {
+        // detection: a valid 640x640 detection lane, then each field out of range
+        ws_lane_config d = good();
+        d.dst_w = d.dst_h = 640;
+        d.det_classes = 80;
+        d.det_max_det = 300;
+        d.det_conf = 0.25f;
+        d.det_iou = 0.45f;
+        CHECK(ws::validate_config(&d) == WS_OK);
+        ws::Plan p;
+        CHECK(ws::make_plan(d, &p) == WS_OK);
+        CHECK(p.det_anchors == 8400 && p.det_level_end[0] == 6400 && p.det_level_end[1] == 8000);
+        CHECK(p.det_grid_w[0] == 80 && p.det_grid_w[1] == 40 && p.det_grid_w[2] == 20);
+        CHECK(p.det_decode_groups == 33);
+        CHECK(p.det_head_bytes == (size_t)144 * 8400 * 4);
+#define BAD_DET(field, value)                                 \
+    do {                                                      \
+        ws_lane_config b = d;                                 \
+        b.field = value;                                      \
+        CHECK(ws::validate_config(&b) == WS_E_INVALID_ARG);   \
+    } while (0)
+        BAD_DET(det_classes, -1);
+        BAD_DET(det_classes, WS_DET_MAX_CLASSES + 1);
+        BAD_DET(batch, 2);
+        BAD_DET(dst_w, 650);
+        BAD_DET(dst_h, 2048);           // 2048 x 640: more than 16384 anchors
+        BAD_DET(det_max_det, 0);
+        BAD_DET(det_max_det, WS_DET_MAX_DET + 1);
+        BAD_DET(det_conf, -0.1f);
+        BAD_DET(det_conf, 1.0f);
+        BAD_DET(det_iou, 1.5f);
+        BAD_DET(det_agnostic, 2);
+        BAD_DET(det_reserved, 1);
+        BAD_DET(det_head_dev, (const float*)8);
+        ws_lane_config z = good();
+        z.det_head_dev = (const float*)64;      // a head without a detection stage
+        CHECK(ws::validate_config(&z) == WS_E_INVALID_ARG);
+        d.dst_w = 1024;
+        d.dst_h = 512;                          // 8192 + 2048 + 512 anchors
+        CHECK(ws::validate_config(&d) == WS_OK);
+    }
     BAD(num_scores, WS_MAX_SCORES + 1);
     {
         ws_lane_config b = good();
@@ -161,6 +202,13 @@ static int layout() {
     std::printf("ws_lane_config tensor_dtype %zu\n", offsetof(ws_lane_config, tensor_dtype));
     std::printf("ws_lane_config channel_order %zu\n", offsetof(ws_lane_config, channel_order));
     std::printf("ws_lane_config autotune %zu\n", offsetof(ws_lane_config, autotune));
+    std::printf("ws_lane_config det_classes %zu\n", offsetof(ws_lane_config, det_classes));
+    std::printf("ws_lane_config det_max_det %zu\n", offsetof(ws_lane_config, det_max_det));
+    std::printf("ws_lane_config det_conf %zu\n", offsetof(ws_lane_config, det_conf));
+    std::printf("ws_lane_config det_iou %zu\n", offsetof(ws_lane_config, det_iou));
+    std::printf("ws_lane_config det_agnostic %zu\n", offsetof(ws_lane_config, det_agnostic));
+    std::printf("ws_lane_config det_reserved %zu\n", offsetof(ws_lane_config, det_reserved));
+    std::printf("ws_lane_config det_head_dev %zu\n", offsetof(ws_lane_config, det_head_dev));
     std::printf("ws_lane_view sizeof %zu\n", sizeof(ws_lane_view));
     std::printf("ws_lane_view input_host %zu\n", offsetof(ws_lane_view, input_host));
     std::printf("ws_lane_view input_dev %zu\n", offsetof(ws_lane_view, input_dev));
@@ -169,6 +217,8 @@ static int layout() {
     std::printf("ws_lane_view result_host %zu\n", offsetof(ws_lane_view, result_host));
     std::printf("ws_lane_view input_bytes %zu\n", offsetof(ws_lane_view, input_bytes));
     std::printf("ws_lane_view tensor_bytes %zu\n", offsetof(ws_lane_view, tensor_bytes));
+    std::printf("ws_lane_view det_head_dev %zu\n", offsetof(ws_lane_view, det_head_dev));
+    std::printf("ws_lane_view det_result_host %zu\n", offsetof(ws_lane_view, det_result_host));
     std::printf("ws_topk_entry sizeof %zu\n", sizeof(ws_topk_entry));
     std::printf("ws_topk_entry score %zu\n", offsetof(ws_topk_entry, score));
     std::printf("ws_topk_entry index %zu\n", offsetof(ws_topk_entry, index));
@@ -182,6 +232,19 @@ static int layout() {
     std::printf("ws_lane_plan topk_chunk %zu\n", offsetof(ws_lane_plan, topk_chunk));
     std::printf("ws_lane_plan graph_nodes %zu\n", offsetof(ws_lane_plan, graph_nodes));
     std::printf("ws_lane_plan pixels_per_thread %zu\n", offsetof(ws_lane_plan, pixels_per_thread));
+    std::printf("ws_lane_plan det_anchors %zu\n", offsetof(ws_lane_plan, det_anchors));
+    std::printf("ws_lane_plan det_decode_groups %zu\n", offsetof(ws_lane_plan, det_decode_groups));
+    std::printf("ws_det sizeof %zu\n", sizeof(ws_det));
+    std::printf("ws_det x1 %zu\n", offsetof(ws_det, x1));
+    std::printf("ws_det y1 %zu\n", offsetof(ws_det, y1));
+    std::printf("ws_det x2 %zu\n", offsetof(ws_det, x2));
+    std::printf("ws_det y2 %zu\n", offsetof(ws_det, y2));
+    std::printf("ws_det score %zu\n", offsetof(ws_det, score));
+    std::printf("ws_det class_id %zu\n", offsetof(ws_det, class_id));
+    std::printf("ws_det_result sizeof %zu\n", sizeof(ws_det_result));
+    std::printf("ws_det_result count %zu\n", offsetof(ws_det_result, count));
+    std::printf("ws_det_result candidates %zu\n", offsetof(ws_det_result, candidates));
+    std::printf("ws_det_result det %zu\n", offsetof(ws_det_result, det));
     return 0;
 }
 

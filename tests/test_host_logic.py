@@ -71,7 +71,8 @@ def test_abi_struct_layout(driver):
     import ctypes
     from post_processing_amd import ws
     mirrors = {"ws_lane_config": ws.LaneConfig, "ws_lane_view": ws.LaneView,
-               "ws_topk_entry": ws.TopkEntry, "ws_lane_plan": ws.LanePlan}
+               "ws_topk_entry": ws.TopkEntry, "ws_lane_plan": ws.LanePlan,
+               "ws_det": ws.Det, "ws_det_result": ws.DetResult}
     seen = {name: set() for name in mirrors}
     for line in run(driver, "layout").splitlines():
         struct, field, value = line.split()

@@ -15,6 +15,8 @@ inputs):
   c4   3840x2160 -> 384x384 + Top-32 of 21843 with 1% duplicates
   c5l  8 lanes, one host thread each, 1920x1080 from mapped host memory, Top-10
   c5t  64 frames 1280x720 -> 224x224 in one launch (preprocess only)
+  c3d  c3's lane plus in-graph detection decode + NMS over a synthetic
+       8400-anchor, 80-class head (conf 0.25, IoU 0.45, at most 300 boxes)
 """
 from __future__ import annotations
 
@@ -47,7 +49,7 @@ MEASURED_TRAFFIC = {
 def kernel_sources_sha() -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in ("ws_kernels.hip", "ws_kernels.h"):
+    for name in ("ws_kernels.hip", "ws_kernels.h", "ws_lanes.h", "ws_detect.hip"):
         with open(os.path.join(ROOT, "post_processing_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -99,6 +101,14 @@ def topk_bytes(w) -> int:
     return 0 if not w.k else 4 * w.num_scores + 8 * w.k
 
 
+def detect_bytes(w, candidates: int, kept: int) -> int:
+    """Decode reads every anchor's class probabilities and each candidate's
+    64 box logits, and writes a 16-byte box and an 8-byte key per candidate;
+    suppression reads those back and writes 24 bytes per kept box."""
+    nc, a = w.det["nc"], w.head.shape[1]
+    return 4 * nc * a + candidates * (256 + 24 + 24) + 24 * kept + 8
+
+
 # ---------------------------------------------------------------------------
 
 def pct(a, q):
@@ -133,6 +143,12 @@ def make_lane(w, torch, host_input=None, use_graph=True):
         keep["scores"] = torch.from_numpy(w.scores).to(dev)
     if not host:
         keep["frames"] = torch.from_numpy(np.ascontiguousarray(w.frames)).to(dev)
+    det = {}
+    if w.head is not None:
+        keep["head"] = torch.from_numpy(np.ascontiguousarray(w.head)).to(dev)
+        det = dict(det_classes=w.det["nc"], det_max_det=w.det["max_det"], det_conf=w.det["conf"],
+                   det_iou=w.det["iou"], det_agnostic=w.det["agnostic"],
+                   det_head_dev=keep["head"])
     torch.cuda.synchronize()
     cfg = ws.make_config(src_w=w.src_w, src_h=w.src_h, dst_w=w.dst_w, dst_h=w.dst_h,
                          batch=w.batch, letterbox=(w.mode == 1), pad=w.pad, mean=w.mean,
@@ -140,7 +156,7 @@ def make_lane(w, torch, host_input=None, use_graph=True):
                          use_graph=use_graph, input_dev=keep.get("frames"),
                          scores_dev=keep.get("scores"), tensor_dev=keep["tensor"],
                          tensor_dtype={"f32": ws.DTYPE_F32, "f16": ws.DTYPE_F16,
-                                       "bf16": ws.DTYPE_BF16}[TENSOR["dtype"]], **KNOBS)
+                                       "bf16": ws.DTYPE_BF16}[TENSOR["dtype"]], **det, **KNOBS)
     lane = ws.Lane(cfg)
     if host:
         lane.input_host_array()[...] = w.frames
@@ -160,6 +176,12 @@ def stage_roofline(lane, w, launches: int) -> dict:
         ms = lane.time_stage(ws.STAGE_TOPK, launches)
         tb = topk_bytes(w)
         out["topk"] = {"us": ms * 1e3, "bytes": tb, "gbs": tb / (ms * 1e-3) / 1e9}
+    if w.head is not None:
+        ms = lane.time_stage(ws.STAGE_DETECT, launches)
+        _, scores, _, cand = lane.detections()
+        db = detect_bytes(w, cand, len(scores))
+        out["detect"] = {"us": ms * 1e3, "bytes": db, "gbs": db / (ms * 1e-3) / 1e9,
+                         "candidates": cand, "kept": len(scores)}
     return out
 
 
@@ -218,13 +240,19 @@ def cpu_model() -> str:
 def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     from threadpoolctl import threadpool_limits
 
-    from oracle import preprocess_batch, topk
+    from oracle import letterbox_region, preprocess_batch, topk
+    from oracle import detect as odet
     with threadpool_limits(1):
         def one():
             preprocess_batch(w.frames, w.dst_w, w.dst_h, w.mean, w.std,
                              letterbox=(w.mode == 1), pad=w.pad)
             if w.k:
                 topk(w.scores, w.k)
+            if w.head is not None:
+                reg = (letterbox_region(w.src_w, w.src_h, w.dst_w, w.dst_h) if w.mode == 1
+                       else (0, 0, w.dst_w, w.dst_h))
+                odet.detect(w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, reg, w.det["nc"],
+                            w.det["conf"], w.det["iou"], w.det["max_det"], w.det["agnostic"])
         one()   # warm-up
         times = []
         t_end = time.perf_counter() + budget_s
@@ -235,7 +263,7 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     med = float(np.median(times))
     return {"value": round(w.batch / med, 3), "unit": "frames/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(times)} frames of {w.name} (float64 preprocess + stable-sort "
-                      f"Top-K), median {med * 1e3:.1f} ms/frame after 1 warm-up, 1 thread",
+                      f"Top-K{' + binary32 decode/NMS' if w.head is not None else ''}), median {med * 1e3:.1f} ms/frame after 1 warm-up, 1 thread",
             "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
@@ -296,7 +324,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="c2",
-                    choices=["c1", "c2", "c3", "c4", "c5l", "c5t", "copy"])
+                    choices=["c1", "c2", "c3", "c4", "c5l", "c5t", "c3d", "copy"])
     ap.add_argument("--copy-mib", type=int, default=256,
                     help="copy workload: bytes per device-to-device copy (MiB)")
     ap.add_argument("--stage-launches", type=int, default=500)
@@ -344,6 +372,8 @@ def main(argv=None) -> int:
         w = work[0]
     elif name == "c5t":
         w = wl.c5_throughput(64)
+    elif name == "c3d":
+        w = wl.c3d()
     else:
         w = wl.ALL_CONFIGS[name]()
     gen_s = time.perf_counter() - t_gen
@@ -400,6 +430,8 @@ def main(argv=None) -> int:
                    "frames_per_step": w.batch, "src": [w.src_w, w.src_h],
                    "dst": [w.dst_w, w.dst_h], "letterbox": w.mode == 1,
                    "topk": {"n": w.num_scores, "k": w.k} if w.k else None,
+                   "detect": ({"anchors": int(w.head.shape[1]), **{k: w.det[k] for k in
+                              ("nc", "conf", "iou", "max_det")}} if w.head is not None else None),
                    "input": args.input or ("mapped" if (w.host_input or name == "c5l") else "device"),
                    "graph": True, "lanes": 8 if name == "c5l" else 1,
                    "parallelism": "single_gpu"},
@@ -408,8 +440,8 @@ def main(argv=None) -> int:
         "p99_over_p50": round(res["p99_over_p50"], 4),
         "preprocess_gbs": round(stages["preprocess"]["gbs"], 2),
         "preprocess_frac_of_hbm_peak": round(stages["preprocess"]["gbs"] / HBM_PEAK_GBS, 5),
-        "kernels": {k: {"us": round(v["us"], 3), "gbs": round(v["gbs"], 2)}
-                    for k, v in stages.items()},
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in stages.items()},
         "plan": res["plan"],
         "roofline": roof,
     }

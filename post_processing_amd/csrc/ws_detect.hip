@@ -6,20 +6,26 @@
 // about 7 KB, cross to pinned memory) and the embedding example (up to 300
 // boxes in source-image coordinates).
 //
-// det_decode_kernel: one thread per anchor.  The best class is the first
-//   maximum of the anchor's class probabilities; an anchor above the
-//   confidence threshold decodes its four DFL distributions, stores its box
-//   by anchor index and appends a 64-bit key to the candidate list (one
-//   atomic per wave).  Key = probability bits (positive, so they order as
-//   integers) : 0x3FFF - anchor : class, so a larger key is a higher score,
-//   then a lower anchor.
-// det_nms_kernel: one 1024-thread workgroup.  Each thread holds up to 16
-//   candidates in registers (keys, and boxes up to 8 per thread).  Every round, the largest live key
-//   in the workgroup is the next box in rank order that no kept box
-//   suppressed -- exactly the next box greedy suppression keeps -- so the
-//   round keeps it, writes it out, and every thread drops its candidates of
-//   the same class whose IoU with it exceeds the threshold.  One barrier per
-//   kept box; suppressed candidates are never sorted.
+// det_decode_kernel (one workgroup per 256 anchors): each thread finds its
+//   anchor's best class; the anchors above the confidence threshold are
+//   compacted in LDS, their DFL distances are computed one lane per
+//   (candidate, box side), and each candidate's box is stored by anchor and
+//   its sort key appended to the candidate list (one atomic per workgroup).
+// det_nms_kernel (one workgroup of 8 waves):
+//   1. sorts the candidate keys descending in LDS (bitonic: DPP exchanges
+//      inside a wave, LDS exchanges across waves).  The key orders by class
+//      first (unless boxes of any class suppress each other), then by
+//      probability descending, then anchor ascending -- so each class is a
+//      contiguous run in rank order;
+//   2. resolves the runs in parallel, one wave per run: 64 candidates at a
+//      time, each is tested against the run's boxes kept so far, then the
+//      first live candidate is kept and suppresses the live ones after it,
+//      and so on.  Boxes of different classes never interact, so this is
+//      exactly greedy suppression restricted to each class, and a class's
+//      run stops once it has max_det boxes;
+//   3. re-sorts the kept boxes of all classes by probability descending,
+//      anchor ascending -- the order in which plain greedy suppression over
+//      all candidates keeps them -- and writes the first max_det.
 //
 // All arithmetic that decides a result (DFL exponentials, boxes, IoU,
 // mapping) is binary32 with one rounding per operation in a fixed order:
@@ -34,8 +40,8 @@ namespace ws {
 namespace {
 
 constexpr int kDecodeBlock = 256;
-constexpr int kNmsBlock = 1024;
-constexpr int kNmsWaves = kNmsBlock / 64;
+constexpr int kNmsThreads = kDetNmsThreads;
+constexpr int kNmsWaves = kNmsThreads / 64;
 constexpr int kBins = WS_DET_REG_MAX;
 
 // e^x for x <= 0 (Cody & Waite, "Software Manual for the Elementary
@@ -105,16 +111,133 @@ __device__ __forceinline__ float to_source(float v, float origin, float scale, f
     return fminf(fmaxf((v - origin) * scale, 0.0f), hi);
 }
 
+// ---------------------------------------------------------------------------
+// Candidate keys.  Larger keys come first; every key is non-zero and unique
+// (the anchor is in it), and bit 0 is free (it marks kept candidates).
+//   by class:  [63:52] 4095 - class, [51:21] probability bits, [20:7] 16383 - anchor
+//   any class: [63:33] probability bits, [32:19] 16383 - anchor, [18:7] class
+// The probability is > conf >= 0, so its sign bit is clear and its bits order
+// as integers.  The second layout is also the rank order of the output.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t make_key(bool any_class, uint32_t prob, int anchor, int cls) {
+    const uint64_t pr = prob & 0x7FFFFFFFu;
+    const uint64_t an = (uint64_t)(0x3FFF - anchor);
+    if (any_class) return (pr << 33) | (an << 19) | ((uint64_t)cls << 7);
+    return ((uint64_t)(0xFFF - cls) << 52) | (pr << 21) | (an << 7);
+}
+
+__device__ __forceinline__ int key_anchor(uint64_t k, bool any_class) {
+    return 0x3FFF - (int)((k >> (any_class ? 19 : 7)) & 0x3FFFu);
+}
+
+__device__ __forceinline__ uint32_t key_group(uint64_t k, bool any_class) {
+    return any_class ? 0u : (uint32_t)(k >> 52);
+}
+
+// A class-ordered key in rank layout (the "any class" layout).
+__device__ __forceinline__ uint64_t to_rank_key(uint64_t k) {
+    const uint64_t cls = 0xFFFu - (k >> 52);
+    return (((k >> 7) & ((1ull << 45) - 1)) << 19) | (cls << 7);
+}
+
+__device__ __forceinline__ float4 readlane4(float4 v, int lane) {
+    return make_float4(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.x), lane)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.y), lane)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.z), lane)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.w), lane)));
+}
+
+// Orders LDS traffic between lanes of one wave.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic stages for block size B with distances J, J/2, ..., 1 over one key
+// per lane.  Lanes in a block whose bit B is clear run ascending, the others
+// descending; DESC flips the whole network.
+template <int B, int J, bool DESC>
+__device__ __forceinline__ uint64_t bitonic_stages(uint64_t x, int lane) {
+    const uint64_t y = xor_lane64<J>(x, lane);
+    const bool lower = (lane & J) == 0;
+    const bool ascending_block = (lane & B) == 0;
+    const bool keep_large = (lower != ascending_block) != DESC;
+    x = ((x > y) == keep_large) ? x : y;
+    if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC>(x, lane);
+    return x;
+}
+
+template <bool DESC>
+__device__ __forceinline__ uint64_t wave_sort(uint64_t x, int lane) {
+    x = bitonic_stages<2, 1, DESC>(x, lane);
+    x = bitonic_stages<4, 2, DESC>(x, lane);
+    x = bitonic_stages<8, 4, DESC>(x, lane);
+    x = bitonic_stages<16, 8, DESC>(x, lane);
+    x = bitonic_stages<32, 16, DESC>(x, lane);
+    return bitonic_stages<64, 32, DESC>(x, lane);
+}
+
+// Sorts s[0, P) descending, P a power of two >= 64, with the whole
+// workgroup.  Distances below 64 are exchanged inside a wave (DPP and
+// permlane swaps), larger ones through LDS.  Ends with a barrier.
+__device__ void sort_desc(uint64_t* s, int P, int tid) {
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int segs = P >> 6;
+    // Blocks up to 64: sort every 64-key run, alternating direction so that
+    // neighbouring runs form bitonic sequences.
+    for (int seg = wave; seg < segs; seg += kNmsWaves) {
+        uint64_t x = s[seg * 64 + lane];
+        x = (seg & 1) == 0 ? wave_sort<true>(x, lane) : wave_sort<false>(x, lane);
+        s[seg * 64 + lane] = x;
+    }
+    __syncthreads();
+    for (int B = 128; B <= P; B <<= 1) {
+        for (int J = B >> 1; J >= 64; J >>= 1) {
+            for (int q = tid; q < (P >> 1); q += kNmsThreads) {
+                const int lo = ((q & ~(J - 1)) << 1) | (q & (J - 1));
+                const int hi = lo + J;
+                const uint64_t a = s[lo], b = s[hi];
+                const bool desc = (lo & B) == 0;
+                if ((a < b) == desc) {
+                    s[lo] = b;
+                    s[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+        for (int seg = wave; seg < segs; seg += kNmsWaves) {
+            uint64_t x = s[seg * 64 + lane];
+            x = ((seg * 64) & B) == 0 ? bitonic_stages<64, 32, true>(x, lane)
+                                      : bitonic_stages<64, 32, false>(x, lane);
+            s[seg * 64 + lane] = x;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kDecodeBlock) void det_decode_kernel(const DetParams p) {
 #pragma clang fp contract(off)
-    const int a = (int)blockIdx.x * kDecodeBlock + (int)threadIdx.x;
-    const int lane = (int)threadIdx.x & 63;
+    __shared__ int s_anchor[kDecodeBlock];
+    __shared__ int s_cls[kDecodeBlock];
+    __shared__ uint32_t s_prob[kDecodeBlock];
+    __shared__ float s_dist[kDecodeBlock][4];
+    __shared__ int s_count;
+    __shared__ uint32_t s_base;
+    const int tid = (int)threadIdx.x;
     const int A = p.anchors;
-    bool cand = false;
-    uint64_t key = 0;
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+
+    // 1. Best class (first maximum; NaN never compares greater) and threshold.
+    const int a = (int)blockIdx.x * kDecodeBlock + tid;
     if (a < A) {
         const float* __restrict__ pr = p.head + (size_t)(4 * kBins) * A + a;
-        float best = -INFINITY;    // NaN never compares greater: it never wins
+        float best = -INFINITY;
         int cls = 0;
         int c = 0;
         for (; c + 8 <= p.nc; c += 8) {
@@ -135,174 +258,234 @@ __global__ __launch_bounds__(kDecodeBlock) void det_decode_kernel(const DetParam
                 cls = c;
             }
         }
-        cand = best > p.conf;
-        if (cand) {
-            const int level = a < p.level_end[0] ? 0 : (a < p.level_end[1] ? 1 : 2);
-            const int cell = a - (level == 0 ? 0 : p.level_end[level - 1]);
-            const int gw = p.grid_w[level];
-            const float cx = (float)(cell % gw) + 0.5f;
-            const float cy = (float)(cell / gw) + 0.5f;
-            const float s = (float)(8 << level);
-            const float* __restrict__ q = p.head + a;
-            const float dl = dfl_side(q, A);
-            const float dt = dfl_side(q + (size_t)kBins * A, A);
-            const float dr = dfl_side(q + (size_t)(2 * kBins) * A, A);
-            const float db = dfl_side(q + (size_t)(3 * kBins) * A, A);
-            p.boxes[a] = make_float4((cx - dl) * s, (cy - dt) * s, (cx + dr) * s, (cy + db) * s);
-            key = ((uint64_t)__float_as_uint(best) << 32) | ((uint64_t)(0x3FFF - a) << 16) |
-                  (uint64_t)(uint32_t)cls;
+        if (best > p.conf) {
+            const int slot = atomicAdd(&s_count, 1);
+            s_anchor[slot] = a;
+            s_cls[slot] = cls;
+            s_prob[slot] = __float_as_uint(best);
         }
     }
-    // Append the wave's candidates with one atomic.
-    const uint64_t m = __ballot(cand);
-    if (m != 0) {
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        uint32_t base = 0;
-        if (lane == leader) base = atomicAdd(p.counter, (uint32_t)__popcll(m));
-        base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
-        if (cand) {
-            const uint32_t idx = base + (uint32_t)lanes_below(m);
-            if (idx < (uint32_t)A) p.keys[idx] = key;
-        }
+    __syncthreads();
+    const int n = s_count;   // uniform
+    if (n == 0) return;
+
+    // 2. DFL distances, one lane per (candidate, side); each lane issues its
+    //    16 loads before any arithmetic.
+    for (int t = tid; t < 4 * n; t += kDecodeBlock) {
+        const int q = t >> 2;
+        const int side = t & 3;
+        s_dist[q][side] = dfl_side(p.head + (size_t)(side * kBins) * A + s_anchor[q], A);
+    }
+    if (tid == 0) s_base = atomicAdd(p.counter, (uint32_t)n);
+    __syncthreads();
+
+    // 3. Boxes by anchor, keys appended to the candidate list.
+    const uint32_t base = s_base;
+    const bool any_class = p.agnostic != 0;
+    for (int q = tid; q < n; q += kDecodeBlock) {
+        const int aq = s_anchor[q];
+        const int level = aq < p.level_end[0] ? 0 : (aq < p.level_end[1] ? 1 : 2);
+        const int cell = aq - (level == 0 ? 0 : p.level_end[level - 1]);
+        const int gw = p.grid_w[level];
+        const float cx = (float)(cell % gw) + 0.5f;
+        const float cy = (float)(cell / gw) + 0.5f;
+        const float st = (float)(8 << level);
+        p.boxes[aq] = make_float4((cx - s_dist[q][0]) * st, (cy - s_dist[q][1]) * st,
+                                  (cx + s_dist[q][2]) * st, (cy + s_dist[q][3]) * st);
+        const uint32_t idx = base + (uint32_t)q;   // < anchors: each anchor appears once
+        if (idx < (uint32_t)A) p.keys[idx] = make_key(any_class, s_prob[q], aq, s_cls[q]);
     }
 }
 
-// S candidates per thread.  REG_BOXES: boxes live in registers beside their
-// keys (up to 8 per thread); otherwise only keys do and boxes are re-read from
-// the anchor-indexed box buffer (L2-resident) when a test needs them -- the
-// rare case of more than 8192 candidates.
-template <int S, bool REG_BOXES>
-__device__ __forceinline__ void nms_rounds(const DetParams& p, int n,
-                                           uint64_t (*s_key)[kNmsWaves],
-                                           float4 (*s_box)[kNmsWaves]) {
+// ---------------------------------------------------------------------------
+// Suppression
+// ---------------------------------------------------------------------------
+
+// Greedy suppression over one class's run s[s0 ..) (all of s when boxes of
+// any class interact), by one wave.  Kept candidates get bit 0 set in s and
+// their positions listed in kept_pos (capacity max_det).  Returns how many
+// were kept.
+__device__ int resolve_run(const DetParams& p, uint64_t* s, int n, int s0, uint16_t* kept_pos,
+                           bool any_class, int lane) {
 #pragma clang fp contract(off)
+    const uint32_t group = key_group(s[s0], any_class);
+    const float thr = p.iou;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    int kept = 0;
+    for (int c0 = s0; c0 < n; c0 += 64) {
+        wave_lds_sync();   // kept_pos writes of the previous block are visible
+        const int e = c0 + lane;
+        const uint64_t key = e < n ? s[e] : 0;
+        const bool valid = e < n && key_group(key, any_class) == group;
+        const uint64_t vmask = __ballot(valid);
+        if (vmask == 0) break;
+        const float4 box = valid ? p.boxes[key_anchor(key, any_class)] : zero;
+        uint64_t alive = vmask;
+
+        // Boxes of this run kept in earlier blocks, 64 at a time.
+        for (int kb = 0; kb < kept && alive != 0; kb += 64) {
+            const int kl = kb + lane;
+            const float4 kbox =
+                kl < kept ? p.boxes[key_anchor(s[kept_pos[kl]], any_class)] : zero;
+            const int lim = min(64, kept - kb);
+            for (int t = 0; t < lim && alive != 0; ++t) {
+                const float4 b = readlane4(kbox, t);
+                const bool sup = valid && iou_xyxy(b, box) > thr;
+                alive &= ~(uint64_t)__ballot(sup);
+            }
+        }
+
+        // This block: the first live candidate is the next kept box.
+        uint64_t pending = alive;
+        while (pending != 0) {
+            const int i = __ffsll((unsigned long long)pending) - 1;
+            if (lane == i) {
+                kept_pos[kept] = (uint16_t)e;
+                s[e] = key | 1u;
+            }
+            ++kept;
+            if (kept == p.max_det) return kept;
+            const float4 b = readlane4(box, i);
+            const bool sup = lane > i && iou_xyxy(b, box) > thr;
+            alive &= ~(uint64_t)__ballot(sup);
+            pending = alive & ~((2ull << i) - 1);   // candidates after i
+        }
+        if (vmask != ~0ull) break;   // the run ended inside this block
+    }
+    return kept;
+}
+
+__global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p) {
+#pragma clang fp contract(off)
+    // Dynamic LDS: keys [sort_cap] | run starts [kDetRunCap] | kept positions
+    // [kNmsWaves][max_det].
+    extern __shared__ uint64_t s_dyn[];
+    uint64_t* s = s_dyn;
+    uint16_t* s_run = reinterpret_cast<uint16_t*>(s_dyn + p.sort_cap);
+    uint16_t* s_kept = s_run + kDetRunCap;
+    __shared__ int s_n, s_runs, s_total;
+
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const float4* __restrict__ boxes = p.boxes;
-    auto box_of = [boxes](uint64_t k) { return boxes[0x3FFF - (int)((k >> 16) & 0x3FFFu)]; };
-    uint64_t key[S];
-    float4 box[REG_BOXES ? S : 1];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int i = s * kNmsBlock + tid;
-        key[s] = i < n ? p.keys[i] : 0;
-        if constexpr (REG_BOXES) box[s] = key[s] ? box_of(key[s]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const bool any_class = p.agnostic != 0;
+    if (tid == 0) {
+        const uint32_t c = *p.counter;
+        s_n = (int)(c < (uint32_t)p.anchors ? c : (uint32_t)p.anchors);
+        *p.counter = 0;   // ready for the next replay's decode
+        s_runs = 0;
+        s_total = 0;
     }
-    const float thr = p.iou;
-    int kept = 0;
-    int buf = 0;
-    while (kept < p.max_det) {
-        // This thread's, then this wave's, largest live key.
-        uint64_t best = 0;
-        int bs = 0;
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-            if (key[s] > best) {
-                best = key[s];
-                bs = s;
-            }
-        uint64_t w = umax64(best, xor_lane64<32>(best, lane));
-        w = umax64(w, xor_lane64<16>(w, lane));
-        w = umax64(w, xor_lane64<8>(w, lane));
-        w = umax64(w, xor_lane64<4>(w, lane));
-        w = umax64(w, xor_lane64<2>(w, lane));
-        w = umax64(w, xor_lane64<1>(w, lane));
-        // Keys are unique, so exactly one lane holds a non-zero wave maximum.
-        if (w != 0 ? best == w : lane == 0) {
-            float4 bb = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (w != 0) {
-                if constexpr (REG_BOXES) {
-#pragma unroll
-                    for (int s = 0; s < S; ++s)
-                        if (s == bs) bb = box[s];
-                } else {
-                    bb = box_of(w);
-                }
-            }
-            s_key[buf][wave] = w;
-            s_box[buf][wave] = bb;
-        }
-        // Double-buffered: the next round writes the other half, and the one
-        // after can only start once every thread has passed this barrier.
-        __syncthreads();
-        uint64_t g = 0;
-        int gw = 0;
-#pragma unroll
-        for (int i = 0; i < kNmsWaves; ++i) {
-            const uint64_t k = s_key[buf][i];
-            if (k > g) {
-                g = k;
-                gw = i;
-            }
-        }
-        if (g == 0) break;    // no live candidate left (uniform)
-        const float4 kb = s_box[buf][gw];
-        const uint32_t kc = (uint32_t)g & 0xFFFFu;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            if (key[s] == 0) continue;
-            if (key[s] == g) {
-                key[s] = 0;
-            } else if (p.agnostic || ((uint32_t)key[s] & 0xFFFFu) == kc) {
-                float4 b;
-                if constexpr (REG_BOXES) b = box[s];
-                else b = box_of(key[s]);
-                if (iou_xyxy(kb, b) > thr) key[s] = 0;
-            }
-        }
+    __syncthreads();
+    const int n = s_n;   // uniform
+    if (n == 0) {
         if (tid == 0) {
-            ws_det d;
-            d.x1 = to_source(kb.x, p.left, p.sx, p.src_w);
-            d.y1 = to_source(kb.y, p.top, p.sy, p.src_h);
-            d.x2 = to_source(kb.z, p.left, p.sx, p.src_w);
-            d.y2 = to_source(kb.w, p.top, p.sy, p.src_h);
-            d.score = __uint_as_float((uint32_t)(g >> 32));
-            d.class_id = (int32_t)kc;
-            p.out->det[kept] = d;
+            p.out->count = 0;
+            p.out->candidates = 0;
         }
-        ++kept;
-        buf ^= 1;
+        return;
+    }
+
+    // 1. Load and sort.
+    int P = 64;
+    while (P < n) P <<= 1;
+    for (int e = tid; e < P; e += kNmsThreads) s[e] = e < n ? p.keys[e] : 0;
+    __syncthreads();
+    sort_desc(s, P, tid);
+
+    // 2. Class runs (one run of everything when any class suppresses any).
+    for (int e = tid; e < n; e += kNmsThreads)
+        if (e == 0 || key_group(s[e], any_class) != key_group(s[e - 1], any_class))
+            s_run[atomicAdd(&s_runs, 1)] = (uint16_t)e;
+    __syncthreads();
+    const int runs = s_runs;
+
+    // 3. Greedy suppression, one wave per run.
+    uint16_t* kept_pos = s_kept + wave * p.max_det;
+    int my_kept = 0;
+    for (int r = wave; r < runs; r += kNmsWaves)
+        my_kept = resolve_run(p, s, n, s_run[r], kept_pos, any_class, lane);
+    __syncthreads();
+
+    // 4. Kept boxes in rank order.  With one run, that is its kept list
+    //    (wave 0 resolved it).  Otherwise gather the flagged keys of all runs
+    //    and sort them.
+    int total;
+    if (any_class) {
+        if (tid == 0) s_total = my_kept;
+        __syncthreads();
+        total = s_total;
+    } else {
+        // Collect into registers first, then write, so no key is overwritten
+        // before it is read.
+        constexpr int kMaxPer = WS_DET_MAX_ANCHORS / kNmsThreads;
+        uint64_t mine[kMaxPer];
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j) {
+            const int e = tid + j * kNmsThreads;
+            const uint64_t k = e < n ? s[e] : 0;
+            mine[j] = (k & 1u) ? to_rank_key(k) : 0;
+            cnt += (k & 1u) ? 1 : 0;
+        }
+        __syncthreads();
+        int slot = cnt > 0 ? atomicAdd(&s_total, cnt) : 0;
+#pragma unroll
+        for (int j = 0; j < kMaxPer; ++j)
+            if (mine[j] != 0) s[slot++] = mine[j];
+        __syncthreads();
+        total = s_total;
+        int P2 = 64;
+        while (P2 < total) P2 <<= 1;
+        for (int e = total + tid; e < P2; e += kNmsThreads) s[e] = 0;
+        __syncthreads();
+        sort_desc(s, P2, tid);
+    }
+
+    // 5. The first max_det, mapped to source pixels, to the mapped slot.
+    const int count = min(total, p.max_det);
+    for (int q = tid; q < count; q += kNmsThreads) {
+        const uint64_t k = any_class ? (s[s_kept[q]] & ~1ull) : s[q];
+        const float4 b = p.boxes[key_anchor(k, true)];
+        ws_det d;
+        d.x1 = to_source(b.x, p.left, p.sx, p.src_w);
+        d.y1 = to_source(b.y, p.top, p.sy, p.src_h);
+        d.x2 = to_source(b.z, p.left, p.sx, p.src_w);
+        d.y2 = to_source(b.w, p.top, p.sy, p.src_h);
+        d.score = __uint_as_float((uint32_t)(k >> 33));
+        d.class_id = (int32_t)((k >> 7) & 0xFFFu);
+        p.out->det[q] = d;
     }
     if (tid == 0) {
-        p.out->count = kept;
+        p.out->count = count;
         p.out->candidates = n;
     }
 }
 
-__global__ __launch_bounds__(kNmsBlock) void det_nms_kernel(const DetParams p) {
-    __shared__ uint64_t s_key[2][kNmsWaves];
-    __shared__ float4 s_box[2][kNmsWaves];
-    __shared__ int s_n;
-    if (threadIdx.x == 0) {
-        const uint32_t c = *p.counter;
-        s_n = (int)(c < (uint32_t)p.anchors ? c : (uint32_t)p.anchors);
-        *p.counter = 0;    // ready for the next replay's decode
-    }
-    __syncthreads();
-    const int n = s_n;    // uniform
-    if (n <= kNmsBlock)
-        nms_rounds<1, true>(p, n, s_key, s_box);
-    else if (n <= 2 * kNmsBlock)
-        nms_rounds<2, true>(p, n, s_key, s_box);
-    else if (n <= 4 * kNmsBlock)
-        nms_rounds<4, true>(p, n, s_key, s_box);
-    else if (n <= 8 * kNmsBlock)
-        nms_rounds<8, true>(p, n, s_key, s_box);
-    else
-        nms_rounds<16, false>(p, n, s_key, s_box);
-}
-
-static_assert(16 * kNmsBlock >= WS_DET_MAX_ANCHORS, "NMS registers must hold every anchor");
+static_assert(WS_DET_MAX_ANCHORS <= 16384, "anchors must fit the 14-bit key field");
+static_assert(WS_DET_MAX_CLASSES <= 4096, "classes must fit the 12-bit key field");
+static_assert(WS_DET_MAX_ANCHORS % kNmsThreads == 0, "gather loop covers every key");
 
 }  // namespace
+
+int det_nms_lds_bytes(int sort_cap, int max_det) {
+    return sort_cap * (int)sizeof(uint64_t) + kDetRunCap * (int)sizeof(uint16_t) +
+           kNmsWaves * max_det * (int)sizeof(uint16_t);
+}
+
+hipError_t set_detect_attributes() {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(det_nms_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               det_nms_lds_bytes(WS_DET_MAX_ANCHORS, WS_DET_MAX_DET));
+}
 
 hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream) {
     hipLaunchKernelGGL(det_decode_kernel, dim3((unsigned)decode_groups), dim3(kDecodeBlock), 0,
                        stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(det_nms_kernel, dim3(1), dim3(kNmsBlock), 0, stream, p);
+    hipLaunchKernelGGL(det_nms_kernel, dim3(1), dim3(kNmsThreads),
+                       (unsigned)det_nms_lds_bytes(p.sort_cap, p.max_det), stream, p);
     return hipGetLastError();
 }
 

@@ -63,6 +63,7 @@ struct DetParams {
     float4* boxes;           // [anchors] network-input xyxy, written for candidates
     uint64_t* keys;          // [anchors] compact candidate keys
     uint32_t* counter;       // candidates appended; zero between replays
+    int32_t sort_cap;        // keys the suppression kernel's LDS holds: a power of two >= anchors
     float left, top;         // image region origin in the network input
     float sx, sy;            // source pixels per network pixel (binary32 of W/rw, H/rh)
     float src_w, src_h;      // clip bounds
@@ -74,6 +75,11 @@ hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 // Decode (one thread per anchor) then NMS (one workgroup), in stream order.
 hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream);
+// Dynamic LDS of the suppression kernel, and raising its limit (once per process).
+constexpr int kDetNmsThreads = 512;
+constexpr int kDetRunCap = WS_DET_MAX_CLASSES;   // class runs: at most one per class
+int det_nms_lds_bytes(int sort_cap, int max_det);
+hipError_t set_detect_attributes();
 
 constexpr int kTopkMaxThreads = 256;   // 4 wave64s: one per SIMD
 

@@ -173,7 +173,6 @@ constexpr int kTopkMaxWaves = 4;           // one wave per SIMD of a CU
 constexpr int kTopkSingleGroupMax = 4096;  // up to here one workgroup, no hand-off
 constexpr int kTopkLargeN = 262144;        // beyond: 8 Ki scores per workgroup
 constexpr int kDetDecodeBlock = 256;       // detection decode: one thread per anchor
-constexpr int kDetNmsBlock = 1024;         // detection NMS: one workgroup
 
 struct Plan {
     Region region;
@@ -199,6 +198,7 @@ struct Plan {
     int32_t det_level_end[3] = {0, 0, 0};  // anchor index where each grid ends
     int32_t det_grid_w[3] = {0, 0, 0};     // cells per row of each grid
     int32_t det_decode_groups = 0;         // 256-thread workgroups, one thread per anchor
+    int32_t det_sort_cap = 0;              // power of two >= max(anchors, 64): keys sorted in LDS
     size_t det_head_bytes = 0;
 };
 
@@ -288,6 +288,9 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
         }
         p->det_anchors = end;
         p->det_decode_groups = (int32_t)ceil_div(end, kDetDecodeBlock);
+        int32_t cap = 64;
+        while (cap < end) cap <<= 1;
+        p->det_sort_cap = cap;
         p->det_head_bytes = (size_t)(4 * WS_DET_REG_MAX + c.det_classes) * (size_t)end * 4u;
     }
 

@@ -202,6 +202,7 @@ void fill_params(ws_lane* L) {
     d.boxes = L->det_boxes;
     d.keys = L->det_keys;
     d.counter = L->det_counter;
+    d.sort_cap = P.det_sort_cap;
     d.left = (float)P.region.left;
     d.top = (float)P.region.top;
     // Source pixels per network pixel inside the image region: the binary32
@@ -321,6 +322,8 @@ int build(ws_lane* L) {
         const hipError_t e = hipGetLastError();
         if (P.lds_bytes > 64 * 1024) return fail(L, e, WS_E_HIP);
     }
+    // The suppression kernel keeps every candidate key in LDS.
+    if (P.det_anchors > 0) WS_HIP(ws::set_detect_attributes(), WS_E_HIP);
 
     // ---- buffers ---------------------------------------------------------
     if (c.input_mode == WS_INPUT_MAPPED_HOST) {

@@ -29,7 +29,7 @@ typedef struct ws_lane_plan {
     int32_t graph_nodes;      /* kernel nodes in the captured graph          */
     int32_t pixels_per_thread;/* output pixels per preprocess thread         */
     int32_t det_anchors;      /* detection anchors (0 = no detection stage)  */
-    int32_t det_decode_groups;/* decode workgroups (one thread per anchor)   */
+    int32_t det_decode_groups;/* decode workgroups (64 anchors each)         */
 } ws_lane_plan;
 
 /* Fill *plan for lane.  Returns WS_OK or WS_E_INVALID_ARG (NULL). */

@@ -6,8 +6,8 @@
 // about 7 KB, cross to pinned memory) and the embedding example (up to 300
 // boxes in source-image coordinates).
 //
-// det_decode_kernel (one workgroup per 256 anchors): each thread finds its
-//   anchor's best class; the anchors above the confidence threshold are
+// det_decode_kernel (one workgroup per 64 anchors, four waves): wave w finds
+//   each anchor's best class within the w-th quarter of the classes; the anchors above the confidence threshold are
 //   compacted in LDS, their DFL distances are computed one lane per
 //   (candidate, box side), and each candidate's box is stored by anchor and
 //   its sort key appended to the candidate list (one atomic per workgroup).
@@ -39,7 +39,9 @@
 namespace ws {
 namespace {
 
-constexpr int kDecodeBlock = 256;
+constexpr int kDecodeBlock = kDetDecodeAnchors;
+constexpr int kDecodeParts = 4;               // class ranges per anchor, one wave each
+constexpr int kDecodeThreads = kDecodeParts * kDecodeBlock;
 constexpr int kNmsThreads = kDetNmsThreads;
 constexpr int kNmsWaves = kNmsThreads / 64;
 constexpr int kBins = WS_DET_REG_MAX;
@@ -181,7 +183,7 @@ __device__ __forceinline__ uint64_t wave_sort(uint64_t x, int lane) {
 // Sorts s[0, P) descending, P a power of two >= 64, with the whole
 // workgroup.  Distances below 64 are exchanged inside a wave (DPP and
 // permlane swaps), larger ones through LDS.  Ends with a barrier.
-__device__ void sort_desc(uint64_t* s, int P, int tid) {
+__device__ __forceinline__ void sort_desc(uint64_t* s, int P, int tid) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int segs = P >> 6;
@@ -220,44 +222,64 @@ __device__ void sort_desc(uint64_t* s, int P, int tid) {
 // ---------------------------------------------------------------------------
 // Decode
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kDecodeBlock) void det_decode_kernel(const DetParams p) {
+__global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(const DetParams p) {
 #pragma clang fp contract(off)
     __shared__ int s_anchor[kDecodeBlock];
     __shared__ int s_cls[kDecodeBlock];
     __shared__ uint32_t s_prob[kDecodeBlock];
     __shared__ float s_dist[kDecodeBlock][4];
+    __shared__ float s_pbest[kDecodeParts][kDecodeBlock];
+    __shared__ int s_pcls[kDecodeParts][kDecodeBlock];
     __shared__ int s_count;
     __shared__ uint32_t s_base;
     const int tid = (int)threadIdx.x;
     const int A = p.anchors;
     if (tid == 0) s_count = 0;
-    __syncthreads();
 
     // 1. Best class (first maximum; NaN never compares greater) and threshold.
-    const int a = (int)blockIdx.x * kDecodeBlock + tid;
+    //    Wave w scans the w-th quarter of the classes of the group's anchors.
+    const int a = (int)blockIdx.x * kDecodeBlock + (tid & (kDecodeBlock - 1));
+    const int part = tid / kDecodeBlock;   // wave-uniform
+    const int per = (p.nc + kDecodeParts - 1) / kDecodeParts;
+    const int c_begin = min(p.nc, part * per);
+    const int c_end = min(p.nc, c_begin + per);
+    float best = -INFINITY;
+    int cls = c_begin;
     if (a < A) {
         const float* __restrict__ pr = p.head + (size_t)(4 * kBins) * A + a;
-        float best = -INFINITY;
-        int cls = 0;
-        int c = 0;
-        for (; c + 8 <= p.nc; c += 8) {
-            float v[8];
+        int c = c_begin;
+        for (; c + 16 <= c_end; c += 16) {
+            float v[16];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = pr[(size_t)(c + j) * A];
+            for (int j = 0; j < 16; ++j) v[j] = pr[(size_t)(c + j) * A];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 16; ++j)
                 if (v[j] > best) {
                     best = v[j];
                     cls = c + j;
                 }
         }
-        for (; c < p.nc; ++c) {
+        for (; c < c_end; ++c) {
             const float v = pr[(size_t)c * A];
             if (v > best) {
                 best = v;
                 cls = c;
             }
         }
+    }
+    s_pbest[part][tid & (kDecodeBlock - 1)] = best;
+    s_pcls[part][tid & (kDecodeBlock - 1)] = cls;
+    __syncthreads();
+    if (part == 0 && a < A) {
+        // Later ranges win only when strictly greater: ties keep the first.
+        best = -INFINITY;
+        cls = 0;
+#pragma unroll
+        for (int q = 0; q < kDecodeParts; ++q)
+            if (s_pbest[q][tid] > best) {
+                best = s_pbest[q][tid];
+                cls = s_pcls[q][tid];
+            }
         if (best > p.conf) {
             const int slot = atomicAdd(&s_count, 1);
             s_anchor[slot] = a;
@@ -271,7 +293,7 @@ __global__ __launch_bounds__(kDecodeBlock) void det_decode_kernel(const DetParam
 
     // 2. DFL distances, one lane per (candidate, side); each lane issues its
     //    16 loads before any arithmetic.
-    for (int t = tid; t < 4 * n; t += kDecodeBlock) {
+    for (int t = tid; t < 4 * n; t += kDecodeThreads) {
         const int q = t >> 2;
         const int side = t & 3;
         s_dist[q][side] = dfl_side(p.head + (size_t)(side * kBins) * A + s_anchor[q], A);
@@ -282,7 +304,7 @@ __global__ __launch_bounds__(kDecodeBlock) void det_decode_kernel(const DetParam
     // 3. Boxes by anchor, keys appended to the candidate list.
     const uint32_t base = s_base;
     const bool any_class = p.agnostic != 0;
-    for (int q = tid; q < n; q += kDecodeBlock) {
+    for (int q = tid; q < n; q += kDecodeThreads) {
         const int aq = s_anchor[q];
         const int level = aq < p.level_end[0] ? 0 : (aq < p.level_end[1] ? 1 : 2);
         const int cell = aq - (level == 0 ? 0 : p.level_end[level - 1]);
@@ -302,11 +324,12 @@ __global__ __launch_bounds__(kDecodeBlock) void det_decode_kernel(const DetParam
 // ---------------------------------------------------------------------------
 
 // Greedy suppression over one class's run s[s0 ..) (all of s when boxes of
-// any class interact), by one wave.  Kept candidates get bit 0 set in s and
+// any class interact), by one wave.  s_box holds the boxes in sorted order,
+// or is null (then they are read by anchor from global memory).  Kept candidates get bit 0 set in s and
 // their positions listed in kept_pos (capacity max_det).  Returns how many
 // were kept.
-__device__ int resolve_run(const DetParams& p, uint64_t* s, int n, int s0, uint16_t* kept_pos,
-                           bool any_class, int lane) {
+__device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, const float4* s_box, int n, int s0,
+                           uint16_t* kept_pos, bool any_class, int lane) {
 #pragma clang fp contract(off)
     const uint32_t group = key_group(s[s0], any_class);
     const float thr = p.iou;
@@ -319,14 +342,16 @@ __device__ int resolve_run(const DetParams& p, uint64_t* s, int n, int s0, uint1
         const bool valid = e < n && key_group(key, any_class) == group;
         const uint64_t vmask = __ballot(valid);
         if (vmask == 0) break;
-        const float4 box = valid ? p.boxes[key_anchor(key, any_class)] : zero;
+        const float4 box =
+            valid ? (s_box ? s_box[e] : p.boxes[key_anchor(key, any_class)]) : zero;
         uint64_t alive = vmask;
 
         // Boxes of this run kept in earlier blocks, 64 at a time.
         for (int kb = 0; kb < kept && alive != 0; kb += 64) {
             const int kl = kb + lane;
-            const float4 kbox =
-                kl < kept ? p.boxes[key_anchor(s[kept_pos[kl]], any_class)] : zero;
+            const float4 kbox = kl >= kept ? zero
+                                : (s_box ? s_box[kept_pos[kl]]
+                                         : p.boxes[key_anchor(s[kept_pos[kl]], any_class)]);
             const int lim = min(64, kept - kb);
             for (int t = 0; t < lim && alive != 0; ++t) {
                 const float4 b = readlane4(kbox, t);
@@ -400,11 +425,18 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
     __syncthreads();
     const int runs = s_runs;
 
-    // 3. Greedy suppression, one wave per run.
+    // 3. Boxes in sorted order, into the LDS the sort left free (when it fits),
+    //    then greedy suppression, one wave per run.
+    float4* s_box = nullptr;
+    if ((int64_t)(p.sort_cap - P) * (int64_t)sizeof(uint64_t) >= (int64_t)n * (int64_t)sizeof(float4)) {
+        s_box = reinterpret_cast<float4*>(s + P);   // P * 8 is a multiple of 512: 16-byte aligned
+        for (int e = tid; e < n; e += kNmsThreads) s_box[e] = p.boxes[key_anchor(s[e], any_class)];
+        __syncthreads();
+    }
     uint16_t* kept_pos = s_kept + wave * p.max_det;
     int my_kept = 0;
     for (int r = wave; r < runs; r += kNmsWaves)
-        my_kept = resolve_run(p, s, n, s_run[r], kept_pos, any_class, lane);
+        my_kept = resolve_run(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
     __syncthreads();
 
     // 4. Kept boxes in rank order.  With one run, that is its kept list
@@ -416,23 +448,15 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
         __syncthreads();
         total = s_total;
     } else {
-        // Collect into registers first, then write, so no key is overwritten
-        // before it is read.
-        constexpr int kMaxPer = WS_DET_MAX_ANCHORS / kNmsThreads;
-        uint64_t mine[kMaxPer];
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < kMaxPer; ++j) {
-            const int e = tid + j * kNmsThreads;
+        // 512 positions at a time: every thread reads its key, then the
+        // flagged ones are appended.  A slot is below the number of keys
+        // flagged so far, hence below every position still to be read.
+        for (int base = 0; base < n; base += kNmsThreads) {   // uniform
+            const int e = base + tid;
             const uint64_t k = e < n ? s[e] : 0;
-            mine[j] = (k & 1u) ? to_rank_key(k) : 0;
-            cnt += (k & 1u) ? 1 : 0;
+            __syncthreads();
+            if (k & 1u) s[atomicAdd(&s_total, 1)] = to_rank_key(k);
         }
-        __syncthreads();
-        int slot = cnt > 0 ? atomicAdd(&s_total, cnt) : 0;
-#pragma unroll
-        for (int j = 0; j < kMaxPer; ++j)
-            if (mine[j] != 0) s[slot++] = mine[j];
         __syncthreads();
         total = s_total;
         int P2 = 64;
@@ -480,7 +504,7 @@ hipError_t set_detect_attributes() {
 }
 
 hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream) {
-    hipLaunchKernelGGL(det_decode_kernel, dim3((unsigned)decode_groups), dim3(kDecodeBlock), 0,
+    hipLaunchKernelGGL(det_decode_kernel, dim3((unsigned)decode_groups), dim3(kDecodeThreads), 0,
                        stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -77,6 +77,7 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream);
 // Dynamic LDS of the suppression kernel, and raising its limit (once per process).
 constexpr int kDetNmsThreads = 512;
+constexpr int kDetDecodeAnchors = 64;            // anchors per decode workgroup
 constexpr int kDetRunCap = WS_DET_MAX_CLASSES;   // class runs: at most one per class
 int det_nms_lds_bytes(int sort_cap, int max_det);
 hipError_t set_detect_attributes();

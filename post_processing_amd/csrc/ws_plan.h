@@ -172,7 +172,7 @@ constexpr int kTopkBatch = 1024;           // scores one wave takes per round
 constexpr int kTopkMaxWaves = 4;           // one wave per SIMD of a CU
 constexpr int kTopkSingleGroupMax = 4096;  // up to here one workgroup, no hand-off
 constexpr int kTopkLargeN = 262144;        // beyond: 8 Ki scores per workgroup
-constexpr int kDetDecodeBlock = 256;       // detection decode: one thread per anchor
+constexpr int kDetDecodeBlock = 64;        // detection decode: anchors per workgroup
 
 struct Plan {
     Region region;
@@ -197,7 +197,7 @@ struct Plan {
     int32_t det_anchors = 0;
     int32_t det_level_end[3] = {0, 0, 0};  // anchor index where each grid ends
     int32_t det_grid_w[3] = {0, 0, 0};     // cells per row of each grid
-    int32_t det_decode_groups = 0;         // 256-thread workgroups, one thread per anchor
+    int32_t det_decode_groups = 0;         // decode workgroups, 64 anchors each
     int32_t det_sort_cap = 0;              // power of two >= max(anchors, 64): keys sorted in LDS
     size_t det_head_bytes = 0;
 };

@@ -60,6 +60,8 @@ struct ws_lane {
     int last_err = 0;
 };
 
+static_assert(ws::kDetDecodeBlock == ws::kDetDecodeAnchors, "decode grid and kernel agree");
+
 namespace {
 
 int fail(ws_lane* L, hipError_t e, int code) {

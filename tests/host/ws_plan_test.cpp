@@ -86,7 +86,7 @@ static int selftest() {
         CHECK(ws::make_plan(d, &p) == WS_OK);
         CHECK(p.det_anchors == 8400 && p.det_level_end[0] == 6400 && p.det_level_end[1] == 8000);
         CHECK(p.det_grid_w[0] == 80 && p.det_grid_w[1] == 40 && p.det_grid_w[2] == 20);
-        CHECK(p.det_decode_groups == 33);
+        CHECK(p.det_decode_groups == 132);
         CHECK(p.det_head_bytes == (size_t)144 * 8400 * 4);
 #define BAD_DET(field, value)                                 \
     do {                                                      \

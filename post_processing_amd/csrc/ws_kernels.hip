@@ -243,13 +243,13 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
 // unique and needs no tie logic.  Key 0 is below every real key (sentinel).
 //
 // Each wave64 keeps a sorted list of its 64 best keys, one per lane (lane 0
-// best).  Scores arrive in batches of 1024 (16 keys per lane).  Only keys
-// above the running K-th best can matter; when more than 64 do, the K-th
-// largest of the 64 lane maxima is also a lower bound (K distinct keys of the
-// batch reach it), which prunes the rest; it is found on the 32-bit value
-// image alone, bit by bit with ballots.  Survivors are compacted through the
-// wave's LDS scratch.  A few are inserted one by one; up to 64 - K are merged
-// by counting ranks; more go in tiles of 64, each bitonic-sorted across lanes
+// best).  Scores arrive in batches of 1024 (16 per lane).  Only scores at or
+// above the running K-th best can matter; in a wave's first batch the K-th
+// largest of the 64 lane maxima is also a lower bound (K distinct scores of
+// the batch reach it), which prunes the rest.  Survivors get exact keys and
+// are compacted through the wave's LDS scratch.  A few are inserted one by
+// one; when the list's K best and the survivors fit one key per lane they are
+// bitonic-sorted together; more go in tiles of 64, each sorted across lanes
 // and merged into the list (elementwise max against the reversed tile, then
 // a bitonic clean-up).  All lane exchanges run on the VALU: DPP for lane
 // distances 1, 2, 4, 8 and the permlane swaps for 16 and 32.  Waves of a
@@ -316,15 +316,6 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k, int lane
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(m, lane), k - 1);
 }
 
-// Raw-bit screen for scores against a strictly positive FP32 threshold value
-// whose bits are `cut_bits` (> 0 as a signed integer): for every non-NaN x,
-// int(bits(x)) >= cut_bits  <=>  x >= threshold (negative values and -0 have
-// negative integer images).  Positive NaNs pass too; the exact order key
-// (NaN -> -inf) then rejects them.
-__device__ __forceinline__ bool raw_at_least(float x, int32_t cut_bits) {
-    return (int32_t)__float_as_uint(x) >= cut_bits;
-}
-
 struct WaveTopK {
     uint64_t best;   // this lane's entry of the wave's sorted list
     uint64_t thr;    // K-th best key so far (wave-uniform)
@@ -352,45 +343,22 @@ struct WaveTopK {
         thr = readlane64(best, k - 1);
     }
 
-    // Merge survivors src[0..c) when k + c <= 64: every lane holds one of the
-    // k list keys or one survivor and counts how many of them beat its key,
-    // reading all of them back through LDS broadcasts (16 bytes at a time,
-    // independent loads, no cross-lane chain); then it writes its key at that
-    // rank.  `stage` is this wave's 64-key LDS row; `out` receives the new
-    // list and may overlap src[0..k) (already consumed).
-    __device__ __forceinline__ void rank_merge(const uint64_t* src, int c, uint64_t* stage,
-                                               uint64_t* out) {
-        const int m = k + c;
-        const uint64_t v = lane < k ? best : (lane < m ? src[lane - k] : 0);
-        stage[lane] = v;
-        wave_lds_sync();
-        int rank = 0;
-        const ulonglong2* pairs = reinterpret_cast<const ulonglong2*>(stage);
-#pragma unroll 4
-        for (int j = 0; j < m; j += 2) {
-            const ulonglong2 q = pairs[j >> 1];
-            rank += (q.x > v ? 1 : 0) + (q.y > v ? 1 : 0);
-        }
-        if (lane < k) out[lane] = 0;
-        wave_lds_sync();
-        if (rank < k && v != 0) out[rank] = v;
-        wave_lds_sync();
-        best = lane < k ? out[lane] : 0;
-        thr = readlane64(best, k - 1);
-        wave_lds_sync();   // both rows are free again
-    }
-
     // Merge `cnt` compacted survivors scratch[0..cnt) into the list.
-    __device__ __forceinline__ void merge_survivors(uint64_t* scratch, int cnt, uint64_t* ranks) {
-        const int room = 64 - k;
+    //  - a few: insert one by one;
+    //  - list and survivors fit one key per lane: one bitonic sort of both;
+    //  - otherwise, 64 at a time: sort ascending, then the elementwise
+    //    maximum against the descending list is the top 64 of their union as
+    //    a bitonic sequence, which a clean-up network sorts.
+    // Lanes at or past k may keep real keys below the K-th best; every
+    // consumer reads the list sorted across all 64 lanes, so they never matter.
+    __device__ __forceinline__ void merge_survivors(uint64_t* scratch, int cnt) {
         if (cnt <= kInsertMax) {
             const uint64_t cand = lane < cnt ? scratch[lane] : 0;
             for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
-        } else if (cnt <= 2 * room) {
-            // Pass p reads scratch[p room ..), then writes the list to
-            // scratch[0, k): k <= room, so only pass-0 survivors are overwritten.
-            for (int off = 0; off < cnt; off += room)
-                rank_merge(scratch + off, min(room, cnt - off), ranks, scratch);
+        } else if (k + cnt <= 64) {
+            const uint64_t x = lane < k ? best : (lane < k + cnt ? scratch[lane - k] : 0);
+            best = wave_sort<true>(x, lane);
+            thr = readlane64(best, k - 1);
         } else {
             for (int t = 0; t < cnt; t += 64) {
                 const uint64_t tile = t + lane < cnt ? scratch[t + lane] : 0;
@@ -401,9 +369,8 @@ struct WaveTopK {
     }
 
     // Offer one batch of order keys, kKeysPerLane per lane (0 = nothing).
-    // `scratch` is this wave's LDS area of kBatch keys, `ranks` its 64-key row.
-    __device__ __forceinline__ void offer(const uint64_t (&key)[kKeysPerLane], uint64_t* scratch,
-                                          uint64_t* ranks) {
+    // `scratch` is this wave's LDS area of kBatch keys.
+    __device__ __forceinline__ void offer(const uint64_t (&key)[kKeysPerLane], uint64_t* scratch) {
         uint64_t cut = thr;
         int cnt = 0;
 #pragma unroll
@@ -433,7 +400,7 @@ struct WaveTopK {
             base += __popcll(b);
         }
         wave_lds_sync();
-        merge_survivors(scratch, cnt, ranks);
+        merge_survivors(scratch, cnt);
         wave_lds_sync();
     }
 
@@ -442,7 +409,7 @@ struct WaveTopK {
     // Once the cut is a positive value, scores are screened on their raw bits
     // and only survivors get exact order keys; otherwise every score does.
     __device__ __forceinline__ void offer_scores(const float (&f)[kKeysPerLane], int32_t wb,
-                                                 int32_t g1, uint64_t* scratch, uint64_t* ranks) {
+                                                 int32_t g1, uint64_t* scratch, float* fstage) {
         uint32_t cut_ord = (uint32_t)(thr >> 32);          // value image of the K-th best
         if (cut_ord <= 0x80000000u) {
             // No positive cut yet: the K-th largest lane maximum bounds the
@@ -465,38 +432,83 @@ struct WaveTopK {
                     key[4 * u + j] = kk & (0ull - (uint64_t)(e + j < g1));
                 }
             }
-            offer(key, scratch, ranks);
+            offer(key, scratch);
             return;
         }
-        const int32_t cut_bits = (int32_t)(cut_ord & 0x7fffffffu);
-        int base = 0;
+        // Positive cut t: a score can be among the K best only if x >= t (a
+        // NaN compares false and ranks as -inf; pad positions hold -inf).
+        // Survivors equal to t are kept too: they are genuine scores, so the
+        // merge still returns the exact K best.  Each lane counts its
+        // survivors and marks their slots; an exclusive scan of the counts
+        // (five ballots, one per count bit) gives each lane its first slot in
+        // `scratch`; each lane then walks its own survivors, reading the
+        // values back from its row of `fstage`, and writes their exact keys.
+        const float tf = __uint_as_float(cut_ord & 0x7fffffffu);
+        int cnt = 0;
+        uint32_t marks = 0;
 #pragma unroll
         for (int j = 0; j < kKeysPerLane; ++j) {
-            const bool pass = raw_at_least(f[j], cut_bits);
-            if (__ballot(pass) == 0) continue;   // wave-uniform skip
-            const int32_t e = wb + 4 * (lane + 64 * (j >> 2)) + (j & 3);
-            const uint64_t kk = ((uint64_t)order_image(f[j]) << 32) | (uint32_t)~(uint32_t)e;
-            const bool take = pass && kk > thr;
-            const uint64_t b = __ballot(take);
-            if (take) scratch[base + lanes_below(b)] = kk;
-            base += __popcll(b);
+            const bool pass = f[j] >= tf;
+            cnt += pass ? 1 : 0;
+            marks |= pass ? (1u << j) : 0u;
         }
-        if (base == 0) return;
+        int off = 0, total = 0;
+#pragma unroll
+        for (int bit = 0; bit < 5; ++bit) {       // cnt <= 16
+            const uint64_t b = __ballot((cnt >> bit) & 1);
+            off += lanes_below(b) << bit;
+            total += __popcll(b) << bit;
+        }
+        if (total == 0) return;
+        float4* row = reinterpret_cast<float4*>(fstage + lane * kKeysPerLane);
+#pragma unroll
+        for (int u = 0; u < kKeysPerLane / 4; ++u)
+            row[u] = make_float4(f[4 * u], f[4 * u + 1], f[4 * u + 2], f[4 * u + 3]);
         wave_lds_sync();
-        merge_survivors(scratch, base, ranks);
+        while (marks != 0) {
+            const int j = __builtin_ctz(marks);
+            marks &= marks - 1;
+            const int32_t e = wb + 4 * (lane + 64 * (j >> 2)) + (j & 3);
+            const float x = fstage[lane * kKeysPerLane + j];
+            scratch[off++] = ((uint64_t)order_image(x) << 32) | (uint32_t)~(uint32_t)e;
+        }
+        wave_lds_sync();
+        merge_survivors(scratch, total);
         wave_lds_sync();
     }
 };
 
-// Pairwise tree merge of the waves' lists into wave 0.
+// Two lists of up to 32 keys per register, one per 32-lane half, each
+// sorted descending within its half.  Folding a list read reversed into each
+// half (ascending) is an elementwise maximum -- the 32 largest of each union
+// as a bitonic sequence -- and a clean-up over distances 16 .. 1, which never
+// crosses the halves.
+__device__ __forceinline__ uint64_t fold_halves(uint64_t desc2, uint64_t asc2, int lane) {
+    return bitonic_stages<64, 16, true>(umax64(desc2, asc2), lane);
+}
+
+// Into wave 0: lanes < k of st.best hold the workgroup's k best, descending,
+// other lanes 0.  Each wave's k best go to its LDS row; wave 0 folds rows 1
+// and 3 into rows 0 and 2 side by side (one per half), then the upper half
+// into the lower.
 __device__ __forceinline__ void block_merge(WaveTopK& st, uint64_t (*s_list)[64], int wave,
                                             int waves) {
-    for (int stride = 1; stride < waves; stride <<= 1) {
-        if ((wave & (2 * stride - 1)) == stride) s_list[wave][st.lane] = st.best;
-        __syncthreads();
-        if ((wave & (2 * stride - 1)) == 0 && wave + stride < waves)
-            st.merge_ascending(s_list[wave + stride][63 - st.lane]);
-    }
+    if (waves == 1) return;
+    const int lane = st.lane, k = st.k;
+    if (lane < k) s_list[wave][lane] = st.best;
+    __syncthreads();
+    if (wave != 0) return;
+    const int h = lane & 31, r = 31 - h;
+    const int dw = lane < 32 ? 0 : 2, aw = dw + 1;
+    const uint64_t d = (dw < waves && h < k) ? s_list[dw][h] : 0;
+    const uint64_t a = (aw < waves && r < k) ? s_list[aw][r] : 0;
+    const uint64_t x = fold_halves(d, a, lane);
+    wave_lds_sync();
+    s_list[0][lane] = x;
+    wave_lds_sync();
+    const uint64_t up = (lane < 32 && r < k) ? s_list[0][32 + r] : 0;
+    st.best = fold_halves(lane < 32 ? x : 0, up, lane);
+    st.thr = readlane64(st.best, k - 1);
 }
 
 __device__ __forceinline__ void write_result(const TopkParams& p, uint64_t key, int lane) {
@@ -528,8 +540,12 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ scores, int
     }
 }
 
+constexpr int kFoldRegs = 2;
+constexpr int kTopkStageKeys = (kTopkMaxThreads / 64) * kBatch;   // the scratch area, in keys
+
 __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
     __shared__ uint64_t s_scratch[kTopkMaxThreads / 64][kBatch];
+    __shared__ float s_fstage[kTopkMaxThreads / 64][kBatch];
     __shared__ uint64_t s_list[kTopkMaxThreads / 64][64];
     __shared__ int s_last;
     const int tid = threadIdx.x;
@@ -558,7 +574,7 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
             f[4 * u + 3] = v[u].w;
         }
         if (rb + round < g1) load_batch(p.scores, wb + round, g1, lane, v);
-        st.offer_scores(f, wb, g1, s_scratch[wave], s_list[wave]);
+        st.offer_scores(f, wb, g1, s_scratch[wave], s_fstage[wave]);
     }
     block_merge(st, s_list, wave, waves);
 
@@ -578,19 +594,66 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
     if (!s_last) return;
     __threadfence();
 
+    // 3. Fold the sorted partial lists.  They are staged in LDS a chunk at a
+    //    time and folded by the waves, which then combine their results.
     WaveTopK mt;
     mt.init(p.k, lane);
-    const int64_t total = (int64_t)p.groups * p.k;
-    for (int64_t rb = 0; rb < total; rb += (int64_t)waves * kBatch) {
-        const int64_t wb = rb + (int64_t)wave * kBatch;
-        uint64_t key[kKeysPerLane];
+    uint64_t* stage = &s_scratch[0][0];
+    // Lists are folded two per register (one per 32-lane half) in
+    // kFoldRegs independent registers: wave w takes lists w, w + W, ...
+    uint64_t acc[kFoldRegs];
 #pragma unroll
-        for (int u = 0; u < kKeysPerLane; ++u) {
-            const int64_t i = wb + lane + 64 * u;
-            key[u] = i < total ? p.partials[i] : 0;
+    for (int c = 0; c < kFoldRegs; ++c) acc[c] = 0;
+    const int h = lane & 31, r = 31 - h, half = lane >> 5;
+    const int lists_per_chunk = kTopkStageKeys / p.k;
+    for (int g0 = 0; g0 < p.groups; g0 += lists_per_chunk) {   // uniform
+        const int lists = min(lists_per_chunk, p.groups - g0);
+        const int keys = lists * p.k;
+        // 16 loads in flight per thread before any LDS write.
+        for (int i0 = 0; i0 < keys; i0 += 64 * waves * 16) {   // uniform
+            uint64_t v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = i0 + tid + j * 64 * waves;
+                v[j] = i < keys ? p.partials[(int64_t)g0 * p.k + i] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = i0 + tid + j * 64 * waves;
+                if (i < keys) stage[i] = v[j];
+            }
         }
-        mt.offer(key, s_scratch[wave], s_list[wave]);
+        __syncthreads();
+        // A list past the end reads as zeros; folding it changes nothing, so
+        // the folds are unconditional and the registers' chains overlap.
+        for (int j0 = 0; wave + j0 * waves < lists; j0 += 2 * kFoldRegs) {   // uniform per wave
+            uint64_t asc[kFoldRegs];
+#pragma unroll
+            for (int c = 0; c < kFoldRegs; ++c) {
+                const int l = wave + (j0 + 2 * c + half) * waves;
+                asc[c] = (l < lists && r < p.k) ? stage[l * p.k + r] : 0;
+            }
+#pragma unroll
+            for (int c = 0; c < kFoldRegs; ++c) acc[c] = fold_halves(acc[c], asc[c], lane);
+        }
+        __syncthreads();   // the stage is rewritten by the next chunk
     }
+    // Combine: the registers into acc[0] (half by half), then its upper half
+    // into its lower, through this wave's rows of the (now free) stage.
+    uint64_t* rows = stage + wave * 64;
+#pragma unroll
+    for (int c = 1; c < kFoldRegs; ++c) {
+        rows[lane] = acc[c];
+        wave_lds_sync();
+        const uint64_t a = r < p.k ? rows[half * 32 + r] : 0;
+        wave_lds_sync();
+        acc[0] = fold_halves(acc[0], a, lane);
+    }
+    rows[lane] = acc[0];
+    wave_lds_sync();
+    const uint64_t up = (lane < 32 && r < p.k) ? rows[32 + r] : 0;
+    mt.best = fold_halves(lane < 32 ? acc[0] : 0, up, lane);
+    mt.thr = readlane64(mt.best, p.k - 1);
     block_merge(mt, s_list, wave, waves);
     if (wave == 0) {
         if (lane < p.k) write_result(p, mt.best, lane);

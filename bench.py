@@ -40,9 +40,11 @@ HBM_PEAK_GBS = 8000.0
 # (x2.0 read, x1.0 write).  Valid only for the kernel sources they were taken
 # on: reported as null once those sources change.
 MEASURED_TRAFFIC = {
-    "kernel_sha256_prefix": "75bccd242c92ca94",
-    "c5t_64x1280x720_to_224": {"preprocess": 112_290_000 + 38_540_000},
-    "c2_1920x1080_to_224": {"preprocess": 2_911_000 + 602_000, "topk": 23_000},
+    "kernel_sha256_prefix": "c2ecc6c5c0681bb9",
+    # c5t: FETCH 54,828.5 KiB x 2.0 + WRITE 37,632.1 KiB per launch (67 launches, median)
+    "c5t_64x1280x720_to_224": {"preprocess": 112_288_768 + 38_535_270},
+    # c2: preprocess FETCH 1,411.0 KiB x 2.0 + WRITE 588.0 KiB; Top-K 13.3 KiB x 2.0 + 0.1 KiB
+    "c2_1920x1080_to_224": {"preprocess": 2_889_728 + 602_112, "topk": 27_238 + 102},
 }
 
 
@@ -341,7 +343,24 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
     ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
+    ap.add_argument("--graph-packet-capture", choices=["off", "runtime-default"],
+                    default="runtime-default",
+                    help="HIP runtime graph mode (DEBUG_CLR_GRAPH_PACKET_CAPTURE), read once when "
+                         "HIP starts; 'off' only for comparison")
+    ap.add_argument("--pin-core", type=int, default=-2,
+                    help="run the submit/wait loop on this host core (-2: the last core this "
+                         "process may use; -1: no pinning)")
     args = ap.parse_args(argv)
+    if args.graph_packet_capture == "off":
+        # Must be in the environment before torch (or anything else) starts HIP.
+        os.environ["DEBUG_CLR_GRAPH_PACKET_CAPTURE"] = "0"
+    pinned = None
+    if args.pin_core != -1 and hasattr(os, "sched_setaffinity"):
+        allowed = sorted(os.sched_getaffinity(0))
+        pinned = allowed[-1] if args.pin_core == -2 else args.pin_core
+        if pinned not in allowed:
+            print(f"bench.py: core {pinned} is not available to this process", file=sys.stderr)
+            return 2
 
     if args.gpus != 1:
         print(f"bench.py: this pipeline runs on one GPU per process; --gpus {args.gpus} is not "
@@ -380,6 +399,8 @@ def main(argv=None) -> int:
     print(f"[bench] inputs for {name} ready in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     extra = {}
+    if pinned is not None:
+        os.sched_setaffinity(0, {pinned})   # this thread runs every submit/wait loop below
     if name == "c5l":
         lanes = [make_lane(x, torch) for x in work]
         ws.bench_lanes(lanes, args.warmup)
@@ -434,6 +455,8 @@ def main(argv=None) -> int:
                               ("nc", "conf", "iou", "max_det")}} if w.head is not None else None),
                    "input": args.input or ("mapped" if (w.host_input or name == "c5l") else "device"),
                    "graph": True, "lanes": 8 if name == "c5l" else 1,
+                   "graph_packet_capture": args.graph_packet_capture,
+                   "host_core": pinned,
                    "parallelism": "single_gpu"},
         "p50_us": round(res["p50_us"], 3),
         "p99_us": round(res["p99_us"], 3),

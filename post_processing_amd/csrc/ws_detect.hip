@@ -7,10 +7,11 @@
 // boxes in source-image coordinates).
 //
 // det_decode_kernel (one workgroup per 64 anchors, four waves): wave w finds
-//   each anchor's best class within the w-th quarter of the classes; the anchors above the confidence threshold are
-//   compacted in LDS, their DFL distances are computed one lane per
-//   (candidate, box side), and each candidate's box is stored by anchor and
-//   its sort key appended to the candidate list (one atomic per workgroup).
+//   each anchor's best class within the w-th quarter of the classes; the
+//   anchors above the confidence threshold are compacted in LDS, their DFL
+//   distances are computed one lane per (candidate, box side), and each
+//   candidate's box is stored by anchor and its sort key appended to the
+//   candidate list (one atomic per workgroup).
 // det_nms_kernel (one workgroup of 8 waves):
 //   1. sorts the candidate keys descending in LDS (bitonic: DPP exchanges
 //      inside a wave, LDS exchanges across waves).  The key orders by class

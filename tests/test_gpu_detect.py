@@ -68,9 +68,9 @@ def _uniform_head_workload(seed, nw, nh, nc, conf, iou, max_det, agnostic=False,
                        det=dict(nc=nc, conf=conf, iou=iou, max_det=max_det, agnostic=agnostic))
 
 
-# Candidate counts in each register layout of the suppression kernel:
-# <= 1024, <= 2048, <= 4096, <= 8192 (boxes in registers) and beyond (boxes
-# re-read from the anchor-indexed buffer).
+# Candidate counts across the suppression kernel's sort sizes (1024 .. 16384
+# keys) and both box sources (staged in the LDS the sort leaves free, up to
+# about 5,400 candidates here, else read by anchor from global memory).
 # One class, so about (1 - conf) * 8400 anchors are candidates.
 @pytest.mark.parametrize("conf,lo,hi", [(0.92, 1, 1024), (0.82, 1025, 2048), (0.64, 2049, 4096),
                                         (0.3, 4097, 8192), (0.01, 8193, 8400)])

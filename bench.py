@@ -285,6 +285,12 @@ def versions() -> dict:
         out["hipcc"] = r.stdout.splitlines()[0] if r.stdout else None
     except Exception:
         pass
+    # The HIP runtime the lanes actually run on (the first one loaded wins).
+    try:
+        with open("/proc/self/maps") as f:
+            out["hip_runtime_files"] = sorted({l.split()[-1] for l in f if "libamdhip64" in l})
+    except OSError:
+        pass
     return out
 
 

@@ -24,6 +24,12 @@
  *
  * Threading: at most one host thread may use a lane at a time.  Different
  * lanes are independent and may be driven from different threads.
+ *
+ * HIP runtime: the library links libamdhip64.so.7.  A process must hold one
+ * HIP runtime: when the same process uses a framework that ships its own
+ * (PyTorch wheels do), load that framework first, so this library binds to
+ * the copy already loaded; loading it afterwards maps a second HIP and HSA
+ * runtime, and device calls then fail (typically WS_E_NO_DEVICE).
  */
 #ifndef WS_H
 #define WS_H

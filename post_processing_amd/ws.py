@@ -117,6 +117,14 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m post_processing_amd.build`")
+    # PyTorch wheels carry their own HIP runtime.  Loaded after the library,
+    # torch would bring a second HIP and HSA runtime into the process, and the
+    # two fight over the device.  Loaded before it, the library binds to
+    # torch's copy (same soname), so the process has exactly one.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     lib.ws_create_lane.argtypes = [POINTER(LaneConfig), POINTER(c_void_p), POINTER(LaneView)]
     lib.ws_create_lane.restype = c_int

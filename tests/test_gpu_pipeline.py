@@ -4,6 +4,8 @@ Bar: the FP32 tensor within 1e-5 absolute of the float64 oracle everywhere;
 Top-K indices and value bits identical.  Every workload is run in the launch
 configuration the benchmark uses (captured graph, automatic geometry).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -382,3 +384,25 @@ def test_eight_lanes_concurrently(gpu_lib):
     finally:
         for r in runs:
             r.close()
+
+
+def test_library_loaded_before_torch_in_a_fresh_process(gpu_lib):
+    """Loading the binding before PyTorch must still leave one HIP runtime in
+    the process (the binding loads PyTorch first), so a lane can be created."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "from post_processing_amd import ws, workloads as wl\n"
+        "ws.load()\n"
+        "import torch\n"
+        "maps = [l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l]\n"
+        "assert len(set(maps)) == 1, sorted(set(maps))\n"
+        "w = wl.c1()\n"
+        "cfg = ws.make_config(src_w=w.src_w, src_h=w.src_h, dst_w=w.dst_w, dst_h=w.dst_h)\n"
+        "with ws.Lane(cfg) as lane:\n"
+        "    lane.run()\n"
+        "print('ok')\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=110)
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stderr[-2000:]

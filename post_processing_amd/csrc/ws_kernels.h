@@ -23,6 +23,8 @@ struct PreParams {
     int32_t reg_w, reg_h;
     float inv_den_x;        // 1 / (2 reg_w)
     float inv_den_y;        // 1 / (2 reg_h)
+    uint32_t magic_x;       // floor(2^32 / (2 reg_w)) + 1: division by 2 reg_w as a multiply
+    uint32_t magic_y;       // floor(2^32 / (2 reg_h)) + 1
     int32_t span_lo;        // first staged byte of a source row
     int32_t slot_chunks;    // 16-byte chunks per staged row
     int32_t pixels_per_thread;  // PX: 1, 2 or 4 adjacent output columns

@@ -37,7 +37,10 @@ namespace {
 //     take PX = 1 (more waves per row, shorter per-thread chains); large
 //     batches PX = 4 (fewer, wider stores).
 // Taps are exact integers: src = ((2d + 1) S - R) / (2R), clamped at 0;
-// i0 = floor, the weight is the remainder times 1/(2R) in FP32.
+// i0 = floor, the weight is the remainder times 1/(2R) in FP32.  The floor
+// is a multiply by M = floor(2^32 / 2R) + 1 keeping the high word: for
+// numerators below 2^29 that exceeds the true quotient by less than 1/8, so
+// it is exact or one too large, which the sign of the remainder shows.
 
 constexpr int kStageUnroll = 16;   // 16-byte loads in flight per thread
 constexpr int kMaxSlots = 128;     // 2 staged rows x at most 64 output rows
@@ -47,12 +50,16 @@ struct AxisTap {
     float w;
 };
 
-__device__ __forceinline__ AxisTap exact_tap(int d, int S, int R, float inv_den) {
+__device__ __forceinline__ AxisTap exact_tap(int d, int S, int R, float inv_den, uint32_t magic) {
     int num = (2 * d + 1) * S - R;
     num = num < 0 ? 0 : num;
     const uint32_t den = 2u * (uint32_t)R;
-    const uint32_t i0 = (uint32_t)num / den;
-    const uint32_t rem = (uint32_t)num - i0 * den;
+    uint32_t i0 = __umulhi((uint32_t)num, magic);
+    uint32_t rem = (uint32_t)num - i0 * den;
+    if ((int32_t)rem < 0) {
+        --i0;
+        rem += den;
+    }
     AxisTap t;
     t.i0 = i0;
     t.i1 = i0 + 1 < (uint32_t)S ? i0 + 1 : (uint32_t)S - 1;
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
         const int dy = y_base + (s >> 1) - p.top;
         int64_t a = -1;
         if (dy >= 0 && dy < p.reg_h) {
-            const AxisTap ty = exact_tap(dy, p.src_h, p.reg_h, p.inv_den_y);
+            const AxisTap ty = exact_tap(dy, p.src_h, p.reg_h, p.inv_den_y, p.magic_y);
             const uint32_t yy = (s & 1) ? ty.i1 : ty.i0;
             a = fbase + (int64_t)yy * row_bytes + p.span_lo;
         }
@@ -181,7 +188,7 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
         float wy = 0.0f;
         uint32_t base0 = 0, base1 = 0;
         if (row_in) {
-            wy = exact_tap(dy, p.src_h, p.reg_h, p.inv_den_y).w;
+            wy = exact_tap(dy, p.src_h, p.reg_h, p.inv_den_y, p.magic_y).w;
             base0 = (uint32_t)(2 * r) * slot_bytes + (uint32_t)(slot_addr[2 * r] & 15);
             base1 = (uint32_t)(2 * r + 1) * slot_bytes + (uint32_t)(slot_addr[2 * r + 1] & 15);
         }
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
         for (int i = 0; i < PX; ++i) {
             const int dx = x_first + i - p.left;
             if (row_in && dx >= 0 && dx < p.reg_w) {
-                const AxisTap tx = exact_tap(dx, p.src_w, p.reg_w, p.inv_den_x);
+                const AxisTap tx = exact_tap(dx, p.src_w, p.reg_w, p.inv_den_x, p.magic_x);
                 const uint32_t o0 = 3u * tx.i0 - (uint32_t)p.span_lo;
                 const uint32_t o1 = 3u * tx.i1 - (uint32_t)p.span_lo;
                 const uint32_t t00 = lds_rgb(lds32, base0 + o0);

@@ -164,6 +164,8 @@ void fill_params(ws_lane* L) {
     q.reg_h = P.region.h;
     q.inv_den_x = (float)(1.0 / (2.0 * P.region.w));
     q.inv_den_y = (float)(1.0 / (2.0 * P.region.h));
+    q.magic_x = (uint32_t)((1ull << 32) / (2ull * (uint64_t)P.region.w) + 1);
+    q.magic_y = (uint32_t)((1ull << 32) / (2ull * (uint64_t)P.region.h) + 1);
     q.span_lo = (int32_t)P.span_lo;
     q.slot_chunks = P.slot_bytes / 16;
     q.pixels_per_thread = P.pixels_per_thread;

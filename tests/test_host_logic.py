@@ -84,3 +84,20 @@ def test_abi_struct_layout(driver):
             seen[struct].add(field)
     for name, mirror in mirrors.items():
         assert seen[name] == {f[0] for f in mirror._fields_}, name
+
+
+def test_tap_division_by_multiplier_is_exact():
+    """The preprocess kernel divides tap numerators (< 2^29, since sides are
+    at most 16384) by 2R as a multiply by M = floor(2^32 / 2R) + 1 keeping
+    the high word, then steps back once when the remainder goes negative."""
+    rng = np.random.default_rng(3)
+    for den in list(range(2, 4098, 2)) + list(range(4098, 32769, 126)) + [32768]:
+        m = (1 << 32) // den + 1
+        num = np.concatenate([rng.integers(0, 1 << 29, 4000, dtype=np.uint64),
+                              np.arange(1, 200, dtype=np.uint64) * np.uint64(den) - np.uint64(1),
+                              np.arange(0, 200, dtype=np.uint64) * np.uint64(den),
+                              np.array([(1 << 29) - 1], dtype=np.uint64)])
+        q = (num * np.uint64(m)) >> np.uint64(32)
+        r = num.astype(np.int64) - (q * np.uint64(den)).astype(np.int64)
+        q = q - (r < 0).astype(np.uint64)
+        np.testing.assert_array_equal(q, num // np.uint64(den))

@@ -44,6 +44,7 @@ struct TopkParams {
     int64_t n;
     int32_t k;
     int32_t chunk;           // scores per workgroup, multiple of 1024
+    int32_t keys_per_lane;   // scores per lane per batch: 16 or 32
     int32_t groups;
     int32_t waves;           // wave64s per workgroup, 1..4
     uint64_t* partials;      // [groups][k] order keys (groups > 1)

@@ -313,8 +313,6 @@ __device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
     return bitonic_stages<64, 32, true>(x, lane);
 }
 
-constexpr int kKeysPerLane = 16;                    // one batch = 1024 keys per wave
-constexpr int kBatch = 64 * kKeysPerLane;
 constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
 
 // K-th largest of one 32-bit value per lane, with multiplicity: a descending
@@ -323,7 +321,12 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k, int lane
     return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(m, lane), k - 1);
 }
 
+// E scores per lane per batch (16 or 32): a batch is 64 E scores per wave.
+template <int E>
 struct WaveTopK {
+    static_assert(E == 16 || E == 32, "16 or 32 scores per lane");
+    static constexpr int kBatchE = 64 * E;
+    static constexpr int kCountBits = E == 16 ? 5 : 6;   // bits of a lane's survivor count
     uint64_t best;   // this lane's entry of the wave's sorted list
     uint64_t thr;    // K-th best key so far (wave-uniform)
     int k;
@@ -375,32 +378,32 @@ struct WaveTopK {
         }
     }
 
-    // Offer one batch of order keys, kKeysPerLane per lane (0 = nothing).
-    // `scratch` is this wave's LDS area of kBatch keys.
-    __device__ __forceinline__ void offer(const uint64_t (&key)[kKeysPerLane], uint64_t* scratch) {
+    // Offer one batch of order keys, E per lane (0 = nothing).
+    // `scratch` is this wave's LDS area of kBatchE keys.
+    __device__ __forceinline__ void offer(const uint64_t (&key)[E], uint64_t* scratch) {
         uint64_t cut = thr;
         int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < kKeysPerLane; ++j) cnt += __popcll(__ballot(key[j] > cut));
+        for (int j = 0; j < E; ++j) cnt += __popcll(__ballot(key[j] > cut));
         if (cnt == 0) return;
         if (cnt > 64) {
             // K lanes hold a key whose value image is at least the K-th largest
             // lane maximum t, so every key of the K best has value image >= t.
             uint32_t m = 0;
 #pragma unroll
-            for (int j = 0; j < kKeysPerLane; ++j) m = max(m, (uint32_t)(key[j] >> 32));
+            for (int j = 0; j < E; ++j) m = max(m, (uint32_t)(key[j] >> 32));
             const uint32_t t = wave_kth_largest(m, k, lane);
             const uint64_t tcut = ((uint64_t)t << 32) - 1;   // key > tcut <=> value image >= t
             if (t != 0 && tcut > cut) {
                 cut = tcut;
                 cnt = 0;
 #pragma unroll
-                for (int j = 0; j < kKeysPerLane; ++j) cnt += __popcll(__ballot(key[j] > cut));
+                for (int j = 0; j < E; ++j) cnt += __popcll(__ballot(key[j] > cut));
             }
         }
         int base = 0;
 #pragma unroll
-        for (int j = 0; j < kKeysPerLane; ++j) {
+        for (int j = 0; j < E; ++j) {
             const bool take = key[j] > cut;
             const uint64_t b = __ballot(take);
             if (take) scratch[base + lanes_below(b)] = key[j];
@@ -415,7 +418,7 @@ struct WaveTopK {
     // wb + 4 (lane + 64 u) + j; positions at or past the end hold -inf.
     // Once the cut is a positive value, scores are screened on their raw bits
     // and only survivors get exact order keys; otherwise every score does.
-    __device__ __forceinline__ void offer_scores(const float (&f)[kKeysPerLane], int32_t wb,
+    __device__ __forceinline__ void offer_scores(const float (&f)[E], int32_t wb,
                                                  int32_t g1, uint64_t* scratch, float* fstage) {
         uint32_t cut_ord = (uint32_t)(thr >> 32);          // value image of the K-th best
         if (cut_ord <= 0x80000000u) {
@@ -423,14 +426,14 @@ struct WaveTopK {
             // batch's K best from below.
             float m = -__builtin_inff();
 #pragma unroll
-            for (int j = 0; j < kKeysPerLane; ++j) m = fmaxf(m, f[j]);
+            for (int j = 0; j < E; ++j) m = fmaxf(m, f[j]);
             const uint32_t t = wave_kth_largest(order_image(m), k, lane);
             cut_ord = max(cut_ord, t);
         }
         if (cut_ord <= 0x80000000u) {   // cut at or below +0: exact keys for all
-            uint64_t key[kKeysPerLane];
+            uint64_t key[E];
 #pragma unroll
-            for (int u = 0; u < kKeysPerLane / 4; ++u) {
+            for (int u = 0; u < E / 4; ++u) {
                 const int32_t e = wb + 4 * (lane + 64 * u);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -447,36 +450,36 @@ struct WaveTopK {
         // Survivors equal to t are kept too: they are genuine scores, so the
         // merge still returns the exact K best.  Each lane counts its
         // survivors and marks their slots; an exclusive scan of the counts
-        // (five ballots, one per count bit) gives each lane its first slot in
+        // (one ballot per count bit) gives each lane its first slot in
         // `scratch`; each lane then walks its own survivors, reading the
         // values back from its row of `fstage`, and writes their exact keys.
         const float tf = __uint_as_float(cut_ord & 0x7fffffffu);
         int cnt = 0;
         uint32_t marks = 0;
 #pragma unroll
-        for (int j = 0; j < kKeysPerLane; ++j) {
+        for (int j = 0; j < E; ++j) {
             const bool pass = f[j] >= tf;
             cnt += pass ? 1 : 0;
             marks |= pass ? (1u << j) : 0u;
         }
         int off = 0, total = 0;
 #pragma unroll
-        for (int bit = 0; bit < 5; ++bit) {       // cnt <= 16
+        for (int bit = 0; bit < kCountBits; ++bit) {   // cnt <= E
             const uint64_t b = __ballot((cnt >> bit) & 1);
             off += lanes_below(b) << bit;
             total += __popcll(b) << bit;
         }
         if (total == 0) return;
-        float4* row = reinterpret_cast<float4*>(fstage + lane * kKeysPerLane);
+        float4* row = reinterpret_cast<float4*>(fstage + lane * E);
 #pragma unroll
-        for (int u = 0; u < kKeysPerLane / 4; ++u)
+        for (int u = 0; u < E / 4; ++u)
             row[u] = make_float4(f[4 * u], f[4 * u + 1], f[4 * u + 2], f[4 * u + 3]);
         wave_lds_sync();
         while (marks != 0) {
             const int j = __builtin_ctz(marks);
             marks &= marks - 1;
             const int32_t e = wb + 4 * (lane + 64 * (j >> 2)) + (j & 3);
-            const float x = fstage[lane * kKeysPerLane + j];
+            const float x = fstage[lane * E + j];
             scratch[off++] = ((uint64_t)order_image(x) << 32) | (uint32_t)~(uint32_t)e;
         }
         wave_lds_sync();
@@ -498,7 +501,8 @@ __device__ __forceinline__ uint64_t fold_halves(uint64_t desc2, uint64_t asc2, i
 // other lanes 0.  Each wave's k best go to its LDS row; wave 0 folds rows 1
 // and 3 into rows 0 and 2 side by side (one per half), then the upper half
 // into the lower.
-__device__ __forceinline__ void block_merge(WaveTopK& st, uint64_t (*s_list)[64], int wave,
+template <int E>
+__device__ __forceinline__ void block_merge(WaveTopK<E>& st, uint64_t (*s_list)[64], int wave,
                                             int waves) {
     if (waves == 1) return;
     const int lane = st.lane, k = st.k;
@@ -527,13 +531,14 @@ __device__ __forceinline__ void write_result(const TopkParams& p, uint64_t key, 
     p.result[lane] = make_uint2(bits, idx);
 }
 
-// One wave's batch: 16 scores per lane as four float4 loads, lane-interleaved
+// One wave's batch: E scores per lane as E / 4 float4 loads, lane-interleaved
 // so each load instruction covers 1 KiB of consecutive scores.  Score
 // positions fit in 31 bits (the vector length is an int32).
+template <int E>
 __device__ __forceinline__ void load_batch(const float* __restrict__ scores, int32_t wb, int32_t g1,
-                                           int lane, float4 (&v)[kKeysPerLane / 4]) {
+                                           int lane, float4 (&v)[E / 4]) {
 #pragma unroll
-    for (int u = 0; u < kKeysPerLane / 4; ++u) {
+    for (int u = 0; u < E / 4; ++u) {
         const int32_t e = wb + 4 * (lane + 64 * u);
         const float ninf = -__builtin_inff();
         v[u] = make_float4(ninf, ninf, ninf, ninf);
@@ -548,40 +553,50 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ scores, int
 }
 
 constexpr int kFoldRegs = 2;
-constexpr int kTopkStageKeys = (kTopkMaxThreads / 64) * kBatch;   // the scratch area, in keys
+constexpr int kTopkWaveSlots = kTopkMaxThreads / 64;
 
+// Dynamic LDS: per wave, 64 E survivor keys, then per wave 64 E staged scores.
+template <int E>
+constexpr int topk_lds_bytes() {
+    return kTopkWaveSlots * 64 * E * (int)(sizeof(uint64_t) + sizeof(float));
+}
+
+template <int E>
 __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
-    __shared__ uint64_t s_scratch[kTopkMaxThreads / 64][kBatch];
-    __shared__ float s_fstage[kTopkMaxThreads / 64][kBatch];
-    __shared__ uint64_t s_list[kTopkMaxThreads / 64][64];
+    constexpr int kBatchE = 64 * E;
+    constexpr int kTopkStageKeys = kTopkWaveSlots * kBatchE;   // the scratch area, in keys
+    extern __shared__ uint4 lds_dyn[];
+    uint64_t* const s_keys = reinterpret_cast<uint64_t*>(lds_dyn);
+    float* const s_vals = reinterpret_cast<float*>(s_keys + kTopkStageKeys);
+    __shared__ uint64_t s_list[kTopkWaveSlots][64];
     __shared__ int s_last;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int waves = p.waves;
 
-    WaveTopK st;
+    WaveTopK<E> st;
     st.init(p.k, lane);
 
-    // 1. This workgroup's chunk, one 1024-score batch per wave per round; the
+    // 1. This workgroup's chunk, one 64 E-score batch per wave per round; the
     //    next round's scores are loaded while the current batch is offered.
     const int32_t g0 = (int32_t)blockIdx.x * p.chunk;
     const int32_t g1 = (int32_t)min(p.n, (int64_t)g0 + p.chunk);
-    const int32_t round = waves * kBatch;
-    float4 v[kKeysPerLane / 4];
-    load_batch(p.scores, g0 + wave * kBatch, g1, lane, v);
+    const int32_t round = waves * kBatchE;
+    float4 v[E / 4];
+    load_batch<E>(p.scores, g0 + wave * kBatchE, g1, lane, v);
     for (int32_t rb = g0; rb < g1; rb += round) {
-        const int32_t wb = rb + wave * kBatch;
-        float f[kKeysPerLane];
+        const int32_t wb = rb + wave * kBatchE;
+        float f[E];
 #pragma unroll
-        for (int u = 0; u < kKeysPerLane / 4; ++u) {
+        for (int u = 0; u < E / 4; ++u) {
             f[4 * u + 0] = v[u].x;
             f[4 * u + 1] = v[u].y;
             f[4 * u + 2] = v[u].z;
             f[4 * u + 3] = v[u].w;
         }
-        if (rb + round < g1) load_batch(p.scores, wb + round, g1, lane, v);
-        st.offer_scores(f, wb, g1, s_scratch[wave], s_fstage[wave]);
+        if (rb + round < g1) load_batch<E>(p.scores, wb + round, g1, lane, v);
+        st.offer_scores(f, wb, g1, s_keys + wave * kBatchE, s_vals + wave * kBatchE);
     }
     block_merge(st, s_list, wave, waves);
 
@@ -603,9 +618,9 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
 
     // 3. Fold the sorted partial lists.  They are staged in LDS a chunk at a
     //    time and folded by the waves, which then combine their results.
-    WaveTopK mt;
+    WaveTopK<E> mt;
     mt.init(p.k, lane);
-    uint64_t* stage = &s_scratch[0][0];
+    uint64_t* stage = s_keys;
     // Lists are folded two per register (one per 32-lane half) in
     // kFoldRegs independent registers: wave w takes lists w, w + W, ...
     uint64_t acc[kFoldRegs];
@@ -712,13 +727,21 @@ hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_
 }
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_kernel, dim3((unsigned)p.groups), dim3((unsigned)(64 * p.waves)), 0,
-                       stream, p);
+    const dim3 g((unsigned)p.groups), b((unsigned)(64 * p.waves));
+    if (p.keys_per_lane == 32)
+        hipLaunchKernelGGL(topk_kernel<32>, g, b, (unsigned)topk_lds_bytes<32>(), stream, p);
+    else if (p.keys_per_lane == 16)
+        hipLaunchKernelGGL(topk_kernel<16>, g, b, (unsigned)topk_lds_bytes<16>(), stream, p);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t set_kernel_attributes() {
-    hipError_t e = raise_lds_limit<float>();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<32>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       topk_lds_bytes<32>());
+    if (e == hipSuccess) e = raise_lds_limit<float>();
     if (e == hipSuccess) e = raise_lds_limit<__half>();
     if (e == hipSuccess) e = raise_lds_limit<__hip_bfloat16>();
     return e;

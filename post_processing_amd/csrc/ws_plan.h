@@ -191,6 +191,7 @@ struct Plan {
     int32_t topk_groups = 0;
     int32_t topk_chunk = 0;
     int32_t topk_waves = 0;        // wave64s per Top-K workgroup
+    int32_t topk_keys_per_lane = 0;// scores per lane per batch: 16, or 32 when a wave's share is larger
     // Sizes
     size_t frame_bytes = 0, input_bytes = 0, tensor_bytes = 0;
     // Detection (det_anchors == 0: no detection stage)
@@ -276,6 +277,9 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
         p->topk_chunk = (int32_t)chunk;
         p->topk_waves = (int32_t)std::min<int64_t>(kTopkMaxWaves, chunk / kTopkBatch);
         p->topk_groups = (int32_t)ceil_div(c.num_scores, chunk);
+        // A wave whose share is 2 Ki scores or more takes them 32 per lane
+        // per batch: one selection pass instead of two.
+        p->topk_keys_per_lane = chunk / p->topk_waves >= 2 * kTopkBatch ? 32 : 16;
     }
 
     if (c.det_classes > 0) {

@@ -188,6 +188,7 @@ void fill_params(ws_lane* L) {
     t.chunk = P.topk_chunk;
     t.groups = P.topk_groups;
     t.waves = P.topk_waves;
+    t.keys_per_lane = P.topk_keys_per_lane;
     t.partials = L->partials;
     t.counter = L->counter;
     t.result = L->res_dev;
@@ -287,6 +288,7 @@ int autotune(ws_lane* L) {
             L->plan.topk_chunk = p.topk_chunk;
             L->plan.topk_waves = p.topk_waves;
             L->plan.topk_groups = p.topk_groups;
+            L->plan.topk_keys_per_lane = p.topk_keys_per_lane;
             fill_params(L);
             const double us = time_stage_us(L, WS_STAGE_TOPK, kReps);
             if (us < 0.98 * best_tk) {
@@ -324,7 +326,7 @@ int build(ws_lane* L) {
     // than the default 64 KiB depends on it succeeding.
     if (ws::set_kernel_attributes() != hipSuccess) {
         const hipError_t e = hipGetLastError();
-        if (P.lds_bytes > 64 * 1024) return fail(L, e, WS_E_HIP);
+        if (P.lds_bytes > 64 * 1024 || P.topk_keys_per_lane == 32) return fail(L, e, WS_E_HIP);
     }
     // The suppression kernel keeps every candidate key in LDS.
     if (P.det_anchors > 0) WS_HIP(ws::set_detect_attributes(), WS_E_HIP);
@@ -535,6 +537,7 @@ int ws_lane_describe(const ws_lane* L, ws_lane_plan* plan) {
     plan->pixels_per_thread = L->plan.pixels_per_thread;
     plan->det_anchors = L->plan.det_anchors;
     plan->det_decode_groups = L->plan.det_decode_groups;
+    plan->topk_keys_per_lane = L->plan.topk_keys_per_lane;
     return WS_OK;
 }
 

@@ -96,7 +96,7 @@ class LanePlan(Structure):
         ("pre_groups", c_int32), ("pre_block", c_int32), ("rows_per_group", c_int32),
         ("pre_lds_bytes", c_int32), ("topk_groups", c_int32), ("topk_block", c_int32),
         ("topk_chunk", c_int32), ("graph_nodes", c_int32), ("pixels_per_thread", c_int32),
-        ("det_anchors", c_int32), ("det_decode_groups", c_int32),
+        ("det_anchors", c_int32), ("det_decode_groups", c_int32), ("topk_keys_per_lane", c_int32),
     ]
 
 

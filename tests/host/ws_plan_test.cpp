@@ -172,6 +172,14 @@ static int selftest() {
     CHECK(ws::make_plan(c, &p) == WS_OK);
     CHECK(p.topk_groups * (int64_t)p.topk_chunk >= 672000);
     CHECK(p.topk_chunk % 1024 == 0);
+    CHECK(p.topk_keys_per_lane == 32);      // 2 Ki scores per wave: one pass of 32 per lane
+    c.num_scores = 21843;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(p.topk_keys_per_lane == 16 && p.topk_groups == 6);
+    c.num_scores = 1000;
+    c.k = 5;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(p.topk_keys_per_lane == 16 && p.topk_groups == 1 && p.topk_waves == 1);
     std::printf("%d failures\n", failures);
     return failures == 0 ? 0 : 1;
 }
@@ -234,6 +242,7 @@ static int layout() {
     std::printf("ws_lane_plan pixels_per_thread %zu\n", offsetof(ws_lane_plan, pixels_per_thread));
     std::printf("ws_lane_plan det_anchors %zu\n", offsetof(ws_lane_plan, det_anchors));
     std::printf("ws_lane_plan det_decode_groups %zu\n", offsetof(ws_lane_plan, det_decode_groups));
+    std::printf("ws_lane_plan topk_keys_per_lane %zu\n", offsetof(ws_lane_plan, topk_keys_per_lane));
     std::printf("ws_det sizeof %zu\n", sizeof(ws_det));
     std::printf("ws_det x1 %zu\n", offsetof(ws_det, x1));
     std::printf("ws_det y1 %zu\n", offsetof(ws_det, y1));

@@ -206,3 +206,30 @@ def test_invalid_detection_configs_rejected(gpu_lib):
                              **bad)
         with pytest.raises(ws.WsError):
             ws.Lane(cfg)
+
+
+@pytest.mark.parametrize("variant", ["f16_tensor", "bgr_mapped_input", "copy_input_bf16"])
+def test_detection_with_other_lane_options(gpu_lib, variant):
+    """The detection stage reads only the head, so the other lane options
+    (tensor type, producer byte order, input mode) leave its result unchanged
+    bit for bit; the tensor still meets its own bar."""
+    from gpu_util import assert_rounded_close
+    w = wl.detect_small(7)
+    ref, _ = oracle_outputs(w)
+    if variant == "f16_tensor":
+        r = Run(w, host_input=False, tensor_dtype=ws.DTYPE_F16)
+    elif variant == "bgr_mapped_input":
+        w = dataclasses.replace(w, frames=np.ascontiguousarray(w.frames[..., ::-1]))
+        r = Run(w, input_mode=ws.INPUT_MAPPED_HOST, channel_order=ws.CHANNELS_BGR)
+    else:
+        r = Run(w, input_mode=ws.INPUT_COPY, tensor_dtype=ws.DTYPE_BF16)
+    try:
+        r.run()
+        assert_detections_exact(r.detections(), oracle_detections(w))
+        t, _ = r.outputs()
+        if variant == "bgr_mapped_input":
+            assert_tensor_close(t, ref)
+        else:
+            assert_rounded_close(t, ref, "f16" if variant == "f16_tensor" else "bf16")
+    finally:
+        r.close()

@@ -150,37 +150,6 @@ __device__ __forceinline__ float4 readlane4(float4 v, int lane) {
                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.w), lane)));
 }
 
-// Orders LDS traffic between lanes of one wave.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Bitonic stages for block size B with distances J, J/2, ..., 1 over one key
-// per lane.  Lanes in a block whose bit B is clear run ascending, the others
-// descending; DESC flips the whole network.
-template <int B, int J, bool DESC>
-__device__ __forceinline__ uint64_t bitonic_stages(uint64_t x, int lane) {
-    const uint64_t y = xor_lane64<J>(x, lane);
-    const bool lower = (lane & J) == 0;
-    const bool ascending_block = (lane & B) == 0;
-    const bool keep_large = (lower != ascending_block) != DESC;
-    x = ((x > y) == keep_large) ? x : y;
-    if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC>(x, lane);
-    return x;
-}
-
-template <bool DESC>
-__device__ __forceinline__ uint64_t wave_sort(uint64_t x, int lane) {
-    x = bitonic_stages<2, 1, DESC>(x, lane);
-    x = bitonic_stages<4, 2, DESC>(x, lane);
-    x = bitonic_stages<8, 4, DESC>(x, lane);
-    x = bitonic_stages<16, 8, DESC>(x, lane);
-    x = bitonic_stages<32, 16, DESC>(x, lane);
-    return bitonic_stages<64, 32, DESC>(x, lane);
-}
-
 // Sorts s[0, P) descending, P a power of two >= 64, with the whole
 // workgroup.  Distances below 64 are exchanged inside a wave (DPP and
 // permlane swaps), larger ones through LDS.  Ends with a barrier.

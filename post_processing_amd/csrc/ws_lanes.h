@@ -62,4 +62,40 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Orders LDS traffic between lanes of one wave (in-order per wave on CDNA).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic network stages for block size B with distances J, J/2, ..., 1.
+// Lanes in a block whose bit B is clear run ascending, the others descending;
+// DESC flips the whole network.  B = 64 with J = 32 is the final merge.  One
+// compare per stage: a lane keeps its own key when "mine is larger" agrees
+// with the side of the pair it must end on.
+template <int B, int J, bool DESC, typename T>
+__device__ __forceinline__ T bitonic_stages(T x, int lane) {
+    T y;
+    if constexpr (sizeof(T) == 8) y = xor_lane64<J>(x, lane);
+    else y = xor_lane32<J>(x, lane);
+    const bool lower = (lane & J) == 0;
+    const bool ascending_block = (lane & B) == 0;
+    const bool keep_large = (lower != ascending_block) != DESC;
+    x = ((x > y) == keep_large) ? x : y;
+    if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC>(x, lane);
+    return x;
+}
+
+// Sort one key per lane across the wave.
+template <bool DESC, typename T>
+__device__ __forceinline__ T wave_sort(T x, int lane) {
+    x = bitonic_stages<2, 1, DESC>(x, lane);
+    x = bitonic_stages<4, 2, DESC>(x, lane);
+    x = bitonic_stages<8, 4, DESC>(x, lane);
+    x = bitonic_stages<16, 8, DESC>(x, lane);
+    x = bitonic_stages<32, 16, DESC>(x, lane);
+    return bitonic_stages<64, 32, DESC>(x, lane);
+}
+
 }  // namespace ws

@@ -233,3 +233,37 @@ def test_detection_with_other_lane_options(gpu_lib, variant):
             assert_rounded_close(t, ref, "f16" if variant == "f16_tensor" else "bf16")
     finally:
         r.close()
+
+
+def test_detection_at_the_class_limit(gpu_lib):
+    """4096 classes: each decode wave scans 1024 of them."""
+    rng = np.random.default_rng(4096)
+    nc, nw, nh = 4096, 64, 64
+    A = wl.head_anchor_grid(nw, nh)[0].size
+    head = np.empty((64 + nc, A), F32)
+    head[:64] = rng.normal(0.0, 1.5, (64, A))
+    head[64:] = rng.uniform(0.0, 0.9, (nc, A))
+    winners = rng.integers(0, nc, A)
+    head[64 + winners, np.arange(A)] = rng.uniform(0.9, 1.0, A).astype(F32)
+    frames = rng.integers(0, 256, size=(1, nh, nw, 3), dtype=np.uint8)
+    w = wl.Workload("classes4096", nw, nh, nw, nh, wl.RESIZE, (0.0, 0.0, 0.0), (1.0, 1.0, 1.0),
+                    114.0, 0, frames, None, head=head,
+                    det=dict(nc=nc, conf=0.95, iou=0.5, max_det=300, agnostic=False))
+    got, _ = _run_detect(w)
+    ref = oracle_detections(w)
+    assert ref[3] > 10
+    assert_detections_exact(got, ref)
+
+
+def test_detection_near_the_anchor_limit(gpu_lib):
+    """A 1024 x 768 network input: 16,128 anchors (the limit is 16,384)."""
+    nw, nh = 1024, 768
+    region = (0, 0, nw, nh)
+    head, planted = wl.detection_head(np.random.default_rng(16128), nw, nh, 3, region, 10)
+    frames = np.random.default_rng(1).integers(0, 256, size=(1, nh, nw, 3), dtype=np.uint8)
+    w = wl.Workload("anchors16128", nw, nh, nw, nh, wl.RESIZE, (0.0, 0.0, 0.0), (1.0, 1.0, 1.0),
+                    114.0, 0, frames, None, head=head,
+                    det=dict(nc=3, conf=0.25, iou=0.45, max_det=300, agnostic=False))
+    assert head.shape[1] == 16128
+    got, _ = _run_detect(w)
+    assert_detections_exact(got, oracle_detections(w))

@@ -406,3 +406,61 @@ def test_library_loaded_before_torch_in_a_fresh_process(gpu_lib):
     out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
                          timeout=110)
     assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stderr[-2000:]
+
+
+@pytest.mark.parametrize("shape", [(16384, 6, 16384, 3, False), (5, 16384, 3, 16384, False),
+                                   (16384, 64, 4096, 64, True)])
+def test_maximum_sides(gpu_lib, shape):
+    """Frames and tensors at the 16384-pixel side limit: the widest rows
+    (49,152 bytes each, two staged per output row) and the tallest columns."""
+    sw, sh, dw, dh, letterbox = shape
+    rng = np.random.default_rng(sw + 7 * sh + dw)
+    frames = rng.integers(0, 256, size=(1, sh, sw, 3), dtype=np.uint8)
+    w = wl.Workload(f"max_side_{sw}x{sh}_to_{dw}x{dh}", sw, sh, dw, dh,
+                    wl.LETTERBOX if letterbox else wl.RESIZE, wl.IMAGENET_MEAN, wl.IMAGENET_STD,
+                    114.0, 0, frames, None)
+    ref, _ = oracle_outputs(w)
+    r = Run(w, host_input=False)
+    try:
+        r.run()
+        t, _ = r.outputs()
+        assert_tensor_close(t, ref)
+    finally:
+        r.close()
+
+
+def _order_keys(s):
+    """(value descending, index ascending) as distinct uint64 keys: NaN ranks as
+    -inf and -0 as +0; larger key = better."""
+    b = s.view(np.uint32).copy()
+    b[(b & 0x7FFFFFFF) > 0x7F800000] = 0xFF800000
+    b[b == 0x80000000] = 0
+    img = np.where(b >> 31 == 1, ~b, b | np.uint32(0x80000000)).astype(np.uint64)
+    idx = np.arange(s.size, dtype=np.uint64)
+    return (img << np.uint64(32)) | (~idx & np.uint64(0xFFFFFFFF))
+
+
+@pytest.mark.parametrize("k", [1, 32])
+def test_topk_four_million_scores(gpu_lib, k):
+    """2^22 scores with ties, NaN and specials: checked by the properties that
+    define the exact top K at any size (distinct keys, descending, and no
+    unselected key above the K-th), then ordered by the oracle on the selected
+    set."""
+    n = 1 << 22
+    w = _topk_workload(n, k, 77)
+    r = Run(w, host_input=False)
+    try:
+        r.run()
+        gv, gi = r.outputs()[1]
+    finally:
+        r.close()
+    keys = _order_keys(w.scores)
+    assert len(set(gi.tolist())) == k and (gi >= 0).all() and (gi < n).all()
+    sel = keys[gi]
+    assert (sel[:-1] > sel[1:]).all()            # strictly descending (integer keys)
+    mask = np.ones(n, dtype=bool)
+    mask[gi] = False
+    assert keys[mask].max() < sel[-1]
+    sub_v, sub_i = topk(w.scores[gi], k)          # the oracle on the selected set
+    np.testing.assert_array_equal(gi[sub_i], gi)
+    np.testing.assert_array_equal(gv.view(np.uint32), sub_v.view(np.uint32))

@@ -150,43 +150,89 @@ __device__ __forceinline__ float4 readlane4(float4 v, int lane) {
                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.w), lane)));
 }
 
-// Sorts s[0, P) descending, P a power of two >= 64, with the whole
-// workgroup.  Distances below 64 are exchanged inside a wave (DPP and
-// permlane swaps), larger ones through LDS.  Ends with a barrier.
-__device__ __forceinline__ void sort_desc(uint64_t* s, int P, int tid) {
+// Block sort of the candidate keys (bitonic network, descending): each wave
+// sorts blocks of 64*K keys in registers (sort_block), and only distances of
+// a whole block or more go through LDS.
+
+// One stage (B, J) with J at least a block, through LDS: one thread per pair,
+// four pairs loaded before any is stored.
+__device__ __forceinline__ void cx_pass_lds(uint64_t* s, int P, int B, int J, int tid) {
+    const int pairs = P >> 1;
+    for (int q0 = tid; q0 < pairs; q0 += 4 * kNmsThreads) {
+        int lo[4];
+        uint64_t a[4], b[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int q = q0 + m * kNmsThreads;
+            lo[m] = ((q & ~(J - 1)) << 1) | (q & (J - 1));
+            if (q < pairs) {
+                a[m] = s[lo[m]];
+                b[m] = s[lo[m] + J];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int q = q0 + m * kNmsThreads;
+            if (q < pairs && (a[m] < b[m]) == ((lo[m] & B) == 0)) {
+                s[lo[m]] = b[m];
+                s[lo[m] + J] = a[m];
+            }
+        }
+    }
+}
+
+// Sorts P keys descending into s[0, P), P a power of two with 64 <= P and
+// P / (64 K) blocks.  The keys come from g[0, n) (zero past n) when g is
+// given, else from s itself.  Ends with a barrier.
+template <int K>
+__device__ __forceinline__ void sort_desc_k(uint64_t* s, int P, int tid, const uint64_t* __restrict__ g,
+                                            int n) {
+    constexpr int Q = 64 * K;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int segs = P >> 6;
-    // Blocks up to 64: sort every 64-key run, alternating direction so that
-    // neighbouring runs form bitonic sequences.
-    for (int seg = wave; seg < segs; seg += kNmsWaves) {
-        uint64_t x = s[seg * 64 + lane];
-        x = (seg & 1) == 0 ? wave_sort<true>(x, lane) : wave_sort<false>(x, lane);
-        s[seg * 64 + lane] = x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int blocks = P / Q;
+    for (int b = wave; b < blocks; b += kNmsWaves) {
+        uint64_t x[K];
+        if (g) {
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+                const int e = b * Q + r * 64 + lane;
+                x[r] = e < n ? g[e] : 0;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < K; ++r) x[r] = s[b * Q + r * 64 + lane];
+        }
+        sort_block<K>(x, (b & 1) == 0, lane);
+#pragma unroll
+        for (int r = 0; r < K; ++r) s[b * Q + r * 64 + lane] = x[r];
     }
     __syncthreads();
-    for (int B = 128; B <= P; B <<= 1) {
-        for (int J = B >> 1; J >= 64; J >>= 1) {
-            for (int q = tid; q < (P >> 1); q += kNmsThreads) {
-                const int lo = ((q & ~(J - 1)) << 1) | (q & (J - 1));
-                const int hi = lo + J;
-                const uint64_t a = s[lo], b = s[hi];
-                const bool desc = (lo & B) == 0;
-                if ((a < b) == desc) {
-                    s[lo] = b;
-                    s[hi] = a;
-                }
-            }
+    for (int B = 2 * Q; B <= P; B <<= 1) {
+        for (int J = B >> 1; J >= Q; J >>= 1) {
+            cx_pass_lds(s, P, B, J, tid);
             __syncthreads();
         }
-        for (int seg = wave; seg < segs; seg += kNmsWaves) {
-            uint64_t x = s[seg * 64 + lane];
-            x = ((seg * 64) & B) == 0 ? bitonic_stages<64, 32, true>(x, lane)
-                                      : bitonic_stages<64, 32, false>(x, lane);
-            s[seg * 64 + lane] = x;
+        for (int b = wave; b < blocks; b += kNmsWaves) {
+            uint64_t x[K];
+#pragma unroll
+            for (int r = 0; r < K; ++r) x[r] = s[b * Q + r * 64 + lane];
+            cx_stages<K, 2 * Q, Q / 2>(x, ((b * Q) & B) == 0, lane);
+#pragma unroll
+            for (int r = 0; r < K; ++r) s[b * Q + r * 64 + lane] = x[r];
         }
         __syncthreads();
     }
+}
+
+// Block sizes: one block per wave up to 4096 keys (64 per lane at most 8),
+// then several blocks of 512 per wave.
+__device__ __forceinline__ void sort_desc(uint64_t* s, int P, int tid, const uint64_t* __restrict__ g = nullptr,
+                                          int n = 0) {
+    if (P <= 512) sort_desc_k<1>(s, P, tid, g, n);
+    else if (P == 1024) sort_desc_k<2>(s, P, tid, g, n);
+    else if (P == 2048) sort_desc_k<4>(s, P, tid, g, n);
+    else sort_desc_k<8>(s, P, tid, g, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -294,16 +340,19 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(const DetPar
 // ---------------------------------------------------------------------------
 
 // Greedy suppression over one class's run s[s0 ..) (all of s when boxes of
-// any class interact), by one wave.  s_box holds the boxes in sorted order,
-// or is null (then they are read by anchor from global memory).  Kept candidates get bit 0 set in s and
-// their positions listed in kept_pos (capacity max_det).  Returns how many
-// were kept.
+// any class interact), by one wave.  With STAGED, s_box holds the boxes in
+// sorted order in LDS; otherwise they are read by anchor from global memory.
+// The choice is a template argument so that each instance loads from one
+// address space (a run-time choice between the two pointers compiles to
+// generic loads that wait on both memory counters).  Kept candidates get
+// bit 0 set in s and their positions listed in kept_pos (capacity max_det).
+// Returns how many were kept.
+template <bool STAGED>
 __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, const float4* s_box, int n, int s0,
                            uint16_t* kept_pos, bool any_class, int lane) {
 #pragma clang fp contract(off)
     const uint32_t group = key_group(s[s0], any_class);
     const float thr = p.iou;
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
     int kept = 0;
     for (int c0 = s0; c0 < n; c0 += 64) {
         wave_lds_sync();   // kept_pos writes of the previous block are visible
@@ -312,16 +361,19 @@ __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, cons
         const bool valid = e < n && key_group(key, any_class) == group;
         const uint64_t vmask = __ballot(valid);
         if (vmask == 0) break;
-        const float4 box =
-            valid ? (s_box ? s_box[e] : p.boxes[key_anchor(key, any_class)]) : zero;
+        // Branches rather than a conditional over lvalues, which would give
+        // the zero box a private-memory copy.
+        float4 box = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) box = STAGED ? s_box[e] : p.boxes[key_anchor(key, any_class)];
         uint64_t alive = vmask;
 
         // Boxes of this run kept in earlier blocks, 64 at a time.
         for (int kb = 0; kb < kept && alive != 0; kb += 64) {
             const int kl = kb + lane;
-            const float4 kbox = kl >= kept ? zero
-                                : (s_box ? s_box[kept_pos[kl]]
-                                         : p.boxes[key_anchor(s[kept_pos[kl]], any_class)]);
+            float4 kbox = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (kl < kept)
+                kbox = STAGED ? s_box[kept_pos[kl]]
+                              : p.boxes[key_anchor(s[kept_pos[kl]], any_class)];
             const int lim = min(64, kept - kb);
             for (int t = 0; t < lim && alive != 0; ++t) {
                 const float4 b = readlane4(kbox, t);
@@ -365,7 +417,9 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
     const int wave = tid >> 6;
     const bool any_class = p.agnostic != 0;
     if (tid == 0) {
-        const uint32_t c = *p.counter;
+        // Written by the decode kernel's atomics: read as a device-scope
+        // atomic (a vector load), never through the scalar cache.
+        const uint32_t c = __hip_atomic_load(p.counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_n = (int)(c < (uint32_t)p.anchors ? c : (uint32_t)p.anchors);
         *p.counter = 0;   // ready for the next replay's decode
         s_runs = 0;
@@ -384,9 +438,7 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
     // 1. Load and sort.
     int P = 64;
     while (P < n) P <<= 1;
-    for (int e = tid; e < P; e += kNmsThreads) s[e] = e < n ? p.keys[e] : 0;
-    __syncthreads();
-    sort_desc(s, P, tid);
+    sort_desc(s, P, tid, p.keys, n);
 
     // 2. Class runs (one run of everything when any class suppresses any).
     for (int e = tid; e < n; e += kNmsThreads)
@@ -405,8 +457,13 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
     }
     uint16_t* kept_pos = s_kept + wave * p.max_det;
     int my_kept = 0;
-    for (int r = wave; r < runs; r += kNmsWaves)
-        my_kept = resolve_run(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
+    if (s_box) {
+        for (int r = wave; r < runs; r += kNmsWaves)
+            my_kept = resolve_run<true>(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
+    } else {
+        for (int r = wave; r < runs; r += kNmsWaves)
+            my_kept = resolve_run<false>(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
+    }
     __syncthreads();
 
     // 4. Kept boxes in rank order.  With one run, that is its kept list

@@ -98,4 +98,49 @@ __device__ __forceinline__ T wave_sort(T x, int lane) {
     return bitonic_stages<64, 32, DESC>(x, lane);
 }
 
+// Bitonic network over a block of 64*K keys held K per lane -- key r*64 +
+// lane of the block is x[r] -- so pairs at distance 64 or more are two
+// registers of one lane and closer pairs one register of two lanes (DPP and
+// permlane swaps); the K independent chains keep a wave's VALU busy.
+
+// Stages (B, J), (B, J/2), ..., (B, 1) on one block.  Inside a bitonic block
+// of size B a pair orders descending when bit B of its index is clear and
+// ascending otherwise; when B exceeds the block that bit is the same for the
+// whole block and blk_desc gives it.
+template <int K, int B, int J>
+__device__ __forceinline__ void cx_stages(uint64_t (&x)[K], bool blk_desc, int lane) {
+    constexpr int Q = 64 * K;
+    if constexpr (J >= 64) {
+        constexpr int R = J / 64;
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            if (r & R) continue;
+            const bool desc = B < Q ? ((r * 64) & B) == 0 : blk_desc;
+            const uint64_t a = x[r], b = x[r + R];
+            const bool swap = (a < b) == desc;
+            x[r] = swap ? b : a;
+            x[r + R] = swap ? a : b;
+        }
+    } else {
+        const bool lower = (lane & J) == 0;
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            bool desc;
+            if constexpr (B < 64) desc = (lane & B) == 0;
+            else desc = B < Q ? ((r * 64) & B) == 0 : blk_desc;
+            const uint64_t y = xor_lane64<J>(x[r], lane);
+            x[r] = ((x[r] > y) == (lower == desc)) ? x[r] : y;
+        }
+    }
+    if constexpr (J > 1) cx_stages<K, B, J / 2>(x, blk_desc, lane);
+}
+
+// Every level of the network inside one block: afterwards the block is sorted
+// descending if blk_desc, else ascending.
+template <int K, int B = 2>
+__device__ __forceinline__ void sort_block(uint64_t (&x)[K], bool blk_desc, int lane) {
+    cx_stages<K, B, B / 2>(x, blk_desc, lane);
+    if constexpr (B < 64 * K) sort_block<K, 2 * B>(x, blk_desc, lane);
+}
+
 }  // namespace ws

@@ -37,8 +37,8 @@ struct PreParams {
     float padv[3];          // (pad / 255 - mean[c]) / std[c]
 };
 
-// Exact Top-K over FP32 scores; G workgroups each select their chunk's top K,
-// the last one to finish merges the G partial lists.
+// Exact Top-K over FP32 scores; G workgroups each select their chunk's top K;
+// for G > 1 a one-workgroup merge kernel selects from the G partial lists.
 struct TopkParams {
     const float* scores;     // [n], 16-byte aligned
     int64_t n;
@@ -48,7 +48,6 @@ struct TopkParams {
     int32_t groups;
     int32_t waves;           // wave64s per workgroup, 1..4
     uint64_t* partials;      // [groups][k] order keys (groups > 1)
-    uint32_t* counter;       // arrival counter, zero between launches
     uint2* result;           // [k] {score bits, index}, device view of the slot
 };
 

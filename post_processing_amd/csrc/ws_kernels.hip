@@ -260,8 +260,11 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
 // and merged into the list (elementwise max against the reversed tile, then
 // a bitonic clean-up).  All lane exchanges run on the VALU: DPP for lane
 // distances 1, 2, 4, 8 and the permlane swaps for 16 and 32.  Waves of a
-// workgroup merge pairwise through LDS; workgroups publish their K best and
-// the last one to arrive merges those lists the same way.
+// workgroup merge pairwise through LDS.  With several workgroups, each
+// publishes its K best; a one-workgroup merge kernel, next in stream order,
+// derives a lower bound on the K-th best from those lists, keeps only the
+// keys at or above it and selects from them.  The kernel boundary orders the
+// two, so no fence or arrival counter sits on the path.
 
 // Order-preserving unsigned image of an FP32 value: NaN -> -inf and -0 -> +0
 // first; then negative values have all bits flipped, others the sign bit set.
@@ -279,10 +282,34 @@ __device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
 
 constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
 
-// K-th largest of one 32-bit value per lane, with multiplicity: a descending
-// bitonic sort across the wave (DPP / permlane exchanges), then lane K - 1.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k, int lane) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(m, lane), k - 1);
+// K-th largest of one 32-bit value per lane, with multiplicity: the largest
+// t that at least K lanes reach, built from the top bit down (a bit stays set
+// when K lanes still reach the prefix with it) -- one compare and one ballot
+// per bit, with no lane exchanges.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        if (__popcll(__ballot(m >= c)) >= k) t = c;
+    }
+    return t;
+}
+
+// Number of the n keys of v (LDS) greater than x; sixteen loads are issued
+// before their compares.
+__device__ __forceinline__ int count_greater(const uint64_t* v, int n, uint64_t x) {
+    int r = 0;
+    int j = 0;
+    for (; j + 16 <= n; j += 16) {
+        uint64_t t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = v[j + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) r += t[u] > x ? 1 : 0;
+    }
+    for (; j < n; ++j) r += v[j] > x ? 1 : 0;
+    return r;
 }
 
 // E scores per lane per batch (16 or 32): a batch is 64 E scores per wave.
@@ -356,7 +383,7 @@ struct WaveTopK {
             uint32_t m = 0;
 #pragma unroll
             for (int j = 0; j < E; ++j) m = max(m, (uint32_t)(key[j] >> 32));
-            const uint32_t t = wave_kth_largest(m, k, lane);
+            const uint32_t t = wave_kth_largest(m, k);
             const uint64_t tcut = ((uint64_t)t << 32) - 1;   // key > tcut <=> value image >= t
             if (t != 0 && tcut > cut) {
                 cut = tcut;
@@ -391,7 +418,7 @@ struct WaveTopK {
             float m = -__builtin_inff();
 #pragma unroll
             for (int j = 0; j < E; ++j) m = fmaxf(m, f[j]);
-            const uint32_t t = wave_kth_largest(order_image(m), k, lane);
+            const uint32_t t = wave_kth_largest(order_image(m), k);
             cut_ord = max(cut_ord, t);
         }
         if (cut_ord <= 0x80000000u) {   // cut at or below +0: exact keys for all
@@ -486,13 +513,18 @@ __device__ __forceinline__ void block_merge(WaveTopK<E>& st, uint64_t (*s_list)[
     st.thr = readlane64(st.best, k - 1);
 }
 
-__device__ __forceinline__ void write_result(const TopkParams& p, uint64_t key, int lane) {
-    // K <= N guarantees K real keys; the guard only keeps a sentinel in bounds.
+// Result slot `slot` from an order key.  The value is the inverse of its
+// order image, which is exact except for a zero's sign (both zeros share an
+// image), so only a zero is read back from the scores.  NaN was ranked as -inf
+// and is reported as -inf.  K <= N guarantees K real keys; the sentinel key 0
+// only keeps a malformed call in bounds.
+__device__ __forceinline__ void write_result(const TopkParams& p, uint64_t key, int slot) {
     const uint32_t idx = ~(uint32_t)key;
-    uint32_t bits = 0xff800000u;
-    if ((int64_t)idx < p.n) bits = __float_as_uint(p.scores[idx]);
-    if ((bits & 0x7fffffffu) > 0x7f800000u) bits = 0xff800000u;   // NaN reported as -inf
-    p.result[lane] = make_uint2(bits, idx);
+    const uint32_t img = (uint32_t)(key >> 32);
+    uint32_t bits = (img & 0x80000000u) ? (img ^ 0x80000000u) : ~img;
+    if (key == 0) bits = 0xff800000u;
+    else if (img == 0x80000000u && (int64_t)idx < p.n) bits = __float_as_uint(p.scores[idx]);
+    p.result[slot] = make_uint2(bits, idx);
 }
 
 // One wave's batch: E scores per lane as E / 4 float4 loads, lane-interleaved
@@ -516,7 +548,6 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ scores, int
     }
 }
 
-constexpr int kFoldRegs = 2;
 constexpr int kTopkWaveSlots = kTopkMaxThreads / 64;
 
 // Dynamic LDS: per wave, 64 E survivor keys, then per wave 64 E staged scores.
@@ -533,7 +564,6 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
     uint64_t* const s_keys = reinterpret_cast<uint64_t*>(lds_dyn);
     float* const s_vals = reinterpret_cast<float*>(s_keys + kTopkStageKeys);
     __shared__ uint64_t s_list[kTopkWaveSlots][64];
-    __shared__ int s_last;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -569,82 +599,113 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
         return;
     }
 
-    // 2. Publish this workgroup's K best; the last workgroup to arrive merges all.
-    if (wave == 0) {
-        if (lane < p.k) p.partials[(int64_t)blockIdx.x * p.k + lane] = st.best;
-        __threadfence();   // release by the only wave that published anything
-    }
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(p.counter, 1u) == (uint32_t)(p.groups - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    // 2. Publish this workgroup's K best for the merge kernel, which follows
+    //    in stream order.
+    if (wave == 0 && lane < p.k) p.partials[(int64_t)blockIdx.x * p.k + lane] = st.best;
+}
 
-    // 3. Fold the sorted partial lists.  They are staged in LDS a chunk at a
-    //    time and folded by the waves, which then combine their results.
-    WaveTopK<E> mt;
-    mt.init(p.k, lane);
-    uint64_t* stage = s_keys;
-    // Lists are folded two per register (one per 32-lane half) in
-    // kFoldRegs independent registers: wave w takes lists w, w + W, ...
-    uint64_t acc[kFoldRegs];
+// Merge of the workgroups' lists (more than one workgroup), by one workgroup
+// of four waves, 256 lists per round.  Any K distinct keys bound the K-th
+// best from below, so the bound is the larger of the K-th key of any one
+// list and the K-th largest of the lists' maxima.  Every key of the K best
+// is in its own workgroup's list, so the keys at or above the bound are all
+// that can matter; they are compacted into LDS.  Keys are distinct, so a
+// survivor's rank is the number of survivors above it, counted against
+// broadcast LDS reads; the K that rank below K write their slots directly.
+// The bound comes from this launch's lists alone: no state carries over
+// between launches.  With more than 256 lists, or more survivors than two per
+// thread, each wave merges a quarter of every round's survivors into its
+// list instead and the lists are merged across waves.
+constexpr int kMergeLists = kTopkMaxThreads;
+constexpr int kMergeKeys = 32;                  // keys per thread per round (K <= 32)
+constexpr int kRankMax = 2 * kTopkMaxThreads;   // survivors ranked by counting
+
+// Survivors' area [kMergeLists * k] then one junk slot per lane.
+int topk_merge_lds_bytes(int k) { return (kMergeLists * k + 64) * (int)sizeof(uint64_t); }
+
+__global__ __launch_bounds__(kTopkMaxThreads) void topk_merge_kernel(TopkParams p) {
+    extern __shared__ uint64_t s_surv[];   // [kMergeLists * k + 64]
+    __shared__ uint64_t s_list[kTopkWaveSlots][64];
+    __shared__ uint64_t s_max[kMergeLists];
+    __shared__ uint64_t s_bound[kTopkWaveSlots];
+    __shared__ int s_cnt;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int k = p.k, G = p.groups;
+    const int junk = kMergeLists * k;
+    uint64_t bound = 1;   // real keys are non-zero
+    WaveTopK<16> st;
+    st.init(k, lane);
+    for (int l0 = 0; l0 < G; l0 += kMergeLists) {   // uniform
+        const int lists = min(kMergeLists, G - l0);
+        const int nkeys = lists * k;
+        const uint64_t* part = p.partials + (int64_t)l0 * k;
+        // This round's keys, coalesced (registers past `regs` stay unused);
+        // and list `tid`'s first and K-th keys.
+        const int regs = (nkeys + kTopkMaxThreads - 1) / kTopkMaxThreads;   // uniform
+        uint64_t key[kMergeKeys];
 #pragma unroll
-    for (int c = 0; c < kFoldRegs; ++c) acc[c] = 0;
-    const int h = lane & 31, r = 31 - h, half = lane >> 5;
-    const int lists_per_chunk = kTopkStageKeys / p.k;
-    for (int g0 = 0; g0 < p.groups; g0 += lists_per_chunk) {   // uniform
-        const int lists = min(lists_per_chunk, p.groups - g0);
-        const int keys = lists * p.k;
-        // 16 loads in flight per thread before any LDS write.
-        for (int i0 = 0; i0 < keys; i0 += 64 * waves * 16) {   // uniform
-            uint64_t v[16];
+        for (int m = 0; m < kMergeKeys; ++m) {
+            const int i = tid + m * kTopkMaxThreads;
+            key[m] = i < nkeys ? part[i] : 0;
+        }
+        const uint64_t mx = tid < lists ? part[tid * k] : 0;
+        uint64_t kth = tid < lists ? part[tid * k + k - 1] : 0;
+        kth = umax64(kth, xor_lane64<32>(kth, lane));
+        kth = umax64(kth, xor_lane64<16>(kth, lane));
+        kth = umax64(kth, xor_lane64<8>(kth, lane));
+        kth = umax64(kth, xor_lane64<4>(kth, lane));
+        kth = umax64(kth, xor_lane64<2>(kth, lane));
+        kth = umax64(kth, xor_lane64<1>(kth, lane));
+        s_max[tid] = mx;
+        if (tid == 0) s_cnt = 0;
+        __syncthreads();
+        // The K-th largest list maximum: the one with exactly K - 1 above it.
+        uint64_t kmax = 0;
+        if (tid < lists && lists >= k && count_greater(s_max, lists, mx) == k - 1) kmax = mx;
+        const uint64_t b = __ballot(kmax != 0);
+        if (b != 0) kmax = readlane64(kmax, __ffsll((unsigned long long)b) - 1);
+        if (lane == 0) s_bound[wave] = umax64(umax64(kmax, kth), st.thr);
+        __syncthreads();
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int i = i0 + tid + j * 64 * waves;
-                v[j] = i < keys ? p.partials[(int64_t)g0 * p.k + i] : 0;
-            }
+        for (int w = 0; w < kTopkWaveSlots; ++w) bound = umax64(bound, s_bound[w]);
+        uint64_t pass[kMergeKeys];
+        int mine = 0;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int i = i0 + tid + j * 64 * waves;
-                if (i < keys) stage[i] = v[j];
+        for (int m = 0; m < kMergeKeys; ++m) {
+            pass[m] = __ballot(key[m] >= bound);   // keys past the round are 0: never pass
+            mine += __popcll(pass[m]);
+        }
+        int base = 0;
+        if (lane == 0 && mine > 0) base = atomicAdd(&s_cnt, mine);
+        base = __builtin_amdgcn_readfirstlane(base);
+        // Every lane stores; a key below the bound goes to the lane's junk
+        // slot past the survivors' area, which no one reads.
+#pragma unroll
+        for (int m = 0; m < kMergeKeys; ++m) {
+            if (m < regs) {   // uniform
+                const uint64_t x = key[m];
+                s_surv[x >= bound ? base + lanes_below(pass[m]) : junk + lane] = x;
+                base += __popcll(pass[m]);
             }
         }
         __syncthreads();
-        // A list past the end reads as zeros; folding it changes nothing, so
-        // the folds are unconditional and the registers' chains overlap.
-        for (int j0 = 0; wave + j0 * waves < lists; j0 += 2 * kFoldRegs) {   // uniform per wave
-            uint64_t asc[kFoldRegs];
-#pragma unroll
-            for (int c = 0; c < kFoldRegs; ++c) {
-                const int l = wave + (j0 + 2 * c + half) * waves;
-                asc[c] = (l < lists && r < p.k) ? stage[l * p.k + r] : 0;
+        const int cnt = s_cnt;
+        if (G <= kMergeLists && cnt <= kRankMax) {
+            for (int i = tid; i < cnt; i += kTopkMaxThreads) {
+                const uint64_t x = s_surv[i];
+                const int r = count_greater(s_surv, cnt, x);
+                if (r < k) write_result(p, x, r);
             }
-#pragma unroll
-            for (int c = 0; c < kFoldRegs; ++c) acc[c] = fold_halves(acc[c], asc[c], lane);
+            return;
         }
-        __syncthreads();   // the stage is rewritten by the next chunk
+        const int lo = wave * cnt / kTopkWaveSlots, hi = (wave + 1) * cnt / kTopkWaveSlots;
+        st.merge_survivors(s_surv + lo, hi - lo);
+        __syncthreads();   // the survivors' area is rewritten by the next round
     }
-    // Combine: the registers into acc[0] (half by half), then its upper half
-    // into its lower, through this wave's rows of the (now free) stage.
-    uint64_t* rows = stage + wave * 64;
-#pragma unroll
-    for (int c = 1; c < kFoldRegs; ++c) {
-        rows[lane] = acc[c];
-        wave_lds_sync();
-        const uint64_t a = r < p.k ? rows[half * 32 + r] : 0;
-        wave_lds_sync();
-        acc[0] = fold_halves(acc[0], a, lane);
-    }
-    rows[lane] = acc[0];
-    wave_lds_sync();
-    const uint64_t up = (lane < 32 && r < p.k) ? rows[32 + r] : 0;
-    mt.best = fold_halves(lane < 32 ? acc[0] : 0, up, lane);
-    mt.thr = readlane64(mt.best, p.k - 1);
-    block_merge(mt, s_list, wave, waves);
-    if (wave == 0) {
-        if (lane < p.k) write_result(p, mt.best, lane);
-        if (lane == 0) *p.counter = 0u;   // ready for the next launch
-    }
+    block_merge(st, s_list, wave, kTopkWaveSlots);
+    if (wave == 0 && lane < k) write_result(p, st.best, lane);
 }
 
 }  // namespace
@@ -698,6 +759,10 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
         hipLaunchKernelGGL(topk_kernel<16>, g, b, (unsigned)topk_lds_bytes<16>(), stream, p);
     else
         return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.groups == 1) return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kTopkMaxThreads),
+                       (unsigned)topk_merge_lds_bytes(p.k), stream, p);
     return hipGetLastError();
 }
 
@@ -705,6 +770,9 @@ hipError_t set_kernel_attributes() {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<32>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        topk_lds_bytes<32>());
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, topk_merge_lds_bytes(32));
     if (e == hipSuccess) e = raise_lds_limit<float>();
     if (e == hipSuccess) e = raise_lds_limit<__half>();
     if (e == hipSuccess) e = raise_lds_limit<__hip_bfloat16>();

@@ -45,7 +45,6 @@ struct ws_lane {
     ws_topk_entry* res_host = nullptr;  // mapped result slot (host view)
     uint2* res_dev = nullptr;           // its device view
     uint64_t* partials = nullptr;
-    uint32_t* counter = nullptr;
     float* det_head = nullptr;
     bool own_det_head = false;
     float4* det_boxes = nullptr;
@@ -100,7 +99,6 @@ void release(ws_lane* L) {
     if (L->own_scores && L->scores) hipFree(L->scores);
     if (L->res_host) hipHostFree(L->res_host);
     if (L->partials) hipFree(L->partials);
-    if (L->counter) hipFree(L->counter);
     if (L->own_det_head && L->det_head) hipFree(L->det_head);
     if (L->det_boxes) hipFree(L->det_boxes);
     if (L->det_keys) hipFree(L->det_keys);
@@ -190,7 +188,6 @@ void fill_params(ws_lane* L) {
     t.waves = P.topk_waves;
     t.keys_per_lane = P.topk_keys_per_lane;
     t.partials = L->partials;
-    t.counter = L->counter;
     t.result = L->res_dev;
     ws::DetParams& d = L->det;
     d.head = L->det_head;
@@ -386,10 +383,6 @@ int build(ws_lane* L) {
         const size_t max_groups = ((size_t)c.num_scores + 1023) / 1024;
         WS_TRY(dev_alloc(L, &pp, max_groups * (size_t)c.k * sizeof(uint64_t)));
         L->partials = static_cast<uint64_t*>(pp);
-        void* cn = nullptr;
-        WS_TRY(dev_alloc(L, &cn, sizeof(uint32_t)));
-        L->counter = static_cast<uint32_t*>(cn);
-        WS_HIP(hipMemset(L->counter, 0, sizeof(uint32_t)), WS_E_HIP);
     }
 
     if (P.det_anchors > 0) {

@@ -246,9 +246,33 @@ def test_topk_chunking_does_not_change_results(gpu_lib, chunk):
         r.close()
 
 
-def test_topk_all_equal_and_all_nan(gpu_lib):
-    for vals in (np.full(3000, 0.5, np.float32), np.full(3000, np.nan, np.float32),
-                 np.where(np.arange(3000) % 2 == 0, 0.0, -0.0).astype(np.float32)):
+@pytest.mark.parametrize("period,chunk", [(8192, 8192), (1000, 8192), (1024, 1024), (3, 4096)])
+def test_topk_every_workgroup_alike(gpu_lib, period, chunk):
+    """Scores repeating with a short period: every workgroup's K best have
+    the same values, so nearly all published keys clear the bound and the
+    merge selects among many survivors (with 1 Ki chunks, over several rounds
+    of published keys)."""
+    rng = np.random.default_rng(period * 7 + chunk)
+    base = rng.normal(0.0, 1.0, period).astype(np.float32)
+    s = np.tile(base, 700_000 // period + 1)[:700_000]
+    frame = np.zeros((1, 4, 4, 3), dtype=np.uint8)
+    w = wl.Workload("periodic", 4, 4, 4, 4, wl.RESIZE, (0, 0, 0), (1, 1, 1), 114.0, 32, frame, s)
+    r = Run(w, host_input=False, topk_chunk=chunk)
+    try:
+        assert r.lane.plan()["topk_groups"] > 1
+        r.run()
+        _, tk = r.outputs()
+        assert_topk_exact(tk, topk(s, 32))
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("n", [3000, 300_000])
+def test_topk_all_equal_and_all_nan(gpu_lib, n):
+    """Ties everywhere; NaN reported as -inf; both zeros keep their own sign
+    bit in the result (3000 scores: one workgroup; 300,000: the merge)."""
+    for vals in (np.full(n, 0.5, np.float32), np.full(n, np.nan, np.float32),
+                 np.where(np.arange(n) % 2 == 0, 0.0, -0.0).astype(np.float32)):
         frame = np.zeros((1, 4, 4, 3), dtype=np.uint8)
         w = wl.Workload("same", 4, 4, 4, 4, wl.RESIZE, (0, 0, 0), (1, 1, 1), 114.0, 32, frame,
                         vals)

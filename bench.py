@@ -362,7 +362,7 @@ def main(argv=None) -> int:
                          "HIP starts; 'off' only for comparison")
     ap.add_argument("--pin-core", type=int, default=-2,
                     help="run the submit/wait loop on this host core (-2: the last core this "
-                         "process may use; -1: no pinning)")
+                         "process may use; -1: no pinning); single-lane workloads only")
     args = ap.parse_args(argv)
     if args.graph_packet_capture == "off":
         # Must be in the environment before torch (or anything else) starts HIP.
@@ -412,6 +412,10 @@ def main(argv=None) -> int:
     print(f"[bench] inputs for {name} ready in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     extra = {}
+    if name == "c5l":
+        # Eight lanes, one host thread each: threads inherit the creator's
+        # affinity, so pinning here would put all eight on one core.
+        pinned = None
     if pinned is not None:
         os.sched_setaffinity(0, {pinned})   # this thread runs every submit/wait loop below
     if name == "c5l":

@@ -641,17 +641,27 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_merge_kernel(TopkParams 
         const int lists = min(kMergeLists, G - l0);
         const int nkeys = lists * k;
         const uint64_t* part = p.partials + (int64_t)l0 * k;
-        // This round's keys, coalesced (registers past `regs` stay unused);
-        // and list `tid`'s first and K-th keys.
-        const int regs = (nkeys + kTopkMaxThreads - 1) / kTopkMaxThreads;   // uniform
-        uint64_t key[kMergeKeys];
-#pragma unroll
-        for (int m = 0; m < kMergeKeys; ++m) {
-            const int i = tid + m * kTopkMaxThreads;
-            key[m] = i < nkeys ? part[i] : 0;
-        }
+        // List `tid`'s first and K-th keys, then this round's keys coalesced
+        // (registers past `regs` stay unused).  The bound needs only the
+        // first two, so it is worked out while the rest are still arriving.
         const uint64_t mx = tid < lists ? part[tid * k] : 0;
         uint64_t kth = tid < lists ? part[tid * k + k - 1] : 0;
+        // Two keys per 16-byte load, every load unconditional so the bound
+        // can start once the first two arrive.  A lane past the last pair
+        // reads an earlier pair (its own index masked below the count, so
+        // lanes stay on distinct addresses) and masks the keys to 0.
+        const int regs = 2 * ((nkeys + 2 * kTopkMaxThreads - 1) / (2 * kTopkMaxThreads));
+        const int last_pair = (nkeys - 1) >> 1;
+        const int spread = (int)((0xffffffffu >> __builtin_clz((uint32_t)last_pair + 1u)) >> 1);   // 2^j - 1 <= last_pair
+        uint64_t key[kMergeKeys];
+#pragma unroll
+        for (int m = 0; m < kMergeKeys / 2; ++m) {
+            const int q = tid + m * kTopkMaxThreads;
+            const ulonglong2 v = reinterpret_cast<const ulonglong2*>(part)[q <= last_pair ? q : (tid & spread)];
+            key[2 * m] = 2 * q < nkeys ? v.x : 0;
+            key[2 * m + 1] = 2 * q + 1 < nkeys ? v.y : 0;
+        }
+        __builtin_amdgcn_sched_barrier(0);   // every load issues before the bound's first use
         kth = umax64(kth, xor_lane64<32>(kth, lane));
         kth = umax64(kth, xor_lane64<16>(kth, lane));
         kth = umax64(kth, xor_lane64<8>(kth, lane));
@@ -670,24 +680,30 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_merge_kernel(TopkParams 
         __syncthreads();
 #pragma unroll
         for (int w = 0; w < kTopkWaveSlots; ++w) bound = umax64(bound, s_bound[w]);
-        uint64_t pass[kMergeKeys];
-        int mine = 0;
+        // Survivors per lane on the VALU, a prefix of those counts across the
+        // wave (one ballot per count bit), one LDS atomic per wave, then each
+        // lane stores its survivors in order.  A key below the bound goes to
+        // the lane's junk slot past the survivors' area, which no one reads.
+        int c = 0;
 #pragma unroll
-        for (int m = 0; m < kMergeKeys; ++m) {
-            pass[m] = __ballot(key[m] >= bound);   // keys past the round are 0: never pass
-            mine += __popcll(pass[m]);
+        for (int m = 0; m < kMergeKeys; ++m) c += key[m] >= bound ? 1 : 0;   // keys past the round are 0
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int bit = 0; bit < 6; ++bit) {   // c <= 32
+            const uint64_t bb = __ballot((c >> bit) & 1);
+            off += lanes_below(bb) << bit;
+            tot += __popcll(bb) << bit;
         }
         int base = 0;
-        if (lane == 0 && mine > 0) base = atomicAdd(&s_cnt, mine);
-        base = __builtin_amdgcn_readfirstlane(base);
-        // Every lane stores; a key below the bound goes to the lane's junk
-        // slot past the survivors' area, which no one reads.
+        if (lane == 0 && tot > 0) base = atomicAdd(&s_cnt, tot);
+        off += __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
         for (int m = 0; m < kMergeKeys; ++m) {
             if (m < regs) {   // uniform
                 const uint64_t x = key[m];
-                s_surv[x >= bound ? base + lanes_below(pass[m]) : junk + lane] = x;
-                base += __popcll(pass[m]);
+                const bool take = x >= bound;
+                s_surv[take ? off : junk + lane] = x;
+                off += take ? 1 : 0;
             }
         }
         __syncthreads();

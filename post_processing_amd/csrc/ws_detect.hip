@@ -31,7 +31,9 @@
 // All arithmetic that decides a result (DFL exponentials, boxes, IoU,
 // mapping) is binary32 with one rounding per operation in a fixed order:
 // fused multiply-add is switched off below, and division is IEEE (the
-// library is built with correctly rounded fp32 division).
+// library is built with correctly rounded fp32 division).  The IoU
+// threshold test reaches the same decision as dividing and comparing, by an
+// exact comparison in binary64 (iou_above).
 #include <hip/hip_runtime.h>
 
 #include "ws_kernels.h"
@@ -94,10 +96,16 @@ __device__ __forceinline__ float dfl_side(const float* __restrict__ q, int A) {
     return num / s;
 }
 
-// IoU of kept box a and candidate b (xyxy): areas, clipped intersection
-// sides, intersection, union = (area_a + area_b) - inter, one division.  A
-// zero union gives NaN, which suppresses nothing.
-__device__ __forceinline__ float iou_xyxy(float4 a, float4 b) {
+// Whether IoU(a, b) > t for kept box a and candidate b (xyxy), where the IoU
+// is binary32: areas, clipped intersection sides, intersection, union =
+// (area_a + area_b) - inter, each rounded once, then inter / union rounded
+// once.  The division is not carried out.  With t+ the next binary32 above
+// t and m their midpoint, the rounded quotient exceeds t exactly when
+// inter / union > m, or equals m and the tie rounds up to t+ (t+ has the
+// even significand, i.e. t's is odd).  inter and union are binary32 and m
+// has 25 significant bits, so m * union is exact in binary64 and the test is
+// exact.  A zero union (0 / 0 = NaN) and NaN boxes suppress nothing.
+__device__ __forceinline__ bool iou_above(float4 a, float4 b, double mid, bool tie_up) {
 #pragma clang fp contract(off)
     const float area_a = (a.z - a.x) * (a.w - a.y);
     const float area_b = (b.z - b.x) * (b.w - b.y);
@@ -105,7 +113,10 @@ __device__ __forceinline__ float iou_xyxy(float4 a, float4 b) {
     const float ih = fmaxf(0.0f, fminf(a.w, b.w) - fmaxf(a.y, b.y));
     const float inter = iw * ih;
     const float uni = (area_a + area_b) - inter;
-    return inter / uni;
+    const double bound = mid * (double)uni;
+    const double in = (double)inter;
+    // Bitwise, not short-circuit: every compare is evaluated, no branches.
+    return (uni > 0.0f) & ((in > bound) | (tie_up & (in == bound)));
 }
 
 // Network-input pixels -> source pixels, clipped to [0, hi].
@@ -351,13 +362,15 @@ template <bool STAGED>
 __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, const float4* s_box, int n, int s0,
                            uint16_t* kept_pos, bool any_class, int lane) {
 #pragma clang fp contract(off)
-    const uint32_t group = key_group(s[s0], any_class);
-    const float thr = p.iou;
+    const double mid = p.iou_mid;
+    const bool tie_up = p.iou_tie_up != 0;
+    uint32_t group = 0;
     int kept = 0;
     for (int c0 = s0; c0 < n; c0 += 64) {
         wave_lds_sync();   // kept_pos writes of the previous block are visible
         const int e = c0 + lane;
         const uint64_t key = e < n ? s[e] : 0;
+        if (c0 == s0) group = key_group(readlane64(key, 0), any_class);   // the run's first key
         const bool valid = e < n && key_group(key, any_class) == group;
         const uint64_t vmask = __ballot(valid);
         if (vmask == 0) break;
@@ -376,8 +389,7 @@ __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, cons
                               : p.boxes[key_anchor(s[kept_pos[kl]], any_class)];
             const int lim = min(64, kept - kb);
             for (int t = 0; t < lim && alive != 0; ++t) {
-                const float4 b = readlane4(kbox, t);
-                const bool sup = valid && iou_xyxy(b, box) > thr;
+                const bool sup = valid & iou_above(readlane4(kbox, t), box, mid, tie_up);
                 alive &= ~(uint64_t)__ballot(sup);
             }
         }
@@ -392,8 +404,7 @@ __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, cons
             }
             ++kept;
             if (kept == p.max_det) return kept;
-            const float4 b = readlane4(box, i);
-            const bool sup = lane > i && iou_xyxy(b, box) > thr;
+            const bool sup = (lane > i) & iou_above(readlane4(box, i), box, mid, tie_up);
             alive &= ~(uint64_t)__ballot(sup);
             pending = alive & ~((2ull << i) - 1);   // candidates after i
         }

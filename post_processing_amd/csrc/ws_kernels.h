@@ -59,7 +59,9 @@ struct DetParams {
     int32_t level_end[3];    // anchor index where the stride-8/16/32 grids end
     int32_t grid_w[3];       // cells per row of each grid
     float conf;              // candidate: best probability > conf
-    float iou;               // suppression: IoU > iou
+    float iou;               // suppression: IoU > iou (binary32 IoU), decided as below
+    double iou_mid;          // midpoint of iou and the next binary32 above it
+    int32_t iou_tie_up;      // an IoU exactly at iou_mid rounds up (iou's significand is odd)
     int32_t max_det;
     int32_t agnostic;
     float4* boxes;           // [anchors] network-input xyxy, written for candidates

@@ -11,7 +11,9 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cmath>
 #include <cstring>
+#include <limits>
 #include <new>
 #include <thread>
 #include <vector>
@@ -199,6 +201,17 @@ void fill_params(ws_lane* L) {
     }
     d.conf = c.det_conf;
     d.iou = c.det_iou;
+    {
+        // The suppression test compares without dividing (ws_detect.hip,
+        // iou_above): the midpoint of the threshold and its binary32
+        // successor (exact in binary64), and which way a tie there rounds.
+        const float t = c.det_iou;
+        const float up = std::nextafter(t, std::numeric_limits<float>::infinity());
+        d.iou_mid = ((double)t + (double)up) * 0.5;
+        uint32_t tb = 0;
+        std::memcpy(&tb, &t, sizeof tb);
+        d.iou_tie_up = (int32_t)(tb & 1u);
+    }
     d.max_det = c.det_max_det;
     d.agnostic = c.det_agnostic;
     d.boxes = L->det_boxes;

@@ -101,3 +101,45 @@ def test_tap_division_by_multiplier_is_exact():
         r = num.astype(np.int64) - (q * np.uint64(den)).astype(np.int64)
         q = q - (r < 0).astype(np.uint64)
         np.testing.assert_array_equal(q, num // np.uint64(den))
+
+
+def _iou_above_without_division(inter, uni, t):
+    """The suppression kernel's decision: the midpoint m of t and the next
+    binary32 above it (exact in binary64), compared with inter against
+    m * union in binary64 (exact: 24 x 25 significant bits)."""
+    t32 = np.float32(t)
+    up = np.nextafter(t32, np.float32(np.inf))
+    mid = (float(t32) + float(up)) * 0.5
+    tie_up = bool(t32.view(np.uint32) & 1)
+    bound = mid * float(uni)
+    return bool(np.float32(uni) > 0) and (float(inter) >= bound if tie_up else float(inter) > bound)
+
+
+def test_iou_threshold_decided_without_division():
+    """The NMS kernel decides IoU > t without dividing; the decision equals
+    binary32 division (rounded to nearest even, gradual underflow) followed
+    by the compare, for random quotients, thresholds at and one step below
+    the rounded quotient, zeros, equal boxes and subnormal intersections."""
+    rng = np.random.default_rng(11)
+    F = np.float32
+    uni = rng.uniform(1e-3, 1e6, 4000).astype(F)
+    inter = (uni * rng.uniform(0.0, 1.0, 4000).astype(F)).astype(F)
+    inter[:200] = 0.0
+    inter[200:400] = uni[200:400]                                  # identical boxes: IoU 1
+    inter[400:600] = (rng.uniform(1, 1000, 200) * 1e-42).astype(F)  # subnormal intersections
+    uni[600:650] = 0.0
+    inter[600:650] = 0.0                                            # 0 / 0: suppresses nothing
+    checked = 0
+    for a, b in zip(inter, uni):
+        with np.errstate(invalid="ignore", divide="ignore"):
+            q = F(a) / F(b)
+        base = [0.0, 1.0, 0.45, 0.5, float(rng.uniform(0, 1))]
+        if np.isfinite(q) and 0 <= q <= 1:
+            base += [float(q), float(np.nextafter(q, F(-1))), float(np.nextafter(q, F(2)))]
+        for t in base:
+            t = F(min(max(t, 0.0), 1.0))
+            with np.errstate(invalid="ignore"):
+                want = bool(q > t)
+            assert _iou_above_without_division(a, b, t) == want, (a, b, t, q)
+            checked += 1
+    assert checked > 25000

@@ -261,12 +261,13 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
 
     if (c.num_scores > 0) {
         // Up to 4 Ki scores one workgroup does everything (its waves take one
-        // 1024-score batch each), so no hand-off between workgroups is needed.
-        // Beyond that, 4-wave workgroups of 4 Ki scores (one batch per wave),
-        // or 8 Ki past 256 Ki scores so that fewer workgroups contend in the
-        // hand-off; the last to finish merges their lists.  (Measured on
-        // MI355X: 21,843 scores 13.0 us with 6 workgroups vs 18.4 us with one;
-        // 672,000 scores 20.3 us with 83 vs 23.9 us with 42.)
+        // 1024-score batch each), so no merge kernel is needed.  Beyond that,
+        // 4-wave workgroups of 4 Ki scores (one batch per wave), or 8 Ki past
+        // 256 Ki scores so that the merge kernel reads fewer lists.  (Measured
+        // on MI355X, Top-K stage with the merge kernel: 672,000 scores 11.9 us
+        // with 8 Ki chunks, 12.1 with 4 Ki, 14.5 with 16 Ki, 18.6 with 2 Ki;
+        // 21,843 scores 10.7 us with 4 Ki chunks, 10.3 with one workgroup,
+        // 12.0 with 2 Ki.)
         int64_t chunk = c.topk_chunk;
         if (chunk == 0) {
             if (c.num_scores <= kTopkSingleGroupMax)

@@ -318,6 +318,7 @@ struct WaveTopK {
     static_assert(E == 16 || E == 32, "16 or 32 scores per lane");
     static constexpr int kBatchE = 64 * E;
     static constexpr int kCountBits = E == 16 ? 5 : 6;   // bits of a lane's survivor count
+    static constexpr int kStageRow = E + 4;               // floats per lane row of the score stage
     uint64_t best;   // this lane's entry of the wave's sorted list
     uint64_t thr;    // K-th best key so far (wave-uniform)
     int k;
@@ -444,6 +445,10 @@ struct WaveTopK {
         // (one ballot per count bit) gives each lane its first slot in
         // `scratch`; each lane then walks its own survivors, reading the
         // values back from its row of `fstage`, and writes their exact keys.
+        // Rows are kStageRow = E + 4 floats apart: the 16-byte row stores
+        // then cover all banks eight lanes at a time, and the read-back of
+        // one float per lane conflicts at most 8 ways (a stride of E floats
+        // put every lane on the same banks).
         const float tf = __uint_as_float(cut_ord & 0x7fffffffu);
         int cnt = 0;
         uint32_t marks = 0;
@@ -461,7 +466,7 @@ struct WaveTopK {
             total += __popcll(b) << bit;
         }
         if (total == 0) return;
-        float4* row = reinterpret_cast<float4*>(fstage + lane * E);
+        float4* row = reinterpret_cast<float4*>(fstage + lane * kStageRow);
 #pragma unroll
         for (int u = 0; u < E / 4; ++u)
             row[u] = make_float4(f[4 * u], f[4 * u + 1], f[4 * u + 2], f[4 * u + 3]);
@@ -470,7 +475,7 @@ struct WaveTopK {
             const int j = __builtin_ctz(marks);
             marks &= marks - 1;
             const int32_t e = wb + 4 * (lane + 64 * (j >> 2)) + (j & 3);
-            const float x = fstage[lane * E + j];
+            const float x = fstage[lane * kStageRow + j];
             scratch[off++] = ((uint64_t)order_image(x) << 32) | (uint32_t)~(uint32_t)e;
         }
         wave_lds_sync();
@@ -550,10 +555,11 @@ __device__ __forceinline__ void load_batch(const float* __restrict__ scores, int
 
 constexpr int kTopkWaveSlots = kTopkMaxThreads / 64;
 
-// Dynamic LDS: per wave, 64 E survivor keys, then per wave 64 E staged scores.
+// Dynamic LDS: per wave, 64 E survivor keys, then per wave 64 staged score
+// rows of E + 4 floats.
 template <int E>
 constexpr int topk_lds_bytes() {
-    return kTopkWaveSlots * 64 * E * (int)(sizeof(uint64_t) + sizeof(float));
+    return kTopkWaveSlots * 64 * (E * (int)sizeof(uint64_t) + (E + 4) * (int)sizeof(float));
 }
 
 template <int E>
@@ -590,7 +596,7 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
             f[4 * u + 3] = v[u].w;
         }
         if (rb + round < g1) load_batch<E>(p.scores, wb + round, g1, lane, v);
-        st.offer_scores(f, wb, g1, s_keys + wave * kBatchE, s_vals + wave * kBatchE);
+        st.offer_scores(f, wb, g1, s_keys + wave * kBatchE, s_vals + wave * 64 * (E + 4));
     }
     block_merge(st, s_list, wave, waves);
 

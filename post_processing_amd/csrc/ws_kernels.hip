@@ -323,12 +323,14 @@ struct WaveTopK {
     uint64_t thr;    // K-th best key so far (wave-uniform)
     int k;
     int lane;
+    bool empty;      // nothing merged yet (wave-uniform)
 
     __device__ __forceinline__ void init(int k_, int lane_) {
         best = 0;
         thr = 0;
         k = k_;
         lane = lane_;
+        empty = true;
     }
 
     // Merge a list sorted ascending across lanes (e.g. a reversed list).
@@ -347,6 +349,7 @@ struct WaveTopK {
 
     // Merge `cnt` compacted survivors scratch[0..cnt) into the list.
     //  - a few: insert one by one;
+    //  - into an empty list, at most 64: sort them;
     //  - list and survivors fit one key per lane: one bitonic sort of both;
     //  - otherwise, 64 at a time: sort ascending, then the elementwise
     //    maximum against the descending list is the top 64 of their union as
@@ -357,6 +360,10 @@ struct WaveTopK {
         if (cnt <= kInsertMax) {
             const uint64_t cand = lane < cnt ? scratch[lane] : 0;
             for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
+        } else if (empty && cnt <= 64) {
+            // The first keys: sorted, they are the list.
+            best = wave_sort<true>(lane < cnt ? scratch[lane] : 0, lane);
+            thr = readlane64(best, k - 1);
         } else if (k + cnt <= 64) {
             const uint64_t x = lane < k ? best : (lane < k + cnt ? scratch[lane - k] : 0);
             best = wave_sort<true>(x, lane);
@@ -368,6 +375,7 @@ struct WaveTopK {
             }
             thr = readlane64(best, k - 1);
         }
+        empty = false;
     }
 
     // Offer one batch of order keys, E per lane (0 = nothing).

@@ -40,12 +40,12 @@ HBM_PEAK_GBS = 8000.0
 # (x2.0 read, x1.0 write).  Valid only for the kernel sources they were taken
 # on: reported as null once those sources change.
 MEASURED_TRAFFIC = {
-    "kernel_sha256_prefix": "d4653cb8a1e88173",
-    # c5t: FETCH 54,830.0 KiB x 2.0 + WRITE 37,632.1 KiB per launch (67 launches, median)
-    "c5t_64x1280x720_to_224": {"preprocess": 112_291_840 + 38_535_270},
-    # c2: preprocess FETCH 1,419.0 KiB x 2.0 + WRITE 588.0 KiB; Top-K 11.5 KiB x 2.0 + 0.1 KiB
+    "kernel_sha256_prefix": "9065ac1e864f21f8",
+    # c5t: FETCH 54,825.7 KiB x 2.0 + WRITE 37,632.1 KiB per launch (67 launches, median)
+    "c5t_64x1280x720_to_224": {"preprocess": 112_283_034 + 38_535_270},
+    # c2: preprocess FETCH 1,409.0 KiB x 2.0 + WRITE 588.0 KiB; Top-K 11.3 KiB x 2.0 + 0.1 KiB
     # (272 launches each, median)
-    "c2_1920x1080_to_224": {"preprocess": 2_906_112 + 602_112, "topk": 23_552 + 102},
+    "c2_1920x1080_to_224": {"preprocess": 2_885_632 + 602_112, "topk": 23_142 + 102},
 }
 
 

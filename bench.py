@@ -210,9 +210,10 @@ def run_single(w, torch, steps, warmup, use_graph=True):
     lane = make_lane(w, torch, use_graph=use_graph)
     lane.bench(warmup)
     torch.cuda.synchronize()
-    ms, wall = lane.bench(steps)
+    ms, wall, host_us = lane.bench(steps, host=True)
     torch.cuda.synchronize()
     res = {"frames_per_s": steps * w.batch / wall, "wall_s": wall, **lat_stats(ms),
+           "host_p50_us": pct(host_us, 50), "host_p99_us": pct(host_us, 99),
            "plan": lane.plan()}
     return lane, res
 
@@ -481,6 +482,10 @@ def main(argv=None) -> int:
         "p50_us": round(res["p50_us"], 3),
         "p99_us": round(res["p99_us"], 3),
         "p99_over_p50": round(res["p99_over_p50"], 4),
+        # Host view of the same replays: just before ws_submit to ws_wait's return.
+        "host_submit_to_return_us": ({"p50": round(res["host_p50_us"], 3),
+                                      "p99": round(res["host_p99_us"], 3)}
+                                     if "host_p50_us" in res else None),
         "preprocess_gbs": round(stages["preprocess"]["gbs"], 2),
         "preprocess_frac_of_hbm_peak": round(stages["preprocess"]["gbs"] / HBM_PEAK_GBS, 5),
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)

@@ -140,7 +140,8 @@ def load(path: str = LIB_PATH):
     lib.ws_lane_hip_error.restype = c_int
     lib.ws_lane_describe.argtypes = [c_void_p, POINTER(LanePlan)]
     lib.ws_lane_describe.restype = c_int
-    lib.ws_bench_replays.argtypes = [c_void_p, c_int32, POINTER(c_float), POINTER(c_double)]
+    lib.ws_bench_replays.argtypes = [c_void_p, c_int32, POINTER(c_float), POINTER(c_float),
+                                     POINTER(c_double)]
     lib.ws_bench_replays.restype = c_int
     lib.ws_bench_lanes.argtypes = [POINTER(c_void_p), c_int32, c_int32, POINTER(c_float),
                                    POINTER(c_double)]
@@ -289,14 +290,18 @@ class Lane:
     def hip_error(self) -> int:
         return self._lib.ws_lane_hip_error(self.handle)
 
-    def bench(self, replays: int) -> tuple[np.ndarray, float]:
-        """Native submit/wait loop: (gpu_ms per replay, wall seconds)."""
+    def bench(self, replays: int, host: bool = False):
+        """Native submit/wait loop: (gpu_ms per replay, wall seconds), plus
+        the host microseconds per replay (submit to wait's return) when
+        `host` is set."""
         ms = (c_float * replays)()
+        us = (c_float * replays)() if host else None
         wall = c_double(0.0)
-        rc = self._lib.ws_bench_replays(self.handle, replays, ms, byref(wall))
+        rc = self._lib.ws_bench_replays(self.handle, replays, ms, us, byref(wall))
         if rc != WS_OK:
             raise WsError(rc, "ws_bench_replays", self.hip_error())
-        return np.ctypeslib.as_array(ms).copy(), wall.value
+        out = np.ctypeslib.as_array(ms).copy(), wall.value
+        return out + (np.ctypeslib.as_array(us).copy(),) if host else out
 
     def time_stage(self, stage: int, launches: int) -> float:
         """Mean ms per direct launch of one stage's kernel (native loop)."""

@@ -236,6 +236,25 @@ def cold_launches(lane, torch, n: int, flush_bytes: int = 1 << 30) -> np.ndarray
     return np.asarray(out, dtype=np.float64)
 
 
+def pinned_h2d_gbs(torch, nbytes: int = 64 << 20, reps: int = 20) -> float:
+    """Host-to-device copy rate from pinned host memory (one DMA copy of
+    `nbytes`, `reps` times, between HIP events): the PCIe reference beside the
+    kernel's own mapped-read rate."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        d.copy_(h, non_blocking=True)
+    e1.record()
+    e1.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del h, d
+    return gbs
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, one thread, on the host of this run.
 
@@ -275,8 +294,54 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
             times.append(time.perf_counter() - t0)
     med = float(np.median(times))
     return {"value": round(w.batch / med, 3), "unit": "frames/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} frames of {w.name} (float64 preprocess + stable-sort "
-                      f"Top-K{' + binary32 decode/NMS' if w.head is not None else ''}), median {med * 1e3:.1f} ms/frame after 1 warm-up, 1 thread",
+            "sample": (f"{len(times)} calls of {w.batch} frame{'s' if w.batch > 1 else ''} of "
+                       f"{w.name} (float64 preprocess"
+                       f"{' + stable-sort Top-K' if w.k else ''}"
+                       f"{' + binary32 decode/NMS' if w.head is not None else ''}), median "
+                       f"{med * 1e3:.1f} ms per call after 1 warm-up, 1 thread"),
+            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
+
+
+_POOL = {}
+
+
+def _pool_init(cores, frames: int) -> None:
+    os.sched_setaffinity(0, cores)
+    from threadpoolctl import threadpool_limits
+    from post_processing_amd import workloads as wl
+    _POOL["limit"] = threadpool_limits(1)
+    _POOL["w"] = wl.c5_throughput(frames)
+
+
+def _pool_frame(i: int) -> float:
+    from oracle import preprocess_batch
+    w = _POOL["w"]
+    out = preprocess_batch(w.frames[i:i + 1], w.dst_w, w.dst_h, w.mean, w.std,
+                           letterbox=(w.mode == 1), pad=w.pad)
+    return float(out[0, 0, 0, 0])
+
+
+def cpu_baseline_pool(w, cores, budget_s: float = 10.0) -> dict:
+    """The same oracle over a process pool, one frame per task and one thread
+    per worker, for the batched workload: whole passes over the batch until
+    the budget is spent."""
+    import multiprocessing as mp
+    n = max(1, min(16, len(cores)))
+    ctx = mp.get_context("spawn")     # children start clean and never touch the GPU
+    with ctx.Pool(n, initializer=_pool_init, initargs=(set(cores), w.batch)) as pool:
+        # Each pass is bounded: a pool whose workers die at start-up would
+        # otherwise wait for them forever.
+        pool.map_async(_pool_frame, range(w.batch), chunksize=1).get(timeout=300)   # warm-up
+        passes = 0
+        t0 = time.perf_counter()
+        while passes < 2 or time.perf_counter() - t0 < budget_s:
+            pool.map_async(_pool_frame, range(w.batch), chunksize=1).get(timeout=120)
+            passes += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(passes * w.batch / dt, 3), "unit": "frames/s", "cores": n,
+            "kind": "oracle",
+            "sample": f"{passes} passes over the {w.batch} frames of {w.name} (float64 "
+                      f"preprocess), {n} worker processes, one frame per task, 1 thread each",
             "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
@@ -372,6 +437,7 @@ def main(argv=None) -> int:
         # Must be in the environment before torch (or anything else) starts HIP.
         os.environ["DEBUG_CLR_GRAPH_PACKET_CAPTURE"] = "0"
     pinned = None
+    all_cores = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
     if args.pin_core != -1 and hasattr(os, "sched_setaffinity"):
         allowed = sorted(os.sched_getaffinity(0))
         pinned = allowed[-1] if args.pin_core == -2 else args.pin_core
@@ -435,6 +501,7 @@ def main(argv=None) -> int:
         stages = stage_roofline(lanes[0], w, args.stage_launches)
         pb = preprocess_bytes(w)
         extra["mapped_host_read_gbs"] = pb["read"] / (stages["preprocess"]["us"] * 1e-6) / 1e9
+        extra["pinned_h2d_copy_gbs"] = pinned_h2d_gbs(torch)
         lane = lanes[0]
         steps_total = frames
     else:
@@ -447,6 +514,12 @@ def main(argv=None) -> int:
             extra["cold_preprocess_us_p50"] = float(np.median(cold))
             extra["cold_hbm_gbs"] = pb["total"] / (np.median(cold) * 1e-6) / 1e9
             extra["cold_frac_of_hbm_peak"] = extra["cold_hbm_gbs"] / HBM_PEAK_GBS
+        if lane.cfg.input_mode != ws.INPUT_DEVICE:
+            pb = preprocess_bytes(w)
+            if lane.cfg.input_mode == ws.INPUT_MAPPED_HOST:
+                extra["mapped_host_read_gbs"] = (pb["read"] / (stages["preprocess"]["us"] * 1e-6)
+                                                 / 1e9)
+            extra["pinned_h2d_copy_gbs"] = pinned_h2d_gbs(torch)
         if not args.no_direct and name != "c5t":
             dl, dres = run_single(w, torch, min(args.steps, 2000), min(args.warmup, 200),
                                   use_graph=False)
@@ -497,6 +570,9 @@ def main(argv=None) -> int:
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w)
+        if name == "c5t" and all_cores:
+            print("[bench] timing the CPU oracle over a process pool", file=sys.stderr, flush=True)
+            line["cpu_baseline_pool"] = cpu_baseline_pool(w, all_cores)
     else:
         line["cpu_baseline"] = None
     if args.report:

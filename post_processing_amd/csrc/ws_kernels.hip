@@ -282,18 +282,13 @@ __device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
 
 constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
 
-// K-th largest of one 32-bit value per lane, with multiplicity: the largest
-// t that at least K lanes reach, built from the top bit down (a bit stays set
-// when K lanes still reach the prefix with it) -- one compare and one ballot
-// per bit, with no lane exchanges.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k) {
-    uint32_t t = 0;
-#pragma unroll
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = t | (1u << bit);
-        if (__popcll(__ballot(m >= c)) >= k) t = c;
-    }
-    return t;
+// K-th largest of one 32-bit value per lane, with multiplicity: lane k - 1 of
+// the 64 values sorted descending across the wave.  The 21 stages of the
+// sorting network are short lane exchanges; selecting the value bit by bit
+// from the top instead takes 32 rounds of compare, ballot and count, each
+// waiting on the last.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(m, lane), k - 1);
 }
 
 // Number of the n keys of v (LDS) greater than x; sixteen loads are issued
@@ -362,11 +357,11 @@ struct WaveTopK {
             for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
         } else if (empty && cnt <= 64) {
             // The first keys: sorted, they are the list.
-            best = wave_sort<true>(lane < cnt ? scratch[lane] : 0, lane);
+            best = wave_sort_desc_first(lane < cnt ? scratch[lane] : 0, lane, cnt);
             thr = readlane64(best, k - 1);
         } else if (k + cnt <= 64) {
             const uint64_t x = lane < k ? best : (lane < k + cnt ? scratch[lane - k] : 0);
-            best = wave_sort<true>(x, lane);
+            best = wave_sort_desc_first(x, lane, k + cnt);
             thr = readlane64(best, k - 1);
         } else {
             for (int t = 0; t < cnt; t += 64) {
@@ -392,7 +387,7 @@ struct WaveTopK {
             uint32_t m = 0;
 #pragma unroll
             for (int j = 0; j < E; ++j) m = max(m, (uint32_t)(key[j] >> 32));
-            const uint32_t t = wave_kth_largest(m, k);
+            const uint32_t t = wave_kth_largest(m, k, lane);
             const uint64_t tcut = ((uint64_t)t << 32) - 1;   // key > tcut <=> value image >= t
             if (t != 0 && tcut > cut) {
                 cut = tcut;
@@ -427,7 +422,7 @@ struct WaveTopK {
             float m = -__builtin_inff();
 #pragma unroll
             for (int j = 0; j < E; ++j) m = fmaxf(m, f[j]);
-            const uint32_t t = wave_kth_largest(order_image(m), k);
+            const uint32_t t = wave_kth_largest(order_image(m), k, lane);
             cut_ord = max(cut_ord, t);
         }
         if (cut_ord <= 0x80000000u) {   // cut at or below +0: exact keys for all

@@ -82,20 +82,45 @@ __device__ __forceinline__ T bitonic_stages(T x, int lane) {
     const bool lower = (lane & J) == 0;
     const bool ascending_block = (lane & B) == 0;
     const bool keep_large = (lower != ascending_block) != DESC;
-    x = ((x > y) == keep_large) ? x : y;
+    if constexpr (sizeof(T) == 4) {
+        // 32-bit keys: maximum and minimum are single instructions, and the
+        // pick between them is a select on a lane mask fixed per stage.
+        const T hi = x < y ? y : x;
+        const T lo = x < y ? x : y;
+        x = keep_large ? hi : lo;
+    } else {
+        x = ((x > y) == keep_large) ? x : y;
+    }
     if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC>(x, lane);
     return x;
+}
+
+// Sort one key per lane within each block of S lanes (S a power of two up to
+// 64): block 0 ends in DESC order, the next block in the other order, and so
+// on.  S = 64 sorts the whole wave.
+template <int S, bool DESC, typename T>
+__device__ __forceinline__ T sort_lanes(T x, int lane) {
+    if constexpr (S > 2) x = sort_lanes<S / 2, DESC>(x, lane);
+    return bitonic_stages<S, S / 2, DESC>(x, lane);
 }
 
 // Sort one key per lane across the wave.
 template <bool DESC, typename T>
 __device__ __forceinline__ T wave_sort(T x, int lane) {
-    x = bitonic_stages<2, 1, DESC>(x, lane);
-    x = bitonic_stages<4, 2, DESC>(x, lane);
-    x = bitonic_stages<8, 4, DESC>(x, lane);
-    x = bitonic_stages<16, 8, DESC>(x, lane);
-    x = bitonic_stages<32, 16, DESC>(x, lane);
-    return bitonic_stages<64, 32, DESC>(x, lane);
+    return sort_lanes<64, DESC>(x, lane);
+}
+
+// Sort one key per lane across the wave when only lanes below n (n <= 64,
+// wave-uniform) hold keys and every other lane holds the smallest key (0 for
+// unsigned keys): a sort of the smallest power-of-two block of lanes that
+// covers n leaves block 0 sorted and the rest all-smallest, which is the whole
+// wave sorted descending.  Fewer stages for few keys: 6 up to 8, 10 up to 16,
+// 21 beyond.
+template <typename T>
+__device__ __forceinline__ T wave_sort_desc_first(T x, int lane, int n) {
+    if (n <= 8) return sort_lanes<8, true>(x, lane);
+    if (n <= 16) return sort_lanes<16, true>(x, lane);
+    return sort_lanes<64, true>(x, lane);
 }
 
 // Bitonic network over a block of 64*K keys held K per lane -- key r*64 +

@@ -261,10 +261,12 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
 // a bitonic clean-up).  All lane exchanges run on the VALU: DPP for lane
 // distances 1, 2, 4, 8 and the permlane swaps for 16 and 32.  Waves of a
 // workgroup merge pairwise through LDS.  With several workgroups, each
-// publishes its K best; a one-workgroup merge kernel, next in stream order,
-// derives a lower bound on the K-th best from those lists, keeps only the
-// keys at or above it and selects from them.  The kernel boundary orders the
-// two, so no fence or arrival counter sits on the path.
+// publishes its K best and a one-workgroup merge kernel, next in stream
+// order, selects the K best of those lists.  Up to 128 lists it folds them
+// pairwise with bitonic merges; beyond that it derives a lower bound on the
+// K-th best from the lists, keeps only the keys at or above it and selects
+// from them.  The kernel boundary orders the two, so no fence or arrival
+// counter sits on the path.
 
 // Order-preserving unsigned image of an FP32 value: NaN -> -inf and -0 -> +0
 // first; then negative values have all bits flipped, others the sign bit set.
@@ -613,8 +615,108 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(TopkParams p) {
     if (wave == 0 && lane < p.k) p.partials[(int64_t)blockIdx.x * p.k + lane] = st.best;
 }
 
-// Merge of the workgroups' lists (more than one workgroup), by one workgroup
-// of four waves, 256 lists per round.  Any K distinct keys bound the K-th
+// Merge of up to kFoldMaxLists workgroup lists by folding.  A register holds
+// two lists of up to 32 keys, one per 32-lane half, zero-padded past K.  A
+// descending register (both halves sorted descending) and an ascending one
+// meet half by half as one descending and one ascending list, so their
+// elementwise maximum holds the 32 largest keys of each half's union as a
+// bitonic sequence, and a clean-up over distances 16 .. 1 sorts it either
+// way.  Keys are distinct (the index is in the low word), so each fold is
+// exact.  Each wave loads R registers (list pairs wave, wave + 4, ...), each
+// in the order its place in a binary fold tree asks for, and folds them; the
+// root leaves the lower half descending and the upper ascending, so the
+// upper half, swapped down, folds into the lower.  The four waves merge
+// through LDS.  Nothing depends on the data: no bound, no survivor count, no
+// atomic.  Lists are loaded in address order (a half whose lanes read
+// descending addresses took several times as long to arrive), and an
+// ascending leaf is reversed in registers.
+constexpr int kFoldMaxLists = 128;
+
+// Order of leaf r under a tree node over [lo, hi) whose output is descending
+// (true) or ascending: left subtrees produce descending, right ones ascending.
+constexpr bool fold_leaf_desc(int r, int lo, int hi, bool desc) {
+    return hi - lo == 1 ? desc
+                        : (r < lo + (hi - lo + 1) / 2
+                               ? fold_leaf_desc(r, lo, lo + (hi - lo + 1) / 2, true)
+                               : fold_leaf_desc(r, lo + (hi - lo + 1) / 2, hi, false));
+}
+
+// Bit r set: leaf r of the tree over [0, R) is loaded descending.
+template <int R>
+constexpr uint32_t fold_leaf_mask() {
+    uint32_t m = 0;
+    for (int r = 0; r < R; ++r) m |= fold_leaf_desc(r, 0, R, true) ? 1u << r : 0u;
+    return m;
+}
+
+template <int LO, int HI, bool DESC, int R>
+__device__ __forceinline__ uint64_t fold_tree(const uint64_t (&x)[R], int lane) {
+    if constexpr (HI - LO == 1) {
+        return x[LO];
+    } else {
+        constexpr int MID = LO + (HI - LO + 1) / 2;
+        const uint64_t a = fold_tree<LO, MID, true>(x, lane);
+        const uint64_t b = fold_tree<MID, HI, false>(x, lane);
+        return bitonic_stages<64, 16, DESC>(umax64(a, b), lane);
+    }
+}
+
+// The root: lower half descending, upper half ascending.  One register is
+// loaded that way; otherwise the last fold runs its two halves opposite ways.
+template <int R>
+__device__ __forceinline__ uint64_t fold_root(const uint64_t (&x)[R], int lane) {
+    if constexpr (R == 1) {
+        return x[0];
+    } else {
+        constexpr int MID = (R + 1) / 2;
+        const uint64_t a = fold_tree<0, MID, true>(x, lane);
+        const uint64_t b = fold_tree<MID, R, false>(x, lane);
+        return bitonic_stages<32, 16, true>(umax64(a, b), lane);
+    }
+}
+
+template <int R>
+__global__ __launch_bounds__(kTopkMaxThreads) void topk_fold_kernel(TopkParams p) {
+    __shared__ uint64_t s_list[kTopkWaveSlots][64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int k = p.k, G = p.groups;
+    const int half = lane >> 5, h = lane & 31;
+    const int last = G * k - 1;   // the published keys are partials[0 .. last]
+    // Every load is issued, in bounds, before any is used: a lane with no key
+    // reads a spare published key (lanes on distinct addresses) and drops it.
+    uint64_t x[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int list = 2 * (wave + kTopkWaveSlots * r) + half;
+        const bool valid = list < G && h < k;
+        x[r] = p.partials[valid ? list * k + h : min(lane + 64 * r, last)];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first is used
+    constexpr uint32_t kLeafDesc = fold_leaf_mask<R>();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int list = 2 * (wave + kTopkWaveSlots * r) + half;
+        const uint64_t v = list < G && h < k ? x[r] : 0;   // descending in both halves
+        if constexpr (R == 1) {
+            const uint64_t rev = reverse_half64(v, lane);
+            x[r] = half == 0 ? v : rev;
+        } else {
+            x[r] = ((kLeafDesc >> r) & 1u) ? v : reverse_half64(v, lane);
+        }
+    }
+    uint64_t w = fold_root<R>(x, lane);
+    w = bitonic_stages<64, 16, true>(umax64(w, xor_lane64<32>(w, lane)), lane);
+    WaveTopK<16> st;
+    st.init(k, lane);
+    st.best = w;
+    block_merge(st, s_list, wave, kTopkWaveSlots);
+    if (wave == 0 && lane < k) write_result(p, st.best, lane);
+}
+
+// Merge of more than kFoldMaxLists workgroup lists, by one workgroup of four
+// waves, 256 lists per round.  Any K distinct keys bound the K-th
 // best from below, so the bound is the larger of the K-th key of any one
 // list and the K-th largest of the lists' maxima.  Every key of the K best
 // is in its own workgroup's list, so the keys at or above the bound are all
@@ -786,8 +888,21 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
         return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.groups == 1) return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(1), dim3(kTopkMaxThreads),
-                       (unsigned)topk_merge_lds_bytes(p.k), stream, p);
+    const dim3 one(1), block(kTopkMaxThreads);
+    if (p.groups <= kFoldMaxLists) {
+        // Registers per wave: list pairs over four waves, rounded up to a
+        // size the fold is built for.
+        const int need = ((p.groups + 1) / 2 + kTopkWaveSlots - 1) / kTopkWaveSlots;
+        if (need <= 1) hipLaunchKernelGGL(topk_fold_kernel<1>, one, block, 0, stream, p);
+        else if (need <= 2) hipLaunchKernelGGL(topk_fold_kernel<2>, one, block, 0, stream, p);
+        else if (need <= 4) hipLaunchKernelGGL(topk_fold_kernel<4>, one, block, 0, stream, p);
+        else if (need <= 8) hipLaunchKernelGGL(topk_fold_kernel<8>, one, block, 0, stream, p);
+        else if (need <= 12) hipLaunchKernelGGL(topk_fold_kernel<12>, one, block, 0, stream, p);
+        else hipLaunchKernelGGL(topk_fold_kernel<16>, one, block, 0, stream, p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(topk_merge_kernel, one, block, (unsigned)topk_merge_lds_bytes(p.k), stream,
+                       p);
     return hipGetLastError();
 }
 

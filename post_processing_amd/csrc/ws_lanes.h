@@ -38,6 +38,15 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v, int lane) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Value held by lane 31 - h of the same 32-lane half (h = lane % 32): DPP
+// row_mirror reverses each row of 16 lanes, then the rows of a half swap.
+__device__ __forceinline__ uint64_t reverse_half64(uint64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, 0x140, 0xF, 0xF, true);
+    const uint32_t hi =
+        (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), 0x140, 0xF, 0xF, true);
+    return xor_lane64<16>(((uint64_t)hi << 32) | lo, lane);
+}
+
 // Value held by lane - 1 (lane 0 keeps its own): DPP wave_shr:1.
 __device__ __forceinline__ uint64_t prev_lane64(uint64_t v) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v,

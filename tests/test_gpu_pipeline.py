@@ -233,6 +233,24 @@ def test_topk_edge_sizes(gpu_lib, n, k):
         r.close()
 
 
+@pytest.mark.parametrize("groups", [2, 13, 24, 50, 83, 128, 129])
+@pytest.mark.parametrize("k", [7, 32])
+def test_topk_merge_sizes(gpu_lib, groups, k):
+    """1 Ki-score workgroups, so `groups` lists are published (the last one
+    ragged): the fold merge at each register count it is built for (1, 2, 4,
+    8, 12 and 16 per wave: 2 .. 128 lists) and the bound merge past 128."""
+    n = groups * 1024 - 5
+    w = _topk_workload(n, k, seed=groups * 101 + k)
+    r = Run(w, host_input=False, topk_chunk=1024)
+    try:
+        assert r.lane.plan()["topk_groups"] == groups
+        r.run()
+        _, tk = r.outputs()
+        assert_topk_exact(tk, topk(w.scores, k))
+    finally:
+        r.close()
+
+
 @pytest.mark.parametrize("chunk", [1024, 2048, 8192, 65536, 688128])
 def test_topk_chunking_does_not_change_results(gpu_lib, chunk):
     w = wl.c3()

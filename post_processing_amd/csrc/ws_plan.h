@@ -170,8 +170,8 @@ constexpr int kMaxPreBlock = 512;          // preprocess threads per workgroup
 constexpr int kMaxLdsBytes = 156 * 1024;   // gfx950: 160 KiB LDS per workgroup, less static use
 constexpr int kTopkBatch = 1024;           // scores one wave takes per round
 constexpr int kTopkMaxWaves = 4;           // one wave per SIMD of a CU
-constexpr int kTopkSingleGroupMax = 4096;  // up to here one workgroup, no hand-off
-constexpr int kTopkLargeN = 262144;        // beyond: 8 Ki scores per workgroup
+constexpr int kTopkSingleGroupMax = 8192;  // up to here one workgroup, no hand-off
+constexpr int kTopkLargeN = 196608;        // beyond: 8 Ki scores per workgroup
 constexpr int kDetDecodeBlock = 64;        // detection decode: anchors per workgroup
 
 struct Plan {
@@ -260,20 +260,25 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
     p->lds_bytes = lds_for_rows(rows, p->slot_bytes);
 
     if (c.num_scores > 0) {
-        // Up to 4 Ki scores one workgroup does everything (its waves take one
-        // 1024-score batch each), so no merge kernel is needed.  Beyond that,
-        // 4-wave workgroups of 4 Ki scores (one batch per wave), or 8 Ki past
-        // 256 Ki scores so that the merge kernel reads fewer lists.  (Measured
-        // on MI355X, Top-K stage with the merge kernel: 672,000 scores 11.9 us
-        // with 8 Ki chunks, 12.1 with 4 Ki, 14.5 with 16 Ki, 18.6 with 2 Ki;
-        // 21,843 scores 10.7 us with 4 Ki chunks, 10.3 with one workgroup,
-        // 12.0 with 2 Ki.)
+        // Up to 8 Ki scores one workgroup does everything, so no merge kernel
+        // is needed: up to 4 Ki its waves take one 1024-score batch each,
+        // beyond that four waves take 2048 (32 per lane) in one round.  Past
+        // 8 Ki, 4-wave workgroups of 4 Ki scores, or 8 Ki past 192 Ki scores
+        // so that the merge kernel folds fewer lists.  (Measured on MI355X,
+        // Top-K stage with the fold merge: 672,000 scores 9.4 us with 8 Ki
+        // chunks, 11.0 with 16 Ki, 12.1 with 4 Ki; 262,144 scores 8.0 us with
+        // 8 Ki, 8.4 with 4 Ki; 131,072 scores 7.6 us with 4 Ki, 8.7 with 8 Ki;
+        // 65,536 scores 7.1 us with 4 Ki, 7.4 with 8 Ki;
+        // 21,843 scores 6.9 us with 4 Ki, 9.1 with one workgroup; 8,192
+        // scores 5.0 us with one workgroup, 6.6 with two.)
         int64_t chunk = c.topk_chunk;
         if (chunk == 0) {
-            if (c.num_scores <= kTopkSingleGroupMax)
+            if (c.num_scores <= kTopkSingleGroupMax / 2)
                 chunk = ceil_div(c.num_scores, kTopkBatch) * kTopkBatch;
+            else if (c.num_scores <= kTopkSingleGroupMax)
+                chunk = kTopkSingleGroupMax;
             else
-                chunk = c.num_scores <= kTopkLargeN ? kTopkSingleGroupMax : 2 * kTopkSingleGroupMax;
+                chunk = c.num_scores <= kTopkLargeN ? kTopkSingleGroupMax / 2 : kTopkSingleGroupMax;
         }
         p->topk_chunk = (int32_t)chunk;
         p->topk_waves = (int32_t)std::min<int64_t>(kTopkMaxWaves, chunk / kTopkBatch);

@@ -40,12 +40,12 @@ HBM_PEAK_GBS = 8000.0
 # (x2.0 read, x1.0 write).  Valid only for the kernel sources they were taken
 # on: reported as null once those sources change.
 MEASURED_TRAFFIC = {
-    "kernel_sha256_prefix": "9065ac1e864f21f8",
-    # c5t: FETCH 54,825.7 KiB x 2.0 + WRITE 37,632.1 KiB per launch (67 launches, median)
-    "c5t_64x1280x720_to_224": {"preprocess": 112_283_034 + 38_535_270},
-    # c2: preprocess FETCH 1,409.0 KiB x 2.0 + WRITE 588.0 KiB; Top-K 11.3 KiB x 2.0 + 0.1 KiB
-    # (272 launches each, median)
-    "c2_1920x1080_to_224": {"preprocess": 2_885_632 + 602_112, "topk": 23_142 + 102},
+    "kernel_sha256_prefix": "c66548d0ae928b7a",
+    # c5t: FETCH 54,819.0 KiB x 2.0 + WRITE 37,632.0 KiB per launch (67 launches, median)
+    "c5t_64x1280x720_to_224": {"preprocess": 112_269_312 + 38_535_168},
+    # c2: preprocess FETCH 1,425.0 KiB x 2.0 + WRITE 588.0 KiB; Top-K 13.75 KiB x 2.0 +
+    # 0.0625 KiB (272 launches each, median)
+    "c2_1920x1080_to_224": {"preprocess": 2_918_400 + 602_112, "topk": 28_160 + 64},
 }
 
 

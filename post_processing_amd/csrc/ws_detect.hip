@@ -12,7 +12,8 @@
 //   distances are computed one lane per (candidate, box side), and each
 //   candidate's box is stored by anchor and its sort key appended to the
 //   candidate list (one atomic per workgroup).
-// det_nms_kernel (one workgroup of 8 waves):
+// det_nms_kernel (one workgroup of 16 waves, or 8 when 16 waves' kept-box
+// lists do not fit LDS beside the keys):
 //   1. sorts the candidate keys descending in LDS (bitonic: DPP exchanges
 //      inside a wave, LDS exchanges across waves).  The key orders by class
 //      first (unless boxes of any class suppress each other), then by
@@ -45,8 +46,10 @@ namespace {
 constexpr int kDecodeBlock = kDetDecodeAnchors;
 constexpr int kDecodeParts = 4;               // class ranges per anchor, one wave each
 constexpr int kDecodeThreads = kDecodeParts * kDecodeBlock;
-constexpr int kNmsThreads = kDetNmsThreads;
-constexpr int kNmsWaves = kNmsThreads / 64;
+// The suppression kernel runs with 1,024 threads when its LDS allows (more
+// class runs in flight: each wave's run is a chain of dependent steps), else
+// with kDetNmsThreads.
+constexpr int kNmsWideThreads = 1024;
 constexpr int kBins = WS_DET_REG_MAX;
 
 // e^x for x <= 0 (Cody & Waite, "Software Manual for the Elementary
@@ -167,14 +170,15 @@ __device__ __forceinline__ float4 readlane4(float4 v, int lane) {
 
 // One stage (B, J) with J at least a block, through LDS: one thread per pair,
 // four pairs loaded before any is stored.
+template <int NT>
 __device__ __forceinline__ void cx_pass_lds(uint64_t* s, int P, int B, int J, int tid) {
     const int pairs = P >> 1;
-    for (int q0 = tid; q0 < pairs; q0 += 4 * kNmsThreads) {
+    for (int q0 = tid; q0 < pairs; q0 += 4 * NT) {
         int lo[4];
         uint64_t a[4], b[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int q = q0 + m * kNmsThreads;
+            const int q = q0 + m * NT;
             lo[m] = ((q & ~(J - 1)) << 1) | (q & (J - 1));
             if (q < pairs) {
                 a[m] = s[lo[m]];
@@ -183,7 +187,7 @@ __device__ __forceinline__ void cx_pass_lds(uint64_t* s, int P, int B, int J, in
         }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int q = q0 + m * kNmsThreads;
+            const int q = q0 + m * NT;
             if (q < pairs && (a[m] < b[m]) == ((lo[m] & B) == 0)) {
                 s[lo[m]] = b[m];
                 s[lo[m] + J] = a[m];
@@ -195,14 +199,14 @@ __device__ __forceinline__ void cx_pass_lds(uint64_t* s, int P, int B, int J, in
 // Sorts P keys descending into s[0, P), P a power of two with 64 <= P and
 // P / (64 K) blocks.  The keys come from g[0, n) (zero past n) when g is
 // given, else from s itself.  Ends with a barrier.
-template <int K>
+template <int NT, int K>
 __device__ __forceinline__ void sort_desc_k(uint64_t* s, int P, int tid, const uint64_t* __restrict__ g,
                                             int n) {
     constexpr int Q = 64 * K;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int blocks = P / Q;
-    for (int b = wave; b < blocks; b += kNmsWaves) {
+    for (int b = wave; b < blocks; b += NT / 64) {
         uint64_t x[K];
         if (g) {
 #pragma unroll
@@ -221,10 +225,10 @@ __device__ __forceinline__ void sort_desc_k(uint64_t* s, int P, int tid, const u
     __syncthreads();
     for (int B = 2 * Q; B <= P; B <<= 1) {
         for (int J = B >> 1; J >= Q; J >>= 1) {
-            cx_pass_lds(s, P, B, J, tid);
+            cx_pass_lds<NT>(s, P, B, J, tid);
             __syncthreads();
         }
-        for (int b = wave; b < blocks; b += kNmsWaves) {
+        for (int b = wave; b < blocks; b += NT / 64) {
             uint64_t x[K];
 #pragma unroll
             for (int r = 0; r < K; ++r) x[r] = s[b * Q + r * 64 + lane];
@@ -238,12 +242,13 @@ __device__ __forceinline__ void sort_desc_k(uint64_t* s, int P, int tid, const u
 
 // Block sizes: one block per wave up to 4096 keys (64 per lane at most 8),
 // then several blocks of 512 per wave.
+template <int NT>
 __device__ __forceinline__ void sort_desc(uint64_t* s, int P, int tid, const uint64_t* __restrict__ g = nullptr,
                                           int n = 0) {
-    if (P <= 512) sort_desc_k<1>(s, P, tid, g, n);
-    else if (P == 1024) sort_desc_k<2>(s, P, tid, g, n);
-    else if (P == 2048) sort_desc_k<4>(s, P, tid, g, n);
-    else sort_desc_k<8>(s, P, tid, g, n);
+    if (P <= 512) sort_desc_k<NT, 1>(s, P, tid, g, n);
+    else if (P == 1024) sort_desc_k<NT, 2>(s, P, tid, g, n);
+    else if (P == 2048) sort_desc_k<NT, 4>(s, P, tid, g, n);
+    else sort_desc_k<NT, 8>(s, P, tid, g, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -413,8 +418,11 @@ __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, cons
     return kept;
 }
 
-__global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p) {
+template <int NT>
+__global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
 #pragma clang fp contract(off)
+    constexpr int kNmsThreads = NT;
+    constexpr int kNmsWaves = NT / 64;
     // Dynamic LDS: keys [sort_cap] | run starts [kDetRunCap] | kept positions
     // [kNmsWaves][max_det].
     extern __shared__ uint64_t s_dyn[];
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
     // 1. Load and sort.
     int P = 64;
     while (P < n) P <<= 1;
-    sort_desc(s, P, tid, p.keys, n);
+    sort_desc<NT>(s, P, tid, p.keys, n);
 
     // 2. Class runs (one run of everything when any class suppresses any).
     for (int e = tid; e < n; e += kNmsThreads)
@@ -501,7 +509,7 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
         while (P2 < total) P2 <<= 1;
         for (int e = total + tid; e < P2; e += kNmsThreads) s[e] = 0;
         __syncthreads();
-        sort_desc(s, P2, tid);
+        sort_desc<NT>(s, P2, tid);
     }
 
     // 5. The first max_det, mapped to source pixels, to the mapped slot.
@@ -526,19 +534,40 @@ __global__ __launch_bounds__(kNmsThreads) void det_nms_kernel(const DetParams p)
 
 static_assert(WS_DET_MAX_ANCHORS <= 16384, "anchors must fit the 14-bit key field");
 static_assert(WS_DET_MAX_CLASSES <= 4096, "classes must fit the 12-bit key field");
-static_assert(WS_DET_MAX_ANCHORS % kNmsThreads == 0, "gather loop covers every key");
+static_assert(WS_DET_MAX_ANCHORS % kDetNmsThreads == 0 && WS_DET_MAX_ANCHORS % kNmsWideThreads == 0,
+              "gather loop covers every key");
 
 }  // namespace
 
-int det_nms_lds_bytes(int sort_cap, int max_det) {
+namespace {
+int nms_lds_bytes(int sort_cap, int max_det, int threads) {
     return sort_cap * (int)sizeof(uint64_t) + kDetRunCap * (int)sizeof(uint16_t) +
-           kNmsWaves * max_det * (int)sizeof(uint16_t);
+           (threads / 64) * max_det * (int)sizeof(uint16_t);
+}
+
+// Dynamic LDS one workgroup may take: 160 KiB on gfx950, less the kernel's
+// few bytes of static LDS.
+constexpr int kNmsLdsCap = 160 * 1024 - 64;
+
+int nms_threads(int sort_cap, int max_det) {
+    return nms_lds_bytes(sort_cap, max_det, kNmsWideThreads) <= kNmsLdsCap ? kNmsWideThreads
+                                                                           : kDetNmsThreads;
+}
+}  // namespace
+
+int det_nms_lds_bytes(int sort_cap, int max_det) {
+    return nms_lds_bytes(sort_cap, max_det, nms_threads(sort_cap, max_det));
 }
 
 hipError_t set_detect_attributes() {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(det_nms_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               det_nms_lds_bytes(WS_DET_MAX_ANCHORS, WS_DET_MAX_DET));
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(det_nms_kernel<kDetNmsThreads>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        nms_lds_bytes(WS_DET_MAX_ANCHORS, WS_DET_MAX_DET, kDetNmsThreads));
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(det_nms_kernel<kNmsWideThreads>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kNmsLdsCap);
+    return e;
 }
 
 hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream) {
@@ -546,8 +575,14 @@ hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stre
                        stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(det_nms_kernel, dim3(1), dim3(kNmsThreads),
-                       (unsigned)det_nms_lds_bytes(p.sort_cap, p.max_det), stream, p);
+    const int nt = nms_threads(p.sort_cap, p.max_det);
+    const unsigned lds = (unsigned)nms_lds_bytes(p.sort_cap, p.max_det, nt);
+    if (nt == kNmsWideThreads)
+        hipLaunchKernelGGL(det_nms_kernel<kNmsWideThreads>, dim3(1), dim3(kNmsWideThreads), lds,
+                           stream, p);
+    else
+        hipLaunchKernelGGL(det_nms_kernel<kDetNmsThreads>, dim3(1), dim3(kDetNmsThreads), lds,
+                           stream, p);
     return hipGetLastError();
 }
 

@@ -45,6 +45,21 @@ def test_c3_detection_full_pipeline(gpu_lib):
     print(f"c3d: {got[3]} candidates, {len(got[1])} kept")
 
 
+def test_suppression_width_does_not_change_results(gpu_lib):
+    """C3D keeps 69 boxes, so max_det 300 and 1,024 give the same result.
+    With 8,400 anchors (16,384-key sort space) the first fits the 16-wave
+    suppression kernel in LDS and the second takes the 8-wave one."""
+    w = wl.c3d()
+    rdet = oracle_detections(w)
+    got16, _ = _run_detect(w)
+    w8 = dataclasses.replace(w, det={**w.det, "max_det": 1024})
+    got8, _ = _run_detect(w8)
+    assert_detections_exact(got16, rdet)
+    assert_detections_exact(got8, oracle_detections(w8))
+    for a, b in zip(got16, got8):
+        np.testing.assert_array_equal(np.asarray(a), np.asarray(b))
+
+
 @pytest.mark.parametrize("seed", range(40))
 def test_detect_small_random(gpu_lib, seed):
     w = wl.detect_small(seed)

@@ -429,7 +429,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     uint64_t* s = s_dyn;
     uint16_t* s_run = reinterpret_cast<uint16_t*>(s_dyn + p.sort_cap);
     uint16_t* s_kept = s_run + kDetRunCap;
-    __shared__ int s_n, s_runs, s_total;
+    __shared__ int s_n, s_runs, s_total, s_next;
 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
@@ -443,6 +443,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
         *p.counter = 0;   // ready for the next replay's decode
         s_runs = 0;
         s_total = 0;
+        s_next = kNmsWaves;
     }
     __syncthreads();
     const int n = s_n;   // uniform
@@ -476,11 +477,19 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     }
     uint16_t* kept_pos = s_kept + wave * p.max_det;
     int my_kept = 0;
+    // Wave w takes run w first, then whichever run is next when it is done,
+    // so long runs do not queue behind each other on one wave.  (With one
+    // run, wave 0 resolves it and its kept list is read below.)
+    auto next_run = [&]() -> int {
+        int r = 0;
+        if (lane == 0) r = atomicAdd(&s_next, 1);
+        return __builtin_amdgcn_readfirstlane(r);
+    };
     if (s_box) {
-        for (int r = wave; r < runs; r += kNmsWaves)
+        for (int r = wave; r < runs; r = next_run())
             my_kept = resolve_run<true>(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
     } else {
-        for (int r = wave; r < runs; r += kNmsWaves)
+        for (int r = wave; r < runs; r = next_run())
             my_kept = resolve_run<false>(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
     }
     __syncthreads();

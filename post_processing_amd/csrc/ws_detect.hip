@@ -467,6 +467,24 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     __syncthreads();
     const int runs = s_runs;
 
+    // Longest runs first (up to 64 runs, by one wave): the run starts sorted
+    // ascending give each run's length as the distance to the next start,
+    // then (length, start) sorted descending is the order the waves take
+    // them in.  A start is below 2^14 and a length at most 2^14, so both fit
+    // one 32-bit key.
+    if (!any_class && runs > 1 && runs <= 64) {   // uniform
+        if (wave == 0) {
+            const uint32_t start = lane < runs ? s_run[lane] : 0xFFFFu;
+            const uint32_t asc = wave_sort<false>(start, lane);
+            const uint32_t next = (uint32_t)__shfl_down((int)asc, 1);
+            const uint32_t len = (lane + 1 < runs ? next : (uint32_t)n) - asc;
+            const uint32_t key = lane < runs ? (len << 16) | asc : 0u;
+            const uint32_t ord = wave_sort<true>(key, lane);
+            if (lane < runs) s_run[lane] = (uint16_t)(ord & 0xFFFFu);
+        }
+        __syncthreads();
+    }
+
     // 3. Boxes in sorted order, into the LDS the sort left free (when it fits),
     //    then greedy suppression, one wave per run.
     float4* s_box = nullptr;

@@ -418,6 +418,25 @@ __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, cons
     return kept;
 }
 
+// Up to this many kept boxes are placed by counting, not sorted.
+constexpr int kRankByCountMax = 256;
+
+// Number of the n keys of v (LDS) above x; sixteen loads are issued before
+// their compares.
+__device__ __forceinline__ int count_above(const uint64_t* v, int n, uint64_t x) {
+    int r = 0;
+    int j = 0;
+    for (; j + 16 <= n; j += 16) {
+        uint64_t t[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) t[u] = v[j + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) r += t[u] > x ? 1 : 0;
+    }
+    for (; j < n; ++j) r += v[j] > x ? 1 : 0;
+    return r;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
 #pragma clang fp contract(off)
@@ -513,8 +532,10 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     __syncthreads();
 
     // 4. Kept boxes in rank order.  With one run, that is its kept list
-    //    (wave 0 resolved it).  Otherwise gather the flagged keys of all runs
-    //    and sort them.
+    //    (wave 0 resolved it).  Otherwise gather the flagged keys of all runs;
+    //    up to kRankByCountMax of them are placed by counting (keys are
+    //    distinct, so a key's place is the number of kept keys above it),
+    //    more are sorted.
     int total;
     if (any_class) {
         if (tid == 0) s_total = my_kept;
@@ -532,17 +553,18 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
         }
         __syncthreads();
         total = s_total;
-        int P2 = 64;
-        while (P2 < total) P2 <<= 1;
-        for (int e = total + tid; e < P2; e += kNmsThreads) s[e] = 0;
-        __syncthreads();
-        sort_desc<NT>(s, P2, tid);
+        if (total > kRankByCountMax) {   // uniform
+            int P2 = 64;
+            while (P2 < total) P2 <<= 1;
+            for (int e = total + tid; e < P2; e += kNmsThreads) s[e] = 0;
+            __syncthreads();
+            sort_desc<NT>(s, P2, tid);
+        }
     }
 
     // 5. The first max_det, mapped to source pixels, to the mapped slot.
     const int count = min(total, p.max_det);
-    for (int q = tid; q < count; q += kNmsThreads) {
-        const uint64_t k = any_class ? (s[s_kept[q]] & ~1ull) : s[q];
+    auto emit = [&](uint64_t k, int q) {
         const float4 b = p.boxes[key_anchor(k, true)];
         ws_det d;
         d.x1 = to_source(b.x, p.left, p.sx, p.src_w);
@@ -552,6 +574,16 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
         d.score = __uint_as_float((uint32_t)(k >> 33));
         d.class_id = (int32_t)((k >> 7) & 0xFFFu);
         p.out->det[q] = d;
+    };
+    if (!any_class && total <= kRankByCountMax) {
+        for (int t = tid; t < total; t += kNmsThreads) {
+            const uint64_t x = s[t];
+            const int r = count_above(s, total, x);
+            if (r < count) emit(x, r);
+        }
+    } else {
+        for (int q = tid; q < count; q += kNmsThreads)
+            emit(any_class ? (s[s_kept[q]] & ~1ull) : s[q], q);
     }
     if (tid == 0) {
         p.out->count = count;

@@ -83,33 +83,25 @@ __device__ __forceinline__ float chan(uint32_t px, uint32_t shift) {
 // Output element types: FP32, or FP16 / BF16 rounded to nearest even.
 template <typename T> struct OutFormat;
 template <> struct OutFormat<float> {
-    using Pack2 = float2;
-    using Pack4 = float4;
     __device__ static float cvt(float x) { return x; }
-    __device__ static float2 pack2(const float* v) { return make_float2(v[0], v[1]); }
-    __device__ static float4 pack4(const float* v) { return make_float4(v[0], v[1], v[2], v[3]); }
 };
 template <> struct OutFormat<__half> {
-    using Pack2 = uint32_t;
-    using Pack4 = uint2;
     __device__ static uint16_t bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
     __device__ static __half cvt(float x) { return __float2half_rn(x); }
     __device__ static uint32_t pack2(const float* v) { return bits(v[0]) | ((uint32_t)bits(v[1]) << 16); }
-    __device__ static uint2 pack4(const float* v) { return make_uint2(pack2(v), pack2(v + 2)); }
 };
 template <> struct OutFormat<__hip_bfloat16> {
-    using Pack2 = uint32_t;
-    using Pack4 = uint2;
     __device__ static uint16_t bits(float x) { return __bfloat16_as_ushort(__float2bfloat16(x)); }
     __device__ static __hip_bfloat16 cvt(float x) { return __float2bfloat16(x); }
     __device__ static uint32_t pack2(const float* v) { return bits(v[0]) | ((uint32_t)bits(v[1]) << 16); }
-    __device__ static uint2 pack4(const float* v) { return make_uint2(pack2(v), pack2(v + 2)); }
 };
 
-// Four output values as one non-temporal store: the tensor is written once
-// per frame and not read again by this kernel, so its lines need not stay
-// in the caches, which keeps more of them for the frames.  (64 frames of
-// 1280x720 -> 224x224: 29.0 -> 28.1 us per launch, 5.11 -> 5.29 TB/s.)
+// Two or four output values as one non-temporal store: the tensor is
+// written once per frame and not read again by this kernel, so its lines
+// need not stay in the caches, which keeps more of them for the frames.
+// (64 frames of 1280x720 -> 224x224: 29.0 -> 28.1 us per launch; 1280x720
+// letterboxed into 640x640, two columns per thread: 5.07 -> 4.83 us.  One
+// column per thread gained nothing, so those stores stay ordinary.)
 __device__ __forceinline__ void store_stream(float* dst, const float (&v)[4]) {
     typedef float V __attribute__((ext_vector_type(4)));
     const V x = {v[0], v[1], v[2], v[3]};
@@ -120,6 +112,15 @@ __device__ __forceinline__ void store_stream(H* dst, const float (&v)[4]) {
     typedef uint32_t V __attribute__((ext_vector_type(2)));
     const V x = {OutFormat<H>::pack2(v), OutFormat<H>::pack2(v + 2)};
     __builtin_nontemporal_store(x, reinterpret_cast<V*>(dst));
+}
+__device__ __forceinline__ void store_stream(float* dst, const float (&v)[2]) {
+    typedef float V __attribute__((ext_vector_type(2)));
+    const V x = {v[0], v[1]};
+    __builtin_nontemporal_store(x, reinterpret_cast<V*>(dst));
+}
+template <typename H>
+__device__ __forceinline__ void store_stream(H* dst, const float (&v)[2]) {
+    __builtin_nontemporal_store(OutFormat<H>::pack2(v), reinterpret_cast<uint32_t*>(dst));
 }
 
 template <int PX, typename OutT>
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
                 if constexpr (PX == 4)
                     store_stream(row_out + c * plane, out[c]);
                 else if constexpr (PX == 2)
-                    *reinterpret_cast<typename Fmt::Pack2*>(row_out + c * plane) = Fmt::pack2(out[c]);
+                    store_stream(row_out + c * plane, out[c]);
                 else
                     row_out[c * plane] = Fmt::cvt(out[c][0]);
             }

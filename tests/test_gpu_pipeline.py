@@ -217,9 +217,13 @@ def _topk_workload(n, k, seed):
                        frame, s)
 
 
-@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 1000, 4097, 65537, 672000])
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 1000, 4096, 4097, 8192, 8193, 65537, 196608,
+                               196609, 672000])
 @pytest.mark.parametrize("k", [1, 5, 10, 31, 32])
 def test_topk_edge_sizes(gpu_lib, n, k):
+    """Sizes at the planner's boundaries too: one workgroup of one batch per
+    wave up to 4 Ki scores, of 32 per lane up to 8 Ki, then 4 Ki chunks, and
+    8 Ki chunks past 192 Ki."""
     if k > n:
         pytest.skip("K > N is rejected at create")
     w = _topk_workload(n, k, seed=n * 37 + k)

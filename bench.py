@@ -422,6 +422,10 @@ def main(argv=None) -> int:
                     help="preprocess tuning knob: 1, 2 or 4 (0 = auto)")
     ap.add_argument("--autotune", action="store_true",
                     help="let each lane time candidate launch geometries at create")
+    ap.add_argument("--lanes", type=int, default=1,
+                    help="c5t: lanes driven at once, one host thread each (each launches the "
+                         "64-frame batch from its own buffers), so one batch runs while the "
+                         "next is launched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
     ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
@@ -482,28 +486,33 @@ def main(argv=None) -> int:
     print(f"[bench] inputs for {name} ready in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     extra = {}
-    if name == "c5l":
-        # Eight lanes, one host thread each: threads inherit the creator's
-        # affinity, so pinning here would put all eight on one core.
+    if args.lanes != 1 and (name != "c5t" or args.lanes < 1 or args.lanes > 8):
+        print("bench.py: --lanes takes 1..8 and applies to c5t", file=sys.stderr)
+        return 2
+    multi = name == "c5l" or args.lanes > 1
+    if multi:
+        # Several lanes, one host thread each: threads inherit the creator's
+        # affinity, so pinning here would put them all on one core.
         pinned = None
     if pinned is not None:
         os.sched_setaffinity(0, {pinned})   # this thread runs every submit/wait loop below
-    if name == "c5l":
-        lanes = [make_lane(x, torch) for x in work]
+    if multi:
+        lanes = [make_lane(x, torch) for x in (work if name == "c5l" else [w] * args.lanes)]
         ws.bench_lanes(lanes, args.warmup)
         torch.cuda.synchronize()
         ms, wall = ws.bench_lanes(lanes, args.steps)
         torch.cuda.synchronize()
-        frames = 8 * args.steps
+        frames = len(lanes) * w.batch * args.steps
         res = {"frames_per_s": frames / wall, "wall_s": wall, **lat_stats(ms.ravel()),
                "per_lane_p50_us": [pct(m * 1e3, 50) for m in ms],
                "plan": lanes[0].plan()}
         stages = stage_roofline(lanes[0], w, args.stage_launches)
         pb = preprocess_bytes(w)
-        extra["mapped_host_read_gbs"] = pb["read"] / (stages["preprocess"]["us"] * 1e-6) / 1e9
-        extra["pinned_h2d_copy_gbs"] = pinned_h2d_gbs(torch)
+        if name == "c5l":
+            extra["mapped_host_read_gbs"] = pb["read"] / (stages["preprocess"]["us"] * 1e-6) / 1e9
+            extra["pinned_h2d_copy_gbs"] = pinned_h2d_gbs(torch)
         lane = lanes[0]
-        steps_total = frames
+        steps_total = len(lanes) * args.steps
     else:
         lane, res = run_single(w, torch, args.steps, args.warmup)
         stages = stage_roofline(lane, w, args.stage_launches)
@@ -548,7 +557,7 @@ def main(argv=None) -> int:
                    "detect": ({"anchors": int(w.head.shape[1]), **{k: w.det[k] for k in
                               ("nc", "conf", "iou", "max_det")}} if w.head is not None else None),
                    "input": args.input or ("mapped" if (w.host_input or name == "c5l") else "device"),
-                   "graph": True, "lanes": 8 if name == "c5l" else 1,
+                   "graph": True, "lanes": 8 if name == "c5l" else args.lanes,
                    "graph_packet_capture": args.graph_packet_capture,
                    "host_core": pinned,
                    "parallelism": "single_gpu"},

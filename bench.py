@@ -423,9 +423,9 @@ def main(argv=None) -> int:
     ap.add_argument("--autotune", action="store_true",
                     help="let each lane time candidate launch geometries at create")
     ap.add_argument("--lanes", type=int, default=1,
-                    help="c5t: lanes driven at once, one host thread each (each launches the "
-                         "64-frame batch from its own buffers), so one batch runs while the "
-                         "next is launched")
+                    help="lanes driven at once, one host thread each, each with its own "
+                         "buffers (not c5l, which is eight lanes): one lane's work runs while "
+                         "another's is launched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
     ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
@@ -486,8 +486,8 @@ def main(argv=None) -> int:
     print(f"[bench] inputs for {name} ready in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     extra = {}
-    if args.lanes != 1 and (name != "c5t" or args.lanes < 1 or args.lanes > 8):
-        print("bench.py: --lanes takes 1..8 and applies to c5t", file=sys.stderr)
+    if args.lanes != 1 and (name == "c5l" or args.lanes < 1 or args.lanes > 8):
+        print("bench.py: --lanes takes 1..8 (c5l is eight lanes by definition)", file=sys.stderr)
         return 2
     multi = name == "c5l" or args.lanes > 1
     if multi:

@@ -240,9 +240,7 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
         if (p.vec) {   // dst_w % PX == 0: the PX columns are one aligned vector
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
-                if constexpr (PX == 4)
-                    store_stream(row_out + c * plane, out[c]);
-                else if constexpr (PX == 2)
+                if constexpr (PX > 1)
                     store_stream(row_out + c * plane, out[c]);
                 else
                     row_out[c * plane] = Fmt::cvt(out[c][0]);
@@ -267,16 +265,17 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
 // unique and needs no tie logic.  Key 0 is below every real key (sentinel).
 //
 // Each wave64 keeps a sorted list of its 64 best keys, one per lane (lane 0
-// best).  Scores arrive in batches of 1024 (16 per lane).  Only scores at or
-// above the running K-th best can matter; in a wave's first batch the K-th
-// largest of the 64 lane maxima is also a lower bound (K distinct scores of
-// the batch reach it), which prunes the rest.  Survivors get exact keys and
-// are compacted through the wave's LDS scratch.  A few are inserted one by
-// one; when the list's K best and the survivors fit one key per lane they are
-// bitonic-sorted together; more go in tiles of 64, each sorted across lanes
-// and merged into the list (elementwise max against the reversed tile, then
-// a bitonic clean-up).  All lane exchanges run on the VALU: DPP for lane
-// distances 1, 2, 4, 8 and the permlane swaps for 16 and 32.  Waves of a
+// best).  Scores arrive in batches of 1024 or 2048 (16 or 32 per lane).  Only
+// scores at or above the running K-th best can matter; in a wave's first
+// batch the K-th largest of the 64 lane maxima is also a lower bound (K
+// distinct scores of the batch reach it), which prunes the rest.  Survivors
+// get exact keys and are compacted through the wave's LDS scratch.  A few are
+// inserted one by one; when the list's K best and the survivors fit one key
+// per lane they are bitonic-sorted together (over the smallest power-of-two
+// block of lanes that holds them); more go in tiles of 64, each sorted
+// across lanes and merged into the list (elementwise max against the reversed
+// tile, then a bitonic clean-up).  All lane exchanges run on the VALU: DPP
+// for lane distances 1, 2, 4, 8 and the permlane swaps for 16 and 32.  Waves of a
 // workgroup merge pairwise through LDS.  With several workgroups, each
 // publishes its K best and a one-workgroup merge kernel, next in stream
 // order, selects the K best of those lists.  Up to 128 lists it folds them

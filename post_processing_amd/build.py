@@ -36,6 +36,9 @@ def lib_command(out: str) -> list[str]:
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # IEEE binary32 division and square root (detection decisions rely on it)
         "-fhip-fp32-correctly-rounded-divide-sqrt",
+        # leading scalar and pointer kernel arguments arrive in scalar
+        # registers at wave launch (gfx950 kernarg preloading)
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         "-I", INCLUDE, "-I", CSRC,
         "-o", out,
     ] + [os.path.join(CSRC, s) for s in SOURCES]

@@ -254,7 +254,13 @@ __device__ __forceinline__ void sort_desc(uint64_t* s, int P, int tid, const uin
 // ---------------------------------------------------------------------------
 // Decode
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(const DetParams p) {
+// Both detection kernels take the fields their first loads need as leading
+// scalar and pointer arguments, which the library's kernarg preloading puts
+// in scalar registers at wave launch, and read them from there; DetParams
+// follows by value and is read in place (a local copy with its arrays
+// indexed at run time would live in private memory).
+__global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(
+    const float* head, int32_t anchors, int32_t nc, const DetParams p) {
 #pragma clang fp contract(off)
     __shared__ int s_anchor[kDecodeBlock];
     __shared__ int s_cls[kDecodeBlock];
@@ -265,20 +271,20 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(const DetPar
     __shared__ int s_count;
     __shared__ uint32_t s_base;
     const int tid = (int)threadIdx.x;
-    const int A = p.anchors;
+    const int A = anchors;
     if (tid == 0) s_count = 0;
 
     // 1. Best class (first maximum; NaN never compares greater) and threshold.
     //    Wave w scans the w-th quarter of the classes of the group's anchors.
     const int a = (int)blockIdx.x * kDecodeBlock + (tid & (kDecodeBlock - 1));
     const int part = tid / kDecodeBlock;   // wave-uniform
-    const int per = (p.nc + kDecodeParts - 1) / kDecodeParts;
-    const int c_begin = min(p.nc, part * per);
-    const int c_end = min(p.nc, c_begin + per);
+    const int per = (nc + kDecodeParts - 1) / kDecodeParts;
+    const int c_begin = min(nc, part * per);
+    const int c_end = min(nc, c_begin + per);
     float best = -INFINITY;
     int cls = c_begin;
     if (a < A) {
-        const float* __restrict__ pr = p.head + (size_t)(4 * kBins) * A + a;
+        const float* __restrict__ pr = head + (size_t)(4 * kBins) * A + a;
         int c = c_begin;
         for (; c + 16 <= c_end; c += 16) {
             float v[16];
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(const DetPar
     for (int t = tid; t < 4 * n; t += kDecodeThreads) {
         const int q = t >> 2;
         const int side = t & 3;
-        s_dist[q][side] = dfl_side(p.head + (size_t)(side * kBins) * A + s_anchor[q], A);
+        s_dist[q][side] = dfl_side(head + (size_t)(side * kBins) * A + s_anchor[q], A);
     }
     if (tid == 0) s_base = atomicAdd(p.counter, (uint32_t)n);
     __syncthreads();
@@ -438,7 +444,9 @@ __device__ __forceinline__ int count_above(const uint64_t* v, int n, uint64_t x)
 }
 
 template <int NT>
-__global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
+__global__ __launch_bounds__(NT) void det_nms_kernel(
+    uint32_t* counter, uint64_t* keys, int32_t anchors, int32_t sort_cap, int32_t agnostic,
+    int32_t max_det, const DetParams p) {
 #pragma clang fp contract(off)
     constexpr int kNmsThreads = NT;
     constexpr int kNmsWaves = NT / 64;
@@ -446,20 +454,20 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     // [kNmsWaves][max_det].
     extern __shared__ uint64_t s_dyn[];
     uint64_t* s = s_dyn;
-    uint16_t* s_run = reinterpret_cast<uint16_t*>(s_dyn + p.sort_cap);
+    uint16_t* s_run = reinterpret_cast<uint16_t*>(s_dyn + sort_cap);
     uint16_t* s_kept = s_run + kDetRunCap;
     __shared__ int s_n, s_runs, s_total, s_next;
 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const bool any_class = p.agnostic != 0;
+    const bool any_class = agnostic != 0;
     if (tid == 0) {
         // Written by the decode kernel's atomics: read as a device-scope
         // atomic (a vector load), never through the scalar cache.
-        const uint32_t c = __hip_atomic_load(p.counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_n = (int)(c < (uint32_t)p.anchors ? c : (uint32_t)p.anchors);
-        *p.counter = 0;   // ready for the next replay's decode
+        const uint32_t c = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_n = (int)(c < (uint32_t)anchors ? c : (uint32_t)anchors);
+        *counter = 0;   // ready for the next replay's decode
         s_runs = 0;
         s_total = 0;
         s_next = kNmsWaves;
@@ -477,7 +485,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     // 1. Load and sort.
     int P = 64;
     while (P < n) P <<= 1;
-    sort_desc<NT>(s, P, tid, p.keys, n);
+    sort_desc<NT>(s, P, tid, keys, n);
 
     // 2. Class runs (one run of everything when any class suppresses any).
     for (int e = tid; e < n; e += kNmsThreads)
@@ -507,12 +515,12 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     // 3. Boxes in sorted order, into the LDS the sort left free (when it fits),
     //    then greedy suppression, one wave per run.
     float4* s_box = nullptr;
-    if ((int64_t)(p.sort_cap - P) * (int64_t)sizeof(uint64_t) >= (int64_t)n * (int64_t)sizeof(float4)) {
+    if ((int64_t)(sort_cap - P) * (int64_t)sizeof(uint64_t) >= (int64_t)n * (int64_t)sizeof(float4)) {
         s_box = reinterpret_cast<float4*>(s + P);   // P * 8 is a multiple of 512: 16-byte aligned
         for (int e = tid; e < n; e += kNmsThreads) s_box[e] = p.boxes[key_anchor(s[e], any_class)];
         __syncthreads();
     }
-    uint16_t* kept_pos = s_kept + wave * p.max_det;
+    uint16_t* kept_pos = s_kept + wave * max_det;
     int my_kept = 0;
     // Wave w takes run w first, then whichever run is next when it is done,
     // so long runs do not queue behind each other on one wave.  (With one
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(const DetParams p) {
     }
 
     // 5. The first max_det, mapped to source pixels, to the mapped slot.
-    const int count = min(total, p.max_det);
+    const int count = min(total, max_det);
     auto emit = [&](uint64_t k, int q) {
         const float4 b = p.boxes[key_anchor(k, true)];
         ws_det d;
@@ -631,17 +639,19 @@ hipError_t set_detect_attributes() {
 
 hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream) {
     hipLaunchKernelGGL(det_decode_kernel, dim3((unsigned)decode_groups), dim3(kDecodeThreads), 0,
-                       stream, p);
+                       stream, p.head, p.anchors, p.nc, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nt = nms_threads(p.sort_cap, p.max_det);
     const unsigned lds = (unsigned)nms_lds_bytes(p.sort_cap, p.max_det, nt);
+    auto nms = [&](auto kernel, int threads) {
+        hipLaunchKernelGGL(kernel, dim3(1), dim3(threads), lds, stream, p.counter, p.keys,
+                           p.anchors, p.sort_cap, p.agnostic, p.max_det, p);
+    };
     if (nt == kNmsWideThreads)
-        hipLaunchKernelGGL(det_nms_kernel<kNmsWideThreads>, dim3(1), dim3(kNmsWideThreads), lds,
-                           stream, p);
+        nms(det_nms_kernel<kNmsWideThreads>, kNmsWideThreads);
     else
-        hipLaunchKernelGGL(det_nms_kernel<kDetNmsThreads>, dim3(1), dim3(kDetNmsThreads), lds,
-                           stream, p);
+        nms(det_nms_kernel<kDetNmsThreads>, kDetNmsThreads);
     return hipGetLastError();
 }
 

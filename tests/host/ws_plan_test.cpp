@@ -158,7 +158,7 @@ static int selftest() {
     c.src_w = 1280;
     c.src_h = 720;
     CHECK(ws::make_plan(c, &p) == WS_OK);
-    CHECK(p.pixels_per_thread == 4);
+    CHECK(p.pixels_per_thread == 1 && p.rows_per_group == 1 && p.pre_groups == 64 * 224);
     CHECK(p.rows_per_group * p.threads_per_row <= p.pre_block);
     CHECK(p.lds_bytes <= ws::kMaxLdsBytes);
     c = good();

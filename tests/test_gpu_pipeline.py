@@ -159,6 +159,28 @@ def test_random_small_shapes(gpu_lib, seed, letterbox):
         r.close()
 
 
+@pytest.mark.parametrize("sw,sh,dw,dh", [(1, 1, 5, 3), (2, 1, 7, 2), (3, 5, 9, 11), (5, 2, 5, 2),
+                                         (7, 3, 13, 8)])
+@pytest.mark.parametrize("batch", [1, 3])
+@pytest.mark.parametrize("host", [False, True])
+def test_gather_windows_at_the_end_of_the_input(gpu_lib, sw, sh, dw, dh, batch, host):
+    """Tiny frames upscaled (or copied) with one column per thread: the last
+    output pixels tap the input's final bytes, whose 12-byte window would run
+    past the end of the input and is read bytewise instead."""
+    rng = np.random.default_rng(sw * 1000 + sh * 100 + dw * 10 + dh + batch)
+    frames = rng.integers(0, 256, size=(batch, sh, sw, 3), dtype=np.uint8)
+    w = wl.Workload(f"tail_{sw}x{sh}_to_{dw}x{dh}_b{batch}", sw, sh, dw, dh, wl.RESIZE,
+                    (0.485, 0.456, 0.406), (0.229, 0.224, 0.225), 114.0, 0, frames, None)
+    ref, _ = oracle_outputs(w)
+    r = Run(w, host_input=host, pixels_per_thread=1)
+    try:
+        r.run()
+        t, _ = r.outputs()
+        assert_tensor_close(t, ref)
+    finally:
+        r.close()
+
+
 @pytest.mark.parametrize("name,rows,px", [("c4", 1, 4), ("c4", 2, 1), ("c4", 3, 2), ("c4", 6, 4),
                                           ("c1", 5, 1), ("c1", 32, 2), ("c2", 9, 4), ("c2", 1, 2),
                                           ("c3", 4, 4), ("c3", 1, 1), ("c3", 2, 2)])

@@ -170,7 +170,10 @@ typedef struct ws_lane_config {
     /* Tuning knobs (0 = automatic choice); they change speed, never results. */
     int32_t rows_per_group;    /* preprocess: output rows per workgroup        */
     int32_t topk_chunk;        /* Top-K: scores per workgroup (multiple of 1024) */
-    int32_t pixels_per_thread; /* preprocess: output columns per thread: 1, 2, 4 */
+    int32_t pixels_per_thread; /* preprocess: output columns per thread: 1
+                                  (the automatic choice: each thread reads its
+                                  taps straight from the frame), or 2 or 4
+                                  (source rows staged through LDS first)       */
     /* Formats (0 = FP32 tensor from RGB bytes). */
     int32_t tensor_dtype;      /* WS_DTYPE_*                                    */
     int32_t channel_order;     /* WS_CHANNELS_*; the tensor planes are always

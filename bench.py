@@ -40,9 +40,9 @@ HBM_PEAK_GBS = 8000.0
 # (x2.0 read, x1.0 write).  Valid only for the kernel sources they were taken
 # on: reported as null once those sources change.
 MEASURED_TRAFFIC = {
-    "kernel_sha256_prefix": "5a0307bec349f237",
+    "kernel_sha256_prefix": "6e458a1100d57905",
     # c5t: FETCH 53,787.5 KiB x 2.0 + WRITE 37,632.0 KiB per launch (67 launches, median)
-    "c5t_64x1280x720_to_224": {"preprocess": 110_158_848 + 38_535_168},
+    "c5t_64x1280x720_to_224": {"preprocess": 110_156_800 + 38_535_168},
     # c2: preprocess FETCH 1,287.5 KiB x 2.0 + WRITE 588.0 KiB; Top-K 13.6875 KiB x 2.0 +
     # 0.0625 KiB (272 launches each, median)
     "c2_1920x1080_to_224": {"preprocess": 2_636_800 + 602_112, "topk": 28_032 + 64},

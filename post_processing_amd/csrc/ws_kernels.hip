@@ -285,7 +285,7 @@ __device__ __forceinline__ uint32_t window_rgb(const uint32_t (&w)[3], uint32_t 
 // source row, so nothing is staged and no barrier precedes the loads.  Same
 // taps and arithmetic as preprocess_kernel<1>.
 template <typename OutT>
-__global__ __launch_bounds__(512) void preprocess_gather_kernel(PreParams p) {
+__global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
     using Fmt = OutFormat<OutT>;
     const int f = blockIdx.x / p.groups_per_frame;
     const int grp = blockIdx.x - f * p.groups_per_frame;

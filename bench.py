@@ -1,26 +1,44 @@
 """Benchmark of the fixed-shape frame pipeline on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --campaign [--report FILE]
 
-One step = one replay of a lane's graph (fused preprocess, then exact Top-K)
-between the lane's two GPU events, driven by the native submit/wait loop; the
-inputs are resident (device memory, or the mapped host slot for the
-host-input lanes) before the timed region starts.  Prints ONE JSON line.
+One step = one replay of a lane's graph between the lane's two GPU events,
+driven by the native submit/wait loop; the inputs are resident (device
+memory, or the mapped host slot for the host-input lanes) before the timed
+region starts.  Prints ONE JSON line.
 
 Workloads (synthetic, seeded; shapes of the pages' classifier and detector
 inputs):
-  c2   1920x1080 RGB8 -> 224x224 ImageNet-normalised + Top-5 of 1000 (default)
+  c5t  64 frames 1280x720 -> 224x224 in one launch (preprocess only): the
+       bandwidth workload and the default
   c1   64x48 -> 32x32 + Top-5 of 1000 with planted ties
+  c2   1920x1080 RGB8 -> 224x224 ImageNet-normalised + Top-5 of 1000
   c3   1280x720 -> 640x640 letterbox (pad 114, /255) + Top-32 of 8400x80
   c4   3840x2160 -> 384x384 + Top-32 of 21843 with 1% duplicates
   c5l  8 lanes, one host thread each, 1920x1080 from mapped host memory, Top-10
-  c5t  64 frames 1280x720 -> 224x224 in one launch (preprocess only)
   c3d  c3's lane plus in-graph detection decode + NMS over a synthetic
        8400-anchor, 80-class head (conf 0.25, IoU 0.45, at most 300 boxes)
+
+Latency percentiles always come from at least 10,000 replays (the timed
+steps when there are that many, else a separate run after them); the sample
+count is in the line.  The roofline describes the preprocess kernel: its
+algorithmic bytes over its duration with cold caches (a flush kernel over a
+buffer larger than the last-level cache runs before each launch, on the
+lane's stream, outside the HIP-event interval), beside the back-to-back
+(warm) duration and the rocprofv3 kernel durations and byte counters
+recorded for the same kernel sources.
+
+--campaign runs every workload (W = 1,000 warm-up and R = 10,000 timed
+replays) in three campaigns with the workload order rotated, each with a
+direct-launch repeat at the same counts, and times the CPU oracle's
+preprocess and Top-K separately per workload (median of 5 after 1 warm-up).
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import platform
@@ -32,42 +50,56 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+CSRC = os.path.join(ROOT, "post_processing_amd", "csrc")
 
 HBM_PEAK_GBS = 8000.0
+MIN_LATENCY_SAMPLES = 10_000
+LATENCY = {"samples": MIN_LATENCY_SAMPLES}
+ALL_CORES: set = set()         # every core this process may use, before any pinning
+FLUSH_BYTES = 1 << 30          # > 256 MiB last-level cache (Infinity Cache)
 
-# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# (two passes), scaled by what the same counters read for a plain 256 MiB copy
-# (x2.0 read, x1.0 write).  Valid only for the kernel sources they were taken
-# on: reported as null once those sources change.
-MEASURED_TRAFFIC = {
-    "kernel_sha256_prefix": "6e458a1100d57905",
-    # c5t: FETCH 53,787.5 KiB x 2.0 + WRITE 37,632.0 KiB per launch (67 launches, median)
-    "c5t_64x1280x720_to_224": {"preprocess": 110_156_800 + 38_535_168},
-    # c2: preprocess FETCH 1,287.5 KiB x 2.0 + WRITE 588.0 KiB; Top-K 13.6875 KiB x 2.0 +
-    # 0.0625 KiB (272 launches each, median)
-    "c2_1920x1080_to_224": {"preprocess": 2_636_800 + 602_112, "topk": 28_032 + 64},
+# Sources each kernel compiles from: a recorded measurement is valid only
+# while the sha256 of their concatenation is unchanged.
+KERNEL_SOURCES = {
+    "preprocess": ("ws_preprocess.hip", "ws_kernels.h"),
+    "topk": ("ws_topk.hip", "ws_kernels.h", "ws_lanes.h"),
+}
+
+# rocprofv3 measurements of the preprocess kernel, per workload (profiles/
+# holds the summaries and the commands).  `cold_us` / `warm_us`: median
+# kernel duration from --kernel-trace of `bench.py` itself, for the launches
+# that follow a cache flush and for the back-to-back ones (`bench.py
+# --trace-summary` splits the trace).  `traffic`: HBM bytes per launch from
+# two --pmc passes (FETCH_SIZE, then WRITE_SIZE), scaled by what the same
+# counters read for a plain 256 MiB device copy.
+MEASURED = {
+    "preprocess": {
+        "sha256_prefix": None,
+        "profile": None,
+    },
 }
 
 
-def kernel_sources_sha() -> str:
-    import hashlib
+def sources_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    # The sources the preprocess and Top-K kernels compile from (the
-    # detection kernels' file is not among them).
-    for name in ("ws_kernels.hip", "ws_kernels.h", "ws_lanes.h"):
-        with open(os.path.join(ROOT, "post_processing_amd", "csrc", name), "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str):
-    if kernel_sources_sha()[:16] != MEASURED_TRAFFIC["kernel_sha256_prefix"]:
+def measured(kernel: str, workload: str):
+    """The recorded rocprofv3 figures for this kernel and workload, or None
+    when the kernel's sources have changed since they were taken."""
+    m = MEASURED.get(kernel, {})
+    if not m.get("sha256_prefix") or sources_sha(kernel)[:16] != m["sha256_prefix"]:
         return None
-    return MEASURED_TRAFFIC.get(workload, {}).get(kernel)
+    rec = m.get(workload)
+    return dict(rec, profile=m["profile"]) if rec else None
 
 
 # ---------------------------------------------------------------------------
-# Algorithmic bytes (what the method must move at minimum, per frame).
+# Algorithmic bytes (what the method must move at minimum, per launch).
 
 def touched_rows(src: int, dst: int) -> int:
     rows = set()
@@ -121,15 +153,15 @@ def pct(a, q):
 
 
 def lat_stats(ms: np.ndarray) -> dict:
-    us = ms.astype(np.float64) * 1e3
-    return {"p50_us": pct(us, 50), "p99_us": pct(us, 99), "mean_us": float(us.mean()),
+    us = np.asarray(ms, dtype=np.float64) * 1e3
+    n = int(us.size)
+    p99 = pct(us, 99) if n >= 1000 else None
+    return {"samples": n, "p50_us": pct(us, 50), "p99_us": p99, "mean_us": float(us.mean()),
             "max_us": float(us.max()), "min_us": float(us.min()),
-            "p99_over_p50": pct(us, 99) / pct(us, 50)}
+            "p99_over_p50": (p99 / pct(us, 50)) if p99 is not None else None}
 
 
 KNOBS = {}
-
-
 INPUT_OVERRIDE = {}
 
 
@@ -169,9 +201,9 @@ def make_lane(w, torch, host_input=None, use_graph=True):
     return lane
 
 
-def stage_roofline(lane, w, launches: int) -> dict:
+def stage_times(lane, w, launches: int) -> dict:
     """Per-kernel mean duration from back-to-back launches between HIP events
-    on the lane's stream, and the algorithmic bandwidth it implies."""
+    on the lane's stream (warm caches), and the algorithmic bandwidth."""
     from post_processing_amd import ws
     pb = preprocess_bytes(w)
     out = {}
@@ -190,50 +222,89 @@ def stage_roofline(lane, w, launches: int) -> dict:
     return out
 
 
-def roofline_obj(stages: dict, workload: str) -> dict:
-    """The preprocess kernel against HBM: it is the stage that moves the
-    frame and the tensor, and the one the metric names.  Top-K (a few KB to
-    2.7 MB) and detection are latency-bound single- or few-workgroup chains,
-    which a bandwidth roofline does not describe; their times are in
-    `kernels`, and `slowest_stage` names the stage that took longest."""
-    name = "preprocess"
-    st = stages[name]
+def cold_times(lane, torch, launches: int = 20) -> dict:
+    """Preprocess launches each after a flush kernel on the lane's stream
+    (HIP events around the launch only): a 1 GiB read flush (the headline),
+    a 2 GiB read flush (if the first evicts everything, doubling it changes
+    nothing) and a 1 GiB write flush.  Medians in microseconds."""
+    from post_processing_amd import ws
+    buf = torch.ones((2 * FLUSH_BYTES) // 4, dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    out = {}
+    for name, nbytes, write in (("read_1GiB", FLUSH_BYTES, False),
+                                ("read_2GiB", 2 * FLUSH_BYTES, False),
+                                ("write_1GiB", FLUSH_BYTES, True)):
+        ms = lane.time_stage_cold(ws.STAGE_PREPROCESS, buf, nbytes, launches, write=write)
+        out[name] = float(np.median(ms)) * 1e3
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def roofline_obj(w, stages: dict, cold: dict | None) -> dict:
+    """The preprocess kernel against HBM: the stage that moves the frame and
+    the tensor, and the one the metric names.  Top-K (a few KB to 2.7 MB)
+    and detection are latency-bound chains of one or a few workgroups, which
+    a bandwidth roofline does not describe; their times are in `kernels`."""
+    pb = preprocess_bytes(w)["total"]
+    warm_us = stages["preprocess"]["us"]
+    us = cold["read_1GiB"] if cold else warm_us
+    gbs = pb / (us * 1e-6) / 1e9
+    rec = measured("preprocess", w.name)
+    out = {"kernel": "preprocess", "bound": "hbm", "achieved": round(gbs, 2),
+           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
+           "traffic": rec["traffic"] if rec else None,
+           "bytes_per_launch": pb, "us_per_launch": round(us, 3),
+           "caches": "cold" if cold else "warm",
+           "warm": {"us_per_launch": round(warm_us, 3),
+                    "frac": round(pb / (warm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)},
+           "profiled": None}
+    if cold:
+        out["flush_check_us"] = {k: round(v, 3) for k, v in cold.items()}
+    if rec:
+        prof = {"profile": rec["profile"], "cold_kernel_us": rec["cold_us"],
+                "warm_kernel_us": rec["warm_us"],
+                "cold_frac": round(pb / (rec["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
+        prof["live_cold_over_profiled"] = round(us / rec["cold_us"], 4) if cold else None
+        out["profiled"] = prof
     slow = max(stages, key=lambda s: stages[s]["us"])
-    return {"kernel": name, "bound": "hbm", "achieved": round(st["gbs"], 2),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(st["gbs"] / HBM_PEAK_GBS, 5),
-            "traffic": measured_traffic(workload, name), "bytes_per_launch": st["bytes"],
-            "us_per_launch": round(st["us"], 3),
-            "slowest_stage": {"kernel": slow, "us_per_launch": round(stages[slow]["us"], 3)}}
+    out["slowest_stage"] = {"kernel": slow, "us_per_launch": round(stages[slow]["us"], 3)}
+    return out
 
 
-def run_single(w, torch, steps, warmup, use_graph=True):
-    lane = make_lane(w, torch, use_graph=use_graph)
+def run_replays(lane, torch, steps: int, warmup: int) -> dict:
+    """Warm-up, then `steps` timed replays (the timed region), then -- when
+    fewer than MIN_LATENCY_SAMPLES were timed -- more replays for the
+    latency percentiles."""
     lane.bench(warmup)
     torch.cuda.synchronize()
     ms, wall, host_us = lane.bench(steps, host=True)
     torch.cuda.synchronize()
-    res = {"frames_per_s": steps * w.batch / wall, "wall_s": wall, **lat_stats(ms),
-           "host_p50_us": pct(host_us, 50), "host_p99_us": pct(host_us, 99),
-           "plan": lane.plan()}
-    return lane, res
-
-
-def cold_launches(lane, torch, n: int, flush_bytes: int = 1 << 30) -> np.ndarray:
-    """Single preprocess launches (HIP events around one direct launch), each
-    after reading a >= 1 GiB buffer, so no cache level holds the frame or the
-    tensor.  The evicting pass only reads (the buffer is written once, before
-    the loop), so no dirty lines are left behind for the timed launch to write
-    back.  Returns microseconds per launch (dispatch overhead included)."""
-    from post_processing_amd import ws
-    flush = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda:0")
-    torch.cuda.synchronize()
-    out = []
-    for _ in range(n):
-        flush.sum()
+    res = {"frames_per_s": steps * lane.cfg.batch / wall, "wall_s": wall}
+    if steps < LATENCY["samples"]:
+        ms, _, host_us = lane.bench(LATENCY["samples"], host=True)
         torch.cuda.synchronize()
-        out.append(lane.time_stage(ws.STAGE_PREPROCESS, 1) * 1e3)
-    del flush
-    return np.asarray(out, dtype=np.float64)
+        res["latency_source"] = f"{LATENCY['samples']} replays after the timed steps"
+    else:
+        res["latency_source"] = "the timed steps"
+    res.update(lat_stats(ms))
+    res["host"] = {"p50_us": pct(host_us, 50), "p99_us": pct(host_us, 99)}
+    return res
+
+
+def run_lanes(lanes, torch, steps: int, warmup: int) -> dict:
+    from post_processing_amd import ws
+    ws.bench_lanes(lanes, warmup)
+    torch.cuda.synchronize()
+    ms, wall = ws.bench_lanes(lanes, steps)
+    torch.cuda.synchronize()
+    res = {"frames_per_s": len(lanes) * lanes[0].cfg.batch * steps / wall, "wall_s": wall,
+           "per_lane_p50_us": [pct(m * 1e3, 50) for m in ms]}
+    if len(lanes) * steps < LATENCY["samples"]:
+        ms, _ = ws.bench_lanes(lanes, -(-LATENCY["samples"] // len(lanes)))
+        torch.cuda.synchronize()
+    res.update(lat_stats(ms.ravel()))
+    return res
 
 
 def pinned_h2d_gbs(torch, nbytes: int = 64 << 20, reps: int = 20) -> float:
@@ -255,6 +326,39 @@ def pinned_h2d_gbs(torch, nbytes: int = 64 << 20, reps: int = 20) -> float:
     return gbs
 
 
+def c5l_figures(torch, steps: int = 1000, warmup: int = 100) -> dict:
+    """C5L beside the default line: eight lanes reading 1920x1080 frames from
+    mapped host memory, one host thread each; the preprocess kernel's
+    mapped-read rate; the pinned-host DMA copy rate on the same box."""
+    from post_processing_amd import workloads as wl
+    from post_processing_amd import ws
+    work = [wl.c5_lane(i) for i in range(8)]
+    lanes = [make_lane(x, torch) for x in work]
+    # Lane threads inherit this thread's affinity: let them spread over every
+    # core this process may use (all eight on the one pinned core drop the
+    # rate by a quarter and add a multi-millisecond tail), then pin back.
+    held = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if held is not None:
+        os.sched_setaffinity(0, ALL_CORES or held)
+    try:
+        res = run_lanes(lanes, torch, steps, warmup)
+        us = lanes[0].time_stage(ws.STAGE_PREPROCESS, 200) * 1e3
+        read = preprocess_bytes(work[0])["read"]
+        out = {"lanes": 8, "frames_per_s": round(res["frames_per_s"], 1),
+               "p50_us": round(res["p50_us"], 3),
+               "p99_us": round(res["p99_us"], 3) if res["p99_us"] else None,
+               "latency_samples": res["samples"], "preprocess_us": round(us, 3),
+               "mapped_host_read_gbs": round(read / (us * 1e-6) / 1e9, 2),
+               "pinned_h2d_copy_gbs": round(pinned_h2d_gbs(torch), 2),
+               "transfers_included": True}
+    finally:
+        if held is not None:
+            os.sched_setaffinity(0, held)
+        for ln in lanes:
+            ln.destroy()
+    return out
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, one thread, on the host of this run.
 
@@ -269,36 +373,47 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+def oracle_stage_times(w, reps: int = 5) -> dict:
+    """O-PRE and O-TOPK (and the detection oracle when the workload has a
+    head) timed separately on one thread: the median of `reps` calls after
+    one warm-up call each, in milliseconds."""
     from threadpoolctl import threadpool_limits
 
     from oracle import letterbox_region, preprocess_batch, topk
     from oracle import detect as odet
+    stages = {"o_pre": lambda: preprocess_batch(w.frames, w.dst_w, w.dst_h, w.mean, w.std,
+                                                letterbox=(w.mode == 1), pad=w.pad)}
+    if w.k:
+        stages["o_topk"] = lambda: topk(w.scores, w.k)
+    if w.head is not None:
+        reg = (letterbox_region(w.src_w, w.src_h, w.dst_w, w.dst_h) if w.mode == 1
+               else (0, 0, w.dst_w, w.dst_h))
+        stages["o_detect"] = lambda: odet.detect(w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, reg,
+                                                 w.det["nc"], w.det["conf"], w.det["iou"],
+                                                 w.det["max_det"], w.det["agnostic"])
+    out = {}
     with threadpool_limits(1):
-        def one():
-            preprocess_batch(w.frames, w.dst_w, w.dst_h, w.mean, w.std,
-                             letterbox=(w.mode == 1), pad=w.pad)
-            if w.k:
-                topk(w.scores, w.k)
-            if w.head is not None:
-                reg = (letterbox_region(w.src_w, w.src_h, w.dst_w, w.dst_h) if w.mode == 1
-                       else (0, 0, w.dst_w, w.dst_h))
-                odet.detect(w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, reg, w.det["nc"],
-                            w.det["conf"], w.det["iou"], w.det["max_det"], w.det["agnostic"])
-        one()   # warm-up
-        times = []
-        t_end = time.perf_counter() + budget_s
-        while time.perf_counter() < t_end or len(times) < 3:
-            t0 = time.perf_counter()
-            one()
-            times.append(time.perf_counter() - t0)
-    med = float(np.median(times))
-    return {"value": round(w.batch / med, 3), "unit": "frames/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{len(times)} calls of {w.batch} frame{'s' if w.batch > 1 else ''} of "
-                       f"{w.name} (float64 preprocess"
-                       f"{' + stable-sort Top-K' if w.k else ''}"
-                       f"{' + binary32 decode/NMS' if w.head is not None else ''}), median "
-                       f"{med * 1e3:.1f} ms per call after 1 warm-up, 1 thread"),
+        for name, fn in stages.items():
+            fn()
+            t = []
+            for _ in range(reps):
+                t0 = time.perf_counter()
+                fn()
+                t.append(time.perf_counter() - t0)
+            out[name + "_ms"] = float(np.median(t)) * 1e3
+    return out
+
+
+def cpu_baseline(w) -> dict:
+    st = oracle_stage_times(w)
+    per_frame_ms = sum(st.values()) / w.batch
+    stages = " + ".join(k[:-3].replace("o_", "O-").upper() for k in st)
+    return {"value": round(1e3 / per_frame_ms, 3), "unit": "frames/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{w.name}: {stages} timed separately, median of 5 calls after 1 "
+                       f"warm-up each, {w.batch} frame{'s' if w.batch > 1 else ''} per call, "
+                       f"1 thread; value = frames / sum of the stage medians"),
+            "stages_ms": {k: round(v, 3) for k, v in st.items()},
             "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
@@ -346,6 +461,7 @@ def cpu_baseline_pool(w, cores, budget_s: float = 10.0) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# Run record: versions, GPU state, PCIe link, inputs.
 
 def versions() -> dict:
     out = {"python": platform.python_version(), "numpy": np.__version__}
@@ -361,6 +477,11 @@ def versions() -> dict:
         out["hipcc"] = r.stdout.splitlines()[0] if r.stdout else None
     except Exception:
         pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            out["rocm"] = f.read().strip()
+    except OSError:
+        pass
     # The HIP runtime the lanes actually run on (the first one loaded wins).
     try:
         with open("/proc/self/maps") as f:
@@ -370,16 +491,86 @@ def versions() -> dict:
     return out
 
 
+def _flatten(obj, prefix=""):
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            yield from _flatten(v, f"{prefix}.{k}" if prefix else str(k))
+    elif isinstance(obj, list):
+        for i, v in enumerate(obj):
+            yield from _flatten(v, f"{prefix}[{i}]")
+    else:
+        yield prefix, obj
+
+
 def gpu_state() -> dict:
-    for cmd in (["amd-smi", "metric", "--json"], ["rocm-smi", "--showclocks", "--showtemp",
-                                                    "--showpower", "--json"]):
+    """Clocks, power and temperature from amd-smi (falling back to
+    rocm-smi), as a flat subset of its JSON."""
+    keys = ("clk", "clock", "power", "temp", "hotspot", "throttle", "energy", "voltage")
+    skip = ("usage", "jpeg", "vcn", "ecc", "unit")
+    for cmd in (["amd-smi", "metric", "--json"],
+                ["rocm-smi", "--showclocks", "--showtemp", "--showpower", "--json"]):
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
-            if r.returncode == 0 and r.stdout.strip():
-                return {"tool": cmd[0], "raw": r.stdout[:4000]}
+            if r.returncode != 0 or not r.stdout.strip():
+                continue
+            try:
+                data = json.loads(r.stdout)
+            except ValueError:
+                return {"tool": cmd[0], "raw": r.stdout[:2000]}
+            flat = {k: v for k, v in _flatten(data)
+                    if any(s in k.lower() for s in keys) and not any(s in k.lower() for s in skip)
+                    and v not in (None, "N/A", "")}
+            return {"tool": cmd[0], "metrics": dict(list(flat.items())[:120])}
         except Exception:
             continue
-    return {}
+    return {"tool": None}
+
+
+def pcie_link() -> dict:
+    """PCIe link of the GPU(s) from sysfs (current and maximum speed and
+    width), plus amd-smi's bus report when available."""
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            with open(os.path.join(dev, "vendor")) as f:
+                if f.read().strip() != "0x1002":
+                    continue
+        except OSError:
+            continue
+        rec = {}
+        for name in ("current_link_speed", "current_link_width", "max_link_speed",
+                     "max_link_width"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    rec[name] = f.read().strip()
+            except OSError:
+                pass
+        if rec:
+            out[os.path.basename(os.path.dirname(dev))] = rec
+    try:
+        r = subprocess.run(["amd-smi", "static", "--bus", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                flat = dict(_flatten(json.loads(r.stdout)))
+                out["amd_smi_bus"] = {k: v for k, v in flat.items()
+                                      if any(s in k.lower() for s in ("pcie", "link", "width",
+                                                                      "speed", "bdf"))}
+            except ValueError:
+                out["amd_smi_bus"] = r.stdout[:1000]
+    except Exception:
+        pass
+    return out
+
+
+def input_hashes(w) -> dict:
+    from post_processing_amd import workloads as wl
+    out = {"frames": wl.sha256(w.frames)}
+    if w.k:
+        out["scores"] = wl.sha256(w.scores)
+    if w.head is not None:
+        out["head"] = wl.sha256(w.head)
+    return out
 
 
 def copy_calibration(torch, args) -> int:
@@ -402,16 +593,147 @@ def copy_calibration(torch, args) -> int:
     return 0
 
 
+def load_workload(name: str):
+    from post_processing_amd import workloads as wl
+    if name == "c5l":
+        return [wl.c5_lane(i) for i in range(8)]
+    if name == "c5t":
+        return wl.c5_throughput(64)
+    if name == "c3d":
+        return wl.c3d()
+    return wl.ALL_CONFIGS[name]()
+
+
+def workload_name(name: str, w) -> str:
+    return "c5l_8lanes_1920x1080_to_224_mapped" if name == "c5l" else w.name
+
+
+# ---------------------------------------------------------------------------
+# Campaign: every workload, graph and direct launch, three rotated passes.
+
+CAMPAIGN_ORDER = ["c1", "c2", "c3", "c4", "c5l", "c5t"]
+
+
+def campaign(torch, args) -> int:
+    warm, reps = args.campaign_warmup, args.campaign_replays
+    works = {}
+    for name in CAMPAIGN_ORDER:
+        t0 = time.perf_counter()
+        works[name] = load_workload(name)
+        print(f"[campaign] inputs for {name} in {time.perf_counter() - t0:.1f} s",
+              file=sys.stderr, flush=True)
+    lanes = {}
+    for name, w in works.items():
+        for graph in (True, False):
+            ws_list = w if name == "c5l" else [w]
+            lanes[(name, graph)] = [make_lane(x, torch, use_graph=graph) for x in ws_list]
+    runs = []
+    for c in range(3):
+        order = CAMPAIGN_ORDER[c:] + CAMPAIGN_ORDER[:c]
+        for name in order:
+            for graph in (True, False):
+                ls = lanes[(name, graph)]
+                if len(ls) > 1:
+                    res = run_lanes(ls, torch, reps, warm)
+                else:
+                    res = run_replays(ls[0], torch, reps, warm)
+                runs.append({"campaign": c, "workload": name, "graph": graph,
+                             **{k: (round(v, 3) if isinstance(v, float) else v)
+                                for k, v in res.items()}})
+                print(f"[campaign] {c} {name} graph={graph}: {res['frames_per_s']:.0f} frames/s,"
+                      f" p50 {res['p50_us']:.2f} us, p99/p50 {res['p99_over_p50']:.3f}",
+                      file=sys.stderr, flush=True)
+    summary = {}
+    for name in CAMPAIGN_ORDER:
+        for graph in (True, False):
+            rs = [r for r in runs if r["workload"] == name and r["graph"] == graph]
+            summary[f"{name}_{'graph' if graph else 'direct'}"] = {
+                "frames_per_s": [r["frames_per_s"] for r in rs],
+                "p50_us": [r["p50_us"] for r in rs], "p99_us": [r["p99_us"] for r in rs],
+                "p99_over_p50": [r["p99_over_p50"] for r in rs],
+                "host_p50_us": [round(r["host"]["p50_us"], 3) for r in rs if "host" in r]}
+    for ls in lanes.values():
+        for ln in ls:
+            ln.destroy()
+    oracle = {}
+    if not args.no_cpu_baseline:
+        for name in CAMPAIGN_ORDER:
+            w = works[name][0] if name == "c5l" else works[name]
+            oracle[name] = {k: round(v, 3) for k, v in oracle_stage_times(w).items()}
+            print(f"[campaign] oracle {name}: {oracle[name]}", file=sys.stderr, flush=True)
+    rec = {"metric": "campaign: frames/s and p50/p99 us per graph replay, graph vs direct launch",
+           "warmup_replays": warm, "timed_replays": reps, "campaigns": 3,
+           "order": [CAMPAIGN_ORDER[c:] + CAMPAIGN_ORDER[:c] for c in range(3)],
+           "summary": summary, "oracle_ms_1_thread": oracle, "cpu": cpu_model(),
+           "host_cpus": os.cpu_count(), "versions": versions(), "gpu_state": gpu_state(),
+           "pcie": pcie_link(),
+           "input_sha256": {n: (input_hashes(w[0]) if n == "c5l" else input_hashes(w))
+                            for n, w in works.items()},
+           "transfers_included": {"c5l": True, **{n: False for n in CAMPAIGN_ORDER if n != "c5l"}}}
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump({**rec, "runs": runs}, f, indent=1)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------
+
+def trace_summary(path: str) -> int:
+    """Summarise a rocprofv3 kernel trace (`*_kernel_trace.csv`) of this
+    benchmark: per kernel, the dispatch count and mean / median duration; for
+    the preprocess kernel, separately the launches that directly follow a
+    cache flush on the same queue (cold) and the others (warm).  Runs on the
+    CPU; prints JSON."""
+    import csv
+    with open(path, newline="") as f:
+        rows = list(csv.DictReader(f))
+    recs = []
+    for r in rows:
+        name = r.get("Kernel_Name") or r.get("KernelName") or r.get("Name") or ""
+        t0 = int(r.get("Start_Timestamp") or r.get("BeginNs") or 0)
+        t1 = int(r.get("End_Timestamp") or r.get("EndNs") or 0)
+        q = r.get("Queue_Id") or r.get("Stream_Id") or "0"
+        recs.append((q, t0, t1, name))
+    recs.sort(key=lambda x: (x[0], x[1]))
+    by = {}
+    cold, warm = [], []
+    prev = {}
+    for q, t0, t1, name in recs:
+        us = (t1 - t0) * 1e-3
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        by.setdefault(short, []).append(us)
+        if "preprocess" in short:
+            (cold if "cache_flush_kernel" in prev.get(q, "") else warm).append(us)
+        prev[q] = short
+    out = {"trace": path, "kernels": {k: {"calls": len(v), "mean_us": round(float(np.mean(v)), 3),
+                                          "median_us": round(float(np.median(v)), 3)}
+                                      for k, v in sorted(by.items())}}
+    for label, v in (("preprocess_cold", cold), ("preprocess_warm", warm)):
+        if v:
+            out[label] = {"calls": len(v), "mean_us": round(float(np.mean(v)), 3),
+                          "median_us": round(float(np.median(v)), 3),
+                          "min_us": round(float(np.min(v)), 3),
+                          "max_us": round(float(np.max(v)), 3)}
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="c2",
+    ap.add_argument("--workload", default="c5t",
                     choices=["c1", "c2", "c3", "c4", "c5l", "c5t", "c3d", "copy"])
+    ap.add_argument("--campaign", action="store_true",
+                    help="every workload, three rotated campaigns, graph and direct launch")
+    ap.add_argument("--campaign-warmup", type=int, default=1000)
+    ap.add_argument("--campaign-replays", type=int, default=10000)
     ap.add_argument("--copy-mib", type=int, default=256,
                     help="copy workload: bytes per device-to-device copy (MiB)")
     ap.add_argument("--stage-launches", type=int, default=500)
+    ap.add_argument("--cold-launches", type=int, default=20)
     ap.add_argument("--rows-per-group", type=int, default=0, help="preprocess tuning knob (0 = auto)")
     ap.add_argument("--topk-chunk", type=int, default=0, help="Top-K tuning knob (0 = auto)")
     ap.add_argument("--dtype", default="f32", choices=["f32", "f16", "bf16"],
@@ -422,12 +744,16 @@ def main(argv=None) -> int:
                     help="preprocess tuning knob: 1, 2 or 4 (0 = auto)")
     ap.add_argument("--autotune", action="store_true",
                     help="let each lane time candidate launch geometries at create")
+    ap.add_argument("--wait", default="spin", choices=["spin", "block"],
+                    help="how ws_wait waits for the done event")
     ap.add_argument("--lanes", type=int, default=1,
                     help="lanes driven at once, one host thread each, each with its own "
                          "buffers (not c5l, which is eight lanes): one lane's work runs while "
                          "another's is launched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-direct", action="store_true", help="skip the direct-launch comparison")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the C5L figures and the cold-cache launches")
     ap.add_argument("--report", default=None, help="also write a detailed JSON report here")
     ap.add_argument("--graph-packet-capture", choices=["off", "runtime-default"],
                     default="runtime-default",
@@ -436,12 +762,21 @@ def main(argv=None) -> int:
     ap.add_argument("--pin-core", type=int, default=-2,
                     help="run the submit/wait loop on this host core (-2: the last core this "
                          "process may use; -1: no pinning); single-lane workloads only")
+    ap.add_argument("--latency-samples", type=int, default=MIN_LATENCY_SAMPLES,
+                    help="replays the latency percentiles are taken over, at least (lower it "
+                         "only for profiler runs, where every dispatch is slowed)")
+    ap.add_argument("--trace-summary", default=None, metavar="CSV",
+                    help="summarise a rocprofv3 kernel trace of this benchmark and exit (CPU)")
     args = ap.parse_args(argv)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary)
+    LATENCY["samples"] = args.latency_samples
     if args.graph_packet_capture == "off":
         # Must be in the environment before torch (or anything else) starts HIP.
         os.environ["DEBUG_CLR_GRAPH_PACKET_CAPTURE"] = "0"
     pinned = None
     all_cores = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
+    ALL_CORES.update(all_cores)
     if args.pin_core != -1 and hasattr(os, "sched_setaffinity"):
         allowed = sorted(os.sched_getaffinity(0))
         pinned = allowed[-1] if args.pin_core == -2 else args.pin_core
@@ -459,31 +794,29 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
-    from post_processing_amd import workloads as wl
     from post_processing_amd import ws
     ws.load()
 
     KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
-                 pixels_per_thread=args.pixels_per_thread, autotune=args.autotune)
+                 pixels_per_thread=args.pixels_per_thread, autotune=args.autotune,
+                 wait_mode=ws.WAIT_BLOCK if args.wait == "block" else ws.WAIT_SPIN)
     TENSOR["dtype"] = args.dtype
     if args.input:
         INPUT_OVERRIDE["mode"] = {"device": ws.INPUT_DEVICE, "mapped": ws.INPUT_MAPPED_HOST,
                                   "copy": ws.INPUT_COPY}[args.input]
-    name = args.workload
-    if name == "copy":
+    if args.workload == "copy":
         return copy_calibration(torch, args)
+    if args.campaign:
+        if pinned is not None:
+            os.sched_setaffinity(0, {pinned})
+        return campaign(torch, args)
+    name = args.workload
     t_gen = time.perf_counter()
-    if name == "c5l":
-        work = [wl.c5_lane(i) for i in range(8)]
-        w = work[0]
-    elif name == "c5t":
-        w = wl.c5_throughput(64)
-    elif name == "c3d":
-        w = wl.c3d()
-    else:
-        w = wl.ALL_CONFIGS[name]()
-    gen_s = time.perf_counter() - t_gen
-    print(f"[bench] inputs for {name} ready in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    loaded = load_workload(name)
+    work = loaded if name == "c5l" else None
+    w = loaded[0] if name == "c5l" else loaded
+    print(f"[bench] inputs for {name} ready in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
 
     extra = {}
     if args.lanes != 1 and (name == "c5l" or args.lanes < 1 or args.lanes > 8):
@@ -496,47 +829,49 @@ def main(argv=None) -> int:
         pinned = None
     if pinned is not None:
         os.sched_setaffinity(0, {pinned})   # this thread runs every submit/wait loop below
+    cold = None
     if multi:
         lanes = [make_lane(x, torch) for x in (work if name == "c5l" else [w] * args.lanes)]
-        ws.bench_lanes(lanes, args.warmup)
-        torch.cuda.synchronize()
-        ms, wall = ws.bench_lanes(lanes, args.steps)
-        torch.cuda.synchronize()
-        frames = len(lanes) * w.batch * args.steps
-        res = {"frames_per_s": frames / wall, "wall_s": wall, **lat_stats(ms.ravel()),
-               "per_lane_p50_us": [pct(m * 1e3, 50) for m in ms],
-               "plan": lanes[0].plan()}
-        stages = stage_roofline(lanes[0], w, args.stage_launches)
-        pb = preprocess_bytes(w)
+        res = run_lanes(lanes, torch, args.steps, args.warmup)
+        res["latency_source"] = "replays of all lanes"
+        res["plan"] = lanes[0].plan()
+        lane = lanes[0]
+        stages = stage_times(lane, w, args.stage_launches)
         if name == "c5l":
+            pb = preprocess_bytes(w)
             extra["mapped_host_read_gbs"] = pb["read"] / (stages["preprocess"]["us"] * 1e-6) / 1e9
             extra["pinned_h2d_copy_gbs"] = pinned_h2d_gbs(torch)
-        lane = lanes[0]
         steps_total = len(lanes) * args.steps
     else:
-        lane, res = run_single(w, torch, args.steps, args.warmup)
-        stages = stage_roofline(lane, w, args.stage_launches)
+        lane = make_lane(w, torch)
+        res = run_replays(lane, torch, args.steps, args.warmup)
+        res["plan"] = lane.plan()
+        stages = stage_times(lane, w, args.stage_launches)
         steps_total = args.steps
-        if name == "c5t":
-            cold = cold_launches(lane, torch, 20)
-            pb = preprocess_bytes(w)
-            extra["cold_preprocess_us_p50"] = float(np.median(cold))
-            extra["cold_hbm_gbs"] = pb["total"] / (np.median(cold) * 1e-6) / 1e9
-            extra["cold_frac_of_hbm_peak"] = extra["cold_hbm_gbs"] / HBM_PEAK_GBS
+        if not args.no_extras and lane.cfg.input_mode == ws.INPUT_DEVICE:
+            print("[bench] cold-cache launches", file=sys.stderr, flush=True)
+            cold = cold_times(lane, torch, args.cold_launches)
         if lane.cfg.input_mode != ws.INPUT_DEVICE:
             pb = preprocess_bytes(w)
             if lane.cfg.input_mode == ws.INPUT_MAPPED_HOST:
                 extra["mapped_host_read_gbs"] = (pb["read"] / (stages["preprocess"]["us"] * 1e-6)
                                                  / 1e9)
             extra["pinned_h2d_copy_gbs"] = pinned_h2d_gbs(torch)
-        if not args.no_direct and name != "c5t":
-            dl, dres = run_single(w, torch, min(args.steps, 2000), min(args.warmup, 200),
-                                  use_graph=False)
-            extra["direct_launch"] = {k: dres[k] for k in ("frames_per_s", "p50_us", "p99_us")}
+        if not args.no_direct:
+            dl = make_lane(w, torch, use_graph=False)
+            dres = run_replays(dl, torch, min(args.steps, LATENCY["samples"]),
+                               min(args.warmup, 1000))
+            extra["direct_launch"] = {"frames_per_s": round(dres["frames_per_s"], 1),
+                                      "p50_us": round(dres["p50_us"], 3),
+                                      "p99_us": round(dres["p99_us"], 3),
+                                      "latency_samples": dres["samples"]}
             dl.destroy()
+        if name == "c5t" and not args.no_extras:
+            print("[bench] C5L lanes", file=sys.stderr, flush=True)
+            extra["c5l"] = c5l_figures(torch)
 
-    roof = roofline_obj(stages, w.name)
-    pb = preprocess_bytes(w)
+    roof = roofline_obj(w, stages, cold)
+    input_mode = args.input or ("mapped" if (w.host_input or name == "c5l") else "device")
     line = {
         "metric": "frames/s and p50/p99 us per graph replay; preprocess HBM GB/s vs peak",
         "value": round(res["frames_per_s"], 2),
@@ -550,26 +885,28 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "f32" if args.dtype == "f32" else f"f32->{args.dtype}",
         "data": "synthetic",
-        "config": {"workload": w.name if name != "c5l" else "c5l_8lanes_1920x1080_to_224_mapped",
+        "config": {"workload": workload_name(name, w),
                    "frames_per_step": w.batch, "src": [w.src_w, w.src_h],
                    "dst": [w.dst_w, w.dst_h], "letterbox": w.mode == 1,
                    "topk": {"n": w.num_scores, "k": w.k} if w.k else None,
                    "detect": ({"anchors": int(w.head.shape[1]), **{k: w.det[k] for k in
                               ("nc", "conf", "iou", "max_det")}} if w.head is not None else None),
-                   "input": args.input or ("mapped" if (w.host_input or name == "c5l") else "device"),
+                   "input": input_mode,
                    "graph": True, "lanes": 8 if name == "c5l" else args.lanes,
+                   "wait": args.wait,
                    "graph_packet_capture": args.graph_packet_capture,
                    "host_core": pinned,
                    "parallelism": "single_gpu"},
         "p50_us": round(res["p50_us"], 3),
-        "p99_us": round(res["p99_us"], 3),
-        "p99_over_p50": round(res["p99_over_p50"], 4),
+        "p99_us": round(res["p99_us"], 3) if res["p99_us"] is not None else None,
+        "p99_over_p50": round(res["p99_over_p50"], 4) if res["p99_over_p50"] else None,
+        "latency_samples": res["samples"],
+        "latency_source": res["latency_source"],
         # Host view of the same replays: just before ws_submit to ws_wait's return.
-        "host_submit_to_return_us": ({"p50": round(res["host_p50_us"], 3),
-                                      "p99": round(res["host_p99_us"], 3)}
-                                     if "host_p50_us" in res else None),
-        "preprocess_gbs": round(stages["preprocess"]["gbs"], 2),
-        "preprocess_frac_of_hbm_peak": round(stages["preprocess"]["gbs"] / HBM_PEAK_GBS, 5),
+        "host_submit_to_return_us": ({"p50": round(res["host"]["p50_us"], 3),
+                                      "p99": round(res["host"]["p99_us"], 3)}
+                                     if "host" in res else None),
+        "transfers_included": input_mode != "device",
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                         for kk, vv in v.items()} for k, v in stages.items()},
         "plan": res["plan"],
@@ -584,15 +921,11 @@ def main(argv=None) -> int:
             line["cpu_baseline_pool"] = cpu_baseline_pool(w, all_cores)
     else:
         line["cpu_baseline"] = None
+    line["env"] = {"versions": versions(), "gpu_state": gpu_state(), "pcie": pcie_link()}
+    line["input_sha256"] = input_hashes(w)
     if args.report:
-        rep = dict(line)
-        rep["latency"] = {k: res[k] for k in res if k.endswith("_us") or k.startswith("p99")}
-        rep["versions"] = versions()
-        rep["gpu_state"] = gpu_state()
-        rep["input_sha256"] = {"frames": wl.sha256(w.frames),
-                               "scores": wl.sha256(w.scores) if w.k else None}
         with open(args.report, "w") as f:
-            json.dump(rep, f, indent=1)
+            json.dump(dict(line, latency=res), f, indent=1)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -74,6 +74,23 @@ int ws_bench_lanes(ws_lane **lanes, int32_t nlanes, int32_t replays, float *gpu_
  */
 int ws_bench_stage(ws_lane *lane, int32_t stage, int32_t launches, double *ms_per_launch);
 
+/*
+ * Time one stage's kernels with the caches evicted before each launch.  For
+ * each of `launches` runs, a flush kernel on the lane's stream streams over
+ * the first `flush_bytes` of the caller's device buffer `flush` (reading it,
+ * or writing zeros over it when `flush_write` is 1); then the start event,
+ * the stage's kernels and the done event follow in stream order, so the
+ * start event fires when the flush ends and the interval holds the stage
+ * alone (its dispatch included).  The flush buffer must be larger than the
+ * last-level cache for the launch to start cold.
+ *   ms  `launches` entries: start->done time of each run, in milliseconds.
+ * The lane must be READY and stays READY.  Returns WS_OK, WS_E_STATE,
+ * WS_E_INVALID_ARG (NULL, flush not 16-byte aligned, flush_bytes < 16,
+ * launches < 1, or a stage the lane does not have) or WS_E_HIP.
+ */
+int ws_bench_stage_cold(ws_lane *lane, int32_t stage, void *flush, size_t flush_bytes,
+                        int32_t flush_write, int32_t launches, float *ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libws.so")
-SOURCES = ["ws_kernels.hip", "ws_detect.hip", "ws_runtime.hip"]
+SOURCES = ["ws_preprocess.hip", "ws_topk.hip", "ws_detect.hip", "ws_runtime.hip"]
 ARCH = "gfx950"
 
 
@@ -57,11 +57,16 @@ def build_lib(verbose: bool = False) -> str:
     return LIB
 
 
-def build_host_test(out: str) -> str:
-    """g++ build of the planning code's host-only test driver (no HIP)."""
+def build_host_test(out: str, sanitize: bool = False) -> str:
+    """g++ build of the planning code's host-only test driver (no HIP);
+    with `sanitize`, instrumented by AddressSanitizer and
+    UndefinedBehaviorSanitizer, any report aborting the run."""
     src = os.path.join(ROOT, "tests", "host", "ws_plan_test.cpp")
-    cmd = ["g++", "-std=c++17", "-O1", "-Wall", "-Werror", "-I", INCLUDE, "-I", CSRC,
-           "-o", out, src]
+    cmd = ["g++", "-std=c++17", "-O1", "-Wall", "-Werror", "-I", INCLUDE, "-I", CSRC]
+    if sanitize:
+        cmd += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                "-fno-sanitize-recover=all"]
+    cmd += ["-o", out, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("g++ failed:\n" + res.stdout + res.stderr)

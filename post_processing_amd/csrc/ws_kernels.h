@@ -1,4 +1,5 @@
-// ws_kernels.h -- launch parameters and launchers of the two pipeline kernels.
+// ws_kernels.h -- launch parameters and launchers of the pipeline's kernels
+// (ws_preprocess.hip, ws_topk.hip, ws_detect.hip).
 // Internal to the library (not part of the C ABI).
 #pragma once
 
@@ -77,6 +78,8 @@ struct DetParams {
 hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_bytes,
                              hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+// Raise the dynamic LDS limit of the staged preprocess kernels.
+hipError_t set_preprocess_attributes();
 // Decode (one thread per anchor) then NMS (one workgroup), in stream order.
 hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream);
 // Dynamic LDS of the suppression kernel, and raising its limit (once per process).

@@ -217,16 +217,6 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
     const Region& g = p->region;
     const int64_t W = c.src_w, H = c.src_h, Dw = c.dst_w, Dh = c.dst_h;
 
-    // The byte span of a source row that the region's horizontal taps read.
-    const Tap first = axis_tap(W, g.w, 0);
-    const Tap last = axis_tap(W, g.w, g.w - 1);
-    p->span_lo = 3 * (int64_t)first.i0;
-    p->span = 3 * (int64_t)last.i1 + 3 - p->span_lo;
-    // A staged row starts at its 16-byte-aligned address below the span, so it
-    // needs up to 15 extra bytes in front.
-    p->slot_bytes = (int32_t)(ceil_div(p->span + 15, 16) * 16);
-    if (lds_for_rows(1, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
-
     // Pixels per thread: 1 by default, which runs as the gather kernel (each
     // thread reads its taps straight from global memory, no row staging).
     // Measured on MI355X it beat the LDS-staged kernels with 2 or 4 columns
@@ -236,6 +226,18 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
     int32_t px = c.pixels_per_thread;
     if (px == 0) px = 1;
     p->pixels_per_thread = px;
+    const bool staged = px > 1;   // only the staged kernels hold source rows in LDS
+
+    // The byte span of a source row that the region's horizontal taps read.
+    const Tap first = axis_tap(W, g.w, 0);
+    const Tap last = axis_tap(W, g.w, g.w - 1);
+    p->span_lo = 3 * (int64_t)first.i0;
+    p->span = 3 * (int64_t)last.i1 + 3 - p->span_lo;
+    // A staged row starts at its 16-byte-aligned address below the span, so it
+    // needs up to 15 extra bytes in front.
+    p->slot_bytes = staged ? (int32_t)(ceil_div(p->span + 15, 16) * 16) : 0;
+    if (staged && lds_for_rows(1, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
+
     p->threads_per_row = (int32_t)ceil_div(Dw, px);
     const int32_t q = p->threads_per_row;
 
@@ -247,23 +249,24 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
         // Tiny rows are packed so a workgroup holds at least one full wave.
         rows = (px == 4 || Dh < 320) ? 1 : 2;
         while (rows < Dh && (int64_t)(rows + 1) * q <= 64) ++rows;
-        while (rows > 1 && lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes / 2) --rows;
+        while (staged && rows > 1 && lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes / 2)
+            --rows;
     }
     if (rows > Dh) rows = (int32_t)Dh;
-    if (lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
+    if (staged && lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
     p->rows_per_group = rows;
     const int64_t threads = (int64_t)rows * q;
     // The gather kernel (PX = 1) holds no LDS per thread and takes workgroups
     // of up to 1024 threads, so a 640-wide row no longer loops over some
     // threads twice (640x640 letterbox 4.31 -> 4.16 us); the staged kernels
     // keep 512.
-    const int64_t block_cap = px == 1 ? kMaxGatherBlock : kMaxPreBlock;
+    const int64_t block_cap = staged ? kMaxPreBlock : kMaxGatherBlock;
     p->pre_block = (int32_t)std::min<int64_t>(block_cap, ceil_div(threads, 64) * 64);
     p->groups_per_frame = (int32_t)ceil_div(Dh, rows);
     const int64_t groups = (int64_t)c.batch * p->groups_per_frame;
     if (groups > 0x7fffffff) return WS_E_INVALID_ARG;
     p->pre_groups = (int32_t)groups;
-    p->lds_bytes = lds_for_rows(rows, p->slot_bytes);
+    p->lds_bytes = staged ? lds_for_rows(rows, p->slot_bytes) : 0;
 
     if (c.num_scores > 0) {
         // Up to 8 Ki scores one workgroup does everything, so no merge kernel

@@ -1,11 +1,11 @@
 // ws_runtime.hip -- lane runtime behind the C ABI in ws.h / ws_bench.h.
 //
-// WarpStream TRT article, lane and initialisation passages: each lane owns a
-// mapped input slot, a device tensor, device scores, a mapped result slot,
-// two timing events, a non-blocking stream and one instantiated graph; all of
-// it is created here once, and submit / wait only record events, replay the
-// graph and wait.  Map-host capability is checked before any mapped
-// allocation and its absence is reported, not ignored.
+// Every resource a lane uses is created in ws_create_lane and released in
+// ws_destroy (WarpStream TRT article, lane and initialisation passages); the
+// per-frame calls only record events, replay the graph and wait.  What a lane
+// holds is the ws_lane struct below.  Whether the device can map pinned host
+// memory is checked before the first mapped allocation, and a device that
+// cannot is reported as an error.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -64,6 +64,25 @@ struct ws_lane {
 static_assert(ws::kDetDecodeBlock == ws::kDetDecodeAnchors, "decode grid and kernel agree");
 
 namespace {
+
+// Benchmark aid: streams over a buffer larger than the last-level cache so
+// that the next kernel starts with cold caches.  Reads accumulate into a
+// value stored only through a pointer the host passes as NULL, which keeps
+// the loads without writing anything.
+__global__ __launch_bounds__(256) void cache_flush_kernel(uint4* buf, size_t n16, int32_t write,
+                                                          uint32_t* sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        if (write) {
+            buf[i] = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+            const uint4 v = buf[i];
+            acc += v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+    if (sink != nullptr && acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
+}
 
 int fail(ws_lane* L, hipError_t e, int code) {
     if (L) L->last_err = (int)e;
@@ -271,6 +290,12 @@ int autotune(ws_lane* L) {
             c.rows_per_group = rows;
             ws::Plan p;
             if (ws::make_plan(c, &p) != WS_OK) continue;
+            // Every preprocess field of the candidate plan: the staged
+            // kernels also need the row span and slot size, which the gather
+            // kernel's plan leaves at zero.
+            L->plan.span_lo = p.span_lo;
+            L->plan.span = p.span;
+            L->plan.slot_bytes = p.slot_bytes;
             L->plan.pixels_per_thread = p.pixels_per_thread;
             L->plan.threads_per_row = p.threads_per_row;
             L->plan.rows_per_group = p.rows_per_group;
@@ -600,23 +625,58 @@ int ws_bench_lanes(ws_lane** lanes, int32_t nlanes, int32_t replays, float* gpu_
     return WS_OK;
 }
 
+namespace {
+
+hipError_t launch_stage(ws_lane* L, int32_t stage) {
+    if (stage == WS_STAGE_PREPROCESS)
+        return ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
+                                     L->plan.lds_bytes, L->stream);
+    if (stage == WS_STAGE_TOPK) return ws::launch_topk(L->tk, L->stream);
+    return ws::launch_detect(L->det, L->plan.det_decode_groups, L->stream);
+}
+
+bool stage_present(const ws_lane* L, int32_t stage) {
+    if (stage == WS_STAGE_PREPROCESS) return true;
+    if (stage == WS_STAGE_TOPK) return L->cfg.num_scores > 0;
+    if (stage == WS_STAGE_DETECT) return L->plan.det_anchors > 0;
+    return false;
+}
+
+}  // namespace
+
+int ws_bench_stage_cold(ws_lane* L, int32_t stage, void* flush, size_t flush_bytes,
+                        int32_t flush_write, int32_t launches, float* ms) {
+    if (!L || !flush || !ms || launches < 1 || flush_bytes < 16 || !ws::aligned16(flush))
+        return WS_E_INVALID_ARG;
+    if (!stage_present(L, stage) || (flush_write != 0 && flush_write != 1))
+        return WS_E_INVALID_ARG;
+    if (ws::begin_submit(L->state) != WS_OK) return WS_E_STATE;
+    hipError_t e = hipSuccess;
+    for (int32_t i = 0; i < launches && e == hipSuccess; ++i) {
+        hipLaunchKernelGGL(cache_flush_kernel, dim3(4096), dim3(256), 0, L->stream,
+                           static_cast<uint4*>(flush), flush_bytes / 16, flush_write,
+                           static_cast<uint32_t*>(nullptr));
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventRecord(L->ev_start, L->stream);
+        if (e == hipSuccess) e = launch_stage(L, stage);
+        if (e == hipSuccess) e = hipEventRecord(L->ev_done, L->stream);
+        const hipError_t se = hipStreamSynchronize(L->stream);
+        if (e == hipSuccess) e = se;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], L->ev_start, L->ev_done);
+    }
+    if (e != hipSuccess) {
+        hipStreamSynchronize(L->stream);
+        return fail(L, e, WS_E_HIP);
+    }
+    return WS_OK;
+}
+
 int ws_bench_stage(ws_lane* L, int32_t stage, int32_t launches, double* ms_per_launch) {
     if (!L || !ms_per_launch || launches < 1) return WS_E_INVALID_ARG;
-    if (stage != WS_STAGE_PREPROCESS && stage != WS_STAGE_TOPK && stage != WS_STAGE_DETECT)
-        return WS_E_INVALID_ARG;
-    if (stage == WS_STAGE_TOPK && L->cfg.num_scores == 0) return WS_E_INVALID_ARG;
-    if (stage == WS_STAGE_DETECT && L->plan.det_anchors == 0) return WS_E_INVALID_ARG;
+    if (!stage_present(L, stage)) return WS_E_INVALID_ARG;
     if (ws::begin_submit(L->state) != WS_OK) return WS_E_STATE;
     hipError_t e = hipEventRecord(L->ev_start, L->stream);
-    for (int32_t i = 0; i < launches && e == hipSuccess; ++i) {
-        if (stage == WS_STAGE_PREPROCESS)
-            e = ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
-                                      L->plan.lds_bytes, L->stream);
-        else if (stage == WS_STAGE_TOPK)
-            e = ws::launch_topk(L->tk, L->stream);
-        else
-            e = ws::launch_detect(L->det, L->plan.det_decode_groups, L->stream);
-    }
+    for (int32_t i = 0; i < launches && e == hipSuccess; ++i) e = launch_stage(L, stage);
     if (e == hipSuccess) e = hipEventRecord(L->ev_done, L->stream);
     const hipError_t se = hipStreamSynchronize(L->stream);
     if (e == hipSuccess) e = se;

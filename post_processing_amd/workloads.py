@@ -1,8 +1,10 @@
 """Seeded synthetic inputs for the frame pipeline (frames and score vectors).
 
 This module draws random numbers and nothing else: it holds none of the
-pipeline's arithmetic (no sampling, normalisation or selection), so both the
-CPU oracle's tests and the HIP path can take their inputs from it.
+pipeline's arithmetic (no sampling, normalisation, letterbox placement,
+decode or selection), so both the CPU oracle's tests and the HIP path can
+take their inputs from it.  Where planted detection objects need a window
+of the network canvas, the window is a constant given by the caller.
 
 Workload shapes follow the WarpStream TRT article (batch-1 interleaved RGB8
 producer frames, fixed-size FP32 classifier logits, Top-K with K <= 32) and the
@@ -267,8 +269,9 @@ def c3d(seed: int = 5, objects: int = 24) -> Workload:
     The Top-K stage ranks the head's class block (the same 8400x80 scores)."""
     rng = np.random.default_rng(seed)
     frame = uniform_frame(rng, 1280, 720)
-    region = (0, 140, 640, 360)       # where a 1280x720 frame lands in 640x640
-    head, planted = detection_head(rng, 640, 640, 80, region, objects)
+    # Objects are planted in canvas rows 140..500, a fixed window (the band a
+    # 16:9 frame covers on a square canvas) given here as constants.
+    head, planted = detection_head(rng, 640, 640, 80, (0, 140, 640, 360), objects)
     return Workload("c3d_1280x720_letterbox_640_detect", 1280, 720, 640, 640, LETTERBOX,
                     (0.0, 0.0, 0.0), (1.0, 1.0, 1.0), 114.0, 32, frame[None],
                     head[4 * HEAD_BINS:].ravel().copy(), head=head,
@@ -285,14 +288,10 @@ def detect_small(seed: int) -> Workload:
     sw, sh = (int(v) for v in rng.integers(8, 400, size=2))
     letterbox = bool(rng.integers(0, 2))
     nc = int(rng.integers(1, 121))
-    if letterbox:
-        r = min(nw / sw, nh / sh)
-        rw = min(max(int(np.floor(sw * r + 0.5)), 1), nw)
-        rh = min(max(int(np.floor(sh * r + 0.5)), 1), nh)
-        region = ((nw - rw) // 2, (nh - rh) // 2, rw, rh)
-    else:
-        region = (0, 0, nw, nh)
-    head, planted = detection_head(rng, nw, nh, nc, region, int(rng.integers(0, 13)),
+    # Objects are planted anywhere on the network canvas (in letterbox mode
+    # some fall on the pad bands, so their boxes are clipped to the frame
+    # when mapped back).
+    head, planted = detection_head(rng, nw, nh, nc, (0, 0, nw, nh), int(rng.integers(0, 13)),
                                    bg_mean=float(rng.uniform(-7.0, -1.0)))
     frames = rng.integers(0, 256, size=(1, sh, sw, 3), dtype=np.uint8)
     det = dict(nc=nc, conf=float(np.float32(rng.uniform(0.05, 0.6))),

@@ -148,6 +148,9 @@ def load(path: str = LIB_PATH):
     lib.ws_bench_lanes.restype = c_int
     lib.ws_bench_stage.argtypes = [c_void_p, c_int32, c_int32, POINTER(c_double)]
     lib.ws_bench_stage.restype = c_int
+    lib.ws_bench_stage_cold.argtypes = [c_void_p, c_int32, c_void_p, c_size_t, c_int32, c_int32,
+                                        POINTER(c_float)]
+    lib.ws_bench_stage_cold.restype = c_int
     _lib = lib
     return lib
 
@@ -268,6 +271,22 @@ class Lane:
                                     shape=(2 * k,)).copy()
         return raw[0::2].view(np.float32), raw[1::2].view(np.int32)
 
+    def result_slot_words(self) -> np.ndarray:
+        """Writable uint32 view of the mapped result slot (score bits, index)
+        x K, e.g. to overwrite it with a marker before a replay."""
+        if self.cfg.k == 0 or not self.view.result_host:
+            raise RuntimeError("lane has no Top-K stage")
+        return np.ctypeslib.as_array(ctypes.cast(self.view.result_host, POINTER(ctypes.c_uint32)),
+                                     shape=(2 * self.cfg.k,))
+
+    def detection_slot_words(self) -> np.ndarray:
+        """Writable uint32 view of the whole mapped detection slot."""
+        if not self.view.det_result_host:
+            raise RuntimeError("lane has no detection stage")
+        return np.ctypeslib.as_array(ctypes.cast(self.view.det_result_host,
+                                                 POINTER(ctypes.c_uint32)),
+                                     shape=(ctypes.sizeof(DetResult) // 4,))
+
     def detections(self) -> tuple[np.ndarray, np.ndarray, np.ndarray, int]:
         """Copy of the detection slot: (float32 boxes[n][4], float32 scores[n],
         int32 classes[n], number of candidates)."""
@@ -310,6 +329,17 @@ class Lane:
         if rc != WS_OK:
             raise WsError(rc, "ws_bench_stage", self.hip_error())
         return ms.value
+
+    def time_stage_cold(self, stage: int, flush, flush_bytes: int, launches: int,
+                        write: bool = False) -> np.ndarray:
+        """ms per launch of one stage, each launch after a flush kernel over
+        `flush_bytes` of the device buffer `flush` (native loop)."""
+        ms = (c_float * launches)()
+        rc = self._lib.ws_bench_stage_cold(self.handle, stage, _addr(flush), flush_bytes,
+                                           1 if write else 0, launches, ms)
+        if rc != WS_OK:
+            raise WsError(rc, "ws_bench_stage_cold", self.hip_error())
+        return np.ctypeslib.as_array(ms).copy()
 
     def destroy(self) -> None:
         if self.handle:

@@ -164,8 +164,27 @@ static int selftest() {
     c = good();
     c.src_w = WS_MAX_SIDE;
     c.dst_w = WS_MAX_SIDE;
+    CHECK(ws::make_plan(c, &p) == WS_OK);  // widest rows, gather kernel: no LDS
+    CHECK(p.lds_bytes == 0 && p.slot_bytes == 0);
+    c.pixels_per_thread = 2;
     CHECK(ws::make_plan(c, &p) == WS_OK);  // widest rows still stage
-    CHECK(p.lds_bytes <= ws::kMaxLdsBytes);
+    CHECK(p.lds_bytes > 0 && p.lds_bytes <= ws::kMaxLdsBytes);
+    // 3840 -> 384 with seven rows per workgroup: the staged kernels would
+    // need more LDS than a workgroup holds and are refused; the gather kernel
+    // holds none, so the same geometry is accepted.
+    c = good();
+    c.src_w = 3840;
+    c.src_h = 2160;
+    c.dst_w = 384;
+    c.dst_h = 384;
+    c.rows_per_group = 7;
+    c.pixels_per_thread = 2;
+    CHECK(ws::make_plan(c, &p) == WS_E_INVALID_ARG);
+    c.pixels_per_thread = 4;
+    CHECK(ws::make_plan(c, &p) == WS_E_INVALID_ARG);
+    c.pixels_per_thread = 1;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(p.rows_per_group == 7 && p.lds_bytes == 0 && p.pre_block == 1024);
     c = good();
     c.num_scores = 672000;
     c.k = 32;

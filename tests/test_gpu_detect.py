@@ -282,3 +282,23 @@ def test_detection_near_the_anchor_limit(gpu_lib):
     assert head.shape[1] == 16128
     got, _ = _run_detect(w)
     assert_detections_exact(got, oracle_detections(w))
+
+
+@pytest.mark.parametrize("case", ["c3d"] + [f"small{i}" for i in range(40)])
+def test_detection_matches_float64_definitions(gpu_lib, case):
+    """The GPU's kept boxes against greedy suppression on the float64
+    definitions directly (not through the oracle's binary32 path): the same
+    candidate count and rank order, each box within the derived binary32
+    bound of its softmax-expectation box mapped to source pixels, and every
+    keep/suppress decision equal to the exact-rational IoU decision wherever
+    |IoU - threshold| exceeds the binary32 error bound.  Decisions inside
+    that band are counted and printed."""
+    from detect_exact import check_against_definitions
+    from gpu_util import workload_region
+    w = wl.c3d() if case == "c3d" else wl.detect_small(int(case[5:]))
+    d = w.det
+    got, _ = _run_detect(w)
+    in_band = check_against_definitions(got, w.head, w.src_w, w.src_h, w.dst_w, w.dst_h,
+                                        workload_region(w), d["conf"], d["iou"], d["max_det"],
+                                        d["agnostic"])
+    print(f"{case}: {got[3]} candidates, {len(got[1])} kept, {in_band} decisions in the band")

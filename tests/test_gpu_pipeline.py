@@ -34,7 +34,7 @@ def test_config_parity_device_input(gpu_lib, name):
         r.close()
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_config_parity_mapped_host_input(gpu_lib, name):
     w = wl.ALL_CONFIGS[name]()
     ref, rtk = oracle_outputs(w)
@@ -48,7 +48,7 @@ def test_config_parity_mapped_host_input(gpu_lib, name):
         r.close()
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_config_parity_copy_input(gpu_lib, name):
     w = wl.ALL_CONFIGS[name]()
     ref, rtk = oracle_outputs(w)
@@ -133,10 +133,13 @@ def test_bgr_input(gpu_lib, name):
         b.close()
 
 
-def test_throughput_batch_parity(gpu_lib):
+@pytest.mark.parametrize("mode", ["device", "mapped"])
+def test_throughput_batch_parity(gpu_lib, mode):
+    """The 64-frame batch, from device memory (the bandwidth workload) and
+    read over the bus from mapped pinned host memory."""
     w = wl.c5_throughput(64)
     ref, _ = oracle_outputs(w)
-    r = Run(w, host_input=False)
+    r = Run(w, input_mode=ws.INPUT_DEVICE if mode == "device" else ws.INPUT_MAPPED_HOST)
     try:
         r.run()
         t, _ = r.outputs()
@@ -224,12 +227,30 @@ def test_autotuned_lane_matches_default_lane(gpu_lib, name):
         b.close()
 
 
-def test_rows_per_group_beyond_lds_rejected(gpu_lib):
+@pytest.mark.parametrize("px", [2, 4])
+def test_rows_per_group_beyond_lds_rejected(gpu_lib, px):
     # 7 staged row pairs of 3840-pixel rows need ~161 KB of LDS: more than a
-    # workgroup may hold, so the lane refuses the plan instead of launching it.
+    # workgroup may hold, so a staged lane refuses the plan instead of
+    # launching it.
     with pytest.raises(ws.WsError) as ei:
-        Run(wl.c4(), host_input=False, rows_per_group=7)
+        Run(wl.c4(), host_input=False, rows_per_group=7, pixels_per_thread=px)
     assert ei.value.status == ws.WS_E_INVALID_ARG
+
+
+def test_gather_kernel_takes_rows_the_staged_kernel_cannot(gpu_lib):
+    # The gather kernel (one column per thread) stages nothing, so the same
+    # seven rows per workgroup are accepted, allocate no LDS, and match the
+    # oracle.
+    w = wl.c4()
+    ref, _ = oracle_outputs(w)
+    r = Run(w, host_input=False, rows_per_group=7, pixels_per_thread=1)
+    try:
+        plan = r.lane.plan()
+        assert plan["rows_per_group"] == 7 and plan["pre_lds_bytes"] == 0
+        r.run()
+        assert_tensor_close(r.outputs()[0], ref)
+    finally:
+        r.close()
 
 
 def _topk_workload(n, k, seed):
@@ -391,6 +412,81 @@ def test_host_slot_sees_each_new_frame(gpu_lib, mode):
             assert_tensor_close(r.outputs()[0], ref)
     finally:
         r.close()
+
+
+POISON = np.uint32(0x7FC0DEAD)   # a NaN pattern no replay writes
+
+
+@pytest.mark.parametrize("n,chunk,lists", [(1000, 0, 1), (65537, 0, 17), (672000, 0, 83),
+                                           (129 * 1024 - 5, 1024, 129)])
+def test_topk_scores_rewritten_between_replays(gpu_lib, n, chunk, lists):
+    """New scores before every replay, with the result slot overwritten by a
+    marker first, through the one-workgroup path, the fold merge (17 and 83
+    lists) and the bound merge (129 lists).  A merge that read a previous
+    launch's partial lists, or a replay that wrote nothing, would leave a
+    stale or marked answer."""
+    import torch
+    w = _topk_workload(n, 32, seed=n + 3)
+    r = Run(w, host_input=False, topk_chunk=chunk)
+    try:
+        assert r.lane.plan()["topk_groups"] == lists
+        slot = r.lane.result_slot_words()
+        for i in range(4):
+            s = wl.scores_with_specials(700 + 13 * i + n % 97, n, tie_frac=0.2, nan_frac=0.01)
+            if i % 2:
+                s = -s          # a different order of magnitude of winners
+            r.scores.copy_(torch.from_numpy(s))
+            torch.cuda.synchronize()
+            slot[:] = POISON
+            r.run()
+            assert not (slot == POISON).any()
+            assert_topk_exact(r.outputs()[1], topk(s, 32))
+    finally:
+        r.close()
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_device_frame_rewritten_between_replays(gpu_lib, name):
+    """A new frame in the borrowed device input and a poisoned tensor before
+    every replay: each replay must produce the new frame's tensor."""
+    import torch
+    w = wl.ALL_CONFIGS[name]()
+    r = Run(w, host_input=False)
+    try:
+        for i in range(3):
+            frame = np.random.default_rng(800 + i).integers(0, 256, size=w.frames.shape,
+                                                            dtype=np.uint8)
+            r.frames.copy_(torch.from_numpy(frame))
+            r.tensor.fill_(float("nan"))
+            torch.cuda.synchronize()
+            r.run()
+            ref = preprocess_batch(frame, w.dst_w, w.dst_h, w.mean, w.std,
+                                   letterbox=(w.mode == wl.LETTERBOX), pad=w.pad)
+            assert_tensor_close(r.outputs()[0], ref)
+    finally:
+        r.close()
+
+
+def test_topk_lanes_created_and_destroyed_back_to_back(gpu_lib):
+    """Lanes of 65,537 scores, K = 10, created, run once and destroyed one
+    after another, each on different scores: freed device buffers (partial
+    lists, result slot) come back at the same addresses, so a read that
+    returned a previous lane's data there would give a wrong answer."""
+    import torch
+    for i in range(8):
+        s = wl.scores_with_specials(900 + i, 65537, tie_frac=0.2, nan_frac=0.02)
+        frame = np.zeros((1, 4, 4, 3), dtype=np.uint8)
+        w = wl.Workload("reuse", 4, 4, 4, 4, wl.RESIZE, (0, 0, 0), (1, 1, 1), 114.0, 10, frame, s)
+        r = Run(w, host_input=False)
+        try:
+            slot = r.lane.result_slot_words()
+            slot[:] = POISON
+            r.run()
+            assert_topk_exact(r.outputs()[1], topk(s, 10))
+        finally:
+            r.close()
+            del r
+            torch.cuda.synchronize()
 
 
 def test_scores_rewritten_between_frames(gpu_lib):

@@ -54,6 +54,42 @@ def test_letterbox_matches_oracle(driver, src, dst):
     assert got == letterbox_region(*src, *dst)
 
 
+@pytest.fixture(scope="module")
+def sanitized_driver(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("host_asan") / "ws_plan_test_asan")
+    return ppbuild.build_host_test(out, sanitize=True)
+
+
+def test_host_logic_under_address_and_undefined_behaviour_sanitizers(sanitized_driver):
+    """The planner's self-test (config checks, plans at the size limits,
+    state machine), the tap tables of every workload axis and a spread of
+    letterbox boxes, run in a build instrumented by AddressSanitizer and
+    UndefinedBehaviorSanitizer: any out-of-bounds access, leak, signed
+    overflow or other undefined behaviour aborts the run."""
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+
+    def srun(*args):
+        res = subprocess.run([sanitized_driver, *map(str, args)], capture_output=True, text=True,
+                             env=env)
+        assert res.returncode == 0 and "runtime error" not in res.stderr, res.stdout + res.stderr
+        return res.stdout
+
+    assert "0 failures" in srun("selftest")
+    for S, R in [(1080, 224), (1920, 224), (720, 360), (1280, 640), (48, 32), (64, 32),
+                 (2160, 384), (3840, 384), (720, 224), (1280, 224), (1, 7), (16384, 1),
+                 (1, 16384), (16384, 16384)]:
+        rows = srun("taps", S, R).splitlines()
+        assert len(rows) == R
+        i0, i1, _ = axis_taps(S, R)
+        assert [int(r.split()[0]) for r in rows] == i0.tolist()
+        assert [int(r.split()[1]) for r in rows] == i1.tolist()
+    for src, dst in [((1280, 720), (640, 640)), ((1, 16384), (16384, 1)), ((16384, 1), (1, 16384)),
+                     ((641, 479), (640, 640)), ((16384, 16384), (16384, 16384))]:
+        got = tuple(int(v) for v in srun("letterbox", *src, *dst).split())
+        assert got == letterbox_region(*src, *dst)
+
+
 def test_library_exports_declared_symbols():
     from post_processing_amd import ws
     if not os.path.exists(ws.LIB_PATH):

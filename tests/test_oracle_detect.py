@@ -274,3 +274,52 @@ def test_planted_objects_are_recovered():
     assert (boxes >= 0).all() and (boxes[:, [0, 2]] <= w.src_w).all()
     assert (boxes[:, [1, 3]] <= w.src_h).all()
     assert np.all(np.diff(scores.astype(np.float64)) <= 0)
+
+
+# ------------------------------------------- binary32 path vs float64 definitions
+def _region(w):
+    from oracle import letterbox_region
+    return (letterbox_region(w.src_w, w.src_h, w.dst_w, w.dst_h) if w.mode == 1
+            else (0, 0, w.dst_w, w.dst_h))
+
+
+@pytest.mark.parametrize("case", ["c3d"] + [f"small{i}" for i in range(40)])
+def test_decision_path_matches_float64_definitions(case):
+    """The binary32 decision path against greedy suppression on the float64
+    definitions (softmax-expectation boxes, exact-rational IoU): the same
+    candidates and rank order, every box within the derived binary32 bound
+    of the exact box, and every keep/suppress decision equal to the exact
+    one wherever |IoU - threshold| is larger than the binary32 error bound
+    (tests/detect_exact.py derives both bounds)."""
+    from detect_exact import check_against_definitions
+    from post_processing_amd import workloads as wl
+    w = wl.c3d() if case == "c3d" else wl.detect_small(int(case[5:]))
+    d = w.det
+    reg = _region(w)
+    res = D.detect(w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, reg, d["nc"], d["conf"],
+                   d["iou"], d["max_det"], d["agnostic"])
+    in_band = check_against_definitions(res, w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, reg,
+                                        d["conf"], d["iou"], d["max_det"], d["agnostic"])
+    print(f"{case}: {res[3]} candidates, {len(res[1])} kept, {in_band} decisions in the band")
+
+
+def test_definition_check_catches_a_flipped_decision():
+    """The float64 check must reject a result that differs from the
+    definition: dropping a kept box, or moving one by 0.01 px."""
+    from detect_exact import check_against_definitions
+    from post_processing_amd import workloads as wl
+    w = wl.c3d()
+    d = w.det
+    reg = _region(w)
+    b, s, c, n = D.detect(w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, reg, d["nc"], d["conf"],
+                          d["iou"], d["max_det"], d["agnostic"])
+    args = (w.head, w.src_w, w.src_h, w.dst_w, w.dst_h, reg, d["conf"], d["iou"], d["max_det"],
+            d["agnostic"])
+    with pytest.raises(AssertionError):
+        check_against_definitions((b[1:], s[1:], c[1:], n), *args)
+    moved = b.copy()
+    moved[3, 0] += F32(0.01)
+    with pytest.raises(AssertionError):
+        check_against_definitions((moved, s, c, n), *args)
+    with pytest.raises(AssertionError):
+        check_against_definitions((b, s, c, n + 1), *args)

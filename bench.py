@@ -56,6 +56,7 @@ HBM_PEAK_GBS = 8000.0
 MIN_LATENCY_SAMPLES = 10_000
 LATENCY = {"samples": MIN_LATENCY_SAMPLES}
 ALL_CORES: set = set()         # every core this process may use, before any pinning
+TRACE_LAST = {"n": 0}
 FLUSH_BYTES = 1 << 30          # > 256 MiB last-level cache (Infinity Cache)
 
 # Sources each kernel compiles from: a recorded measurement is valid only
@@ -224,20 +225,50 @@ def stage_times(lane, w, launches: int) -> dict:
 
 def cold_times(lane, torch, launches: int = 20) -> dict:
     """Preprocess launches each after a flush kernel on the lane's stream
-    (HIP events around the launch only): a 1 GiB read flush (the headline),
-    a 2 GiB read flush (if the first evicts everything, doubling it changes
-    nothing) and a 1 GiB write flush.  Medians in microseconds."""
+    (HIP events around the launch only, so each interval also holds one
+    dispatch and the events' own overhead): a 1 GiB read flush, a 2 GiB read
+    flush (if the first evicts everything, doubling it changes nothing) and
+    a 1 GiB write flush (whose dirty lines the timed launch writes back).
+    Medians in microseconds."""
     from post_processing_amd import ws
     buf = torch.ones((2 * FLUSH_BYTES) // 4, dtype=torch.float32, device="cuda:0")
     torch.cuda.synchronize()
     out = {}
-    for name, nbytes, write in (("read_1GiB", FLUSH_BYTES, False),
-                                ("read_2GiB", 2 * FLUSH_BYTES, False),
-                                ("write_1GiB", FLUSH_BYTES, True)):
+    for name, nbytes, write in (("flush_read_1GiB", FLUSH_BYTES, False),
+                                ("flush_read_2GiB", 2 * FLUSH_BYTES, False),
+                                ("flush_write_1GiB", FLUSH_BYTES, True)):
         ms = lane.time_stage_cold(ws.STAGE_PREPROCESS, buf, nbytes, launches, write=write)
         out[name] = float(np.median(ms)) * 1e3
     del buf
     torch.cuda.empty_cache()
+    return out
+
+
+ROTATE_LANES = 4          # 3 x 148.6 MB touched between a batch's turns: > 256 MiB
+ROTATE_LAUNCHES = 400
+
+
+def rotated_times(w, torch, lane0) -> dict:
+    """Preprocess launches back to back over several lanes' buffers in turn
+    (HIP events around the whole run on the first lane's stream): with 4
+    lanes of the 64-frame batch, 446 MB pass through the caches between two
+    turns of a batch, so each launch reads its frames from HBM.  2 and 6
+    lanes bracket it (2 leaves part of the batch cached; 6 must match 4 if 4
+    already evicts everything).  The 4-lane run goes last, so its launches
+    are the last ones of this grid in a profiler trace.  Microseconds per
+    launch."""
+    from post_processing_amd import ws
+    lanes = [lane0] + [make_lane(w, torch) for _ in range(5)]
+    try:
+        out = {}
+        for n in (2, 6, ROTATE_LANES):
+            out[f"rotate_{n}_lanes"] = ws.time_stage_rotate(
+                lanes[:n], ws.STAGE_PREPROCESS, ROTATE_LAUNCHES, warmup=2 * n) * 1e3
+    finally:
+        for ln in lanes[1:]:
+            ln.destroy()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return out
 
 
@@ -248,24 +279,26 @@ def roofline_obj(w, stages: dict, cold: dict | None) -> dict:
     a bandwidth roofline does not describe; their times are in `kernels`."""
     pb = preprocess_bytes(w)["total"]
     warm_us = stages["preprocess"]["us"]
-    us = cold["read_1GiB"] if cold else warm_us
+    key = f"rotate_{ROTATE_LANES}_lanes"
+    us = cold[key] if cold and key in cold else warm_us
     gbs = pb / (us * 1e-6) / 1e9
     rec = measured("preprocess", w.name)
     out = {"kernel": "preprocess", "bound": "hbm", "achieved": round(gbs, 2),
            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5),
            "traffic": rec["traffic"] if rec else None,
            "bytes_per_launch": pb, "us_per_launch": round(us, 3),
-           "caches": "cold" if cold else "warm",
+           "caches": (f"cold: {ROTATE_LAUNCHES} launches back to back over {ROTATE_LANES} "
+                      f"lanes' buffers in turn" if cold else "warm: back to back on one lane"),
            "warm": {"us_per_launch": round(warm_us, 3),
                     "frac": round(pb / (warm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)},
            "profiled": None}
     if cold:
-        out["flush_check_us"] = {k: round(v, 3) for k, v in cold.items()}
+        out["cold_checks_us"] = {k: round(v, 3) for k, v in cold.items() if k != key}
     if rec:
         prof = {"profile": rec["profile"], "cold_kernel_us": rec["cold_us"],
                 "warm_kernel_us": rec["warm_us"],
                 "cold_frac": round(pb / (rec["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
-        prof["live_cold_over_profiled"] = round(us / rec["cold_us"], 4) if cold else None
+        prof["live_over_profiled"] = round(us / rec["cold_us"], 4) if cold else None
         out["profiled"] = prof
     slow = max(stages, key=lambda s: stages[s]["us"])
     out["slowest_stage"] = {"kernel": slow, "us_per_launch": round(stages[slow]["us"], 3)}
@@ -463,18 +496,20 @@ def cpu_baseline_pool(w, cores, budget_s: float = 10.0) -> dict:
 # ---------------------------------------------------------------------------
 # Run record: versions, GPU state, PCIe link, inputs.
 
+def under_profiler() -> bool:
+    """True when a profiler's library is preloaded into this process: then
+    every child process initialises the GPU before it runs, so the helpers
+    below start no other program."""
+    return ("rocprof" in os.environ.get("LD_PRELOAD", "")
+            or any(k.startswith("ROCPROF") for k in os.environ))
+
+
 def versions() -> dict:
     out = {"python": platform.python_version(), "numpy": np.__version__}
     try:
         import torch
         out["torch"] = torch.__version__
         out["hip"] = getattr(torch.version, "hip", None)
-    except Exception:
-        pass
-    try:
-        r = subprocess.run(["/opt/rocm/bin/hipcc", "--version"], capture_output=True, text=True,
-                           timeout=30)
-        out["hipcc"] = r.stdout.splitlines()[0] if r.stdout else None
     except Exception:
         pass
     try:
@@ -503,27 +538,35 @@ def _flatten(obj, prefix=""):
 
 
 def gpu_state() -> dict:
-    """Clocks, power and temperature from amd-smi (falling back to
-    rocm-smi), as a flat subset of its JSON."""
-    keys = ("clk", "clock", "power", "temp", "hotspot", "throttle", "energy", "voltage")
-    skip = ("usage", "jpeg", "vcn", "ecc", "unit")
-    for cmd in (["amd-smi", "metric", "--json"],
-                ["rocm-smi", "--showclocks", "--showtemp", "--showpower", "--json"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
-            if r.returncode != 0 or not r.stdout.strip():
-                continue
-            try:
-                data = json.loads(r.stdout)
-            except ValueError:
-                return {"tool": cmd[0], "raw": r.stdout[:2000]}
-            flat = {k: v for k, v in _flatten(data)
-                    if any(s in k.lower() for s in keys) and not any(s in k.lower() for s in skip)
-                    and v not in (None, "N/A", "")}
-            return {"tool": cmd[0], "metrics": dict(list(flat.items())[:120])}
-        except Exception:
-            continue
-    return {"tool": None}
+    """Clocks, power, temperature and PCIe link of GPU 0 from `amd-smi metric
+    --json`: the graphics clock of every XCD, the memory clock, socket power,
+    hotspot and memory temperatures, link width and speed."""
+    if under_profiler():
+        return {"tool": None, "skipped": "profiled run"}
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as e:   # amd-smi absent or its output not JSON
+        return {"tool": None, "error": str(e)[:200]}
+    g = (data.get("gpu_data") or [data])[0] if isinstance(data, dict) else data[0]
+
+    def val(*path):
+        o = g
+        for k in path:
+            if not isinstance(o, dict) or k not in o:
+                return None
+            o = o[k]
+        return o.get("value") if isinstance(o, dict) else (None if o == "N/A" else o)
+
+    clocks = g.get("clock", {}) if isinstance(g, dict) else {}
+    gfx = [val("clock", k, "clk") for k in sorted(clocks) if k.startswith("gfx_")]
+    return {"tool": "amd-smi", "gfx_clk_mhz": gfx, "gfx_max_clk_mhz": val("clock", "gfx_0", "max_clk"),
+            "mem_clk_mhz": val("clock", "mem_0", "clk"),
+            "socket_power_w": val("power", "socket_power"),
+            "hotspot_temp_c": val("temperature", "hotspot"),
+            "mem_temp_c": val("temperature", "mem"),
+            "pcie_width": val("pcie", "width"), "pcie_speed_gts": val("pcie", "speed")}
 
 
 def pcie_link() -> dict:
@@ -547,6 +590,8 @@ def pcie_link() -> dict:
                 pass
         if rec:
             out[os.path.basename(os.path.dirname(dev))] = rec
+    if under_profiler():
+        return out
     try:
         r = subprocess.run(["amd-smi", "static", "--bus", "--json"], capture_output=True,
                            text=True, timeout=30)
@@ -681,10 +726,11 @@ def campaign(torch, args) -> int:
 
 def trace_summary(path: str) -> int:
     """Summarise a rocprofv3 kernel trace (`*_kernel_trace.csv`) of this
-    benchmark: per kernel, the dispatch count and mean / median duration; for
-    the preprocess kernel, separately the launches that directly follow a
-    cache flush on the same queue (cold) and the others (warm).  Runs on the
-    CPU; prints JSON."""
+    benchmark: per kernel and grid, the dispatch count and mean / median
+    duration; for the preprocess kernel, separately the launches that
+    directly follow a cache flush on the same queue and the others; with
+    --last N, also the last N dispatches of each kernel and grid (the rotated
+    cold launches, which bench.py runs last).  Runs on the CPU; prints JSON."""
     import csv
     with open(path, newline="") as f:
         rows = list(csv.DictReader(f))
@@ -694,27 +740,54 @@ def trace_summary(path: str) -> int:
         t0 = int(r.get("Start_Timestamp") or r.get("BeginNs") or 0)
         t1 = int(r.get("End_Timestamp") or r.get("EndNs") or 0)
         q = r.get("Queue_Id") or r.get("Stream_Id") or "0"
-        recs.append((q, t0, t1, name))
+        grid = r.get("Grid_Size") or r.get("Grid_Size_X") or ""
+        recs.append((q, t0, t1, name, grid))
     recs.sort(key=lambda x: (x[0], x[1]))
     by = {}
-    cold, warm = [], []
+    spans = {}
+    cold, warm = {}, {}
     prev = {}
-    for q, t0, t1, name in recs:
+    for q, t0, t1, name, grid in recs:
         us = (t1 - t0) * 1e-3
         short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
-        by.setdefault(short, []).append(us)
+        key = f"{short} grid={grid}" if grid else short
+        by.setdefault(key, []).append(us)
+        spans.setdefault(key, []).append((t0, t1))
         if "preprocess" in short:
-            (cold if "cache_flush_kernel" in prev.get(q, "") else warm).append(us)
+            side = cold if "cache_flush_kernel" in prev.get(q, "") else warm
+            side.setdefault(key, []).append(us)
         prev[q] = short
-    out = {"trace": path, "kernels": {k: {"calls": len(v), "mean_us": round(float(np.mean(v)), 3),
-                                          "median_us": round(float(np.median(v)), 3)}
-                                      for k, v in sorted(by.items())}}
-    for label, v in (("preprocess_cold", cold), ("preprocess_warm", warm)):
-        if v:
-            out[label] = {"calls": len(v), "mean_us": round(float(np.mean(v)), 3),
-                          "median_us": round(float(np.median(v)), 3),
-                          "min_us": round(float(np.min(v)), 3),
-                          "max_us": round(float(np.max(v)), 3)}
+
+    if TRACE_LAST["n"]:
+        # The last N dispatches of each kernel and grid (bench.py runs its
+        # rotated cold launches last among the preprocess launches of a grid).
+        out_last = {k: v[-TRACE_LAST["n"]:] for k, v in by.items()}
+    else:
+        out_last = None
+
+    def stats(v):
+        return {"calls": len(v), "mean_us": round(float(np.mean(v)), 3),
+                "median_us": round(float(np.median(v)), 3), "min_us": round(float(np.min(v)), 3),
+                "max_us": round(float(np.max(v)), 3)}
+
+    out = {"trace": path, "kernels": {k: stats(v) for k, v in sorted(by.items())}}
+    if out_last:
+        last = {}
+        for k, v in sorted(out_last.items()):
+            rec = stats(v)
+            sp = sorted(spans[k][-TRACE_LAST["n"]:])
+            if len(sp) > 1:
+                # Start-to-start period of consecutive dispatches (what a
+                # back-to-back run's event time per launch measures) and the
+                # idle time between one dispatch's end and the next's start.
+                rec["period_mean_us"] = round((sp[-1][0] - sp[0][0]) * 1e-3 / (len(sp) - 1), 3)
+                rec["gap_mean_us"] = round(float(np.mean([(b[0] - a[1]) * 1e-3
+                                                          for a, b in zip(sp, sp[1:])])), 3)
+            last[k] = rec
+        out[f"last_{TRACE_LAST['n']}"] = last
+    for label, side in (("preprocess_after_flush", cold), ("preprocess_other", warm)):
+        if side:
+            out[label] = {k: stats(v) for k, v in sorted(side.items())}
     print(json.dumps(out, indent=1))
     return 0
 
@@ -767,8 +840,12 @@ def main(argv=None) -> int:
                          "only for profiler runs, where every dispatch is slowed)")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="summarise a rocprofv3 kernel trace of this benchmark and exit (CPU)")
+    ap.add_argument("--last", type=int, default=0,
+                    help="with --trace-summary: also summarise the last N dispatches of each "
+                         "kernel and grid")
     args = ap.parse_args(argv)
     if args.trace_summary:
+        TRACE_LAST["n"] = args.last
         return trace_summary(args.trace_summary)
     LATENCY["samples"] = args.latency_samples
     if args.graph_packet_capture == "off":
@@ -848,9 +925,6 @@ def main(argv=None) -> int:
         res["plan"] = lane.plan()
         stages = stage_times(lane, w, args.stage_launches)
         steps_total = args.steps
-        if not args.no_extras and lane.cfg.input_mode == ws.INPUT_DEVICE:
-            print("[bench] cold-cache launches", file=sys.stderr, flush=True)
-            cold = cold_times(lane, torch, args.cold_launches)
         if lane.cfg.input_mode != ws.INPUT_DEVICE:
             pb = preprocess_bytes(w)
             if lane.cfg.input_mode == ws.INPUT_MAPPED_HOST:
@@ -866,6 +940,11 @@ def main(argv=None) -> int:
                                       "p99_us": round(dres["p99_us"], 3),
                                       "latency_samples": dres["samples"]}
             dl.destroy()
+        if not args.no_extras and lane.cfg.input_mode == ws.INPUT_DEVICE:
+            print("[bench] cold-cache launches", file=sys.stderr, flush=True)
+            cold = cold_times(lane, torch, args.cold_launches)
+            cold.update(rotated_times(w, torch, lane))
+            extra["rotate_launches"] = ROTATE_LAUNCHES
         if name == "c5t" and not args.no_extras:
             print("[bench] C5L lanes", file=sys.stderr, flush=True)
             extra["c5l"] = c5l_figures(torch)

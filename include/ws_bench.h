@@ -91,6 +91,23 @@ int ws_bench_stage(ws_lane *lane, int32_t stage, int32_t launches, double *ms_pe
 int ws_bench_stage_cold(ws_lane *lane, int32_t stage, void *flush, size_t flush_bytes,
                         int32_t flush_write, int32_t launches, float *ms);
 
+/*
+ * Time one stage's kernels launched back to back over several lanes in turn:
+ * launch i runs the stage of lanes[i % nlanes], every launch on lanes[0]'s
+ * stream, between lanes[0]'s two events.  When the lanes' buffers together
+ * exceed the last-level cache, each launch finds its own inputs evicted by
+ * the other lanes' launches since its last turn, while the launches still
+ * follow each other with no host gap.
+ *   warmup         untimed launches first, in the same rotation.
+ *   ms_per_launch  receives the elapsed event time divided by `launches`.
+ * Every lane must be READY (and stays READY) and on one device.  Returns
+ * WS_OK, WS_E_STATE, WS_E_INVALID_ARG (NULL, nlanes < 1, launches < 1,
+ * warmup < 0, lanes on different devices, or a stage a lane does not have)
+ * or WS_E_HIP.
+ */
+int ws_bench_stage_rotate(ws_lane **lanes, int32_t nlanes, int32_t stage, int32_t warmup,
+                          int32_t launches, double *ms_per_launch);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@
 #include "ws.h"
 #include "ws_bench.h"
 #include "ws_kernels.h"
+#include "ws_params.h"
 #include "ws_plan.h"
 
 namespace ws {
@@ -168,48 +169,8 @@ int mapped_alloc(ws_lane* L, void** host, void** dev, size_t bytes) {
 void fill_params(ws_lane* L) {
     const ws_lane_config& c = L->cfg;
     const ws::Plan& P = L->plan;
-    ws::PreParams& q = L->pre;
-    q.src = L->in_dev;
-    q.dst = L->tensor;
-    q.frame_bytes = (int64_t)P.frame_bytes;
-    q.total_bytes = (int64_t)P.input_bytes;
-    q.src_w = c.src_w;
-    q.src_h = c.src_h;
-    q.dst_w = c.dst_w;
-    q.dst_h = c.dst_h;
-    q.left = P.region.left;
-    q.top = P.region.top;
-    q.reg_w = P.region.w;
-    q.reg_h = P.region.h;
-    q.inv_den_x = (float)(1.0 / (2.0 * P.region.w));
-    q.inv_den_y = (float)(1.0 / (2.0 * P.region.h));
-    q.magic_x = (uint32_t)((1ull << 32) / (2ull * (uint64_t)P.region.w) + 1);
-    q.magic_y = (uint32_t)((1ull << 32) / (2ull * (uint64_t)P.region.h) + 1);
-    q.span_lo = (int32_t)P.span_lo;
-    q.slot_chunks = P.slot_bytes / 16;
-    q.pixels_per_thread = P.pixels_per_thread;
-    q.threads_per_row = P.threads_per_row;
-    q.rows_per_group = P.rows_per_group;
-    q.groups_per_frame = P.groups_per_frame;
-    q.vec = (c.dst_w % P.pixels_per_thread) == 0;
-    q.dtype = c.tensor_dtype;
-    for (int i = 0; i < 3; ++i)   // output plane i reads byte i (RGB) or byte 2 - i (BGR)
-        q.shift[i] = 8u * (uint32_t)(c.channel_order == WS_CHANNELS_BGR ? 2 - i : i);
-    for (int i = 0; i < 3; ++i) {
-        q.a[i] = (float)(1.0 / (255.0 * c.std[i]));
-        q.b[i] = (float)(-c.mean[i] / c.std[i]);
-        q.padv[i] = (float)((c.pad_value / 255.0 - c.mean[i]) / c.std[i]);
-    }
-    ws::TopkParams& t = L->tk;
-    t.scores = L->scores;
-    t.n = c.num_scores;
-    t.k = c.k;
-    t.chunk = P.topk_chunk;
-    t.groups = P.topk_groups;
-    t.waves = P.topk_waves;
-    t.keys_per_lane = P.topk_keys_per_lane;
-    t.partials = L->partials;
-    t.result = L->res_dev;
+    ws::fill_pre_params(c, P, L->in_dev, L->tensor, &L->pre);
+    ws::fill_topk_params(c, P, L->scores, L->partials, L->res_dev, &L->tk);
     ws::DetParams& d = L->det;
     d.head = L->det_head;
     d.anchors = P.det_anchors;
@@ -627,13 +588,16 @@ int ws_bench_lanes(ws_lane** lanes, int32_t nlanes, int32_t replays, float* gpu_
 
 namespace {
 
-hipError_t launch_stage(ws_lane* L, int32_t stage) {
+// One stage's kernels of lane L, on `stream`.
+hipError_t launch_stage_on(ws_lane* L, int32_t stage, hipStream_t stream) {
     if (stage == WS_STAGE_PREPROCESS)
         return ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
-                                     L->plan.lds_bytes, L->stream);
-    if (stage == WS_STAGE_TOPK) return ws::launch_topk(L->tk, L->stream);
-    return ws::launch_detect(L->det, L->plan.det_decode_groups, L->stream);
+                                     L->plan.lds_bytes, stream);
+    if (stage == WS_STAGE_TOPK) return ws::launch_topk(L->tk, stream);
+    return ws::launch_detect(L->det, L->plan.det_decode_groups, stream);
 }
+
+hipError_t launch_stage(ws_lane* L, int32_t stage) { return launch_stage_on(L, stage, L->stream); }
 
 bool stage_present(const ws_lane* L, int32_t stage) {
     if (stage == WS_STAGE_PREPROCESS) return true;
@@ -668,6 +632,33 @@ int ws_bench_stage_cold(ws_lane* L, int32_t stage, void* flush, size_t flush_byt
         hipStreamSynchronize(L->stream);
         return fail(L, e, WS_E_HIP);
     }
+    return WS_OK;
+}
+
+int ws_bench_stage_rotate(ws_lane** lanes, int32_t nlanes, int32_t stage, int32_t warmup,
+                          int32_t launches, double* ms_per_launch) {
+    if (!lanes || nlanes < 1 || launches < 1 || warmup < 0 || !ms_per_launch)
+        return WS_E_INVALID_ARG;
+    for (int32_t i = 0; i < nlanes; ++i) {
+        if (!lanes[i] || !stage_present(lanes[i], stage) || lanes[i]->device != lanes[0]->device)
+            return WS_E_INVALID_ARG;
+        if (ws::begin_submit(lanes[i]->state) != WS_OK) return WS_E_STATE;
+    }
+    ws_lane* L = lanes[0];
+    hipError_t e = hipSuccess;
+    for (int32_t i = 0; i < warmup && e == hipSuccess; ++i)
+        e = launch_stage_on(lanes[i % nlanes], stage, L->stream);
+    if (e == hipSuccess) e = hipEventRecord(L->ev_start, L->stream);
+    for (int32_t i = 0; i < launches && e == hipSuccess; ++i)
+        e = launch_stage_on(lanes[i % nlanes], stage, L->stream);
+    if (e == hipSuccess) e = hipEventRecord(L->ev_done, L->stream);
+    const hipError_t se = hipStreamSynchronize(L->stream);
+    if (e == hipSuccess) e = se;
+    if (e != hipSuccess) return fail(L, e, WS_E_HIP);
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, L->ev_start, L->ev_done);
+    if (e != hipSuccess) return fail(L, e, WS_E_HIP);
+    *ms_per_launch = (double)ms / (double)launches;
     return WS_OK;
 }
 

@@ -151,6 +151,9 @@ def load(path: str = LIB_PATH):
     lib.ws_bench_stage_cold.argtypes = [c_void_p, c_int32, c_void_p, c_size_t, c_int32, c_int32,
                                         POINTER(c_float)]
     lib.ws_bench_stage_cold.restype = c_int
+    lib.ws_bench_stage_rotate.argtypes = [POINTER(c_void_p), c_int32, c_int32, c_int32, c_int32,
+                                          POINTER(c_double)]
+    lib.ws_bench_stage_rotate.restype = c_int
     _lib = lib
     return lib
 
@@ -357,6 +360,19 @@ class Lane:
             self.destroy()
         except Exception:
             pass
+
+
+def time_stage_rotate(lanes: list[Lane], stage: int, launches: int, warmup: int = 0) -> float:
+    """Mean ms per launch of one stage launched back to back over the lanes
+    in turn, on the first lane's stream (native loop)."""
+    lib = load()
+    n = len(lanes)
+    handles = (c_void_p * n)(*[ln.handle for ln in lanes])
+    ms = c_double(0.0)
+    rc = lib.ws_bench_stage_rotate(handles, n, stage, warmup, launches, byref(ms))
+    if rc != WS_OK:
+        raise WsError(rc, "ws_bench_stage_rotate", lanes[0].hip_error())
+    return ms.value
 
 
 def bench_lanes(lanes: list[Lane], replays: int) -> tuple[np.ndarray, float]:

@@ -51,11 +51,18 @@ def test_trace_summary_splits_cold_and_warm(tmp_path):
                      else "void ws::(anonymous namespace)::preprocess_gather_kernel<float>(x)")
             f.write(f"\"{kname}\",{a},{b},{q}\n")
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--trace-summary",
-                          str(p)], capture_output=True, text=True, timeout=60)
+                          str(p), "--last", "3"], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0, out.stderr
     d = json.loads(out.stdout)
-    assert d["preprocess_cold"]["calls"] == 2 and d["preprocess_warm"]["calls"] == 2
-    assert d["preprocess_cold"]["median_us"] == 25.5 and d["preprocess_warm"]["mean_us"] == 23.0
+    key = "ws::preprocess_gather_kernel<float>"
+    cold = d["preprocess_after_flush"][key]
+    warm = d["preprocess_other"][key]
+    assert cold["calls"] == 2 and warm["calls"] == 2
+    assert cold["median_us"] == 25.5 and warm["mean_us"] == 23.0
+    last = d["last_3"][key]
+    assert last["calls"] == 3 and last["max_us"] == 26.0 and last["min_us"] == 23.0
+    assert last["period_mean_us"] == (900.4 - 430.0) / 2
+    assert last["gap_mean_us"] == round(((453.1 - 453.0) + (900.4 - 476.1)) / 2, 3)
 
 
 def test_recorded_figures_need_matching_sources(monkeypatch):

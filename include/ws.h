@@ -265,6 +265,37 @@ int ws_wait(ws_lane *lane, float *gpu_ms);
  */
 int ws_destroy(ws_lane *lane);
 
+/*
+ * ws_run_noalloc -- for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Enqueues
+ * one frame of the launch sequence ws_submit replays -- preprocess, then
+ * Top-K when num_scores > 0 -- as direct launches on `stream`, reading and
+ * writing only the caller's buffers, and allocates nothing.
+ *   cfg     as for ws_create_lane, with input_mode WS_INPUT_DEVICE and the
+ *           borrowed device buffers input_dev, tensor_dev and (when
+ *           num_scores > 0) scores_dev set; det_classes and autotune 0;
+ *           use_graph and wait_mode are ignored.  cfg->device must be the
+ *           calling thread's current device.  Read only; not retained.
+ *   result  device-visible memory (device or mapped host, 8-byte aligned)
+ *           for k ws_topk_entry in rank order; NULL when num_scores == 0.
+ *   stream  a hipStream_t of that device, or NULL for its null stream.
+ * When the scores span several Top-K workgroups, their partial lists live in
+ * a scratch array of the library: WS_NOALLOC_SCRATCH_BYTES on each device
+ * the call runs on, held until the process ends.  A plan that needs more
+ * (workgroups x k x 8 bytes) is rejected.  Every call on one device shares
+ * that array and the last call's contents stay in it: calls that may
+ * overlap on one device (other streams, other threads) race, so the caller
+ * serialises them.  The first call on a device also looks up the array's
+ * address and sets the kernels' LDS limits.  The call returns once the
+ * launches are enqueued; the tensor and result are complete when the
+ * stream's work before the next event on it has finished.
+ * Returns WS_OK, WS_E_INVALID_ARG (a field out of range or unsupported, a
+ * missing buffer, a plan beyond the scratch limit, a device that is not
+ * current), WS_E_NO_DEVICE or WS_E_HIP (a launch failed).
+ */
+#define WS_NOALLOC_SCRATCH_BYTES (1u << 20)
+int ws_run_noalloc(const ws_lane_config *cfg, ws_topk_entry *result, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *ws_status_str(int status);
 

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libws.so")
-SOURCES = ["ws_preprocess.hip", "ws_topk.hip", "ws_detect.hip", "ws_runtime.hip"]
+SOURCES = ["ws_preprocess.hip", "ws_topk.hip", "ws_detect.hip", "ws_runtime.hip",
+           "ws_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -320,6 +320,12 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
     return WS_OK;
 }
 
+// Keys of Top-K partial lists a plan needs: one sorted list of K keys per
+// workgroup when the scores span several workgroups, else none.
+inline int64_t topk_scratch_keys(const Plan& p, int32_t k) {
+    return p.topk_groups > 1 ? (int64_t)p.topk_groups * k : 0;
+}
+
 // ---------------------------------------------------------------------------
 // Lane state machine: READY --submit--> IN_FLIGHT --wait--> READY.
 // A busy lane rejects a second submit (no hidden queue); a wait with nothing

@@ -154,6 +154,8 @@ def load(path: str = LIB_PATH):
     lib.ws_bench_stage_rotate.argtypes = [POINTER(c_void_p), c_int32, c_int32, c_int32, c_int32,
                                           POINTER(c_double)]
     lib.ws_bench_stage_rotate.restype = c_int
+    lib.ws_run_noalloc.argtypes = [POINTER(LaneConfig), c_void_p, c_void_p]
+    lib.ws_run_noalloc.restype = c_int
     _lib = lib
     return lib
 
@@ -360,6 +362,16 @@ class Lane:
             self.destroy()
         except Exception:
             pass
+
+
+NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def run_noalloc(cfg: LaneConfig, result=None, stream=None) -> int:
+    """ws_run_noalloc: one frame on the caller's buffers and stream, with no
+    allocation.  `result` is a device-visible address (or tensor) for K
+    entries; `stream` a hipStream_t handle (int) or None.  Returns the status."""
+    return load().ws_run_noalloc(byref(cfg), _addr(result), stream)
 
 
 def time_stage_rotate(lanes: list[Lane], stage: int, launches: int, warmup: int = 0) -> float:

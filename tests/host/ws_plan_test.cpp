@@ -199,6 +199,23 @@ static int selftest() {
     c.k = 5;
     CHECK(ws::make_plan(c, &p) == WS_OK);
     CHECK(p.topk_keys_per_lane == 16 && p.topk_groups == 1 && p.topk_waves == 1);
+    // Partial-list keys the allocation-free entry point keeps in its 1 MiB
+    // scratch: none for one workgroup; groups x K beyond.
+    const int64_t scratch_keys = WS_NOALLOC_SCRATCH_BYTES / 8;
+    CHECK(ws::topk_scratch_keys(p, c.k) == 0);
+    c.k = 32;
+    c.num_scores = 672000;   // 83 workgroups of 8 Ki scores
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(ws::topk_scratch_keys(p, c.k) == 83 * 32);
+    c.num_scores = 4096 * 8192;   // the most scores whose lists fit at K = 32
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(ws::topk_scratch_keys(p, c.k) == scratch_keys);
+    c.num_scores = 4096 * 8192 + 1;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(ws::topk_scratch_keys(p, c.k) > scratch_keys);
+    c.num_scores = 40000000;
+    CHECK(ws::make_plan(c, &p) == WS_OK);
+    CHECK(ws::topk_scratch_keys(p, c.k) == 4883 * 32 && 4883 * 32 > scratch_keys);
     std::printf("%d failures\n", failures);
     return failures == 0 ? 0 : 1;
 }

@@ -223,6 +223,53 @@ def stage_times(lane, w, launches: int) -> dict:
     return out
 
 
+def topk_marks(lane, reps: int = 30) -> dict:
+    """Phase times of the Top-K kernels from the clock-mark build
+    (libws_marks.so): one Top-K launch at a time, its marks read back; the
+    median over `reps` launches of each phase, in microseconds (100 MHz
+    clock, 0.01 us resolution)."""
+    import ctypes
+    from post_processing_amd import ws
+    lib = ws.load()
+    fn = lib.ws_debug_topk_marks
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32]
+    fn.restype = ctypes.c_int
+    plan = lane.plan()
+    G, W = plan["topk_groups"], plan["topk_block"] // 64
+    merge0 = 1 << 16
+    n = merge0 + 64
+    buf = np.zeros(n, dtype=np.uint64)
+    rows = []
+    for _ in range(reps):
+        fn(None, 0, 1)
+        lane.time_stage(ws.STAGE_TOPK, 1)
+        fn(buf.ctypes.data, n, 0)
+        m = buf[:G * 4 * 8].reshape(G, 4, 8)[:, :W, :].astype(np.int64)
+        t0 = m[:, :, 0].min()
+        us = lambda a: float(a) * 0.01   # noqa: E731
+        r = {"partial_wave_start_spread": us(m[:, :, 0].max() - t0),
+             "partial_load": us(np.median(m[:, :, 1] - m[:, :, 0])),
+             "partial_select": us(np.median(m[:, :, 2] - m[:, :, 1])),
+             "select_threshold": us(np.median(m[:, :, 5] - m[:, :, 1])),
+             "select_screen_compact": us(np.median(m[:, :, 6] - m[:, :, 5])),
+             "select_merge_survivors": us(np.median(m[:, :, 7] - m[:, :, 6])),
+             "partial_block_merge": us(np.median(m[:, 0, 3] - m[:, 0, 2])),
+             "partial_publish": us(np.median(m[:, 0, 4] - m[:, 0, 3])),
+             "partial_span": us(m[:, 0, 4].max() - t0)}
+        if G > 1:
+            f = buf[merge0:merge0 + 32].reshape(4, 8)[:, :5].astype(np.int64)
+            if (f[:, 0] > 0).all():
+                r.update({"merge_start_after_partials": us(f[:, 0].min() - m[:, 0, 4].max()),
+                          "merge_load": us(np.median(f[:, 1] - f[:, 0])),
+                          "merge_fold": us(np.median(f[:, 2] - f[:, 1])),
+                          "merge_block_merge": us(f[0, 3] - f[0, 2]),
+                          "merge_write": us(f[0, 4] - f[0, 3]),
+                          "total_span": us(f[0, 4] - t0)})
+        rows.append(r)
+    keys = rows[0].keys()
+    return {k: round(float(np.median([r[k] for r in rows if k in r])), 3) for k in keys}
+
+
 def cold_times(lane, torch, launches: int = 20) -> dict:
     """Preprocess launches each after a flush kernel on the lane's stream
     (HIP events around the launch only, so each interval also holds one
@@ -679,7 +726,14 @@ def campaign(torch, args) -> int:
             for graph in (True, False):
                 ls = lanes[(name, graph)]
                 if len(ls) > 1:
-                    res = run_lanes(ls, torch, reps, warm)
+                    # One host thread per lane, spread over every core (the
+                    # threads inherit this thread's affinity).
+                    held = os.sched_getaffinity(0)
+                    os.sched_setaffinity(0, ALL_CORES or held)
+                    try:
+                        res = run_lanes(ls, torch, reps, warm)
+                    finally:
+                        os.sched_setaffinity(0, held)
                 else:
                     res = run_replays(ls[0], torch, reps, warm)
                 runs.append({"campaign": c, "workload": name, "graph": graph,
@@ -752,16 +806,18 @@ def trace_summary(path: str) -> int:
         short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         key = f"{short} grid={grid}" if grid else short
         by.setdefault(key, []).append(us)
-        spans.setdefault(key, []).append((t0, t1))
+        spans.setdefault(key, []).append((t0, t1, q))
         if "preprocess" in short:
             side = cold if "cache_flush_kernel" in prev.get(q, "") else warm
             side.setdefault(key, []).append(us)
         prev[q] = short
 
     if TRACE_LAST["n"]:
-        # The last N dispatches of each kernel and grid (bench.py runs its
-        # rotated cold launches last among the preprocess launches of a grid).
-        out_last = {k: v[-TRACE_LAST["n"]:] for k, v in by.items()}
+        # The last N dispatches (by start time) of each kernel and grid:
+        # bench.py runs its rotated cold launches last among the preprocess
+        # launches of a grid.
+        last_spans = {k: sorted(v)[-TRACE_LAST["n"]:] for k, v in spans.items()}
+        out_last = {k: [(b - a) * 1e-3 for a, b, _ in v] for k, v in last_spans.items()}
     else:
         out_last = None
 
@@ -775,7 +831,8 @@ def trace_summary(path: str) -> int:
         last = {}
         for k, v in sorted(out_last.items()):
             rec = stats(v)
-            sp = sorted(spans[k][-TRACE_LAST["n"]:])
+            sp = last_spans[k]
+            rec["queues"] = len({q for _, _, q in sp})
             if len(sp) > 1:
                 # Start-to-start period of consecutive dispatches (what a
                 # back-to-back run's event time per launch measures) and the
@@ -838,6 +895,9 @@ def main(argv=None) -> int:
     ap.add_argument("--latency-samples", type=int, default=MIN_LATENCY_SAMPLES,
                     help="replays the latency percentiles are taken over, at least (lower it "
                          "only for profiler runs, where every dispatch is slowed)")
+    ap.add_argument("--marks", action="store_true",
+                    help="load the clock-mark build (libws_marks.so, built with `python -m "
+                         "post_processing_amd.build --marks`) and add Top-K phase times")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="summarise a rocprofv3 kernel trace of this benchmark and exit (CPU)")
     ap.add_argument("--last", type=int, default=0,
@@ -872,6 +932,9 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     from post_processing_amd import ws
+    if args.marks:
+        from post_processing_amd import build as ppbuild
+        ws.load(ppbuild.LIB_MARKS)
     ws.load()
 
     KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
@@ -949,6 +1012,8 @@ def main(argv=None) -> int:
             print("[bench] C5L lanes", file=sys.stderr, flush=True)
             extra["c5l"] = c5l_figures(torch)
 
+    if args.marks and w.k:
+        extra["topk_marks_us"] = topk_marks(lane)
     roof = roofline_obj(w, stages, cold)
     input_mode = args.input or ("mapped" if (w.host_input or name == "c5l") else "device")
     line = {

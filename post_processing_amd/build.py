@@ -29,9 +29,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the lane library)")
 
 
-def lib_command(out: str) -> list[str]:
+LIB_MARKS = os.path.join(PKG, "libws_marks.so")
+
+
+def lib_command(out: str, marks: bool = False) -> list[str]:
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        hipcc(), *(["-DWS_CLOCK_MARKS"] if marks else []), f"--offload-arch={ARCH}", "-O3",
+        "-std=c++17", "-fPIC", "-shared",
         "-Wall", "-Wno-unused-command-line-argument",
         # keep the compiler from forming packed FP32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -45,17 +49,20 @@ def lib_command(out: str) -> list[str]:
     ] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build_lib(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = lib_command(tmp)
+def build_lib(verbose: bool = False, marks: bool = False) -> str:
+    """Build libws.so, or with `marks` the clock-mark instrumented
+    libws_marks.so (phase timing only; never loaded by default)."""
+    lib = LIB_MARKS if marks else LIB
+    tmp = lib + ".tmp"
+    cmd = lib_command(tmp, marks)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def build_host_test(out: str, sanitize: bool = False) -> str:
@@ -75,4 +82,4 @@ def build_host_test(out: str, sanitize: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_lib(verbose=True))
+    print(build_lib(verbose=True, marks="--marks" in sys.argv[1:]))

@@ -9,9 +9,18 @@
 
 #include "ws_kernels.h"
 #include "ws_lanes.h"
+#include "ws_marks.h"
 
 namespace ws {
 namespace {
+
+#ifdef WS_CLOCK_MARKS
+// Phase marks of the Top-K kernels: the partial kernel's wave w of workgroup
+// g writes slots (4 g + w) * 8 + phase, the merge kernels' wave w slots
+// kMergeMarks + 8 w + phase.
+__device__ uint64_t g_marks[kMarkSlots];
+#endif
+constexpr int kMergeMarks = 1 << 16;
 
 // ===========================================================================
 // Top-K
@@ -83,6 +92,21 @@ __device__ __forceinline__ int count_greater(const uint64_t* v, int n, uint64_t 
     return r;
 }
 
+// Largest of N floats as a pairwise tree (log2 N dependent steps instead of
+// N - 1); a NaN never wins over a number, as with a running fmaxf.
+template <int N>
+__device__ __forceinline__ float tree_max(const float (&f)[N]) {
+    float m[N / 2];
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) m[j] = fmaxf(f[2 * j], f[2 * j + 1]);
+#pragma unroll
+    for (int w = N / 4; w >= 1; w /= 2) {
+#pragma unroll
+        for (int j = 0; j < w; ++j) m[j] = fmaxf(m[2 * j], m[2 * j + 1]);
+    }
+    return m[0];
+}
+
 // E scores per lane per batch (16 or 32): a batch is 64 E scores per wave.
 template <int E>
 struct WaveTopK {
@@ -95,6 +119,7 @@ struct WaveTopK {
     int k;
     int lane;
     bool empty;      // nothing merged yet (wave-uniform)
+    int mark = -1;   // clock-mark slot of the first batch's phases (marks builds)
 
     __device__ __forceinline__ void init(int k_, int lane_) {
         best = 0;
@@ -195,11 +220,9 @@ struct WaveTopK {
         if (cut_ord <= 0x80000000u) {
             // No positive cut yet: the K-th largest lane maximum bounds the
             // batch's K best from below.
-            float m = -__builtin_inff();
-#pragma unroll
-            for (int j = 0; j < E; ++j) m = fmaxf(m, f[j]);
-            const uint32_t t = wave_kth_largest(order_image(m), k, lane);
+            const uint32_t t = wave_kth_largest(order_image(tree_max<E>(f)), k, lane);
             cut_ord = max(cut_ord, t);
+            if (mark >= 0) WS_MARK(mark + 5);
         }
         if (cut_ord <= 0x80000000u) {   // cut at or below +0: exact keys for all
             uint64_t key[E];
@@ -258,8 +281,11 @@ struct WaveTopK {
             scratch[off++] = ((uint64_t)order_image(x) << 32) | (uint32_t)~(uint32_t)e;
         }
         wave_lds_sync();
+        if (mark >= 0) WS_MARK(mark + 6);
         merge_survivors(scratch, total);
         wave_lds_sync();
+        if (mark >= 0) WS_MARK(mark + 7);
+        mark = -1;
     }
 };
 
@@ -383,6 +409,9 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(
 
     WaveTopK<E> st;
     st.init(p.k, lane);
+    const int mark = ((int)blockIdx.x * kTopkWaveSlots + wave) * 8;
+    (void)mark;
+    WS_MARK(mark + 0);
 
     // 1. This workgroup's chunk, one 64 E-score batch per wave per round; the
     //    next round's scores are loaded while the current batch is offered.
@@ -391,6 +420,10 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(
     const int32_t round = waves * kBatchE;
     float4 v[E / 4];
     load_batch<E>(p.scores, g0 + wave * kBatchE, g1, lane, v);
+    WS_MARK_AFTER_LOADS(mark + 1);
+#ifdef WS_CLOCK_MARKS
+    st.mark = mark;
+#endif
     for (int32_t rb = g0; rb < g1; rb += round) {
         const int32_t wb = rb + wave * kBatchE;
         float f[E];
@@ -404,16 +437,20 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(
         if (rb + round < g1) load_batch<E>(p.scores, wb + round, g1, lane, v);
         st.offer_scores(f, wb, g1, s_keys + wave * kBatchE, s_vals + wave * 64 * (E + 4));
     }
+    WS_MARK(mark + 2);
     block_merge(st, s_list, wave, waves);
+    WS_MARK(mark + 3);
 
     if (p.groups == 1) {
         if (wave == 0 && lane < p.k) write_result(p, st.best, lane);
+        WS_MARK(mark + 4);
         return;
     }
 
     // 2. Publish this workgroup's K best for the merge kernel, which follows
     //    in stream order.
     if (wave == 0 && lane < p.k) p.partials[(int64_t)blockIdx.x * p.k + lane] = st.best;
+    WS_MARK(mark + 4);
 }
 
 // Merge of up to kFoldMaxLists workgroup lists by folding.  A register holds
@@ -489,6 +526,9 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_fold_kernel(
     const int k = p.k, G = p.groups;
     const int half = lane >> 5, h = lane & 31;
     const int last = G * k - 1;   // the published keys are partials[0 .. last]
+    const int mark = kMergeMarks + 8 * wave;
+    (void)mark;
+    WS_MARK(mark + 0);
     // Every load is issued, in bounds, before any is used: a lane with no key
     // reads a spare published key (lanes on distinct addresses) and drops it.
     uint64_t x[R];
@@ -499,6 +539,7 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_fold_kernel(
         x[r] = p.partials[valid ? list * k + h : min(lane + 64 * r, last)];
     }
     __builtin_amdgcn_sched_barrier(0);   // all loads in flight before the first is used
+    WS_MARK_AFTER_LOADS(mark + 1);
     constexpr uint32_t kLeafDesc = fold_leaf_mask<R>();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -513,11 +554,14 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_fold_kernel(
     }
     uint64_t w = fold_root<R>(x, lane);
     w = bitonic_stages<64, 16, true>(umax64(w, xor_lane64<32>(w, lane)), lane);
+    WS_MARK(mark + 2);
     WaveTopK<16> st;
     st.init(k, lane);
     st.best = w;
     block_merge(st, s_list, wave, kTopkWaveSlots);
+    WS_MARK(mark + 3);
     if (wave == 0 && lane < k) write_result(p, st.best, lane);
+    WS_MARK(mark + 4);
 }
 
 // Merge of more than kFoldMaxLists workgroup lists, by one workgroup of four
@@ -690,3 +734,21 @@ hipError_t set_kernel_attributes() {
 }
 
 }  // namespace ws
+
+#ifdef WS_CLOCK_MARKS
+// Instrumented builds only: copy out (or clear) the Top-K kernels' marks.
+extern "C" int ws_debug_topk_marks(uint64_t* host, size_t n, int32_t clear) {
+    if (n > (size_t)ws::kMarkSlots) n = ws::kMarkSlots;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess && host && n)
+        e = hipMemcpyFromSymbol(host, HIP_SYMBOL(ws::g_marks), n * sizeof(uint64_t), 0,
+                                hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(ws::g_marks));
+        if (e == hipSuccess) e = hipMemset(p, 0, sizeof(uint64_t) * ws::kMarkSlots);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+    }
+    return e == hipSuccess ? 0 : -6;
+}
+#endif

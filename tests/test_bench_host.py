@@ -61,7 +61,7 @@ def test_trace_summary_splits_cold_and_warm(tmp_path):
     assert cold["median_us"] == 25.5 and warm["mean_us"] == 23.0
     last = d["last_3"][key]
     assert last["calls"] == 3 and last["max_us"] == 26.0 and last["min_us"] == 23.0
-    assert last["period_mean_us"] == (900.4 - 430.0) / 2
+    assert last["period_mean_us"] == (900.4 - 430.0) / 2 and last["queues"] == 1
     assert last["gap_mean_us"] == round(((453.1 - 453.0) + (900.4 - 476.1)) / 2, 3)
 
 

@@ -75,8 +75,16 @@ KERNEL_SOURCES = {
 # counters read for a plain 256 MiB device copy.
 MEASURED = {
     "preprocess": {
-        "sha256_prefix": None,
-        "profile": None,
+        "sha256_prefix": "25e34857211feb98",
+        "profile": "profiles/preprocess_c5t_64x1280x720_to_224.md",
+        # cold: the 400 launches rotated over four lanes' batches, start-to-
+        # start period (kernel median 28.396 us); warm: the median of the
+        # other launches of this grid (back-to-back stage launches and graph
+        # replays).  traffic: FETCH_SIZE 53,791 KiB x 2.0 + WRITE_SIZE
+        # 37,632 KiB per launch (median of 47 dispatches), calibrated on a
+        # 256 MiB device copy (FETCH_SIZE 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
+        "c5t_64x1280x720_to_224": {"cold_us": 28.522, "cold_kernel_us": 28.396,
+                                   "warm_us": 23.197, "traffic": 110_163_968 + 38_535_168},
     },
 }
 
@@ -319,6 +327,42 @@ def rotated_times(w, torch, lane0) -> dict:
     return out
 
 
+def rotation_probe(torch, launches: int = 400) -> int:
+    """Which costs a rotated launch pays: 400 preprocess launches of the
+    64-frame batch back to back over four lanes in turn, with the lanes'
+    inputs and tensors shared or distinct.  Prints one JSON line
+    (microseconds per launch, three repeats each)."""
+    from post_processing_amd import workloads as wl
+    from post_processing_amd import ws
+    w = wl.c5_throughput(64)
+    dev = torch.device("cuda:0")
+    frames = [torch.from_numpy(w.frames).to(dev) for _ in range(4)]
+    tensors = [torch.empty((64, 3, 224, 224), dtype=torch.float32, device=dev) for _ in range(4)]
+    torch.cuda.synchronize()
+
+    def lane(fi, ti):
+        cfg = ws.make_config(src_w=w.src_w, src_h=w.src_h, dst_w=w.dst_w, dst_h=w.dst_h,
+                             batch=w.batch, mean=w.mean, std=w.std, input_mode=ws.INPUT_DEVICE,
+                             input_dev=frames[fi], tensor_dev=tensors[ti])
+        return ws.Lane(cfg)
+
+    cases = {"shared_inputs_shared_tensors": [(0, 0)] * 4,
+             "shared_inputs_distinct_tensors": [(0, i) for i in range(4)],
+             "distinct_inputs_shared_tensors": [(i, 0) for i in range(4)],
+             "distinct_inputs_distinct_tensors": [(i, i) for i in range(4)]}
+    out = {"metric": "preprocess us per launch, 400 launches rotated over 4 lanes",
+           "workload": w.name}
+    for name, pairs in cases.items():
+        lanes = [lane(f, t) for f, t in pairs]
+        ws.time_stage_rotate(lanes, ws.STAGE_PREPROCESS, 40, warmup=8)
+        out[name] = [round(ws.time_stage_rotate(lanes, ws.STAGE_PREPROCESS, launches,
+                                                warmup=8) * 1e3, 3) for _ in range(3)]
+        for ln in lanes:
+            ln.destroy()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def roofline_obj(w, stages: dict, cold: dict | None) -> dict:
     """The preprocess kernel against HBM: the stage that moves the frame and
     the tensor, and the one the metric names.  Top-K (a few KB to 2.7 MB)
@@ -342,8 +386,8 @@ def roofline_obj(w, stages: dict, cold: dict | None) -> dict:
     if cold:
         out["cold_checks_us"] = {k: round(v, 3) for k, v in cold.items() if k != key}
     if rec:
-        prof = {"profile": rec["profile"], "cold_kernel_us": rec["cold_us"],
-                "warm_kernel_us": rec["warm_us"],
+        prof = {"profile": rec["profile"], "cold_period_us": rec["cold_us"],
+                "cold_kernel_us": rec["cold_kernel_us"], "warm_kernel_us": rec["warm_us"],
                 "cold_frac": round(pb / (rec["cold_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
         prof["live_over_profiled"] = round(us / rec["cold_us"], 4) if cold else None
         out["profiled"] = prof
@@ -358,17 +402,20 @@ def run_replays(lane, torch, steps: int, warmup: int) -> dict:
     latency percentiles."""
     lane.bench(warmup)
     torch.cuda.synchronize()
-    ms, wall, host_us = lane.bench(steps, host=True)
+    ms, wall, host_us, sub_us = lane.bench(steps, host=True)
     torch.cuda.synchronize()
     res = {"frames_per_s": steps * lane.cfg.batch / wall, "wall_s": wall}
     if steps < LATENCY["samples"]:
-        ms, _, host_us = lane.bench(LATENCY["samples"], host=True)
+        ms, _, host_us, sub_us = lane.bench(LATENCY["samples"], host=True)
         torch.cuda.synchronize()
         res["latency_source"] = f"{LATENCY['samples']} replays after the timed steps"
     else:
         res["latency_source"] = "the timed steps"
     res.update(lat_stats(ms))
-    res["host"] = {"p50_us": pct(host_us, 50), "p99_us": pct(host_us, 99)}
+    wait_us = host_us - sub_us
+    res["host"] = {"p50_us": pct(host_us, 50), "p99_us": pct(host_us, 99),
+                   "submit_p50_us": pct(sub_us, 50), "submit_p99_us": pct(sub_us, 99),
+                   "wait_p50_us": pct(wait_us, 50), "wait_p99_us": pct(wait_us, 99)}
     return res
 
 
@@ -750,7 +797,9 @@ def campaign(torch, args) -> int:
                 "frames_per_s": [r["frames_per_s"] for r in rs],
                 "p50_us": [r["p50_us"] for r in rs], "p99_us": [r["p99_us"] for r in rs],
                 "p99_over_p50": [r["p99_over_p50"] for r in rs],
-                "host_p50_us": [round(r["host"]["p50_us"], 3) for r in rs if "host" in r]}
+                "host_p50_us": [round(r["host"]["p50_us"], 3) for r in rs if "host" in r],
+                "host_in_submit_p50_us": [round(r["host"]["submit_p50_us"], 3)
+                                          for r in rs if "host" in r]}
     for ls in lanes.values():
         for ln in ls:
             ln.destroy()
@@ -895,6 +944,9 @@ def main(argv=None) -> int:
     ap.add_argument("--latency-samples", type=int, default=MIN_LATENCY_SAMPLES,
                     help="replays the latency percentiles are taken over, at least (lower it "
                          "only for profiler runs, where every dispatch is slowed)")
+    ap.add_argument("--rotation-probe", action="store_true",
+                    help="preprocess launches rotated over lanes with shared or distinct "
+                         "inputs and tensors (which costs a cold launch pays)")
     ap.add_argument("--marks", action="store_true",
                     help="load the clock-mark build (libws_marks.so, built with `python -m "
                          "post_processing_amd.build --marks`) and add Top-K phase times")
@@ -946,6 +998,8 @@ def main(argv=None) -> int:
                                   "copy": ws.INPUT_COPY}[args.input]
     if args.workload == "copy":
         return copy_calibration(torch, args)
+    if args.rotation_probe:
+        return rotation_probe(torch)
     if args.campaign:
         if pinned is not None:
             os.sched_setaffinity(0, {pinned})
@@ -1048,7 +1102,11 @@ def main(argv=None) -> int:
         "latency_source": res["latency_source"],
         # Host view of the same replays: just before ws_submit to ws_wait's return.
         "host_submit_to_return_us": ({"p50": round(res["host"]["p50_us"], 3),
-                                      "p99": round(res["host"]["p99_us"], 3)}
+                                      "p99": round(res["host"]["p99_us"], 3),
+                                      "in_submit_p50": round(res["host"]["submit_p50_us"], 3),
+                                      "in_submit_p99": round(res["host"]["submit_p99_us"], 3),
+                                      "in_wait_p50": round(res["host"]["wait_p50_us"], 3),
+                                      "in_wait_p99": round(res["host"]["wait_p99_us"], 3)}
                                      if "host" in res else None),
         "transfers_included": input_mode != "device",
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)

@@ -38,15 +38,18 @@ int ws_lane_describe(const ws_lane *lane, ws_lane_plan *plan);
 
 /*
  * Run `replays` x (ws_submit, ws_wait) on one lane from the calling thread.
- *   gpu_ms   optional, `replays` entries: start->done event time per replay.
- *   host_us  optional, `replays` entries: host time from just before
- *            ws_submit to the return of ws_wait, per replay.
- *   wall_s   optional: host wall time from before the first submit to after
- *            the last wait.
+ *   gpu_ms     optional, `replays` entries: start->done event time per replay.
+ *   host_us    optional, `replays` entries: host time from just before
+ *              ws_submit to the return of ws_wait, per replay.
+ *   submit_us  optional, `replays` entries: host time spent inside ws_submit
+ *              (the two event records and the graph launch), per replay; the
+ *              rest of host_us is ws_wait.
+ *   wall_s     optional: host wall time from before the first submit to after
+ *              the last wait.
  * Returns the first non-OK status of any call, else WS_OK.
  */
 int ws_bench_replays(ws_lane *lane, int32_t replays, float *gpu_ms, float *host_us,
-                     double *wall_s);
+                     float *submit_us, double *wall_s);
 
 /*
  * Drive `nlanes` lanes concurrently, one host thread per lane, each running

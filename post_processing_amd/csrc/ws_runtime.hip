@@ -534,17 +534,23 @@ int ws_lane_describe(const ws_lane* L, ws_lane_plan* plan) {
 }
 
 int ws_bench_replays(ws_lane* L, int32_t replays, float* gpu_ms, float* host_us,
-                     double* wall_s) {
+                     float* submit_us, double* wall_s) {
     if (!L || replays < 0) return WS_E_INVALID_ARG;
     int rc = WS_OK;
-    const auto t0 = std::chrono::steady_clock::now();
+    using clk = std::chrono::steady_clock;
+    const auto t0 = clk::now();
     auto ts = t0;
     for (int32_t i = 0; i < replays && rc == WS_OK; ++i) {
         rc = ws_submit(L);
+        if (submit_us) {
+            submit_us[i] =
+                (float)std::chrono::duration<double, std::micro>(clk::now() - ts).count();
+        }
         if (rc == WS_OK) rc = ws_wait(L, gpu_ms ? &gpu_ms[i] : nullptr);
-        if (host_us) {
-            const auto te = std::chrono::steady_clock::now();
-            host_us[i] = (float)std::chrono::duration<double, std::micro>(te - ts).count();
+        if (host_us || submit_us) {
+            const auto te = clk::now();
+            if (host_us)
+                host_us[i] = (float)std::chrono::duration<double, std::micro>(te - ts).count();
             ts = te;
         }
     }
@@ -571,7 +577,7 @@ int ws_bench_lanes(ws_lane** lanes, int32_t nlanes, int32_t replays, float* gpu_
             }
             rcs[(size_t)i] = ws_bench_replays(lanes[i], replays,
                                               gpu_ms ? gpu_ms + (size_t)i * replays : nullptr,
-                                              nullptr, nullptr);
+                                              nullptr, nullptr, nullptr);
         });
     }
     while (ready.load() < nlanes) {

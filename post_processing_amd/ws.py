@@ -141,7 +141,7 @@ def load(path: str = LIB_PATH):
     lib.ws_lane_describe.argtypes = [c_void_p, POINTER(LanePlan)]
     lib.ws_lane_describe.restype = c_int
     lib.ws_bench_replays.argtypes = [c_void_p, c_int32, POINTER(c_float), POINTER(c_float),
-                                     POINTER(c_double)]
+                                     POINTER(c_float), POINTER(c_double)]
     lib.ws_bench_replays.restype = c_int
     lib.ws_bench_lanes.argtypes = [POINTER(c_void_p), c_int32, c_int32, POINTER(c_float),
                                    POINTER(c_double)]
@@ -316,16 +316,19 @@ class Lane:
 
     def bench(self, replays: int, host: bool = False):
         """Native submit/wait loop: (gpu_ms per replay, wall seconds), plus
-        the host microseconds per replay (submit to wait's return) when
-        `host` is set."""
+        the host microseconds per replay (submit to wait's return) and the
+        part of it spent inside ws_submit, when `host` is set."""
         ms = (c_float * replays)()
         us = (c_float * replays)() if host else None
+        sub = (c_float * replays)() if host else None
         wall = c_double(0.0)
-        rc = self._lib.ws_bench_replays(self.handle, replays, ms, us, byref(wall))
+        rc = self._lib.ws_bench_replays(self.handle, replays, ms, us, sub, byref(wall))
         if rc != WS_OK:
             raise WsError(rc, "ws_bench_replays", self.hip_error())
         out = np.ctypeslib.as_array(ms).copy(), wall.value
-        return out + (np.ctypeslib.as_array(us).copy(),) if host else out
+        if not host:
+            return out
+        return out + (np.ctypeslib.as_array(us).copy(), np.ctypeslib.as_array(sub).copy())
 
     def time_stage(self, stage: int, launches: int) -> float:
         """Mean ms per direct launch of one stage's kernel (native loop)."""

@@ -278,6 +278,80 @@ def topk_marks(lane, reps: int = 30) -> dict:
     return {k: round(float(np.median([r[k] for r in rows if k in r])), 3) for k in keys}
 
 
+def detect_marks(lane, reps: int = 30) -> dict:
+    """Phase times of the detection kernels from the clock-mark build
+    (libws_marks.so): one detection launch (decode + suppression) at a time,
+    its marks read back; the median over `reps` launches of each phase, in
+    microseconds (100 MHz clock)."""
+    import ctypes
+    from post_processing_amd import ws
+    lib = ws.load()
+    fn = lib.ws_debug_detect_marks
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32]
+    fn.restype = ctypes.c_int
+    nms0 = 1 << 16
+    prof0 = nms0 + 4096
+    n = prof0 + 16 * 8
+    buf = np.zeros(n, dtype=np.uint64)
+    rows = []
+    us = lambda a: float(a) * 0.01   # noqa: E731
+    for _ in range(reps):
+        fn(None, 0, 1)
+        lane.time_stage(ws.STAGE_DETECT, 1)
+        fn(buf.ctypes.data, n, 0)
+        d = buf[:nms0].reshape(-1, 8).astype(np.int64)
+        d = d[d[:, 0] > 0]
+        t = buf[nms0:nms0 + 256].reshape(16, 16).astype(np.int64)
+        live = t[:, 0] > 0
+        t = t[live]
+        pf = buf[prof0:prof0 + 128].reshape(16, 8).astype(np.int64)[live]
+        t0 = d[:, 0].min()
+        full = d[d[:, 5] > 0]
+        r = {"decode_waves": int(d.shape[0]),
+             "decode_start_spread": us(d[:, 0].max() - t0),
+             "decode_class_scan": us(np.median(d[:, 1] - d[:, 0])),
+             "decode_compact": us(np.median(d[:, 2] - d[:, 1])),
+             "decode_dfl": us(np.median(full[:, 3] - full[:, 2])) if len(full) else 0.0,
+             "decode_sync": us(np.median(full[:, 4] - full[:, 3])) if len(full) else 0.0,
+             "decode_store": us(np.median(full[:, 5] - full[:, 4])) if len(full) else 0.0,
+             "decode_span": us(d[:, 1:6].max() - t0),
+             "nms_start_after_decode": us(t[:, 0].min() - d[:, 1:6].max()),
+             "nms_counts": us(t[0, 1] - t[0, 0]),
+             "nms_gather": us(t[0, 2] - t[0, 1]),
+             "nms_bucket": us(t[0, 3] - t[0, 2]),
+             "nms_sort_all": us(t[0, 4] - t[0, 3]),
+             "nms_runs_busiest": us(t[:, 5].max() - t[0, 4]),
+             "nms_runs_median_wave": us(np.median(t[:, 5] - t[:, 4])),
+             "nms_runs_barrier": us(t[0, 6] - t[:, 5].max()),
+             "nms_order": us(t[0, 7] - t[0, 6]),
+             "nms_output": us(t[0, 8] - t[0, 7]),
+             "nms_span": us(t[0, 8] - t[:, 0].min()),
+             "runs_per_wave_max": int(t[:, 9].max()),
+             "nms_counts_load": us(t[0, 10] - t[0, 0]),
+             "nms_fill": us(t[0, 11] - t[0, 1]),
+             "nms_gather_loads": us(t[0, 2] - t[0, 11]),
+             "bucket_atomics": us(t[0, 12] - t[0, 2]),
+             "bucket_scan": us(t[0, 13] - t[0, 12]),
+             "bucket_scatter": us(t[0, 14] - t[0, 13]),
+             "bucket_order": us(t[0, 3] - t[0, 14]),
+             "first_run_sort_busiest_wave": us(t[int(np.argmax(t[:, 5])), 15] - t[0, 4]),
+             "cycles_busiest_wave": {k: int(pf[int(np.argmax(t[:, 5])), i]) for i, k in enumerate(
+                 ("loads", "screen", "settle", "screen_steps", "kept", "blocks", "round_waits",
+                  "w0_round_screen"))},
+             "cycles_wave0": {k: int(pf[0, i]) for i, k in enumerate(
+                 ("loads", "screen", "settle", "screen_steps", "kept", "blocks", "round_waits",
+                  "w0_round_screen"))},
+             "total_span": us(t[0, 8] - t0)}
+        rows.append(r)
+    out = {}
+    for k in rows[0].keys():
+        if isinstance(rows[0][k], dict):
+            out[k] = {j: int(np.median([r[k][j] for r in rows])) for j in rows[0][k]}
+        else:
+            out[k] = round(float(np.median([r[k] for r in rows])), 3)
+    return out
+
+
 def cold_times(lane, torch, launches: int = 20) -> dict:
     """Preprocess launches each after a flush kernel on the lane's stream
     (HIP events around the launch only, so each interval also holds one
@@ -740,6 +814,8 @@ def load_workload(name: str):
         return wl.c5_throughput(64)
     if name == "c3d":
         return wl.c3d()
+    if name in ("dense_any", "dense_class"):
+        return wl.dense_detect(agnostic=name == "dense_any")
     return wl.ALL_CONFIGS[name]()
 
 
@@ -904,7 +980,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10000)
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="c5t",
-                    choices=["c1", "c2", "c3", "c4", "c5l", "c5t", "c3d", "copy"])
+                    choices=["c1", "c2", "c3", "c4", "c5l", "c5t", "c3d", "dense_any", "dense_class",
+                             "copy"])
     ap.add_argument("--campaign", action="store_true",
                     help="every workload, three rotated campaigns, graph and direct launch")
     ap.add_argument("--campaign-warmup", type=int, default=1000)
@@ -949,7 +1026,8 @@ def main(argv=None) -> int:
                          "inputs and tensors (which costs a cold launch pays)")
     ap.add_argument("--marks", action="store_true",
                     help="load the clock-mark build (libws_marks.so, built with `python -m "
-                         "post_processing_amd.build --marks`) and add Top-K phase times")
+                         "post_processing_amd.build --marks`) and add Top-K and detection "
+                         "phase times")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="summarise a rocprofv3 kernel trace of this benchmark and exit (CPU)")
     ap.add_argument("--last", type=int, default=0,
@@ -1068,6 +1146,8 @@ def main(argv=None) -> int:
 
     if args.marks and w.k:
         extra["topk_marks_us"] = topk_marks(lane)
+    if args.marks and w.det:
+        extra["detect_marks_us"] = detect_marks(lane)
     roof = roofline_obj(w, stages, cold)
     input_mode = args.input or ("mapped" if (w.host_input or name == "c5l") else "device")
     line = {

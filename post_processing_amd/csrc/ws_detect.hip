@@ -7,27 +7,37 @@
 // boxes in source-image coordinates).
 //
 // det_decode_kernel (one workgroup per 64 anchors, four waves): wave w finds
-//   each anchor's best class within the w-th quarter of the classes; the
-//   anchors above the confidence threshold are compacted in LDS, their DFL
-//   distances are computed one lane per (candidate, box side), and each
-//   candidate's box is stored by anchor and its sort key appended to the
-//   candidate list (one atomic per workgroup).
+//   each anchor's best class within the w-th quarter of the classes (all of
+//   a lane's loads in flight together); the anchors above the confidence
+//   threshold are numbered in anchor order by a ballot, their DFL distances
+//   computed one lane per (candidate, box side), and the workgroup writes its
+//   candidate count, their keys and their boxes to its own 64 slots.  No
+//   atomics: the slot order is the anchor order.
 // det_nms_kernel (one workgroup of 16 waves, or 8 when 16 waves' kept-box
 // lists do not fit LDS beside the keys):
-//   1. sorts the candidate keys descending in LDS (bitonic: DPP exchanges
-//      inside a wave, LDS exchanges across waves).  The key orders by class
-//      first (unless boxes of any class suppress each other), then by
-//      probability descending, then anchor ascending -- so each class is a
-//      contiguous run in rank order;
-//   2. resolves the runs in parallel, one wave per run: 64 candidates at a
-//      time, each is tested against the run's boxes kept so far, then the
-//      first live candidate is kept and suppresses the live ones after it,
-//      and so on.  Boxes of different classes never interact, so this is
-//      exactly greedy suppression restricted to each class, and a class's
-//      run stops once it has max_det boxes;
-//   3. re-sorts the kept boxes of all classes by probability descending,
-//      anchor ascending -- the order in which plain greedy suppression over
-//      all candidates keeps them -- and writes the first max_det.
+//   1. gathers the candidates of all decode workgroups into LDS (wave 0's
+//      prefix sum of the counts places them), with their boxes when LDS has
+//      room;
+//   2. class-aware mode: buckets the keys by class (a counting pass), so each
+//      class is a contiguous run, and one wave resolves a run of up to 512
+//      candidates from its registers by selection -- the largest live key is
+//      the next kept box and suppresses the live candidates it overlaps --
+//      switching to a sort of the live keys once the run has kept eight
+//      boxes.  With any longer run, or when boxes of any class suppress each
+//      other, the whole list is sorted by the workgroup instead (bitonic; the
+//      key orders by class first in class-aware mode, so runs stay
+//      contiguous);
+//   3. greedy suppression of sorted runs: 64 candidates at a time; each is
+//      tested against the run's boxes kept so far, then the first live
+//      candidate is kept and suppresses the live ones after it, and so on.
+//      Boxes of different classes never interact, so class runs are
+//      independent and resolved one wave per run; the any-class run and any
+//      class run longer than 512 are resolved by all waves together (each
+//      wave screens one block against the kept boxes, then one wave settles
+//      the blocks in order);
+//   4. orders the kept boxes of all classes by probability descending, anchor
+//      ascending -- the order in which plain greedy suppression over all
+//      candidates keeps them -- and writes the first max_det.
 //
 // All arithmetic that decides a result (DFL exponentials, boxes, IoU,
 // mapping) is binary32 with one rounding per operation in a fixed order:
@@ -37,20 +47,75 @@
 // exact comparison in binary64 (iou_above).
 #include <hip/hip_runtime.h>
 
-#include "ws_kernels.h"
+#include "ws_detect.h"
 #include "ws_lanes.h"
+#include "ws_marks.h"
 
 namespace ws {
 namespace {
 
+#ifdef WS_CLOCK_MARKS
+// Phase marks of the detection kernels: the decode kernel's wave w of
+// workgroup g writes slots (4 g + w) * 8 + phase, the suppression kernel's
+// wave w slots kNmsMarks + 16 w + phase.
+__device__ uint64_t g_marks[kMarkSlots];
+#endif
+constexpr int kNmsMarks = 1 << 16;
+// Instrumented builds: per-wave totals (shader clock cycles, counts) of the
+// suppression phases at kNmsProf + 8 w + {0 block loads, 1 screening
+// (cooperative runs: every wave's part of each round), 2 settling
+// (cooperative runs: wave 0's part of each round), 3 screening steps, 4 kept
+// boxes, 5 blocks, 6 round barrier waits, 7 wave 0's screening within
+// rounds}.
+[[maybe_unused]] constexpr int kNmsProf = kNmsMarks + 4096;
+#ifdef WS_CLOCK_MARKS
+#define WS_PROF_T(v) const uint64_t v = __builtin_amdgcn_s_memtime()
+#define WS_PROF_WAIT() asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory")
+#define WS_PROF_DECL uint64_t prof_[8] = {0, 0, 0, 0, 0, 0, 0, 0}
+#define WS_PROF_ACC(slot_, val_) prof_[slot_] += (uint64_t)(val_)
+#define WS_PROF_FLUSH()                                                                  \
+    do {                                                                                 \
+        if ((threadIdx.x & 63) == 0)                                                     \
+            for (int q_ = 0; q_ < 8; ++q_) g_marks[kNmsProf + 8 * (threadIdx.x >> 6) + q_] += prof_[q_]; \
+    } while (0)
+#else
+#define WS_PROF_T(v)
+#define WS_PROF_WAIT()
+#define WS_PROF_DECL
+#define WS_PROF_ACC(slot_, val_)
+#define WS_PROF_FLUSH()
+#endif
+
 constexpr int kDecodeBlock = kDetDecodeAnchors;
 constexpr int kDecodeParts = 4;               // class ranges per anchor, one wave each
 constexpr int kDecodeThreads = kDecodeParts * kDecodeBlock;
+constexpr int kScanBatch = 32;                // class loads a lane keeps in flight
+constexpr int kBins = WS_DET_REG_MAX;
 // The suppression kernel runs with 1,024 threads when its LDS allows (more
 // class runs in flight: each wave's run is a chain of dependent steps), else
-// with kDetNmsThreads.
-constexpr int kNmsWideThreads = 1024;
-constexpr int kBins = WS_DET_REG_MAX;
+// with 512.
+constexpr int kNmsWide = 1024;
+constexpr int kNmsNarrow = 512;
+// Class runs up to this long are sorted by one wave in registers.
+constexpr int kRunSortMax = 512;
+// LDS of the suppression kernel, in 16-bit words: run starts (one per
+// class, a sentinel, and 64 run lengths), prefix sums of the decode counts.
+constexpr int kRunCap = WS_DET_MAX_CLASSES;
+constexpr int kRunLen = kRunCap + 1;          // run lengths (ordered runs only) start here
+constexpr int kRunSlots = kRunCap + 1 + 64 + 7;
+constexpr int kPreSlots = kDetMaxGroups + 8;
+// Long runs resolved by all waves: at most WS_DET_MAX_ANCHORS / 513.
+constexpr int kCoopCap = 32;
+
+static_assert(WS_DET_MAX_ANCHORS <= 16384, "slots must fit the 14-bit key field");
+static_assert(WS_DET_MAX_CLASSES <= 4096, "classes must fit the 12-bit key field");
+static_assert(WS_DET_MAX_ANCHORS % kNmsNarrow == 0 && WS_DET_MAX_ANCHORS % kNmsWide == 0,
+              "bucketing registers cover every key");
+static_assert(WS_DET_MAX_CLASSES % kNmsNarrow == 0 && WS_DET_MAX_CLASSES % kNmsWide == 0,
+              "class prefix sums cover every class");
+static_assert(kDetMaxGroups < kNmsNarrow, "one thread per decode workgroup count, and the total");
+static_assert(WS_DET_MAX_ANCHORS / (kRunSortMax + 1) < kCoopCap, "long-run list capacity");
+static_assert((kRunSlots * 2) % 16 == 0 && (kPreSlots * 2) % 16 == 0, "16-byte aligned regions");
 
 // e^x for x <= 0 (Cody & Waite, "Software Manual for the Elementary
 // Functions", exp): x = n ln2 + r with ln 2 split into a 15-significant-bit
@@ -99,19 +164,25 @@ __device__ __forceinline__ float dfl_side(const float* __restrict__ q, int A) {
     return num / s;
 }
 
-// Whether IoU(a, b) > t for kept box a and candidate b (xyxy), where the IoU
-// is binary32: areas, clipped intersection sides, intersection, union =
-// (area_a + area_b) - inter, each rounded once, then inter / union rounded
-// once.  The division is not carried out.  With t+ the next binary32 above
-// t and m their midpoint, the rounded quotient exceeds t exactly when
-// inter / union > m, or equals m and the tie rounds up to t+ (t+ has the
-// even significand, i.e. t's is odd).  inter and union are binary32 and m
-// has 25 significant bits, so m * union is exact in binary64 and the test is
-// exact.  A zero union (0 / 0 = NaN) and NaN boxes suppress nothing.
-__device__ __forceinline__ bool iou_above(float4 a, float4 b, double mid, bool tie_up) {
+// Area of an xyxy box, binary32: (x2 - x1) * (y2 - y1).
+__device__ __forceinline__ float box_area(float4 b) {
 #pragma clang fp contract(off)
-    const float area_a = (a.z - a.x) * (a.w - a.y);
-    const float area_b = (b.z - b.x) * (b.w - b.y);
+    return (b.z - b.x) * (b.w - b.y);
+}
+
+// Whether IoU(a, b) > t for kept box a and candidate b (xyxy) with their
+// areas, where the IoU is binary32: areas, clipped intersection sides,
+// intersection, union = (area_a + area_b) - inter, each rounded once, then
+// inter / union rounded once.  The division is not carried out.  With t+
+// the next binary32 above t and m their midpoint, the rounded quotient
+// exceeds t exactly when inter / union > m, or equals m and the tie rounds
+// up to t+ (t+ has the even significand, i.e. t's is odd).  inter and union
+// are binary32 and m has 25 significant bits, so m * union is exact in
+// binary64 and the test is exact.  A zero union (0 / 0 = NaN) and NaN boxes
+// suppress nothing.
+__device__ __forceinline__ bool iou_above(float4 a, float area_a, float4 b, float area_b, double mid,
+                                          bool tie_up) {
+#pragma clang fp contract(off)
     const float iw = fmaxf(0.0f, fminf(a.z, b.z) - fmaxf(a.x, b.x));
     const float ih = fmaxf(0.0f, fminf(a.w, b.w) - fmaxf(a.y, b.y));
     const float inter = iw * ih;
@@ -130,26 +201,26 @@ __device__ __forceinline__ float to_source(float v, float origin, float scale, f
 
 // ---------------------------------------------------------------------------
 // Candidate keys.  Larger keys come first; every key is non-zero and unique
-// (the anchor is in it), and bit 0 is free (it marks kept candidates).
-//   by class:  [63:52] 4095 - class, [51:21] probability bits, [20:7] 16383 - anchor
-//   any class: [63:33] probability bits, [32:19] 16383 - anchor, [18:7] class
+// (the slot is in it), and bit 0 is free (it marks kept candidates).
+//   by class:  [63:52] 4095 - class, [51:21] probability bits, [20:7] 16383 - slot
+//   any class: [63:33] probability bits, [32:19] 16383 - slot, [18:7] class
 // The probability is > conf >= 0, so its sign bit is clear and its bits order
-// as integers.  The second layout is also the rank order of the output.
+// as integers.  Slots order candidates as their anchors do, so the second
+// layout is also the rank order of the output.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint64_t make_key(bool any_class, uint32_t prob, int anchor, int cls) {
+__device__ __forceinline__ uint64_t make_key(bool any_class, uint32_t prob, int slot, int cls) {
     const uint64_t pr = prob & 0x7FFFFFFFu;
-    const uint64_t an = (uint64_t)(0x3FFF - anchor);
-    if (any_class) return (pr << 33) | (an << 19) | ((uint64_t)cls << 7);
-    return ((uint64_t)(0xFFF - cls) << 52) | (pr << 21) | (an << 7);
+    const uint64_t sl = (uint64_t)(0x3FFF - slot);
+    if (any_class) return (pr << 33) | (sl << 19) | ((uint64_t)cls << 7);
+    return ((uint64_t)(0xFFF - cls) << 52) | (pr << 21) | (sl << 7);
 }
 
-__device__ __forceinline__ int key_anchor(uint64_t k, bool any_class) {
+__device__ __forceinline__ int key_slot(uint64_t k, bool any_class) {
     return 0x3FFF - (int)((k >> (any_class ? 19 : 7)) & 0x3FFFu);
 }
 
-__device__ __forceinline__ uint32_t key_group(uint64_t k, bool any_class) {
-    return any_class ? 0u : (uint32_t)(k >> 52);
-}
+// Class of a class-ordered key.
+__device__ __forceinline__ int key_class(uint64_t k) { return 0xFFF - (int)(k >> 52); }
 
 // A class-ordered key in rank layout (the "any class" layout).
 __device__ __forceinline__ uint64_t to_rank_key(uint64_t k) {
@@ -164,9 +235,69 @@ __device__ __forceinline__ float4 readlane4(float4 v, int lane) {
                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.w), lane)));
 }
 
-// Block sort of the candidate keys (bitonic network, descending): each wave
-// sorts blocks of 64*K keys in registers (sort_block), and only distances of
-// a whole block or more go through LDS.
+__device__ __forceinline__ float readlanef(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// ---------------------------------------------------------------------------
+// Prefix sums
+// ---------------------------------------------------------------------------
+
+// Inclusive prefix sum across a wave64 by DPP: shifts of 1, 2, 4 and 8
+// lanes inside each row of 16 (a lane with no source adds 0), then row 0's
+// total to row 1 and row 2's to row 3 (row_bcast:15), then rows 0-1's total
+// to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+    return v;
+}
+
+// Largest 64-bit value across a wave64 (every lane gets it).
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v, int lane) {
+    v = umax64(v, xor_lane64<1>(v, lane));
+    v = umax64(v, xor_lane64<2>(v, lane));
+    v = umax64(v, xor_lane64<4>(v, lane));
+    v = umax64(v, xor_lane64<8>(v, lane));
+    v = umax64(v, xor_lane64<16>(v, lane));
+    v = umax64(v, xor_lane64<32>(v, lane));
+    return v;
+}
+
+// Exclusive prefix sum of one value per thread over the workgroup, and the
+// total (uniform).  Starts and ends with a barrier, so s_tot may be reused
+// right after.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tot, uint32_t& total, int tid) {
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const uint32_t incl = wave_incl_scan(v);
+    __syncthreads();
+    if (lane == 63) s_tot[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const uint32_t t = s_tot[w];
+        base += w < wave ? t : 0u;
+        tot += t;
+    }
+    __syncthreads();
+    total = tot;
+    return base + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// Sorting
+// ---------------------------------------------------------------------------
+
+// Block sort of keys in LDS (bitonic network, descending): each wave sorts
+// blocks of 64*K keys in registers (sort_block), and only distances of a
+// whole block or more go through LDS.
 
 // One stage (B, J) with J at least a block, through LDS: one thread per pair,
 // four pairs loaded before any is stored.
@@ -196,28 +327,18 @@ __device__ __forceinline__ void cx_pass_lds(uint64_t* s, int P, int B, int J, in
     }
 }
 
-// Sorts P keys descending into s[0, P), P a power of two with 64 <= P and
-// P / (64 K) blocks.  The keys come from g[0, n) (zero past n) when g is
-// given, else from s itself.  Ends with a barrier.
+// Sorts s[0, P) descending, P a power of two with 64 <= P and P / (64 K)
+// blocks.  Ends with a barrier.
 template <int NT, int K>
-__device__ __forceinline__ void sort_desc_k(uint64_t* s, int P, int tid, const uint64_t* __restrict__ g,
-                                            int n) {
+__device__ __forceinline__ void sort_desc_k(uint64_t* s, int P, int tid) {
     constexpr int Q = 64 * K;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int blocks = P / Q;
     for (int b = wave; b < blocks; b += NT / 64) {
         uint64_t x[K];
-        if (g) {
 #pragma unroll
-            for (int r = 0; r < K; ++r) {
-                const int e = b * Q + r * 64 + lane;
-                x[r] = e < n ? g[e] : 0;
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < K; ++r) x[r] = s[b * Q + r * 64 + lane];
-        }
+        for (int r = 0; r < K; ++r) x[r] = s[b * Q + r * 64 + lane];
         sort_block<K>(x, (b & 1) == 0, lane);
 #pragma unroll
         for (int r = 0; r < K; ++r) s[b * Q + r * 64 + lane] = x[r];
@@ -243,12 +364,11 @@ __device__ __forceinline__ void sort_desc_k(uint64_t* s, int P, int tid, const u
 // Block sizes: one block per wave up to 4096 keys (64 per lane at most 8),
 // then several blocks of 512 per wave.
 template <int NT>
-__device__ __forceinline__ void sort_desc(uint64_t* s, int P, int tid, const uint64_t* __restrict__ g = nullptr,
-                                          int n = 0) {
-    if (P <= 512) sort_desc_k<NT, 1>(s, P, tid, g, n);
-    else if (P == 1024) sort_desc_k<NT, 2>(s, P, tid, g, n);
-    else if (P == 2048) sort_desc_k<NT, 4>(s, P, tid, g, n);
-    else sort_desc_k<NT, 8>(s, P, tid, g, n);
+__device__ __forceinline__ void sort_desc(uint64_t* s, int P, int tid) {
+    if (P <= 512) sort_desc_k<NT, 1>(s, P, tid);
+    else if (P == 1024) sort_desc_k<NT, 2>(s, P, tid);
+    else if (P == 2048) sort_desc_k<NT, 4>(s, P, tid);
+    else sort_desc_k<NT, 8>(s, P, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -268,15 +388,19 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(
     __shared__ float s_dist[kDecodeBlock][4];
     __shared__ float s_pbest[kDecodeParts][kDecodeBlock];
     __shared__ int s_pcls[kDecodeParts][kDecodeBlock];
-    __shared__ int s_count;
-    __shared__ uint32_t s_base;
+    __shared__ int s_n;
     const int tid = (int)threadIdx.x;
+    const int lane = tid & (kDecodeBlock - 1);
     const int A = anchors;
-    if (tid == 0) s_count = 0;
+    const int g = (int)blockIdx.x;
+    [[maybe_unused]] const int mark = (g * 4 + (tid >> 6)) * 8;
+    WS_MARK(mark + 0);
 
     // 1. Best class (first maximum; NaN never compares greater) and threshold.
-    //    Wave w scans the w-th quarter of the classes of the group's anchors.
-    const int a = (int)blockIdx.x * kDecodeBlock + (tid & (kDecodeBlock - 1));
+    //    Wave w scans the w-th quarter of the classes of the group's anchors,
+    //    up to kScanBatch loads in flight per lane (past the range a lane
+    //    re-reads the range's last class and ignores it).
+    const int a = g * kDecodeBlock + lane;
     const int part = tid / kDecodeBlock;   // wave-uniform
     const int per = (nc + kDecodeParts - 1) / kDecodeParts;
     const int c_begin = min(nc, part * per);
@@ -285,48 +409,50 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(
     int cls = c_begin;
     if (a < A) {
         const float* __restrict__ pr = head + (size_t)(4 * kBins) * A + a;
-        int c = c_begin;
-        for (; c + 16 <= c_end; c += 16) {
-            float v[16];
+        for (int c0 = c_begin; c0 < c_end; c0 += kScanBatch) {
+            float v[kScanBatch];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] = pr[(size_t)(c + j) * A];
+            for (int j = 0; j < kScanBatch; ++j) v[j] = pr[(size_t)min(c0 + j, c_end - 1) * A];
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (v[j] > best) {
+            for (int j = 0; j < kScanBatch; ++j)
+                if (c0 + j < c_end && v[j] > best) {
                     best = v[j];
-                    cls = c + j;
+                    cls = c0 + j;
                 }
         }
-        for (; c < c_end; ++c) {
-            const float v = pr[(size_t)c * A];
-            if (v > best) {
-                best = v;
-                cls = c;
-            }
-        }
     }
-    s_pbest[part][tid & (kDecodeBlock - 1)] = best;
-    s_pcls[part][tid & (kDecodeBlock - 1)] = cls;
+    WS_MARK(mark + 1);
+    s_pbest[part][lane] = best;
+    s_pcls[part][lane] = cls;
     __syncthreads();
-    if (part == 0 && a < A) {
+    if (part == 0) {
         // Later ranges win only when strictly greater: ties keep the first.
         best = -INFINITY;
         cls = 0;
 #pragma unroll
         for (int q = 0; q < kDecodeParts; ++q)
-            if (s_pbest[q][tid] > best) {
-                best = s_pbest[q][tid];
-                cls = s_pcls[q][tid];
+            if (s_pbest[q][lane] > best) {
+                best = s_pbest[q][lane];
+                cls = s_pcls[q][lane];
             }
-        if (best > p.conf) {
-            const int slot = atomicAdd(&s_count, 1);
-            s_anchor[slot] = a;
-            s_cls[slot] = cls;
-            s_prob[slot] = __float_as_uint(best);
+        // Candidates numbered in anchor (lane) order.
+        const bool cand = a < A && best > p.conf;
+        const uint64_t m = __ballot(cand);
+        if (cand) {
+            const int q = lanes_below(m);
+            s_anchor[q] = a;
+            s_cls[q] = cls;
+            s_prob[q] = __float_as_uint(best);
+        }
+        if (lane == 0) {
+            const int n = __popcll(m);
+            s_n = n;
+            p.counts[g] = (uint32_t)n;
         }
     }
     __syncthreads();
-    const int n = s_count;   // uniform
+    WS_MARK(mark + 2);
+    const int n = s_n;   // uniform
     if (n == 0) return;
 
     // 2. DFL distances, one lane per (candidate, side); each lane issues its
@@ -336,77 +462,120 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(
         const int side = t & 3;
         s_dist[q][side] = dfl_side(head + (size_t)(side * kBins) * A + s_anchor[q], A);
     }
-    if (tid == 0) s_base = atomicAdd(p.counter, (uint32_t)n);
+    WS_MARK_AFTER_LOADS(mark + 3);
     __syncthreads();
+    WS_MARK(mark + 4);
 
-    // 3. Boxes by anchor, keys appended to the candidate list.
-    const uint32_t base = s_base;
+    // 3. Boxes and keys to the group's slots.  The grid bounds are read with
+    //    constant indices (scalar loads of the kernel arguments).
     const bool any_class = p.agnostic != 0;
+    const int le0 = p.level_end[0], le1 = p.level_end[1];
+    const int gw0 = p.grid_w[0], gw1 = p.grid_w[1], gw2 = p.grid_w[2];
     for (int q = tid; q < n; q += kDecodeThreads) {
         const int aq = s_anchor[q];
-        const int level = aq < p.level_end[0] ? 0 : (aq < p.level_end[1] ? 1 : 2);
-        const int cell = aq - (level == 0 ? 0 : p.level_end[level - 1]);
-        const int gw = p.grid_w[level];
+        const int level = aq < le0 ? 0 : (aq < le1 ? 1 : 2);
+        const int cell = aq - (level == 0 ? 0 : (level == 1 ? le0 : le1));
+        const int gw = level == 0 ? gw0 : (level == 1 ? gw1 : gw2);
         const float cx = (float)(cell % gw) + 0.5f;
         const float cy = (float)(cell / gw) + 0.5f;
         const float st = (float)(8 << level);
-        p.boxes[aq] = make_float4((cx - s_dist[q][0]) * st, (cy - s_dist[q][1]) * st,
-                                  (cx + s_dist[q][2]) * st, (cy + s_dist[q][3]) * st);
-        const uint32_t idx = base + (uint32_t)q;   // < anchors: each anchor appears once
-        if (idx < (uint32_t)A) p.keys[idx] = make_key(any_class, s_prob[q], aq, s_cls[q]);
+        const int slot = g * kDecodeBlock + q;   // < anchors: q counts anchors of this group
+        p.boxes[slot] = make_float4((cx - s_dist[q][0]) * st, (cy - s_dist[q][1]) * st,
+                                    (cx + s_dist[q][2]) * st, (cy + s_dist[q][3]) * st);
+        p.keys[slot] = make_key(any_class, s_prob[q], slot, s_cls[q]);
     }
+    WS_MARK(mark + 5);
 }
 
 // ---------------------------------------------------------------------------
 // Suppression
 // ---------------------------------------------------------------------------
 
-// Greedy suppression over one class's run s[s0 ..) (all of s when boxes of
-// any class interact), by one wave.  With STAGED, s_box holds the boxes in
-// sorted order in LDS; otherwise they are read by anchor from global memory.
-// The choice is a template argument so that each instance loads from one
-// address space (a run-time choice between the two pointers compiles to
-// generic loads that wait on both memory counters).  Kept candidates get
-// bit 0 set in s and their positions listed in kept_pos (capacity max_det).
-// Returns how many were kept.
+// Box of sorted position e holding key k: staged in sorted order in LDS, or
+// read by slot from global memory.  The choice is a template argument so
+// that each instance loads from one address space (a run-time choice between
+// the two pointers compiles to generic loads that wait on both memory
+// counters).
 template <bool STAGED>
-__device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, const float4* s_box, int n, int s0,
-                           uint16_t* kept_pos, bool any_class, int lane) {
+__device__ __forceinline__ float4 box_at(const DetParams& p, const float4* s_box, int e, uint64_t k,
+                                         bool any_class) {
+    return STAGED ? s_box[e] : p.boxes[key_slot(k, any_class)];
+}
+
+// Tests the 64 candidates of one block (box and area per lane; alive: the
+// live ones) against kept boxes k0 .. k1 - 1 of the run and returns the
+// candidates still alive.  U kept boxes per step, all fetched before any
+// test so that the U tests overlap (a last step short of U boxes repeats
+// box k1 - 1, which changes nothing).  kept(j, box, area) gives kept box j
+// and its area (wave-uniform j).
+template <int U, typename Kept>
+__device__ __forceinline__ uint64_t screen(uint64_t alive, float4 box, float area, int k0, int k1, Kept kept,
+                                          double mid, bool tie_up, int& steps) {
+    for (int k = k0; k < k1 && alive != 0; k += U) {
+        ++steps;
+        float4 a[U];
+        float aa[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) kept(min(k + u, k1 - 1), a[u], aa[u]);
+        bool sup = false;
+#pragma unroll
+        for (int u = 0; u < U; ++u) sup |= iou_above(a[u], aa[u], box, area, mid, tie_up);
+        alive &= ~(uint64_t)__ballot(sup);
+    }
+    return alive;
+}
+
+// Greedy suppression of one run s[s0, s0 + len) by one wave, in rank order
+// (s sorted descending).  kept_pos holds the positions of the kept0 boxes of
+// the run kept before s0 (all ranked above it).  Kept candidates get bit 0
+// set in s and their positions listed in kept_pos (capacity max_det).
+// Returns how many the run keeps in all.
+template <bool STAGED>
+__device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, const float4* s_box, int s0, int len,
+                           uint16_t* kept_pos, bool any_class, int lane, int kept0 = 0) {
 #pragma clang fp contract(off)
     const double mid = p.iou_mid;
     const bool tie_up = p.iou_tie_up != 0;
-    uint32_t group = 0;
-    int kept = 0;
-    for (int c0 = s0; c0 < n; c0 += 64) {
+    const int end = s0 + len;
+    int kept = kept0;
+    [[maybe_unused]] int steps = 0;
+    WS_PROF_DECL;
+    for (int c0 = s0; c0 < end; c0 += 64) {
         wave_lds_sync();   // kept_pos writes of the previous block are visible
+        WS_PROF_T(t0);
         const int e = c0 + lane;
-        const uint64_t key = e < n ? s[e] : 0;
-        if (c0 == s0) group = key_group(readlane64(key, 0), any_class);   // the run's first key
-        const bool valid = e < n && key_group(key, any_class) == group;
-        const uint64_t vmask = __ballot(valid);
-        if (vmask == 0) break;
+        const bool valid = e < end;
+        const uint64_t key = valid ? s[e] : 0;
         // Branches rather than a conditional over lvalues, which would give
         // the zero box a private-memory copy.
         float4 box = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (valid) box = STAGED ? s_box[e] : p.boxes[key_anchor(key, any_class)];
-        uint64_t alive = vmask;
+        if (valid) box = box_at<STAGED>(p, s_box, e, key, any_class);
+        const float area = box_area(box);
+        uint64_t alive = __ballot(valid);
+        WS_PROF_WAIT();
+        WS_PROF_T(t1);
 
-        // Boxes of this run kept in earlier blocks, 64 at a time.
+        // Boxes of this run kept in earlier blocks, 64 at a time in registers.
         for (int kb = 0; kb < kept && alive != 0; kb += 64) {
             const int kl = kb + lane;
             float4 kbox = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kl < kept)
-                kbox = STAGED ? s_box[kept_pos[kl]]
-                              : p.boxes[key_anchor(s[kept_pos[kl]], any_class)];
-            const int lim = min(64, kept - kb);
-            for (int t = 0; t < lim && alive != 0; ++t) {
-                const bool sup = valid & iou_above(readlane4(kbox, t), box, mid, tie_up);
-                alive &= ~(uint64_t)__ballot(sup);
+            if (kl < kept) {
+                const int pos = kept_pos[kl];
+                kbox = STAGED ? s_box[pos] : p.boxes[key_slot(s[pos], any_class)];
             }
+            const float karea = box_area(kbox);
+            alive = screen<4>(alive, box, area, kb, min(kb + 64, kept),
+                              [&](int j, float4& a, float& aa) {
+                                  a = readlane4(kbox, j - kb);
+                                  aa = readlanef(karea, j - kb);
+                              },
+                              mid, tie_up, steps);
         }
+        WS_PROF_T(t2);
 
         // This block: the first live candidate is the next kept box.
         uint64_t pending = alive;
+        bool full = false;
         while (pending != 0) {
             const int i = __ffsll((unsigned long long)pending) - 1;
             if (lane == i) {
@@ -414,14 +583,306 @@ __device__ __forceinline__ int resolve_run(const DetParams& p, uint64_t* s, cons
                 s[e] = key | 1u;
             }
             ++kept;
-            if (kept == p.max_det) return kept;
-            const bool sup = (lane > i) & iou_above(readlane4(box, i), box, mid, tie_up);
+            WS_PROF_ACC(4, 1);
+            if (kept == p.max_det) {
+                full = true;
+                break;
+            }
+            const bool sup =
+                (lane > i) & iou_above(readlane4(box, i), readlanef(area, i), box, area, mid, tie_up);
             alive &= ~(uint64_t)__ballot(sup);
             pending = alive & ~((2ull << i) - 1);   // candidates after i
         }
-        if (vmask != ~0ull) break;   // the run ended inside this block
+        WS_PROF_T(t3);
+        WS_PROF_ACC(0, t1 - t0);
+        WS_PROF_ACC(1, t2 - t1);
+        WS_PROF_ACC(2, t3 - t2);
+        WS_PROF_ACC(5, 1);
+        if (full) break;
     }
+    WS_PROF_ACC(3, steps);
+    WS_PROF_FLUSH();
     return kept;
+}
+
+// Greedy suppression of one long run s[s0, s0 + len) by all waves, NT
+// candidates per round: every wave screens one block of 64 against the boxes
+// kept before the round (the bulk of the tests, in parallel), then wave 0
+// takes the round's blocks in order, screens each against the boxes kept
+// earlier in the round and settles it as resolve_run does.  Kept boxes,
+// their areas and positions go to k_box / k_area / k_pos in rank order
+// (capacity max_det); kept candidates get bit 0 set in s.  Returns how many
+// were kept (uniform).
+template <bool STAGED, int NT>
+__device__ __forceinline__ int coop_resolve(const DetParams& p, uint64_t* s, const float4* s_box, int s0, int len,
+                            float4* k_box, float* k_area, uint16_t* k_pos, uint64_t* s_alive, int* s_kept,
+                            bool any_class, int tid) {
+#pragma clang fp contract(off)
+    constexpr int W = NT / 64;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const double mid = p.iou_mid;
+    const bool tie_up = p.iou_tie_up != 0;
+    const int end = s0 + len;
+    // Uniform LDS addresses: broadcast reads.
+    auto kept = [&](int j, float4& a, float& aa) {
+        a = k_box[j];
+        aa = k_area[j];
+    };
+    int K = 0;
+    [[maybe_unused]] int steps = 0, round_steps = 0;
+    WS_PROF_DECL;
+    for (int w0 = s0; w0 < end; w0 += NT) {
+        const int K0 = K;
+        WS_PROF_T(ta);
+        {
+            const int e = w0 + wave * 64 + lane;
+            const bool valid = e < end;
+            float4 box = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (valid) box = box_at<STAGED>(p, s_box, e, s[e], any_class);
+            const uint64_t alive =
+                screen<8>((uint64_t)__ballot(valid), box, box_area(box), 0, K0, kept, mid, tie_up, steps);
+            if (lane == 0) s_alive[wave] = alive;
+        }
+        WS_PROF_T(tb);
+        WS_PROF_ACC(1, tb - ta);
+        __syncthreads();
+        WS_PROF_T(tc);
+        WS_PROF_ACC(6, tc - tb);
+        if (wave == 0) {
+            bool full = false;
+            for (int b = 0; b < W && !full; ++b) {
+                const int c0 = w0 + b * 64;
+                if (c0 >= end) break;
+                wave_lds_sync();   // k_box writes of earlier blocks are visible
+                WS_PROF_T(t0);
+                const int e = c0 + lane;
+                const bool valid = e < end;
+                const uint64_t key = valid ? s[e] : 0;
+                float4 box = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (valid) box = box_at<STAGED>(p, s_box, e, key, any_class);
+                const float area = box_area(box);
+                WS_PROF_WAIT();
+                WS_PROF_T(t1);
+                uint64_t alive = screen<4>(s_alive[b], box, area, K0, K, kept, mid, tie_up, round_steps);
+                WS_PROF_T(t2);
+                WS_PROF_ACC(0, t1 - t0);
+                WS_PROF_ACC(7, t2 - t1);
+                WS_PROF_ACC(5, 1);
+                uint64_t pending = alive;
+                while (pending != 0) {
+                    const int i = __ffsll((unsigned long long)pending) - 1;
+                    if (lane == i) {
+                        k_box[K] = box;
+                        k_area[K] = area;
+                        k_pos[K] = (uint16_t)e;
+                        s[e] = key | 1u;
+                    }
+                    ++K;
+                    WS_PROF_ACC(4, 1);
+                    if (K == p.max_det) {
+                        full = true;
+                        break;
+                    }
+                    const bool sup = (lane > i) & iou_above(readlane4(box, i), readlanef(area, i), box,
+                                                            area, mid, tie_up);
+                    alive &= ~(uint64_t)__ballot(sup);
+                    pending = alive & ~((2ull << i) - 1);
+                }
+            }
+            if (lane == 0) *s_kept = K;
+        }
+        WS_PROF_T(td);
+        if (wave == 0) WS_PROF_ACC(2, td - tc);
+        __syncthreads();
+        K = *s_kept;
+        if (K >= p.max_det) break;
+    }
+    WS_PROF_ACC(3, steps);
+    WS_PROF_FLUSH();
+    return K;
+}
+
+// Kept boxes a class run resolves by selection before it switches to
+// sorting what is left (selection costs a pass over the run per kept box).
+constexpr int kSelectBudget = 8;
+
+// Greedy suppression of one class run s[s0, s0 + len), len <= 64 K, in one
+// wave.  The run is held K keys per lane in registers and resolved by
+// selection: the largest live key is the next kept box (every candidate of
+// the run ranked above it is kept or suppressed by then, which is the greedy
+// order), it suppresses the live candidates it overlaps, and so on; dead
+// candidates get key 0.  A run that keeps kSelectBudget boxes with
+// candidates still alive is finished in rank order instead: the live keys
+// are sorted in registers and laid out after the kept ones, the rest of the
+// run is cleared, and resolve_run continues from the kept list.  Boxes are
+// staged by compact position in s_tmp (STAGED) or read by slot.  Kept
+// candidates get bit 0 set in s.  Returns how many were kept.
+template <int K, bool STAGED>
+__device__ __forceinline__ int select_run_k(const DetParams& p, uint64_t* s, float4* s_box, const float4* s_tmp,
+                            const uint16_t* s_pre, int s0, int len, uint16_t* kept_pos, int lane) {
+#pragma clang fp contract(off)
+    const double mid = p.iou_mid;
+    const bool tie_up = p.iou_tie_up != 0;
+    auto staged_box = [&](uint64_t k) {
+        const int slot = key_slot(k, false);
+        return s_tmp[s_pre[slot >> 6] + (slot & 63)];
+    };
+    uint64_t key[K];
+    float4 box[K];
+    float area[K];
+#pragma unroll
+    for (int r = 0; r < K; ++r) {
+        const int e = r * 64 + lane;
+        key[r] = e < len ? s[s0 + e] : 0;
+        box[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e < len) box[r] = STAGED ? staged_box(key[r]) : p.boxes[key_slot(key[r], false)];
+        area[r] = box_area(box[r]);
+    }
+    int kept = 0;
+    bool live = false;
+    WS_PROF_DECL;
+    while (true) {
+        uint64_t m = key[0];
+#pragma unroll
+        for (int r = 1; r < K; ++r) m = umax64(m, key[r]);
+        const uint64_t top = readlane64(wave_max64(m, lane), 0);
+        if (top == 0) break;
+        if (kept == kSelectBudget && K > 1) {   // uniform
+            live = true;
+            break;
+        }
+        // Its register and lane (keys are distinct).
+        int rs = 0, ls = 0;
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            const uint64_t b = __ballot(key[r] == top);
+            if (b) {
+                rs = r;
+                ls = __ffsll((unsigned long long)b) - 1;
+            }
+        }
+        float4 kb = make_float4(0.f, 0.f, 0.f, 0.f);
+        float ka = 0.0f;
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            if (r == rs) {
+                kb = readlane4(box[r], ls);
+                ka = readlanef(area[r], ls);
+                if (lane == ls) {
+                    s[s0 + r * 64 + ls] = top | 1u;
+                    kept_pos[kept] = (uint16_t)(s0 + r * 64 + ls);
+                    key[r] = 0;
+                }
+            }
+        }
+        ++kept;
+        WS_PROF_ACC(4, 1);
+        if (kept == p.max_det) break;
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            if (__ballot(key[r] != 0) != 0) {
+                if (iou_above(kb, ka, box[r], area[r], mid, tie_up)) key[r] = 0;
+            }
+        }
+    }
+    if (live) {   // uniform
+        // Kept keys first, then the live ones in rank order, then zeros.
+        sort_block<K>(key, true, lane);
+        int nlive = 0;
+#pragma unroll
+        for (int r = 0; r < K; ++r) nlive += __popcll(__ballot(key[r] != 0));
+        wave_lds_sync();   // kept_pos written
+        const uint64_t kk = lane < kept ? s[kept_pos[lane]] : 0;
+        wave_lds_sync();   // kept keys read before the run is rewritten
+        if (lane < kept) {
+            s[s0 + lane] = kk;
+            kept_pos[lane] = (uint16_t)(s0 + lane);
+        }
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            const int e = r * 64 + lane;
+            if (e < nlive) s[s0 + kept + e] = key[r];
+        }
+        for (int e = kept + nlive + lane; e < len; e += 64) s[s0 + e] = 0;
+        wave_lds_sync();
+        if (STAGED) {
+            for (int e = lane; e < kept + nlive; e += 64) s_box[s0 + e] = staged_box(s[s0 + e]);
+            wave_lds_sync();
+        }
+        kept = resolve_run<STAGED>(p, s, s_box, s0 + kept, nlive, kept_pos, false, lane, kept);
+    }
+    WS_PROF_FLUSH();
+    return kept;
+}
+
+// A class run of up to kRunSortMax candidates, by one wave (select_run_k).
+template <bool STAGED>
+__device__ __forceinline__ int select_run(const DetParams& p, uint64_t* s, float4* s_box, const float4* s_tmp,
+                                          const uint16_t* s_pre, int s0, int len, uint16_t* kept_pos,
+                                          int lane) {
+    if (len == 1) {   // a lone candidate is kept
+        if (lane == 0) s[s0] |= 1u;
+        return 1;
+    }
+    if (len <= 64) return select_run_k<1, STAGED>(p, s, s_box, s_tmp, s_pre, s0, len, kept_pos, lane);
+    if (len <= 128) return select_run_k<2, STAGED>(p, s, s_box, s_tmp, s_pre, s0, len, kept_pos, lane);
+    if (len <= 256) return select_run_k<4, STAGED>(p, s, s_box, s_tmp, s_pre, s0, len, kept_pos, lane);
+    return select_run_k<8, STAGED>(p, s, s_box, s_tmp, s_pre, s0, len, kept_pos, lane);
+}
+
+// Decode group holding compact position i: the last g with s_pre[g] <= i
+// (binary search over s_pre[0 .. groups], s_pre[groups] = n > i).
+__device__ __forceinline__ int group_of(const uint16_t* s_pre, int groups, int i) {
+    int lo = 0, hi = groups;   // s_pre[lo] <= i < s_pre[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)s_pre[mid] <= i) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Keys (and, with STAGED, boxes) of compact positions 0 .. n-1: each thread
+// takes positions tid, tid + NT, ..., finds each one's slot and issues the
+// loads of up to four positions before storing any.
+template <int NT, bool STAGED>
+__device__ __forceinline__ void gather(const DetParams& p, const uint64_t* __restrict__ keys, uint64_t* s,
+                                       float4* s_tmp, const uint16_t* s_pre, int groups, int n, int tid) {
+    for (int i0 = tid; i0 < n; i0 += 4 * NT) {
+        int sl[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * NT;
+            sl[u] = 0;
+            if (i < n) {
+                const int g = group_of(s_pre, groups, i);
+                sl[u] = g * kDecodeBlock + (i - (int)s_pre[g]);
+            }
+        }
+        uint64_t k0 = keys[sl[0]], k1 = keys[sl[1]], k2 = keys[sl[2]], k3 = keys[sl[3]];
+        float4 b0, b1, b2, b3;
+        if (STAGED) {
+            b0 = p.boxes[sl[0]];
+            b1 = p.boxes[sl[1]];
+            b2 = p.boxes[sl[2]];
+            b3 = p.boxes[sl[3]];
+        }
+        s[i0] = k0;
+        if (STAGED) s_tmp[i0] = b0;
+        if (i0 + NT < n) {
+            s[i0 + NT] = k1;
+            if (STAGED) s_tmp[i0 + NT] = b1;
+        }
+        if (i0 + 2 * NT < n) {
+            s[i0 + 2 * NT] = k2;
+            if (STAGED) s_tmp[i0 + 2 * NT] = b2;
+        }
+        if (i0 + 3 * NT < n) {
+            s[i0 + 3 * NT] = k3;
+            if (STAGED) s_tmp[i0 + 3 * NT] = b3;
+        }
+    }
 }
 
 // Up to this many kept boxes are placed by counting, not sorted.
@@ -443,137 +904,374 @@ __device__ __forceinline__ int count_above(const uint64_t* v, int n, uint64_t x)
     return r;
 }
 
+// Bytes of the suppression kernel's shared region after the keys, run
+// starts and prefix sums: per-wave kept-position lists, or (at other times)
+// the class counters (two 16-bit counters per word) or the kept boxes and
+// positions of a run resolved by all waves.
+__host__ __device__ constexpr int nms_aux_bytes(int max_det, int nc, int waves) {
+    const int lists = waves * max_det * 2;
+    const int hist = ((nc + 1) / 2) * 4;
+    const int coop = max_det * (16 + 4 + 2);
+    const int m = lists > hist ? (lists > coop ? lists : coop) : (hist > coop ? hist : coop);
+    return (m + 15) & ~15;
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void det_nms_kernel(
-    uint32_t* counter, uint64_t* keys, int32_t anchors, int32_t sort_cap, int32_t agnostic,
+    const uint32_t* counts, const uint64_t* keys, int32_t groups, int32_t sort_cap, int32_t agnostic,
     int32_t max_det, const DetParams p) {
 #pragma clang fp contract(off)
-    constexpr int kNmsThreads = NT;
-    constexpr int kNmsWaves = NT / 64;
-    // Dynamic LDS: keys [sort_cap] | run starts [kDetRunCap] | kept positions
-    // [kNmsWaves][max_det].
+    constexpr int W = NT / 64;
+    // Dynamic LDS: keys [sort_cap] | run starts [kRunSlots] | decode prefix
+    // sums [kPreSlots] | aux (nms_aux_bytes).  The keys' region past the
+    // sort size holds the boxes when they fit.
     extern __shared__ uint64_t s_dyn[];
     uint64_t* s = s_dyn;
     uint16_t* s_run = reinterpret_cast<uint16_t*>(s_dyn + sort_cap);
-    uint16_t* s_kept = s_run + kDetRunCap;
-    __shared__ int s_n, s_runs, s_total, s_next;
+    uint16_t* s_pre = s_run + kRunSlots;
+    uint8_t* aux = reinterpret_cast<uint8_t*>(s_pre + kPreSlots);
+    __shared__ uint32_t s_tot[W];
+    __shared__ uint64_t s_alive[W];
+    __shared__ uint32_t s_coop[kCoopCap];   // long class runs: start | length << 16
+    __shared__ int s_n, s_runs, s_total, s_next, s_maxlen, s_kept, s_ncoop;
 
     const int tid = (int)threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const bool any_class = agnostic != 0;
+    [[maybe_unused]] const int mark = 16 * wave;
+#ifdef WS_CLOCK_MARKS
+    // Marks go to LDS and are copied out at the end, so that taking them
+    // adds no global stores for the barriers to wait on.
+    __shared__ uint64_t s_mk[W * 16];
+    if (lane < 16) s_mk[mark + lane] = 0;
+#define NMS_MARK(slot)                                                  \
+    do {                                                                \
+        __builtin_amdgcn_sched_barrier(0);                              \
+        const uint64_t t_ = __builtin_amdgcn_s_memrealtime();           \
+        __builtin_amdgcn_sched_barrier(0);                              \
+        if (lane == 0) s_mk[(slot)] = t_;                               \
+    } while (0)
+#define NMS_MARK_AFTER_LOADS(slot)                       \
+    do {                                                 \
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); \
+        NMS_MARK(slot);                                  \
+    } while (0)
+#define NMS_MARKS_OUT()                                                              \
+    do {                                                                             \
+        if (lane < 16) g_marks[kNmsMarks + mark + lane] = s_mk[mark + lane];         \
+    } while (0)
+#else
+#define NMS_MARK(slot) do {} while (0)
+#define NMS_MARK_AFTER_LOADS(slot) do {} while (0)
+#define NMS_MARKS_OUT() do {} while (0)
+#endif
+    NMS_MARK(mark + 0);
     if (tid == 0) {
-        // Written by the decode kernel's atomics: read as a device-scope
-        // atomic (a vector load), never through the scalar cache.
-        const uint32_t c = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_n = (int)(c < (uint32_t)anchors ? c : (uint32_t)anchors);
-        *counter = 0;   // ready for the next replay's decode
-        s_runs = 0;
         s_total = 0;
-        s_next = kNmsWaves;
+        s_next = W;
+        s_maxlen = 0;
+        s_ncoop = 0;
+    }
+    if (!any_class) {
+        uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
+        for (int w = tid; w < (p.nc + 1) / 2; w += NT) hist[w] = 0;
+    }
+
+    // 0. Candidates per decode workgroup (written by the decode kernel) and
+    //    their prefix sums, by wave 0 (four groups per lane): group g's
+    //    candidates take compact positions s_pre[g] .. s_pre[g + 1] - 1.
+    if (wave == 0) {
+        uint32_t c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int g = lane * 4 + j;
+            c[j] = g < groups ? counts[g] : 0u;
+        }
+        NMS_MARK_AFTER_LOADS(mark + 10);
+        const uint32_t t = c[0] + c[1] + c[2] + c[3];
+        const uint32_t incl = wave_incl_scan(t);
+        uint32_t base = incl - t;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int g = lane * 4 + j;
+            if (g < groups) s_pre[g] = (uint16_t)base;
+            base += c[j];
+        }
+        if (lane == 63) {
+            s_pre[groups] = (uint16_t)incl;
+            s_n = (int)incl;
+        }
     }
     __syncthreads();
     const int n = s_n;   // uniform
+    NMS_MARK(mark + 1);
     if (n == 0) {
         if (tid == 0) {
             p.out->count = 0;
             p.out->candidates = 0;
         }
+        NMS_MARKS_OUT();
         return;
     }
 
-    // 1. Load and sort.
+    // 1. Gather: the keys (and boxes) of every candidate to its compact
+    //    position.  Boxes are staged when the sort space past P has room for
+    //    them twice (by position, and later in rank or bucket order).
     int P = 64;
     while (P < n) P <<= 1;
-    sort_desc<NT>(s, P, tid, keys, n);
-
-    // 2. Class runs (one run of everything when any class suppresses any).
-    for (int e = tid; e < n; e += kNmsThreads)
-        if (e == 0 || key_group(s[e], any_class) != key_group(s[e - 1], any_class))
-            s_run[atomicAdd(&s_runs, 1)] = (uint16_t)e;
+    const bool staged = (int64_t)P + 4 * (int64_t)n <= (int64_t)sort_cap;   // uniform
+    float4* s_box = reinterpret_cast<float4*>(s + P);   // P * 8 is a multiple of 512
+    float4* s_tmp = s_box + n;
+    if (staged) gather<NT, true>(p, keys, s, s_tmp, s_pre, groups, n, tid);
+    else gather<NT, false>(p, keys, s, s_tmp, s_pre, groups, n, tid);
+    NMS_MARK(mark + 11);
     __syncthreads();
-    const int runs = s_runs;
+    NMS_MARK(mark + 2);
 
-    // Longest runs first (up to 64 runs, by one wave): the run starts sorted
-    // ascending give each run's length as the distance to the next start,
-    // then (length, start) sorted descending is the order the waves take
-    // them in.  A start is below 2^14 and a length at most 2^14, so both fit
-    // one 32-bit key.
-    if (!any_class && runs > 1 && runs <= 64) {   // uniform
-        if (wave == 0) {
-            const uint32_t start = lane < runs ? s_run[lane] : 0xFFFFu;
-            const uint32_t asc = wave_sort<false>(start, lane);
-            const uint32_t next = (uint32_t)__shfl_down((int)asc, 1);
-            const uint32_t len = (lane + 1 < runs ? next : (uint32_t)n) - asc;
-            const uint32_t key = lane < runs ? (len << 16) | asc : 0u;
-            const uint32_t ord = wave_sort<true>(key, lane);
-            if (lane < runs) s_run[lane] = (uint16_t)(ord & 0xFFFFu);
+    // 2. Runs.  Class-aware: bucket the keys by class.  Any class: one run.
+    int runs = 1;
+    bool ordered = false;
+    bool run_sort = false;
+    if (!any_class) {
+        constexpr int M = WS_DET_MAX_ANCHORS / NT;
+        constexpr int E = WS_DET_MAX_CLASSES / NT;
+        uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
+        uint16_t* cstart = reinterpret_cast<uint16_t*>(aux);
+        const int nc = p.nc;
+        // 2a. Count each class and take an offset inside it.
+        uint64_t k[M];
+        uint32_t off[M];
+        // (Register arrays, indexed by constants; the uniform break leaves
+        // the unrolled sequence once the positions run out.)
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            if (j * NT >= n) break;
+            const int i = tid + j * NT;
+            k[j] = 0;
+            off[j] = 0;
+            if (i < n) {
+                k[j] = s[i];
+                const int c = key_class(k[j]);
+                const uint32_t sh = (uint32_t)(c & 1) * 16u;
+                off[j] = (atomicAdd(&hist[c >> 1], 1u << sh) >> sh) & 0xFFFFu;
+            }
+        }
+        NMS_MARK(mark + 12);
+        __syncthreads();
+        // 2b. Class starts and run starts: one prefix sum of (count | nonempty
+        //     << 16) over the classes (counts stay below 2^15, so the low
+        //     half never carries).  Up to 256 classes wave 0 does it alone,
+        //     four consecutive classes per lane, while the other waves wait;
+        //     more take the whole workgroup, E per thread.  The class starts
+        //     overwrite the counters once all are read.
+        auto publish = [&](int c, uint32_t cn, uint32_t run) {
+            cstart[c] = (uint16_t)(run & 0xFFFFu);
+            if (cn > 0) {
+                s_run[run >> 16] = (uint16_t)(run & 0xFFFFu);
+                if (cn > (uint32_t)kRunSortMax) s_coop[atomicAdd(&s_ncoop, 1)] = (run & 0xFFFFu) | (cn << 16);
+            }
+        };
+        if (nc <= 256) {   // uniform
+            if (wave == 0) {
+                uint32_t loc[4];
+                uint32_t sum = 0;
+                int maxc = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = lane * 4 + e;
+                    const uint32_t cn = c < nc ? (hist[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu : 0u;
+                    loc[e] = cn | (cn ? 1u << 16 : 0u);
+                    sum += loc[e];
+                    maxc = max(maxc, (int)cn);
+                }
+                const uint32_t incl = wave_incl_scan(sum);
+                wave_lds_sync();   // every counter is read before any start is written
+                uint32_t run = incl - sum;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = lane * 4 + e;
+                    if (c < nc) publish(c, loc[e] & 0xFFFFu, run);
+                    run += loc[e];
+                }
+                if (maxc > 0) atomicMax(&s_maxlen, maxc);
+                if (lane == 63) {
+                    s_runs = (int)(incl >> 16);
+                    s_run[incl >> 16] = (uint16_t)n;   // sentinel: a run ends where the next starts
+                }
+            }
+        } else {
+            uint32_t loc[E];
+            uint32_t sum = 0;
+            int maxc = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int c = tid * E + e;
+                const uint32_t cn = c < nc ? (hist[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu : 0u;
+                loc[e] = cn | (cn ? 1u << 16 : 0u);
+                sum += loc[e];
+                maxc = max(maxc, (int)cn);
+            }
+            uint32_t tot2;
+            uint32_t run = block_excl_scan<NT>(sum, s_tot, tot2, tid);   // all counters are read
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int c = tid * E + e;
+                if (c < nc) publish(c, loc[e] & 0xFFFFu, run);
+                run += loc[e];
+            }
+            if (maxc > 0) atomicMax(&s_maxlen, maxc);
+            if (tid == 0) {
+                s_runs = (int)(tot2 >> 16);
+                s_run[tot2 >> 16] = (uint16_t)n;
+            }
+        }
+        NMS_MARK(mark + 13);
+        __syncthreads();
+        runs = s_runs;
+        // 2c. Scatter into the buckets (boxes too, when staged).
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            if (j * NT >= n) break;
+            const int i = tid + j * NT;
+            if (i < n) {
+                const int pos = cstart[key_class(k[j])] + off[j];
+                s[pos] = k[j];
+                if (staged) s_box[pos] = s_tmp[i];
+            }
+        }
+        NMS_MARK(mark + 14);
+        run_sort = s_maxlen <= kRunSortMax;   // uniform
+        // Longest runs first (up to 64 runs, by one wave): (length, start)
+        // sorted descending; a start is below 2^14 and a length at most 2^14,
+        // so both fit one 32-bit key.  The lengths go to s_run[kRunLen + r].
+        ordered = runs > 1 && runs <= 64;
+        if (ordered && wave == 0) {
+            const uint32_t start = lane < runs ? s_run[lane] : 0u;
+            const uint32_t len = lane < runs ? (uint32_t)s_run[lane + 1] - start : 0u;
+            const uint32_t ord = wave_sort<true>(lane < runs ? (len << 16) | start : 0u, lane);
+            wave_lds_sync();   // every start was read before any is overwritten
+            if (lane < runs) {
+                s_run[lane] = (uint16_t)(ord & 0xFFFFu);
+                s_run[kRunLen + lane] = (uint16_t)(ord >> 16);
+            }
         }
         __syncthreads();
     }
-
-    // 3. Boxes in sorted order, into the LDS the sort left free (when it fits),
-    //    then greedy suppression, one wave per run.
-    float4* s_box = nullptr;
-    if ((int64_t)(sort_cap - P) * (int64_t)sizeof(uint64_t) >= (int64_t)n * (int64_t)sizeof(float4)) {
-        s_box = reinterpret_cast<float4*>(s + P);   // P * 8 is a multiple of 512: 16-byte aligned
-        for (int e = tid; e < n; e += kNmsThreads) s_box[e] = p.boxes[key_anchor(s[e], any_class)];
-        __syncthreads();
-    }
-    uint16_t* kept_pos = s_kept + wave * max_det;
-    int my_kept = 0;
-    // Wave w takes run w first, then whichever run is next when it is done,
-    // so long runs do not queue behind each other on one wave.  (With one
-    // run, wave 0 resolves it and its kept list is read below.)
+    NMS_MARK(mark + 3);
+    auto run_len = [&](int r) -> int {
+        return ordered ? (int)s_run[kRunLen + r] : (int)s_run[r + 1] - (int)s_run[r];
+    };
+    // Each wave takes run `wave` first, then whichever run is next when it is
+    // done, so long runs do not queue behind each other on one wave.
     auto next_run = [&]() -> int {
         int r = 0;
         if (lane == 0) r = atomicAdd(&s_next, 1);
         return __builtin_amdgcn_readfirstlane(r);
     };
-    if (s_box) {
-        for (int r = wave; r < runs; r = next_run())
-            my_kept = resolve_run<true>(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
-    } else {
-        for (int r = wave; r < runs; r = next_run())
-            my_kept = resolve_run<false>(p, s, s_box, n, s_run[r], kept_pos, any_class, lane);
-    }
-    __syncthreads();
+    uint16_t* kept_pos = reinterpret_cast<uint16_t*>(aux) + wave * max_det;
+    float4* k_box = reinterpret_cast<float4*>(aux);
+    float* k_area = reinterpret_cast<float*>(k_box + max_det);
+    uint16_t* k_pos = reinterpret_cast<uint16_t*>(k_area + max_det);
+    int any_kept = 0;
+#ifdef WS_CLOCK_MARKS
+    int runs_done = 0;
+#define WS_COUNT_RUN() ++runs_done
+#else
+#define WS_COUNT_RUN()
+#endif
 
-    // 4. Kept boxes in rank order.  With one run, that is its kept list
-    //    (wave 0 resolved it).  Otherwise gather the flagged keys of all runs;
-    //    up to kRankByCountMax of them are placed by counting (keys are
-    //    distinct, so a key's place is the number of kept keys above it),
-    //    more are sorted.
-    int total;
-    if (any_class) {
-        if (tid == 0) s_total = my_kept;
-        __syncthreads();
-        total = s_total;
+    if (run_sort) {
+        // 3a. Class runs of at most kRunSortMax: one wave holds a run in its
+        //     registers and resolves it by selection (no sort).
+        NMS_MARK(mark + 4);
+        for (int r = wave; r < runs; r = next_run()) {
+            const int start = s_run[r];
+            const int len = run_len(r);
+            if (staged) select_run<true>(p, s, s_box, s_tmp, s_pre, start, len, kept_pos, lane);
+            else select_run<false>(p, s, s_box, s_tmp, s_pre, start, len, kept_pos, lane);
+            WS_COUNT_RUN();
+        }
     } else {
-        // 512 positions at a time: every thread reads its key, then the
-        // flagged ones are appended.  A slot is below the number of keys
-        // flagged so far, hence below every position still to be read.
-        for (int base = 0; base < n; base += kNmsThreads) {   // uniform
+        // 3b. One sort of everything (class-major order in class-aware mode,
+        //     so the buckets stay where they are), boxes staged in sorted
+        //     order, then the long runs by all waves and the rest one wave per
+        //     run.
+        for (int e = n + tid; e < P; e += NT) s[e] = 0;
+        __syncthreads();
+        sort_desc<NT>(s, P, tid);
+        if (staged) {
+            for (int e = tid; e < n; e += NT) {
+                const int slot = key_slot(s[e], any_class);
+                s_box[e] = s_tmp[s_pre[slot >> 6] + (slot & 63)];
+            }
+            __syncthreads();
+        }
+        NMS_MARK(mark + 4);
+        if (any_class) {
+            any_kept = staged
+                ? coop_resolve<true, NT>(p, s, s_box, 0, n, k_box, k_area, k_pos, s_alive, &s_kept, true, tid)
+                : coop_resolve<false, NT>(p, s, s_box, 0, n, k_box, k_area, k_pos, s_alive, &s_kept, true, tid);
+        } else {
+            const int ncoop = s_ncoop;
+            for (int c = 0; c < ncoop; ++c) {
+                const int start = (int)(s_coop[c] & 0xFFFFu);
+                const int len = (int)(s_coop[c] >> 16);
+                if (staged)
+                    coop_resolve<true, NT>(p, s, s_box, start, len, k_box, k_area, k_pos, s_alive, &s_kept, false, tid);
+                else
+                    coop_resolve<false, NT>(p, s, s_box, start, len, k_box, k_area, k_pos, s_alive, &s_kept, false, tid);
+            }
+            for (int r = wave; r < runs; r = next_run()) {
+                const int len = run_len(r);
+                if (len > kRunSortMax) continue;
+                if (staged) resolve_run<true>(p, s, s_box, s_run[r], len, kept_pos, false, lane);
+                else resolve_run<false>(p, s, s_box, s_run[r], len, kept_pos, false, lane);
+                WS_COUNT_RUN();
+            }
+        }
+    }
+#undef WS_COUNT_RUN
+    NMS_MARK(mark + 5);
+#ifdef WS_CLOCK_MARKS
+    if (lane == 0) s_mk[mark + 9] = (uint64_t)runs_done;
+#endif
+    __syncthreads();
+    NMS_MARK(mark + 6);
+
+    // 4. Kept boxes in rank order.  Any class: the kept list, in rank order
+    //    already.  Otherwise gather the flagged keys of all runs; up to
+    //    kRankByCountMax of them are placed by counting (keys are distinct,
+    //    so a key's place is the number of kept keys above it), more are
+    //    sorted.
+    int kept_total;
+    if (any_class) {
+        kept_total = any_kept;   // uniform: every wave took part
+    } else {
+        // NT positions at a time: every thread reads its key, then the flagged
+        // ones are appended.  A slot is below the number of keys flagged so
+        // far, hence below every position still to be read.
+        for (int base = 0; base < n; base += NT) {   // uniform
             const int e = base + tid;
             const uint64_t k = e < n ? s[e] : 0;
             __syncthreads();
             if (k & 1u) s[atomicAdd(&s_total, 1)] = to_rank_key(k);
         }
         __syncthreads();
-        total = s_total;
-        if (total > kRankByCountMax) {   // uniform
+        kept_total = s_total;
+        if (kept_total > kRankByCountMax) {   // uniform
             int P2 = 64;
-            while (P2 < total) P2 <<= 1;
-            for (int e = total + tid; e < P2; e += kNmsThreads) s[e] = 0;
+            while (P2 < kept_total) P2 <<= 1;
+            for (int e = kept_total + tid; e < P2; e += NT) s[e] = 0;
             __syncthreads();
             sort_desc<NT>(s, P2, tid);
         }
     }
+    NMS_MARK(mark + 7);
 
     // 5. The first max_det, mapped to source pixels, to the mapped slot.
-    const int count = min(total, max_det);
-    auto emit = [&](uint64_t k, int q) {
-        const float4 b = p.boxes[key_anchor(k, true)];
+    const int count = min(kept_total, max_det);
+    auto emit = [&](uint64_t k, const float4 b, int q) {
         ws_det d;
         d.x1 = to_source(b.x, p.left, p.sx, p.src_w);
         d.y1 = to_source(b.y, p.top, p.sy, p.src_h);
@@ -583,76 +1281,119 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         d.class_id = (int32_t)((k >> 7) & 0xFFFu);
         p.out->det[q] = d;
     };
-    if (!any_class && total <= kRankByCountMax) {
-        for (int t = tid; t < total; t += kNmsThreads) {
+    // Box of a rank key: staged by compact position, else by slot (separate
+    // loops, so each loads from one address space).
+    auto staged_box = [&](uint64_t k) {
+        const int slot = key_slot(k, true);
+        return s_tmp[s_pre[slot >> 6] + (slot & 63)];
+    };
+    auto global_box = [&](uint64_t k) { return p.boxes[key_slot(k, true)]; };
+    if (any_class) {
+        for (int q = tid; q < count; q += NT) emit(s[k_pos[q]] & ~1ull, k_box[q], q);
+    } else if (kept_total <= kRankByCountMax) {
+        for (int t = tid; t < kept_total; t += NT) {
             const uint64_t x = s[t];
-            const int r = count_above(s, total, x);
-            if (r < count) emit(x, r);
+            const int r = count_above(s, kept_total, x);
+            if (r < count) {
+                if (staged) emit(x, staged_box(x), r);
+                else emit(x, global_box(x), r);
+            }
         }
+    } else if (staged) {
+        for (int q = tid; q < count; q += NT) emit(s[q], staged_box(s[q]), q);
     } else {
-        for (int q = tid; q < count; q += kNmsThreads)
-            emit(any_class ? (s[s_kept[q]] & ~1ull) : s[q], q);
+        for (int q = tid; q < count; q += NT) emit(s[q], global_box(s[q]), q);
     }
     if (tid == 0) {
         p.out->count = count;
         p.out->candidates = n;
     }
+    NMS_MARK(mark + 8);
+    NMS_MARKS_OUT();
+#undef NMS_MARK
+#undef NMS_MARK_AFTER_LOADS
+#undef NMS_MARKS_OUT
 }
 
-static_assert(WS_DET_MAX_ANCHORS <= 16384, "anchors must fit the 14-bit key field");
-static_assert(WS_DET_MAX_CLASSES <= 4096, "classes must fit the 12-bit key field");
-static_assert(WS_DET_MAX_ANCHORS % kDetNmsThreads == 0 && WS_DET_MAX_ANCHORS % kNmsWideThreads == 0,
-              "gather loop covers every key");
+// Dynamic LDS one workgroup may take: 160 KiB on gfx950, less room for the
+// kernels' static LDS (under 1 KiB; 3 KiB in builds with clock marks, which
+// do not take lanes at the limits of ws.h).
+#ifdef WS_CLOCK_MARKS
+constexpr int kNmsLdsCap = 160 * 1024 - 3 * 1024;
+#else
+constexpr int kNmsLdsCap = 160 * 1024 - 1024;
+#endif
+
+constexpr int nms_lds_bytes(int sort_cap, int max_det, int nc, int threads) {
+    return sort_cap * (int)sizeof(uint64_t) + (kRunSlots + kPreSlots) * (int)sizeof(uint16_t) +
+           nms_aux_bytes(max_det, nc, threads / 64);
+}
+
+#ifndef WS_CLOCK_MARKS
+static_assert(nms_lds_bytes(WS_DET_MAX_ANCHORS, WS_DET_MAX_DET, WS_DET_MAX_CLASSES, kNmsNarrow) <=
+                  kNmsLdsCap,
+              "the narrow suppression kernel fits every lane within the limits of ws.h");
+#endif
+
+int nms_threads(int sort_cap, int max_det, int nc) {
+    if (nms_lds_bytes(sort_cap, max_det, nc, kNmsWide) <= kNmsLdsCap) return kNmsWide;
+    if (nms_lds_bytes(sort_cap, max_det, nc, kNmsNarrow) <= kNmsLdsCap) return kNmsNarrow;
+    return 0;
+}
 
 }  // namespace
 
-namespace {
-int nms_lds_bytes(int sort_cap, int max_det, int threads) {
-    return sort_cap * (int)sizeof(uint64_t) + kDetRunCap * (int)sizeof(uint16_t) +
-           (threads / 64) * max_det * (int)sizeof(uint16_t);
-}
-
-// Dynamic LDS one workgroup may take: 160 KiB on gfx950, less the kernel's
-// few bytes of static LDS.
-constexpr int kNmsLdsCap = 160 * 1024 - 64;
-
-int nms_threads(int sort_cap, int max_det) {
-    return nms_lds_bytes(sort_cap, max_det, kNmsWideThreads) <= kNmsLdsCap ? kNmsWideThreads
-                                                                           : kDetNmsThreads;
-}
-}  // namespace
-
-int det_nms_lds_bytes(int sort_cap, int max_det) {
-    return nms_lds_bytes(sort_cap, max_det, nms_threads(sort_cap, max_det));
+int det_nms_lds_bytes(int sort_cap, int max_det, int nc) {
+    const int nt = nms_threads(sort_cap, max_det, nc);
+    return nt ? nms_lds_bytes(sort_cap, max_det, nc, nt) : 0;
 }
 
 hipError_t set_detect_attributes() {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(det_nms_kernel<kDetNmsThreads>),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        nms_lds_bytes(WS_DET_MAX_ANCHORS, WS_DET_MAX_DET, kDetNmsThreads));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(det_nms_kernel<kNmsNarrow>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kNmsLdsCap);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(det_nms_kernel<kNmsWideThreads>),
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(det_nms_kernel<kNmsWide>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kNmsLdsCap);
     return e;
 }
 
-hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream) {
-    hipLaunchKernelGGL(det_decode_kernel, dim3((unsigned)decode_groups), dim3(kDecodeThreads), 0,
-                       stream, p.head, p.anchors, p.nc, p);
+hipError_t launch_detect(const DetParams& p, hipStream_t stream) {
+    const int nt = nms_threads(p.sort_cap, p.max_det, p.nc);
+    if (nt == 0 || p.groups < 1 || p.groups > kDetMaxGroups ||
+        (int64_t)p.groups * kDetDecodeAnchors < (int64_t)p.anchors || p.sort_cap < p.anchors)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(det_decode_kernel, dim3((unsigned)p.groups), dim3(kDecodeThreads), 0, stream,
+                       p.head, p.anchors, p.nc, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nt = nms_threads(p.sort_cap, p.max_det);
-    const unsigned lds = (unsigned)nms_lds_bytes(p.sort_cap, p.max_det, nt);
+    const unsigned lds = (unsigned)nms_lds_bytes(p.sort_cap, p.max_det, p.nc, nt);
     auto nms = [&](auto kernel, int threads) {
-        hipLaunchKernelGGL(kernel, dim3(1), dim3(threads), lds, stream, p.counter, p.keys,
-                           p.anchors, p.sort_cap, p.agnostic, p.max_det, p);
+        hipLaunchKernelGGL(kernel, dim3(1), dim3(threads), lds, stream, p.counts, p.keys, p.groups,
+                           p.sort_cap, p.agnostic, p.max_det, p);
     };
-    if (nt == kNmsWideThreads)
-        nms(det_nms_kernel<kNmsWideThreads>, kNmsWideThreads);
+    if (nt == kNmsWide)
+        nms(det_nms_kernel<kNmsWide>, kNmsWide);
     else
-        nms(det_nms_kernel<kDetNmsThreads>, kDetNmsThreads);
+        nms(det_nms_kernel<kNmsNarrow>, kNmsNarrow);
     return hipGetLastError();
 }
 
 }  // namespace ws
+
+#ifdef WS_CLOCK_MARKS
+// Instrumented builds only: copy out (or clear) the detection kernels' marks.
+extern "C" int ws_debug_detect_marks(uint64_t* host, size_t n, int32_t clear) {
+    if (n > (size_t)ws::kMarkSlots) n = ws::kMarkSlots;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess && host && n)
+        e = hipMemcpyFromSymbol(host, HIP_SYMBOL(ws::g_marks), n * sizeof(uint64_t), 0,
+                                hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(ws::g_marks));
+        if (e == hipSuccess) e = hipMemset(p, 0, sizeof(uint64_t) * ws::kMarkSlots);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+    }
+    return e == hipSuccess ? 0 : -6;
+}
+#endif

@@ -1,5 +1,6 @@
-// ws_kernels.h -- launch parameters and launchers of the pipeline's kernels
-// (ws_preprocess.hip, ws_topk.hip, ws_detect.hip).
+// ws_kernels.h -- launch parameters and launchers of the preprocess and
+// Top-K kernels (ws_preprocess.hip, ws_topk.hip); detection's are in
+// ws_detect.h.
 // Internal to the library (not part of the C ABI).
 #pragma once
 
@@ -52,43 +53,11 @@ struct TopkParams {
     uint2* result;           // [k] {score bits, index}, device view of the slot
 };
 
-// Detection decode + greedy NMS over a YOLO-style head (layout in ws.h).
-struct DetParams {
-    const float* head;       // [4 * 16 + nc][anchors], 16-byte aligned
-    int32_t anchors;         // A <= WS_DET_MAX_ANCHORS
-    int32_t nc;
-    int32_t level_end[3];    // anchor index where the stride-8/16/32 grids end
-    int32_t grid_w[3];       // cells per row of each grid
-    float conf;              // candidate: best probability > conf
-    float iou;               // suppression: IoU > iou (binary32 IoU), decided as below
-    double iou_mid;          // midpoint of iou and the next binary32 above it
-    int32_t iou_tie_up;      // an IoU exactly at iou_mid rounds up (iou's significand is odd)
-    int32_t max_det;
-    int32_t agnostic;
-    float4* boxes;           // [anchors] network-input xyxy, written for candidates
-    uint64_t* keys;          // [anchors] compact candidate keys
-    uint32_t* counter;       // candidates appended; zero between replays
-    int32_t sort_cap;        // keys the suppression kernel's LDS holds: a power of two >= anchors
-    float left, top;         // image region origin in the network input
-    float sx, sy;            // source pixels per network pixel (binary32 of W/rw, H/rh)
-    float src_w, src_h;      // clip bounds
-    ws_det_result* out;      // device view of the mapped result slot
-};
-
 hipError_t launch_preprocess(const PreParams& p, int groups, int block, int lds_bytes,
                              hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 // Raise the dynamic LDS limit of the staged preprocess kernels.
 hipError_t set_preprocess_attributes();
-// Decode (one thread per anchor) then NMS (one workgroup), in stream order.
-hipError_t launch_detect(const DetParams& p, int decode_groups, hipStream_t stream);
-// Dynamic LDS of the suppression kernel, and raising its limit (once per process).
-constexpr int kDetNmsThreads = 512;
-constexpr int kDetDecodeAnchors = 64;            // anchors per decode workgroup
-constexpr int kDetRunCap = WS_DET_MAX_CLASSES;   // class runs: at most one per class
-int det_nms_lds_bytes(int sort_cap, int max_det);
-hipError_t set_detect_attributes();
-
 constexpr int kTopkMaxThreads = 256;   // 4 wave64s: one per SIMD
 
 }  // namespace ws

@@ -20,6 +20,7 @@
 
 #include "ws.h"
 #include "ws_bench.h"
+#include "ws_detect.h"
 #include "ws_kernels.h"
 #include "ws_params.h"
 #include "ws_plan.h"
@@ -52,7 +53,7 @@ struct ws_lane {
     bool own_det_head = false;
     float4* det_boxes = nullptr;
     uint64_t* det_keys = nullptr;
-    uint32_t* det_counter = nullptr;
+    uint32_t* det_counts = nullptr;
     ws_det_result* det_host = nullptr;  // mapped detection result slot
     ws_det_result* det_dev = nullptr;   // its device view
     ws::PreParams pre{};
@@ -103,7 +104,7 @@ hipError_t launch_all(ws_lane* L) {
     if (e != hipSuccess) return e;
     if (L->cfg.num_scores > 0) e = ws::launch_topk(L->tk, L->stream);
     if (e != hipSuccess) return e;
-    if (L->plan.det_anchors > 0) e = ws::launch_detect(L->det, L->plan.det_decode_groups, L->stream);
+    if (L->plan.det_anchors > 0) e = ws::launch_detect(L->det, L->stream);
     return e;
 }
 
@@ -124,7 +125,7 @@ void release(ws_lane* L) {
     if (L->own_det_head && L->det_head) hipFree(L->det_head);
     if (L->det_boxes) hipFree(L->det_boxes);
     if (L->det_keys) hipFree(L->det_keys);
-    if (L->det_counter) hipFree(L->det_counter);
+    if (L->det_counts) hipFree(L->det_counts);
     if (L->det_host) hipHostFree(L->det_host);
     delete L;
 }
@@ -196,7 +197,8 @@ void fill_params(ws_lane* L) {
     d.agnostic = c.det_agnostic;
     d.boxes = L->det_boxes;
     d.keys = L->det_keys;
-    d.counter = L->det_counter;
+    d.groups = P.det_decode_groups;
+    d.counts = L->det_counts;
     d.sort_cap = P.det_sort_cap;
     d.left = (float)P.region.left;
     d.top = (float)P.region.top;
@@ -325,7 +327,12 @@ int build(ws_lane* L) {
         if (P.lds_bytes > 64 * 1024 || P.topk_keys_per_lane == 32) return fail(L, e, WS_E_HIP);
     }
     // The suppression kernel keeps every candidate key in LDS.
-    if (P.det_anchors > 0) WS_HIP(ws::set_detect_attributes(), WS_E_HIP);
+    if (P.det_anchors > 0) {
+        // Every lane within the limits of ws.h fits (checked at compile time).
+        if (ws::det_nms_lds_bytes(P.det_sort_cap, c.det_max_det, c.det_classes) == 0)
+            return fail(L, hipSuccess, WS_E_INVALID_ARG);
+        WS_HIP(ws::set_detect_attributes(), WS_E_HIP);
+    }
 
     // ---- buffers ---------------------------------------------------------
     if (c.input_mode == WS_INPUT_MAPPED_HOST) {
@@ -400,9 +407,10 @@ int build(ws_lane* L) {
         L->det_boxes = static_cast<float4*>(bx);
         WS_TRY(dev_alloc(L, &ky, A * sizeof(uint64_t)));
         L->det_keys = static_cast<uint64_t*>(ky);
-        WS_TRY(dev_alloc(L, &cn, sizeof(uint32_t)));
-        L->det_counter = static_cast<uint32_t*>(cn);
-        WS_HIP(hipMemset(L->det_counter, 0, sizeof(uint32_t)), WS_E_HIP);
+        const size_t G = (size_t)P.det_decode_groups;
+        WS_TRY(dev_alloc(L, &cn, G * sizeof(uint32_t)));
+        L->det_counts = static_cast<uint32_t*>(cn);
+        WS_HIP(hipMemset(L->det_counts, 0, G * sizeof(uint32_t)), WS_E_HIP);
         void *h = nullptr, *d = nullptr;
         WS_TRY(mapped_alloc(L, &h, &d, sizeof(ws_det_result)));
         L->det_host = static_cast<ws_det_result*>(h);
@@ -600,7 +608,7 @@ hipError_t launch_stage_on(ws_lane* L, int32_t stage, hipStream_t stream) {
         return ws::launch_preprocess(L->pre, L->plan.pre_groups, L->plan.pre_block,
                                      L->plan.lds_bytes, stream);
     if (stage == WS_STAGE_TOPK) return ws::launch_topk(L->tk, stream);
-    return ws::launch_detect(L->det, L->plan.det_decode_groups, stream);
+    return ws::launch_detect(L->det, stream);
 }
 
 hipError_t launch_stage(ws_lane* L, int32_t stage) { return launch_stage_on(L, stage, L->stream); }

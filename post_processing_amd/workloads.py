@@ -303,4 +303,32 @@ def detect_small(seed: int) -> Workload:
                     114.0, 0, frames, None, head=head, det=det)
 
 
+def uniform_head(seed: int, nw: int, nh: int, nc: int, conf: float, iou: float, max_det: int,
+                 agnostic: bool = False, box_scale: float = 1.5) -> Workload:
+    """A head whose class probabilities are uniform in [0, 1): about
+    1 - conf**nc of the anchors become candidates (each anchor's best class
+    is the largest of nc uniforms), with box logits N(0, box_scale).  Small
+    box_scale flattens every side's DFL softmax, so all boxes are about 15
+    cells wide and overlap their neighbours heavily."""
+    rng = np.random.default_rng(50_000 + seed)
+    A = head_anchor_grid(nw, nh)[0].size
+    head = np.empty((4 * HEAD_BINS + nc, A), np.float32)
+    head[:4 * HEAD_BINS] = rng.normal(0.0, box_scale, (4 * HEAD_BINS, A))
+    head[4 * HEAD_BINS:] = rng.uniform(0.0, 1.0, (nc, A))
+    frames = rng.integers(0, 256, size=(1, nh, nw, 3), dtype=np.uint8)
+    return Workload(f"uniform_head{seed}", nw, nh, nw, nh, RESIZE, (0.0, 0.0, 0.0),
+                    (1.0, 1.0, 1.0), 114.0, 0, frames, None, head=head,
+                    det=dict(nc=nc, conf=conf, iou=iou, max_det=max_det, agnostic=agnostic))
+
+
+def dense_detect(agnostic: bool = True) -> Workload:
+    """The suppression stress case: a 1024x512 network (10,752 anchors), 80
+    uniform classes with conf 0.75 (every anchor is a candidate), IoU > 0.3,
+    up to 1,024 boxes, heavily overlapping boxes; by default boxes of any
+    class suppress each other, so all candidates form one run."""
+    w = uniform_head(2, 1024, 512, 80, 0.75, 0.3, 1024, agnostic=agnostic, box_scale=0.3)
+    w.name = "dense_detect_1024x512_10752_anchors_" + ("any_class" if agnostic else "by_class")
+    return w
+
+
 ALL_CONFIGS = {"c1": c1, "c2": c2, "c3": c3, "c4": c4}

@@ -70,17 +70,7 @@ def test_detect_small_random(gpu_lib, seed):
 
 
 def _uniform_head_workload(seed, nw, nh, nc, conf, iou, max_det, agnostic=False, box_scale=1.5):
-    """A head whose class probabilities are uniform in [0, 1): about
-    (1 - conf) of the anchors become candidates, with random boxes."""
-    rng = np.random.default_rng(50_000 + seed)
-    A = wl.head_anchor_grid(nw, nh)[0].size
-    head = np.empty((64 + nc, A), F32)
-    head[:64] = rng.normal(0.0, box_scale, (64, A))
-    head[64:] = rng.uniform(0.0, 1.0, (nc, A))
-    frames = rng.integers(0, 256, size=(1, nh, nw, 3), dtype=np.uint8)
-    return wl.Workload(f"uniform_head{seed}", nw, nh, nw, nh, wl.RESIZE, (0.0, 0.0, 0.0),
-                       (1.0, 1.0, 1.0), 114.0, 0, frames, None, head=head,
-                       det=dict(nc=nc, conf=conf, iou=iou, max_det=max_det, agnostic=agnostic))
+    return wl.uniform_head(seed, nw, nh, nc, conf, iou, max_det, agnostic, box_scale)
 
 
 # Candidate counts across the suppression kernel's sort sizes (1024 .. 16384

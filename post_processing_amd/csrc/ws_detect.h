@@ -47,7 +47,7 @@ struct DetParams {
 hipError_t launch_detect(const DetParams& p, hipStream_t stream);
 // Dynamic LDS of the suppression kernel for a lane's sizes; 0 if no
 // workgroup size fits (never for sizes within the ws.h limits).
-int det_nms_lds_bytes(int sort_cap, int max_det, int nc);
+int det_nms_lds_bytes(int sort_cap, int max_det, int nc, bool any_class);
 // Raise the suppression kernels' dynamic LDS limit (once per process).
 hipError_t set_detect_attributes();
 

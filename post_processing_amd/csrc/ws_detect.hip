@@ -106,6 +106,8 @@ constexpr int kRunSlots = kRunCap + 1 + 64 + 7;
 constexpr int kPreSlots = kDetMaxGroups + 8;
 // Long runs resolved by all waves: at most WS_DET_MAX_ANCHORS / 513.
 constexpr int kCoopCap = 32;
+// NaN boxes past the kept list of a run resolved by all waves.
+constexpr int kCoopPad = 8;
 
 static_assert(WS_DET_MAX_ANCHORS <= 16384, "slots must fit the 14-bit key field");
 static_assert(WS_DET_MAX_CLASSES <= 4096, "classes must fit the 12-bit key field");
@@ -191,6 +193,39 @@ __device__ __forceinline__ bool iou_above(float4 a, float area_a, float4 b, floa
     const double in = (double)inter;
     // Bitwise, not short-circuit: every compare is evaluated, no branches.
     return (uni > 0.0f) & ((in > bound) | (tie_up & (in == bound)));
+}
+
+// v_min_f32 / v_max_f32 as written: the compiler would first quiet every
+// operand it cannot prove canonical (one more instruction per value read
+// from memory).  Boxes are results of arithmetic, never signalling NaNs, and
+// on quiet NaNs these give what fminf / fmaxf give.
+__device__ __forceinline__ float min_raw(float a, float b) {
+    float r;
+    asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// iou_above with the tie rule fixed at compile time, for the screening
+// loops.  Candidate boxes have x2 >= x1 and y2 >= y1 (the DFL distances are
+// expectations over non-negative bins), so union >= 0, and union == 0 gives
+// bound == 0 == inter, which "inter > bound" already rejects; only the tie
+// case needs union > 0 spelled out.  NaN boxes compare false everywhere.
+template <bool TIE>
+__device__ __forceinline__ bool iou_above_fixed(float4 a, float area_a, float4 b, float area_b, double mid) {
+#pragma clang fp contract(off)
+    const float iw = max_raw(0.0f, min_raw(a.z, b.z) - max_raw(a.x, b.x));
+    const float ih = max_raw(0.0f, min_raw(a.w, b.w) - max_raw(a.y, b.y));
+    const float inter = iw * ih;
+    const float uni = (area_a + area_b) - inter;
+    const double bound = mid * (double)uni;
+    const double in = (double)inter;
+    if (TIE) return (in > bound) | ((in == bound) & (uni > 0.0f));
+    return in > bound;
 }
 
 // Network-input pixels -> source pixels, clipped to [0, hi].
@@ -508,21 +543,30 @@ __device__ __forceinline__ float4 box_at(const DetParams& p, const float4* s_box
 // test so that the U tests overlap (a last step short of U boxes repeats
 // box k1 - 1, which changes nothing).  kept(j, box, area) gives kept box j
 // and its area (wave-uniform j).
-template <int U, typename Kept>
-__device__ __forceinline__ uint64_t screen(uint64_t alive, float4 box, float area, int k0, int k1, Kept kept,
-                                          double mid, bool tie_up, int& steps) {
+template <int U, bool TIE, bool PADDED, typename Kept>
+__device__ __forceinline__ uint64_t screen_t(uint64_t alive, float4 box, float area, int k0, int k1, Kept kept,
+                                            double mid, int& steps) {
     for (int k = k0; k < k1 && alive != 0; k += U) {
         ++steps;
         float4 a[U];
         float aa[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) kept(min(k + u, k1 - 1), a[u], aa[u]);
+        for (int u = 0; u < U; ++u) kept(PADDED ? k + u : min(k + u, k1 - 1), a[u], aa[u]);
         bool sup = false;
 #pragma unroll
-        for (int u = 0; u < U; ++u) sup |= iou_above(a[u], aa[u], box, area, mid, tie_up);
+        for (int u = 0; u < U; ++u) sup |= iou_above_fixed<TIE>(a[u], aa[u], box, area, mid);
         alive &= ~(uint64_t)__ballot(sup);
     }
     return alive;
+}
+
+// PADDED: kept(j) is defined (a box that suppresses nothing) up to k1 + U - 1,
+// so a short last step reads past k1 instead of repeating box k1 - 1.
+template <int U, bool PADDED = false, typename Kept>
+__device__ __forceinline__ uint64_t screen(uint64_t alive, float4 box, float area, int k0, int k1, Kept kept,
+                                          double mid, bool tie_up, int& steps) {
+    return tie_up ? screen_t<U, true, PADDED>(alive, box, area, k0, k1, kept, mid, steps)
+                  : screen_t<U, false, PADDED>(alive, box, area, k0, k1, kept, mid, steps);
 }
 
 // Greedy suppression of one run s[s0, s0 + len) by one wave, in rank order
@@ -624,11 +668,19 @@ __device__ __forceinline__ int coop_resolve(const DetParams& p, uint64_t* s, con
     const double mid = p.iou_mid;
     const bool tie_up = p.iou_tie_up != 0;
     const int end = s0 + len;
-    // Uniform LDS addresses: broadcast reads.
+    // Uniform LDS addresses: broadcast reads.  Entries past the kept ones
+    // hold NaN boxes, which suppress nothing (the screening reads up to
+    // seven past the end).
     auto kept = [&](int j, float4& a, float& aa) {
         a = k_box[j];
         aa = k_area[j];
     };
+    const float qnan = __uint_as_float(0x7FC00000u);
+    for (int j = tid; j < p.max_det + kCoopPad; j += NT) {
+        k_box[j] = make_float4(qnan, qnan, qnan, qnan);
+        k_area[j] = qnan;
+    }
+    __syncthreads();
     int K = 0;
     [[maybe_unused]] int steps = 0, round_steps = 0;
     WS_PROF_DECL;
@@ -641,7 +693,7 @@ __device__ __forceinline__ int coop_resolve(const DetParams& p, uint64_t* s, con
             float4 box = make_float4(0.f, 0.f, 0.f, 0.f);
             if (valid) box = box_at<STAGED>(p, s_box, e, s[e], any_class);
             const uint64_t alive =
-                screen<8>((uint64_t)__ballot(valid), box, box_area(box), 0, K0, kept, mid, tie_up, steps);
+                screen<8, true>((uint64_t)__ballot(valid), box, box_area(box), 0, K0, kept, mid, tie_up, steps);
             if (lane == 0) s_alive[wave] = alive;
         }
         WS_PROF_T(tb);
@@ -664,7 +716,7 @@ __device__ __forceinline__ int coop_resolve(const DetParams& p, uint64_t* s, con
                 const float area = box_area(box);
                 WS_PROF_WAIT();
                 WS_PROF_T(t1);
-                uint64_t alive = screen<4>(s_alive[b], box, area, K0, K, kept, mid, tie_up, round_steps);
+                uint64_t alive = screen<4, true>(s_alive[b], box, area, K0, K, kept, mid, tie_up, round_steps);
                 WS_PROF_T(t2);
                 WS_PROF_ACC(0, t1 - t0);
                 WS_PROF_ACC(7, t2 - t1);
@@ -906,12 +958,13 @@ __device__ __forceinline__ int count_above(const uint64_t* v, int n, uint64_t x)
 
 // Bytes of the suppression kernel's shared region after the keys, run
 // starts and prefix sums: per-wave kept-position lists, or (at other times)
-// the class counters (two 16-bit counters per word) or the kept boxes and
-// positions of a run resolved by all waves.
-__host__ __device__ constexpr int nms_aux_bytes(int max_det, int nc, int waves) {
-    const int lists = waves * max_det * 2;
-    const int hist = ((nc + 1) / 2) * 4;
-    const int coop = max_det * (16 + 4 + 2);
+// the class counters (two 16-bit counters per word) or the kept boxes, areas
+// and positions of a run resolved by all waves (the only use in any-class
+// mode).
+__host__ __device__ constexpr int nms_aux_bytes(int max_det, int nc, int waves, bool any_class) {
+    const int lists = any_class ? 0 : waves * max_det * 2;
+    const int hist = any_class ? 0 : ((nc + 1) / 2) * 4;
+    const int coop = (max_det + kCoopPad) * (16 + 4) + max_det * 2;
     const int m = lists > hist ? (lists > coop ? lists : coop) : (hist > coop ? hist : coop);
     return (m + 15) & ~15;
 }
@@ -941,16 +994,14 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     const bool any_class = agnostic != 0;
     [[maybe_unused]] const int mark = 16 * wave;
 #ifdef WS_CLOCK_MARKS
-    // Marks go to LDS and are copied out at the end, so that taking them
-    // adds no global stores for the barriers to wait on.
-    __shared__ uint64_t s_mk[W * 16];
-    if (lane < 16) s_mk[mark + lane] = 0;
+    // Marks stay in registers and are written out at the end, so that taking
+    // them adds no stores for the barriers to wait on.
+    uint64_t mk_[16] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
 #define NMS_MARK(slot)                                                  \
     do {                                                                \
         __builtin_amdgcn_sched_barrier(0);                              \
-        const uint64_t t_ = __builtin_amdgcn_s_memrealtime();           \
+        mk_[(slot)] = __builtin_amdgcn_s_memrealtime();                 \
         __builtin_amdgcn_sched_barrier(0);                              \
-        if (lane == 0) s_mk[(slot)] = t_;                               \
     } while (0)
 #define NMS_MARK_AFTER_LOADS(slot)                       \
     do {                                                 \
@@ -959,14 +1010,15 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     } while (0)
 #define NMS_MARKS_OUT()                                                              \
     do {                                                                             \
-        if (lane < 16) g_marks[kNmsMarks + mark + lane] = s_mk[mark + lane];         \
+        if (lane == 0)                                                               \
+            for (int k_ = 0; k_ < 16; ++k_) g_marks[kNmsMarks + mark + k_] = mk_[k_];  \
     } while (0)
 #else
 #define NMS_MARK(slot) do {} while (0)
 #define NMS_MARK_AFTER_LOADS(slot) do {} while (0)
 #define NMS_MARKS_OUT() do {} while (0)
 #endif
-    NMS_MARK(mark + 0);
+    NMS_MARK(0);
     if (tid == 0) {
         s_total = 0;
         s_next = W;
@@ -988,7 +1040,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
             const int g = lane * 4 + j;
             c[j] = g < groups ? counts[g] : 0u;
         }
-        NMS_MARK_AFTER_LOADS(mark + 10);
+        NMS_MARK_AFTER_LOADS(10);
         const uint32_t t = c[0] + c[1] + c[2] + c[3];
         const uint32_t incl = wave_incl_scan(t);
         uint32_t base = incl - t;
@@ -1005,7 +1057,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     }
     __syncthreads();
     const int n = s_n;   // uniform
-    NMS_MARK(mark + 1);
+    NMS_MARK(1);
     if (n == 0) {
         if (tid == 0) {
             p.out->count = 0;
@@ -1025,9 +1077,9 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     float4* s_tmp = s_box + n;
     if (staged) gather<NT, true>(p, keys, s, s_tmp, s_pre, groups, n, tid);
     else gather<NT, false>(p, keys, s, s_tmp, s_pre, groups, n, tid);
-    NMS_MARK(mark + 11);
+    NMS_MARK(11);
     __syncthreads();
-    NMS_MARK(mark + 2);
+    NMS_MARK(2);
 
     // 2. Runs.  Class-aware: bucket the keys by class.  Any class: one run.
     int runs = 1;
@@ -1057,7 +1109,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
                 off[j] = (atomicAdd(&hist[c >> 1], 1u << sh) >> sh) & 0xFFFFu;
             }
         }
-        NMS_MARK(mark + 12);
+        NMS_MARK(12);
         __syncthreads();
         // 2b. Class starts and run starts: one prefix sum of (count | nonempty
         //     << 16) over the classes (counts stay below 2^15, so the low
@@ -1126,7 +1178,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
                 s_run[tot2 >> 16] = (uint16_t)n;
             }
         }
-        NMS_MARK(mark + 13);
+        NMS_MARK(13);
         __syncthreads();
         runs = s_runs;
         // 2c. Scatter into the buckets (boxes too, when staged).
@@ -1140,7 +1192,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
                 if (staged) s_box[pos] = s_tmp[i];
             }
         }
-        NMS_MARK(mark + 14);
+        NMS_MARK(14);
         run_sort = s_maxlen <= kRunSortMax;   // uniform
         // Longest runs first (up to 64 runs, by one wave): (length, start)
         // sorted descending; a start is below 2^14 and a length at most 2^14,
@@ -1158,7 +1210,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         }
         __syncthreads();
     }
-    NMS_MARK(mark + 3);
+    NMS_MARK(3);
     auto run_len = [&](int r) -> int {
         return ordered ? (int)s_run[kRunLen + r] : (int)s_run[r + 1] - (int)s_run[r];
     };
@@ -1171,8 +1223,8 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     };
     uint16_t* kept_pos = reinterpret_cast<uint16_t*>(aux) + wave * max_det;
     float4* k_box = reinterpret_cast<float4*>(aux);
-    float* k_area = reinterpret_cast<float*>(k_box + max_det);
-    uint16_t* k_pos = reinterpret_cast<uint16_t*>(k_area + max_det);
+    float* k_area = reinterpret_cast<float*>(k_box + max_det + kCoopPad);
+    uint16_t* k_pos = reinterpret_cast<uint16_t*>(k_area + max_det + kCoopPad);
     int any_kept = 0;
 #ifdef WS_CLOCK_MARKS
     int runs_done = 0;
@@ -1184,7 +1236,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     if (run_sort) {
         // 3a. Class runs of at most kRunSortMax: one wave holds a run in its
         //     registers and resolves it by selection (no sort).
-        NMS_MARK(mark + 4);
+        NMS_MARK(4);
         for (int r = wave; r < runs; r = next_run()) {
             const int start = s_run[r];
             const int len = run_len(r);
@@ -1207,7 +1259,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
             }
             __syncthreads();
         }
-        NMS_MARK(mark + 4);
+        NMS_MARK(4);
         if (any_class) {
             any_kept = staged
                 ? coop_resolve<true, NT>(p, s, s_box, 0, n, k_box, k_area, k_pos, s_alive, &s_kept, true, tid)
@@ -1232,12 +1284,12 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         }
     }
 #undef WS_COUNT_RUN
-    NMS_MARK(mark + 5);
+    NMS_MARK(5);
 #ifdef WS_CLOCK_MARKS
-    if (lane == 0) s_mk[mark + 9] = (uint64_t)runs_done;
+    mk_[9] = (uint64_t)runs_done;
 #endif
     __syncthreads();
-    NMS_MARK(mark + 6);
+    NMS_MARK(6);
 
     // 4. Kept boxes in rank order.  Any class: the kept list, in rank order
     //    already.  Otherwise gather the flagged keys of all runs; up to
@@ -1267,7 +1319,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
             sort_desc<NT>(s, P2, tid);
         }
     }
-    NMS_MARK(mark + 7);
+    NMS_MARK(7);
 
     // 5. The first max_det, mapped to source pixels, to the mapped slot.
     const int count = min(kept_total, max_det);
@@ -1308,7 +1360,7 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         p.out->count = count;
         p.out->candidates = n;
     }
-    NMS_MARK(mark + 8);
+    NMS_MARK(8);
     NMS_MARKS_OUT();
 #undef NMS_MARK
 #undef NMS_MARK_AFTER_LOADS
@@ -1316,36 +1368,29 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
 }
 
 // Dynamic LDS one workgroup may take: 160 KiB on gfx950, less room for the
-// kernels' static LDS (under 1 KiB; 3 KiB in builds with clock marks, which
-// do not take lanes at the limits of ws.h).
-#ifdef WS_CLOCK_MARKS
-constexpr int kNmsLdsCap = 160 * 1024 - 3 * 1024;
-#else
+// kernels' static LDS (under 1 KiB).
 constexpr int kNmsLdsCap = 160 * 1024 - 1024;
-#endif
 
-constexpr int nms_lds_bytes(int sort_cap, int max_det, int nc, int threads) {
+constexpr int nms_lds_bytes(int sort_cap, int max_det, int nc, int threads, bool any_class) {
     return sort_cap * (int)sizeof(uint64_t) + (kRunSlots + kPreSlots) * (int)sizeof(uint16_t) +
-           nms_aux_bytes(max_det, nc, threads / 64);
+           nms_aux_bytes(max_det, nc, threads / 64, any_class);
 }
 
-#ifndef WS_CLOCK_MARKS
-static_assert(nms_lds_bytes(WS_DET_MAX_ANCHORS, WS_DET_MAX_DET, WS_DET_MAX_CLASSES, kNmsNarrow) <=
+static_assert(nms_lds_bytes(WS_DET_MAX_ANCHORS, WS_DET_MAX_DET, WS_DET_MAX_CLASSES, kNmsNarrow, false) <=
                   kNmsLdsCap,
               "the narrow suppression kernel fits every lane within the limits of ws.h");
-#endif
 
-int nms_threads(int sort_cap, int max_det, int nc) {
-    if (nms_lds_bytes(sort_cap, max_det, nc, kNmsWide) <= kNmsLdsCap) return kNmsWide;
-    if (nms_lds_bytes(sort_cap, max_det, nc, kNmsNarrow) <= kNmsLdsCap) return kNmsNarrow;
+int nms_threads(int sort_cap, int max_det, int nc, bool any_class) {
+    if (nms_lds_bytes(sort_cap, max_det, nc, kNmsWide, any_class) <= kNmsLdsCap) return kNmsWide;
+    if (nms_lds_bytes(sort_cap, max_det, nc, kNmsNarrow, any_class) <= kNmsLdsCap) return kNmsNarrow;
     return 0;
 }
 
 }  // namespace
 
-int det_nms_lds_bytes(int sort_cap, int max_det, int nc) {
-    const int nt = nms_threads(sort_cap, max_det, nc);
-    return nt ? nms_lds_bytes(sort_cap, max_det, nc, nt) : 0;
+int det_nms_lds_bytes(int sort_cap, int max_det, int nc, bool any_class) {
+    const int nt = nms_threads(sort_cap, max_det, nc, any_class);
+    return nt ? nms_lds_bytes(sort_cap, max_det, nc, nt, any_class) : 0;
 }
 
 hipError_t set_detect_attributes() {
@@ -1358,7 +1403,7 @@ hipError_t set_detect_attributes() {
 }
 
 hipError_t launch_detect(const DetParams& p, hipStream_t stream) {
-    const int nt = nms_threads(p.sort_cap, p.max_det, p.nc);
+    const int nt = nms_threads(p.sort_cap, p.max_det, p.nc, p.agnostic != 0);
     if (nt == 0 || p.groups < 1 || p.groups > kDetMaxGroups ||
         (int64_t)p.groups * kDetDecodeAnchors < (int64_t)p.anchors || p.sort_cap < p.anchors)
         return hipErrorInvalidValue;
@@ -1366,7 +1411,7 @@ hipError_t launch_detect(const DetParams& p, hipStream_t stream) {
                        p.head, p.anchors, p.nc, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned lds = (unsigned)nms_lds_bytes(p.sort_cap, p.max_det, p.nc, nt);
+    const unsigned lds = (unsigned)nms_lds_bytes(p.sort_cap, p.max_det, p.nc, nt, p.agnostic != 0);
     auto nms = [&](auto kernel, int threads) {
         hipLaunchKernelGGL(kernel, dim3(1), dim3(threads), lds, stream, p.counts, p.keys, p.groups,
                            p.sort_cap, p.agnostic, p.max_det, p);

@@ -329,7 +329,7 @@ int build(ws_lane* L) {
     // The suppression kernel keeps every candidate key in LDS.
     if (P.det_anchors > 0) {
         // Every lane within the limits of ws.h fits (checked at compile time).
-        if (ws::det_nms_lds_bytes(P.det_sort_cap, c.det_max_det, c.det_classes) == 0)
+        if (ws::det_nms_lds_bytes(P.det_sort_cap, c.det_max_det, c.det_classes, c.det_agnostic != 0) == 0)
             return fail(L, hipSuccess, WS_E_INVALID_ARG);
         WS_HIP(ws::set_detect_attributes(), WS_E_HIP);
     }

@@ -75,16 +75,16 @@ KERNEL_SOURCES = {
 # counters read for a plain 256 MiB device copy.
 MEASURED = {
     "preprocess": {
-        "sha256_prefix": "25e34857211feb98",
+        "sha256_prefix": "df03631e4b730143",
         "profile": "profiles/preprocess_c5t_64x1280x720_to_224.md",
         # cold: the 400 launches rotated over four lanes' batches, start-to-
-        # start period (kernel median 28.396 us); warm: the median of the
+        # start period (kernel median 28.557 us); warm: the median of the
         # other launches of this grid (back-to-back stage launches and graph
         # replays).  traffic: FETCH_SIZE 53,791 KiB x 2.0 + WRITE_SIZE
         # 37,632 KiB per launch (median of 47 dispatches), calibrated on a
         # 256 MiB device copy (FETCH_SIZE 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
-        "c5t_64x1280x720_to_224": {"cold_us": 28.522, "cold_kernel_us": 28.396,
-                                   "warm_us": 23.197, "traffic": 110_163_968 + 38_535_168},
+        "c5t_64x1280x720_to_224": {"cold_us": 28.687, "cold_kernel_us": 28.557,
+                                   "warm_us": 23.077, "traffic": 110_163_968 + 38_535_168},
     },
 }
 

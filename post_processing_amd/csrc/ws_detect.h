@@ -17,8 +17,11 @@ constexpr int kDetMaxGroups = WS_DET_MAX_ANCHORS / kDetDecodeAnchors;
 // Hand-off between the two kernels: decode workgroup g writes how many of
 // its 64 anchors are candidates to counts[g], and their keys and boxes to
 // slots g * 64 + q, q = 0, 1, ... in anchor order.  A slot therefore orders
-// candidates exactly as their anchors do.  Every decode launch rewrites
-// every count, so nothing is reset between frames.
+// candidates exactly as their anchors do.  Each candidate also takes a place
+// among the frame's candidates of its class from cls_counts[class] (one
+// counter in any-class mode), written to offs[slot]; the suppression kernel
+// reads the counters and sets them back to zero for the next frame.  Every
+// decode launch rewrites every count in counts.
 struct DetParams {
     const float* head;       // [4 * 16 + nc][anchors], 16-byte aligned
     int32_t anchors;         // A <= WS_DET_MAX_ANCHORS
@@ -35,6 +38,8 @@ struct DetParams {
     float4* boxes;           // [groups * 64] network-input xyxy by slot
     uint64_t* keys;          // [groups * 64] candidate keys by slot
     uint32_t* counts;        // [groups] candidates per decode workgroup
+    uint32_t* cls_counts;    // [nc, or 1 in any-class mode] candidates per class, zero between frames
+    uint16_t* offs;          // [groups * 64] each candidate's place in its class, by slot
     int32_t sort_cap;        // keys the suppression kernel's LDS holds: a power of two >= anchors
     float left, top;         // image region origin in the network input
     float sx, sy;            // source pixels per network pixel (binary32 of W/rw, H/rh)

@@ -147,11 +147,13 @@ __device__ __forceinline__ float exp_nonpos(float x) {
 // Expected bin index under the softmax of one side's 16 logits (bin b at
 // q[b * A]): the maximum, the shifted exponentials, the weight sum and the
 // index-weighted sum accumulated bin 0..15 in order, one division.
-__device__ __forceinline__ float dfl_side(const float* __restrict__ q, int A) {
-#pragma clang fp contract(off)
-    float l[kBins];
+__device__ __forceinline__ void dfl_load(const float* __restrict__ q, int A, float (&l)[kBins]) {
 #pragma unroll
     for (int b = 0; b < kBins; ++b) l[b] = q[(size_t)b * A];
+}
+
+__device__ __forceinline__ float dfl_side(const float (&l)[kBins]) {
+#pragma clang fp contract(off)
     float m = l[0];
 #pragma unroll
     for (int b = 1; b < kBins; ++b) m = fmaxf(m, l[b]);
@@ -423,6 +425,7 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(
     __shared__ float s_dist[kDecodeBlock][4];
     __shared__ float s_pbest[kDecodeParts][kDecodeBlock];
     __shared__ int s_pcls[kDecodeParts][kDecodeBlock];
+    __shared__ uint16_t s_off[kDecodeBlock];
     __shared__ int s_n;
     const int tid = (int)threadIdx.x;
     const int lane = tid & (kDecodeBlock - 1);
@@ -490,20 +493,52 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(
     const int n = s_n;   // uniform
     if (n == 0) return;
 
-    // 2. DFL distances, one lane per (candidate, side); each lane issues its
-    //    16 loads before any arithmetic.
-    for (int t = tid; t < 4 * n; t += kDecodeThreads) {
-        const int q = t >> 2;
-        const int side = t & 3;
-        s_dist[q][side] = dfl_side(head + (size_t)(side * kBins) * A + s_anchor[q], A);
+    const bool any_class = p.agnostic != 0;
+    if (part == 0) {
+        // 2a. Each candidate's place among the frame's candidates of its
+        //     class (any-class mode: all are one class): the lanes sort
+        //     (class, candidate) pairs, the first lane of each class takes
+        //     that many places from the class's counter (one atomic per
+        //     class present, all in one instruction), and the others follow
+        //     it.  Overlaps the other waves' DFL loads.
+        const bool v = lane < n;
+        const uint32_t c = v ? (any_class ? 0u : (uint32_t)s_cls[lane]) : 0xFFFFu;
+        const uint32_t e = wave_sort<false>((c << 6) | (uint32_t)lane, lane);
+        const uint32_t ec = e >> 6;
+        const bool ev = lane < n;   // invalid pairs sort last
+        const uint32_t prev = (uint32_t)__shfl_up((int)ec, 1);
+        const bool head = ev && (lane == 0 || prev != ec);
+        const uint64_t heads = __ballot(head);
+        const uint64_t above = heads & ~((2ull << lane) - 1);
+        const int next = above ? __ffsll((unsigned long long)above) - 1 : n;
+        uint32_t base = 0;
+        if (head) base = atomicAdd(&p.cls_counts[ec], (uint32_t)(next - lane));
+        const int mine = 63 - __clzll((long long)(heads & ((2ull << lane) - 1)));
+        const uint32_t hb = (uint32_t)__shfl((int)base, mine);
+        if (ev) s_off[e & 63u] = (uint16_t)(hb + (uint32_t)(lane - mine));
+    } else {
+        // 2b. DFL distances, one lane per (candidate, side), on waves 1-3:
+        //     up to two pairs per lane, all 16 or 32 loads issued before any
+        //     arithmetic.
+        const int t0 = tid - kDecodeBlock;
+        constexpr int kPairStride = kDecodeThreads - kDecodeBlock;
+        const bool h0 = t0 < 4 * n, h1 = t0 + kPairStride < 4 * n;
+        float l0[kBins], l1[kBins];
+        if (h0) dfl_load(head + (size_t)((t0 & 3) * kBins) * A + s_anchor[t0 >> 2], A, l0);
+        if (h1) {
+            const int t1 = t0 + kPairStride;
+            dfl_load(head + (size_t)((t1 & 3) * kBins) * A + s_anchor[t1 >> 2], A, l1);
+        }
+        if (h0) s_dist[t0 >> 2][t0 & 3] = dfl_side(l0);
+        if (h1) s_dist[(t0 + kPairStride) >> 2][(t0 + kPairStride) & 3] = dfl_side(l1);
     }
     WS_MARK_AFTER_LOADS(mark + 3);
     __syncthreads();
     WS_MARK(mark + 4);
 
-    // 3. Boxes and keys to the group's slots.  The grid bounds are read with
-    //    constant indices (scalar loads of the kernel arguments).
-    const bool any_class = p.agnostic != 0;
+    // 3. Boxes, keys and class places to the group's slots.  The grid bounds
+    //    are read with constant indices (scalar loads of the kernel
+    //    arguments).
     const int le0 = p.level_end[0], le1 = p.level_end[1];
     const int gw0 = p.grid_w[0], gw1 = p.grid_w[1], gw2 = p.grid_w[2];
     for (int q = tid; q < n; q += kDecodeThreads) {
@@ -518,6 +553,7 @@ __global__ __launch_bounds__(kDecodeThreads) void det_decode_kernel(
         p.boxes[slot] = make_float4((cx - s_dist[q][0]) * st, (cy - s_dist[q][1]) * st,
                                     (cx + s_dist[q][2]) * st, (cy + s_dist[q][3]) * st);
         p.keys[slot] = make_key(any_class, s_prob[q], slot, s_cls[q]);
+        p.offs[slot] = s_off[q];
     }
     WS_MARK(mark + 5);
 }
@@ -768,7 +804,8 @@ constexpr int kSelectBudget = 8;
 // candidates still alive is finished in rank order instead: the live keys
 // are sorted in registers and laid out after the kept ones, the rest of the
 // run is cleared, and resolve_run continues from the kept list.  Boxes are
-// staged by compact position in s_tmp (STAGED) or read by slot.  Kept
+// staged at the run's positions in s_box and by compact position in s_tmp
+// (STAGED), or read by slot.  Kept
 // candidates get bit 0 set in s.  Returns how many were kept.
 template <int K, bool STAGED>
 __device__ __forceinline__ int select_run_k(const DetParams& p, uint64_t* s, float4* s_box, const float4* s_tmp,
@@ -788,7 +825,7 @@ __device__ __forceinline__ int select_run_k(const DetParams& p, uint64_t* s, flo
         const int e = r * 64 + lane;
         key[r] = e < len ? s[s0 + e] : 0;
         box[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e < len) box[r] = STAGED ? staged_box(key[r]) : p.boxes[key_slot(key[r], false)];
+        if (e < len) box[r] = STAGED ? s_box[s0 + e] : p.boxes[key_slot(key[r], false)];
         area[r] = box_area(box[r]);
     }
     int kept = 0;
@@ -895,12 +932,15 @@ __device__ __forceinline__ int group_of(const uint16_t* s_pre, int groups, int i
     return lo;
 }
 
-// Keys (and, with STAGED, boxes) of compact positions 0 .. n-1: each thread
-// takes positions tid, tid + NT, ..., finds each one's slot and issues the
-// loads of up to four positions before storing any.
+// Keys (and, with STAGED, boxes) of every candidate: each thread takes
+// compact positions i = tid, tid + NT, ..., finds each one's slot and issues
+// the loads of up to four positions before storing any.  A candidate goes
+// to its class bucket, cstart[class] + its place in the class (the boxes to
+// s_box at the same place), and with STAGED its box also to s_tmp[i].
 template <int NT, bool STAGED>
 __device__ __forceinline__ void gather(const DetParams& p, const uint64_t* __restrict__ keys, uint64_t* s,
-                                       float4* s_tmp, const uint16_t* s_pre, int groups, int n, int tid) {
+                                       float4* s_box, float4* s_tmp, const uint16_t* s_pre,
+                                       const uint16_t* cstart, int groups, int n, bool any_class, int tid) {
     for (int i0 = tid; i0 < n; i0 += 4 * NT) {
         int sl[4];
 #pragma unroll
@@ -912,27 +952,26 @@ __device__ __forceinline__ void gather(const DetParams& p, const uint64_t* __res
                 sl[u] = g * kDecodeBlock + (i - (int)s_pre[g]);
             }
         }
-        uint64_t k0 = keys[sl[0]], k1 = keys[sl[1]], k2 = keys[sl[2]], k3 = keys[sl[3]];
-        float4 b0, b1, b2, b3;
-        if (STAGED) {
-            b0 = p.boxes[sl[0]];
-            b1 = p.boxes[sl[1]];
-            b2 = p.boxes[sl[2]];
-            b3 = p.boxes[sl[3]];
+        uint64_t k[4];
+        uint32_t o[4];
+        float4 b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            k[u] = keys[sl[u]];
+            o[u] = p.offs[sl[u]];
+            if (STAGED) b[u] = p.boxes[sl[u]];
         }
-        s[i0] = k0;
-        if (STAGED) s_tmp[i0] = b0;
-        if (i0 + NT < n) {
-            s[i0 + NT] = k1;
-            if (STAGED) s_tmp[i0 + NT] = b1;
-        }
-        if (i0 + 2 * NT < n) {
-            s[i0 + 2 * NT] = k2;
-            if (STAGED) s_tmp[i0 + 2 * NT] = b2;
-        }
-        if (i0 + 3 * NT < n) {
-            s[i0 + 3 * NT] = k3;
-            if (STAGED) s_tmp[i0 + 3 * NT] = b3;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * NT;
+            if (i < n) {
+                const int pos = (int)cstart[any_class ? 0 : key_class(k[u])] + (int)o[u];
+                s[pos] = k[u];
+                if (STAGED) {
+                    s_box[pos] = b[u];
+                    s_tmp[i] = b[u];
+                }
+            }
         }
     }
 }
@@ -1025,14 +1064,23 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         s_maxlen = 0;
         s_ncoop = 0;
     }
-    if (!any_class) {
-        uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
-        for (int w = tid; w < (p.nc + 1) / 2; w += NT) hist[w] = 0;
-    }
 
     // 0. Candidates per decode workgroup (written by the decode kernel) and
     //    their prefix sums, by wave 0 (four groups per lane): group g's
     //    candidates take compact positions s_pre[g] .. s_pre[g + 1] - 1.
+    //    Meanwhile every thread reads two class counters (packed as 16-bit
+    //    halves) and clears them for the next frame.
+    const int nc = any_class ? 1 : p.nc;
+    uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
+    uint16_t* cstart = reinterpret_cast<uint16_t*>(aux);
+    for (int w = tid; w < (nc + 1) / 2; w += NT) {
+        const int c0 = 2 * w;
+        const uint32_t a = p.cls_counts[c0];
+        const uint32_t b = c0 + 1 < nc ? p.cls_counts[c0 + 1] : 0u;
+        hist[w] = a | (b << 16);
+        p.cls_counts[c0] = 0;
+        if (c0 + 1 < nc) p.cls_counts[c0 + 1] = 0;
+    }
     if (wave == 0) {
         uint32_t c[4];
 #pragma unroll
@@ -1067,50 +1115,13 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         return;
     }
 
-    // 1. Gather: the keys (and boxes) of every candidate to its compact
-    //    position.  Boxes are staged when the sort space past P has room for
-    //    them twice (by position, and later in rank or bucket order).
-    int P = 64;
-    while (P < n) P <<= 1;
-    const bool staged = (int64_t)P + 4 * (int64_t)n <= (int64_t)sort_cap;   // uniform
-    float4* s_box = reinterpret_cast<float4*>(s + P);   // P * 8 is a multiple of 512
-    float4* s_tmp = s_box + n;
-    if (staged) gather<NT, true>(p, keys, s, s_tmp, s_pre, groups, n, tid);
-    else gather<NT, false>(p, keys, s, s_tmp, s_pre, groups, n, tid);
-    NMS_MARK(11);
-    __syncthreads();
-    NMS_MARK(2);
-
-    // 2. Runs.  Class-aware: bucket the keys by class.  Any class: one run.
+    // 1. Runs: the class counts' prefix sums give each class's start
+    //    (its candidates' places in the class follow it) and the runs.
     int runs = 1;
     bool ordered = false;
     bool run_sort = false;
-    if (!any_class) {
-        constexpr int M = WS_DET_MAX_ANCHORS / NT;
+    {
         constexpr int E = WS_DET_MAX_CLASSES / NT;
-        uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
-        uint16_t* cstart = reinterpret_cast<uint16_t*>(aux);
-        const int nc = p.nc;
-        // 2a. Count each class and take an offset inside it.
-        uint64_t k[M];
-        uint32_t off[M];
-        // (Register arrays, indexed by constants; the uniform break leaves
-        // the unrolled sequence once the positions run out.)
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            if (j * NT >= n) break;
-            const int i = tid + j * NT;
-            k[j] = 0;
-            off[j] = 0;
-            if (i < n) {
-                k[j] = s[i];
-                const int c = key_class(k[j]);
-                const uint32_t sh = (uint32_t)(c & 1) * 16u;
-                off[j] = (atomicAdd(&hist[c >> 1], 1u << sh) >> sh) & 0xFFFFu;
-            }
-        }
-        NMS_MARK(12);
-        __syncthreads();
         // 2b. Class starts and run starts: one prefix sum of (count | nonempty
         //     << 16) over the classes (counts stay below 2^15, so the low
         //     half never carries).  Up to 256 classes wave 0 does it alone,
@@ -1178,21 +1189,25 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
                 s_run[tot2 >> 16] = (uint16_t)n;
             }
         }
-        NMS_MARK(13);
         __syncthreads();
         runs = s_runs;
-        // 2c. Scatter into the buckets (boxes too, when staged).
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            if (j * NT >= n) break;
-            const int i = tid + j * NT;
-            if (i < n) {
-                const int pos = cstart[key_class(k[j])] + off[j];
-                s[pos] = k[j];
-                if (staged) s_box[pos] = s_tmp[i];
-            }
-        }
-        NMS_MARK(14);
+    }
+    NMS_MARK(12);
+
+    // 2. Gather: every candidate's key (and box) to its class bucket, the
+    //    box also by compact position (for lookups by slot).  Boxes are
+    //    staged when the sort space past P has room for them twice.
+    int P = 64;
+    while (P < n) P <<= 1;
+    const bool staged = (int64_t)P + 4 * (int64_t)n <= (int64_t)sort_cap;   // uniform
+    float4* s_box = reinterpret_cast<float4*>(s + P);   // P * 8 is a multiple of 512
+    float4* s_tmp = s_box + n;
+    if (staged) gather<NT, true>(p, keys, s, s_box, s_tmp, s_pre, cstart, groups, n, any_class, tid);
+    else gather<NT, false>(p, keys, s, s_box, s_tmp, s_pre, cstart, groups, n, any_class, tid);
+    NMS_MARK(11);
+    __syncthreads();
+    NMS_MARK(2);
+    if (!any_class) {
         run_sort = s_maxlen <= kRunSortMax;   // uniform
         // Longest runs first (up to 64 runs, by one wave): (length, start)
         // sorted descending; a start is below 2^14 and a length at most 2^14,

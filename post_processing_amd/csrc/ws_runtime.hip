@@ -54,6 +54,8 @@ struct ws_lane {
     float4* det_boxes = nullptr;
     uint64_t* det_keys = nullptr;
     uint32_t* det_counts = nullptr;
+    uint32_t* det_cls_counts = nullptr;
+    uint16_t* det_offs = nullptr;
     ws_det_result* det_host = nullptr;  // mapped detection result slot
     ws_det_result* det_dev = nullptr;   // its device view
     ws::PreParams pre{};
@@ -126,6 +128,8 @@ void release(ws_lane* L) {
     if (L->det_boxes) hipFree(L->det_boxes);
     if (L->det_keys) hipFree(L->det_keys);
     if (L->det_counts) hipFree(L->det_counts);
+    if (L->det_cls_counts) hipFree(L->det_cls_counts);
+    if (L->det_offs) hipFree(L->det_offs);
     if (L->det_host) hipHostFree(L->det_host);
     delete L;
 }
@@ -199,6 +203,8 @@ void fill_params(ws_lane* L) {
     d.keys = L->det_keys;
     d.groups = P.det_decode_groups;
     d.counts = L->det_counts;
+    d.cls_counts = L->det_cls_counts;
+    d.offs = L->det_offs;
     d.sort_cap = P.det_sort_cap;
     d.left = (float)P.region.left;
     d.top = (float)P.region.top;
@@ -411,6 +417,15 @@ int build(ws_lane* L) {
         WS_TRY(dev_alloc(L, &cn, G * sizeof(uint32_t)));
         L->det_counts = static_cast<uint32_t*>(cn);
         WS_HIP(hipMemset(L->det_counts, 0, G * sizeof(uint32_t)), WS_E_HIP);
+        // Class counters start at zero; the suppression kernel clears them
+        // after every frame.
+        const size_t ncc = c.det_agnostic ? 1u : (size_t)c.det_classes;
+        void *cc = nullptr, *of = nullptr;
+        WS_TRY(dev_alloc(L, &cc, ncc * sizeof(uint32_t)));
+        L->det_cls_counts = static_cast<uint32_t*>(cc);
+        WS_HIP(hipMemset(L->det_cls_counts, 0, ncc * sizeof(uint32_t)), WS_E_HIP);
+        WS_TRY(dev_alloc(L, &of, G * 64u * sizeof(uint16_t)));
+        L->det_offs = static_cast<uint16_t*>(of);
         void *h = nullptr, *d = nullptr;
         WS_TRY(mapped_alloc(L, &h, &d, sizeof(ws_det_result)));
         L->det_host = static_cast<ws_det_result*>(h);

@@ -64,6 +64,7 @@ FLUSH_BYTES = 1 << 30          # > 256 MiB last-level cache (Infinity Cache)
 KERNEL_SOURCES = {
     "preprocess": ("ws_preprocess.hip", "ws_kernels.h"),
     "topk": ("ws_topk.hip", "ws_kernels.h", "ws_lanes.h"),
+    "detect": ("ws_detect.hip", "ws_detect.h", "ws_lanes.h"),
 }
 
 # rocprofv3 measurements of the preprocess kernel, per workload (profiles/
@@ -149,10 +150,14 @@ def topk_bytes(w) -> int:
 
 def detect_bytes(w, candidates: int, kept: int) -> int:
     """Decode reads every anchor's class probabilities and each candidate's
-    64 box logits, and writes a 16-byte box and an 8-byte key per candidate;
-    suppression reads those back and writes 24 bytes per kept box."""
+    64 box logits, and writes a 16-byte box, an 8-byte key and a 2-byte place
+    in its class per candidate, a count per 64 anchors and the per-class
+    counts; suppression reads those back (clearing the class counts) and
+    writes 24 bytes per kept box plus the 8-byte header."""
     nc, a = w.det["nc"], w.head.shape[1]
-    return 4 * nc * a + candidates * (256 + 24 + 24) + 24 * kept + 8
+    groups = (a + 63) // 64
+    return (4 * nc * a + candidates * (256 + 2 * (16 + 8 + 2)) + 24 * kept + 8
+            + 8 * groups + 12 * nc)
 
 
 # ---------------------------------------------------------------------------
@@ -317,24 +322,18 @@ def detect_marks(lane, reps: int = 30) -> dict:
              "decode_span": us(d[:, 1:6].max() - t0),
              "nms_start_after_decode": us(t[:, 0].min() - d[:, 1:6].max()),
              "nms_counts": us(t[0, 1] - t[0, 0]),
-             "nms_gather": us(t[0, 2] - t[0, 1]),
-             "nms_bucket": us(t[0, 3] - t[0, 2]),
+             "nms_class_starts": us(t[0, 12] - t[0, 1]),
+             "nms_gather": us(t[0, 11] - t[0, 12]),
+             "nms_gather_barrier": us(t[0, 2] - t[0, 11]),
+             "nms_order": us(t[0, 3] - t[0, 2]),
              "nms_sort_all": us(t[0, 4] - t[0, 3]),
              "nms_runs_busiest": us(t[:, 5].max() - t[0, 4]),
              "nms_runs_median_wave": us(np.median(t[:, 5] - t[:, 4])),
              "nms_runs_barrier": us(t[0, 6] - t[:, 5].max()),
-             "nms_order": us(t[0, 7] - t[0, 6]),
+             "nms_kept_rank": us(t[0, 7] - t[0, 6]),
              "nms_output": us(t[0, 8] - t[0, 7]),
              "nms_span": us(t[0, 8] - t[:, 0].min()),
              "runs_per_wave_max": int(t[:, 9].max()),
-             "nms_counts_load": us(t[0, 10] - t[0, 0]),
-             "nms_fill": us(t[0, 11] - t[0, 1]),
-             "nms_gather_loads": us(t[0, 2] - t[0, 11]),
-             "bucket_atomics": us(t[0, 12] - t[0, 2]),
-             "bucket_scan": us(t[0, 13] - t[0, 12]),
-             "bucket_scatter": us(t[0, 14] - t[0, 13]),
-             "bucket_order": us(t[0, 3] - t[0, 14]),
-             "first_run_sort_busiest_wave": us(t[int(np.argmax(t[:, 5])), 15] - t[0, 4]),
              "cycles_busiest_wave": {k: int(pf[int(np.argmax(t[:, 5])), i]) for i, k in enumerate(
                  ("loads", "screen", "settle", "screen_steps", "kept", "blocks", "round_waits",
                   "w0_round_screen"))},

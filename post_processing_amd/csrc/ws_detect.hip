@@ -9,32 +9,35 @@
 // det_decode_kernel (one workgroup per 64 anchors, four waves): wave w finds
 //   each anchor's best class within the w-th quarter of the classes (all of
 //   a lane's loads in flight together); the anchors above the confidence
-//   threshold are numbered in anchor order by a ballot, their DFL distances
-//   computed one lane per (candidate, box side), and the workgroup writes its
-//   candidate count, their keys and their boxes to its own 64 slots.  No
-//   atomics: the slot order is the anchor order.
+//   threshold are numbered in anchor order by a ballot, and the workgroup
+//   writes its candidate count, their keys and boxes to its own 64 slots
+//   (slot order is anchor order).  Wave 0 also gives each candidate its
+//   place among the frame's candidates of its class: one atomic per class
+//   present on that class's counter.  Waves 1-3 compute the DFL distances,
+//   one lane per (candidate, box side).
 // det_nms_kernel (one workgroup of 16 waves, or 8 when 16 waves' kept-box
 // lists do not fit LDS beside the keys):
-//   1. gathers the candidates of all decode workgroups into LDS (wave 0's
-//      prefix sum of the counts places them), with their boxes when LDS has
-//      room;
-//   2. class-aware mode: buckets the keys by class (a counting pass), so each
-//      class is a contiguous run, and one wave resolves a run of up to 512
-//      candidates from its registers by selection -- the largest live key is
-//      the next kept box and suppresses the live candidates it overlaps --
-//      switching to a sort of the live keys once the run has kept eight
-//      boxes.  With any longer run, or when boxes of any class suppress each
-//      other, the whole list is sorted by the workgroup instead (bitonic; the
-//      key orders by class first in class-aware mode, so runs stay
-//      contiguous);
-//   3. greedy suppression of sorted runs: 64 candidates at a time; each is
-//      tested against the run's boxes kept so far, then the first live
-//      candidate is kept and suppresses the live ones after it, and so on.
-//      Boxes of different classes never interact, so class runs are
-//      independent and resolved one wave per run; the any-class run and any
-//      class run longer than 512 are resolved by all waves together (each
-//      wave screens one block against the kept boxes, then one wave settles
-//      the blocks in order);
+//   0. reads the class counters (and clears them for the next frame) and
+//      the per-workgroup candidate counts, whose prefix sums number the
+//      candidates;
+//   1. class-aware mode: the class counts' prefix sums give each class's
+//      start, so each class is a contiguous run; any-class mode: one run;
+//   2. gathers every candidate's key (and box, when LDS has room) straight
+//      to its class's start plus its place;
+//   3. one wave resolves a class run of up to 512 candidates from its
+//      registers by selection -- the largest live key is the next kept box
+//      and suppresses the live candidates it overlaps -- switching to a sort
+//      of the live keys once the run has kept eight boxes (runs longest
+//      first, one wave each).  With any longer run, or when boxes of any
+//      class suppress each other, the whole list is sorted by the workgroup
+//      instead (bitonic; the key orders by class first in class-aware mode,
+//      so runs stay contiguous) and resolved in rank order, 64 candidates at
+//      a time: each is tested against the run's boxes kept so far, then the
+//      first live candidate is kept and suppresses the live ones after it,
+//      and so on.  The any-class run and any class run longer than 512 are
+//      resolved by all waves together (each wave screens one block against
+//      the kept boxes, then one wave settles the blocks in order).  Boxes of
+//      different classes never interact, so class runs are independent;
 //   4. orders the kept boxes of all classes by probability descending, anchor
 //      ascending -- the order in which plain greedy suppression over all
 //      candidates keeps them -- and writes the first max_det.

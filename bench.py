@@ -321,8 +321,8 @@ def detect_marks(lane, reps: int = 30) -> dict:
              "decode_store": us(np.median(full[:, 5] - full[:, 4])) if len(full) else 0.0,
              "decode_span": us(d[:, 1:6].max() - t0),
              "nms_start_after_decode": us(t[:, 0].min() - d[:, 1:6].max()),
-             "nms_counts": us(t[0, 1] - t[0, 0]),
-             "nms_class_starts": us(t[0, 12] - t[0, 1]),
+             "nms_counts_starts_runs": us(t[0, 1] - t[0, 0]),
+             "nms_clear_and_wide_scan": us(t[0, 12] - t[0, 1]),
              "nms_gather": us(t[0, 11] - t[0, 12]),
              "nms_gather_barrier": us(t[0, 2] - t[0, 11]),
              "nms_order": us(t[0, 3] - t[0, 2]),

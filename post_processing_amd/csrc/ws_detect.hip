@@ -308,6 +308,16 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v, int lane) {
     return v;
 }
 
+// Largest 32-bit value across a wave64 (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v, int lane) {
+    v = max(v, xor_lane32<1>(v, lane));
+    v = max(v, xor_lane32<2>(v, lane));
+    v = max(v, xor_lane32<4>(v, lane));
+    v = max(v, xor_lane32<8>(v, lane));
+    v = max(v, xor_lane32<16>(v, lane));
+    return max(v, xor_lane32<32>(v, lane));
+}
+
 // Exclusive prefix sum of one value per thread over the workgroup, and the
 // total (uniform).  Starts and ends with a barrier, so s_tot may be reused
 // right after.
@@ -835,23 +845,45 @@ __device__ __forceinline__ int select_run_k(const DetParams& p, uint64_t* s, flo
     bool live = false;
     WS_PROF_DECL;
     while (true) {
-        uint64_t m = key[0];
+        // The largest live key: first its bits 52..21 (the run's class bit
+        // and the probability; a dead key is 0) by a 32-bit reduction, then,
+        // only when several candidates share that probability, the largest
+        // full key among them.
+        uint32_t hp[K];
 #pragma unroll
-        for (int r = 1; r < K; ++r) m = umax64(m, key[r]);
-        const uint64_t top = readlane64(wave_max64(m, lane), 0);
-        if (top == 0) break;
+        for (int r = 0; r < K; ++r) hp[r] = (uint32_t)(key[r] >> 21);
+        uint32_t mh = hp[0];
+#pragma unroll
+        for (int r = 1; r < K; ++r) mh = max(mh, hp[r]);
+        mh = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max_u32(mh, lane));
+        if (mh == 0) break;
         if (kept == kSelectBudget && K > 1) {   // uniform
             live = true;
             break;
         }
         // Its register and lane (keys are distinct).
-        int rs = 0, ls = 0;
+        int rs = 0, ls = 0, ties = 0;
 #pragma unroll
         for (int r = 0; r < K; ++r) {
-            const uint64_t b = __ballot(key[r] == top);
+            const uint64_t b = __ballot(hp[r] == mh);
+            ties += __popcll(b);
             if (b) {
                 rs = r;
                 ls = __ffsll((unsigned long long)b) - 1;
+            }
+        }
+        if (ties > 1) {   // uniform: equal probabilities, the slot decides
+            uint64_t m = 0;
+#pragma unroll
+            for (int r = 0; r < K; ++r) m = umax64(m, hp[r] == mh ? key[r] : 0);
+            const uint64_t t = readlane64(wave_max64(m, lane), 0);
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+                const uint64_t b = __ballot(key[r] == t);
+                if (b) {
+                    rs = r;
+                    ls = __ffsll((unsigned long long)b) - 1;
+                }
             }
         }
         float4 kb = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -862,7 +894,7 @@ __device__ __forceinline__ int select_run_k(const DetParams& p, uint64_t* s, flo
                 kb = readlane4(box[r], ls);
                 ka = readlanef(area[r], ls);
                 if (lane == ls) {
-                    s[s0 + r * 64 + ls] = top | 1u;
+                    s[s0 + r * 64 + ls] = key[r] | 1u;
                     kept_pos[kept] = (uint16_t)(s0 + r * 64 + ls);
                     key[r] = 0;
                 }
@@ -1068,48 +1100,114 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         s_ncoop = 0;
     }
 
-    // 0. Candidates per decode workgroup (written by the decode kernel) and
-    //    their prefix sums, by wave 0 (four groups per lane): group g's
-    //    candidates take compact positions s_pre[g] .. s_pre[g + 1] - 1.
-    //    Meanwhile every thread reads two class counters (packed as 16-bit
-    //    halves) and clears them for the next frame.
+    // 0. One round trip for everything the candidate layout needs.  Wave 0
+    //    loads every decode workgroup's candidate count (four per lane) and,
+    //    up to 256 classes, every class's count (four per lane), then works
+    //    out alone the candidates' numbering, the class starts and the runs
+    //    (longest first).  With more classes the workgroup reads and scans
+    //    the class counts.
     const int nc = any_class ? 1 : p.nc;
+    const bool few_classes = nc <= 4 * 64;   // uniform
     uint32_t* hist = reinterpret_cast<uint32_t*>(aux);
     uint16_t* cstart = reinterpret_cast<uint16_t*>(aux);
-    for (int w = tid; w < (nc + 1) / 2; w += NT) {
-        const int c0 = 2 * w;
-        const uint32_t a = p.cls_counts[c0];
-        const uint32_t b = c0 + 1 < nc ? p.cls_counts[c0 + 1] : 0u;
-        hist[w] = a | (b << 16);
-        p.cls_counts[c0] = 0;
-        if (c0 + 1 < nc) p.cls_counts[c0 + 1] = 0;
-    }
+    // The loads are unconditional, their indices clamped into the arrays (a
+    // lane past the end re-reads the last element and drops it), so that all
+    // are in flight before the first is used.
+    uint32_t gc[4] = {0u, 0u, 0u, 0u}, cc[4] = {0u, 0u, 0u, 0u};
     if (wave == 0) {
-        uint32_t c[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gc[j] = counts[min(lane * 4 + j, groups - 1)];
+        if (few_classes) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cc[j] = p.cls_counts[min(lane * 4 + j, nc - 1)];
+        }
+    }
+    if (!few_classes) {
+        for (int w = tid; w < (nc + 1) / 2; w += NT) {
+            const int c0 = 2 * w;
+            const uint32_t a = p.cls_counts[c0];
+            const uint32_t b = c0 + 1 < nc ? p.cls_counts[c0 + 1] : 0u;
+            hist[w] = a | (b << 16);
+        }
+    }
+    // Class starts and run starts: one prefix sum of (count | nonempty << 16)
+    // over the classes (counts stay below 2^15, so the low half never
+    // carries).  A class with more than kRunSortMax candidates is also listed
+    // as a long run.
+    auto publish = [&](int c, uint32_t cn, uint32_t run) {
+        cstart[c] = (uint16_t)(run & 0xFFFFu);
+        if (cn > 0) {
+            s_run[run >> 16] = (uint16_t)(run & 0xFFFFu);
+            if (cn > (uint32_t)kRunSortMax) s_coop[atomicAdd(&s_ncoop, 1)] = (run & 0xFFFFu) | (cn << 16);
+        }
+    };
+    if (wave == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int g = lane * 4 + j;
-            c[j] = g < groups ? counts[g] : 0u;
+            gc[j] = lane * 4 + j < groups ? gc[j] : 0u;
+            cc[j] = lane * 4 + j < nc ? cc[j] : 0u;
         }
-        NMS_MARK_AFTER_LOADS(10);
-        const uint32_t t = c[0] + c[1] + c[2] + c[3];
+        const uint32_t t = gc[0] + gc[1] + gc[2] + gc[3];
         const uint32_t incl = wave_incl_scan(t);
         uint32_t base = incl - t;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int g = lane * 4 + j;
             if (g < groups) s_pre[g] = (uint16_t)base;
-            base += c[j];
+            base += gc[j];
         }
         if (lane == 63) {
             s_pre[groups] = (uint16_t)incl;
             s_n = (int)incl;
         }
+        if (few_classes) {
+            uint32_t loc[4];
+            uint32_t sum = 0;
+            int maxc = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t cn = cc[e];
+                loc[e] = cn | (cn ? 1u << 16 : 0u);
+                sum += loc[e];
+                maxc = max(maxc, (int)cn);
+            }
+            const uint32_t cincl = wave_incl_scan(sum);
+            uint32_t run = cincl - sum;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = lane * 4 + e;
+                if (c < nc) publish(c, loc[e] & 0xFFFFu, run);
+                run += loc[e];
+            }
+            maxc = (int)wave_max_u32((uint32_t)maxc, lane);
+            const int nruns = (int)(cincl >> 16);   // lane 63: all runs
+            const int total_runs = __builtin_amdgcn_readlane(nruns, 63);
+            if (lane == 63) {
+                s_runs = total_runs;
+                s_maxlen = maxc;
+                s_run[total_runs] = (uint16_t)(cincl & 0xFFFFu);   // sentinel: a run ends where the next starts
+            }
+            // Longest runs first (up to 64 runs): (length, start) sorted
+            // descending; a start is below 2^14 and a length at most 2^14,
+            // so both fit one 32-bit key.  The lengths go to
+            // s_run[kRunLen + r].
+            if (!any_class && total_runs > 1 && total_runs <= 64) {
+                wave_lds_sync();   // the run starts and the sentinel are written
+                const uint32_t start = lane < total_runs ? s_run[lane] : 0u;
+                const uint32_t len = lane < total_runs ? (uint32_t)s_run[lane + 1] - start : 0u;
+                const uint32_t ord = wave_sort<true>(lane < total_runs ? (len << 16) | start : 0u, lane);
+                wave_lds_sync();   // every start was read before any is overwritten
+                if (lane < total_runs) {
+                    s_run[lane] = (uint16_t)(ord & 0xFFFFu);
+                    s_run[kRunLen + lane] = (uint16_t)(ord >> 16);
+                }
+            }
+        }
     }
     __syncthreads();
     const int n = s_n;   // uniform
     NMS_MARK(1);
-    if (n == 0) {
+    if (n == 0) {   // no candidates: every class count is zero already
         if (tid == 0) {
             p.out->count = 0;
             p.out->candidates = 0;
@@ -1117,84 +1215,43 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
         NMS_MARKS_OUT();
         return;
     }
+    // The class counts are read: clear them for the next frame.
+    for (int c = tid; c < nc; c += NT) p.cls_counts[c] = 0;
 
-    // 1. Runs: the class counts' prefix sums give each class's start
-    //    (its candidates' places in the class follow it) and the runs.
+    // 1. More than 256 classes: the workgroup scans the class counts, E per
+    //    thread; the class starts overwrite the counters once all are read.
     int runs = 1;
     bool ordered = false;
     bool run_sort = false;
-    {
+    if (!few_classes) {
         constexpr int E = WS_DET_MAX_CLASSES / NT;
-        // 2b. Class starts and run starts: one prefix sum of (count | nonempty
-        //     << 16) over the classes (counts stay below 2^15, so the low
-        //     half never carries).  Up to 256 classes wave 0 does it alone,
-        //     four consecutive classes per lane, while the other waves wait;
-        //     more take the whole workgroup, E per thread.  The class starts
-        //     overwrite the counters once all are read.
-        auto publish = [&](int c, uint32_t cn, uint32_t run) {
-            cstart[c] = (uint16_t)(run & 0xFFFFu);
-            if (cn > 0) {
-                s_run[run >> 16] = (uint16_t)(run & 0xFFFFu);
-                if (cn > (uint32_t)kRunSortMax) s_coop[atomicAdd(&s_ncoop, 1)] = (run & 0xFFFFu) | (cn << 16);
-            }
-        };
-        if (nc <= 256) {   // uniform
-            if (wave == 0) {
-                uint32_t loc[4];
-                uint32_t sum = 0;
-                int maxc = 0;
+        uint32_t loc[E];
+        uint32_t sum = 0;
+        int maxc = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = lane * 4 + e;
-                    const uint32_t cn = c < nc ? (hist[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu : 0u;
-                    loc[e] = cn | (cn ? 1u << 16 : 0u);
-                    sum += loc[e];
-                    maxc = max(maxc, (int)cn);
-                }
-                const uint32_t incl = wave_incl_scan(sum);
-                wave_lds_sync();   // every counter is read before any start is written
-                uint32_t run = incl - sum;
+        for (int e = 0; e < E; ++e) {
+            const int c = tid * E + e;
+            const uint32_t cn = c < nc ? (hist[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu : 0u;
+            loc[e] = cn | (cn ? 1u << 16 : 0u);
+            sum += loc[e];
+            maxc = max(maxc, (int)cn);
+        }
+        uint32_t tot2;
+        uint32_t run = block_excl_scan<NT>(sum, s_tot, tot2, tid);   // all counters are read
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = lane * 4 + e;
-                    if (c < nc) publish(c, loc[e] & 0xFFFFu, run);
-                    run += loc[e];
-                }
-                if (maxc > 0) atomicMax(&s_maxlen, maxc);
-                if (lane == 63) {
-                    s_runs = (int)(incl >> 16);
-                    s_run[incl >> 16] = (uint16_t)n;   // sentinel: a run ends where the next starts
-                }
-            }
-        } else {
-            uint32_t loc[E];
-            uint32_t sum = 0;
-            int maxc = 0;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int c = tid * E + e;
-                const uint32_t cn = c < nc ? (hist[c >> 1] >> ((c & 1) * 16)) & 0xFFFFu : 0u;
-                loc[e] = cn | (cn ? 1u << 16 : 0u);
-                sum += loc[e];
-                maxc = max(maxc, (int)cn);
-            }
-            uint32_t tot2;
-            uint32_t run = block_excl_scan<NT>(sum, s_tot, tot2, tid);   // all counters are read
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int c = tid * E + e;
-                if (c < nc) publish(c, loc[e] & 0xFFFFu, run);
-                run += loc[e];
-            }
-            if (maxc > 0) atomicMax(&s_maxlen, maxc);
-            if (tid == 0) {
-                s_runs = (int)(tot2 >> 16);
-                s_run[tot2 >> 16] = (uint16_t)n;
-            }
+        for (int e = 0; e < E; ++e) {
+            const int c = tid * E + e;
+            if (c < nc) publish(c, loc[e] & 0xFFFFu, run);
+            run += loc[e];
+        }
+        if (maxc > 0) atomicMax(&s_maxlen, maxc);
+        if (tid == 0) {
+            s_runs = (int)(tot2 >> 16);
+            s_run[tot2 >> 16] = (uint16_t)n;
         }
         __syncthreads();
-        runs = s_runs;
     }
+    runs = s_runs;
     NMS_MARK(12);
 
     // 2. Gather: every candidate's key (and box) to its class bucket, the
@@ -1212,21 +1269,21 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     NMS_MARK(2);
     if (!any_class) {
         run_sort = s_maxlen <= kRunSortMax;   // uniform
-        // Longest runs first (up to 64 runs, by one wave): (length, start)
-        // sorted descending; a start is below 2^14 and a length at most 2^14,
-        // so both fit one 32-bit key.  The lengths go to s_run[kRunLen + r].
         ordered = runs > 1 && runs <= 64;
-        if (ordered && wave == 0) {
-            const uint32_t start = lane < runs ? s_run[lane] : 0u;
-            const uint32_t len = lane < runs ? (uint32_t)s_run[lane + 1] - start : 0u;
-            const uint32_t ord = wave_sort<true>(lane < runs ? (len << 16) | start : 0u, lane);
-            wave_lds_sync();   // every start was read before any is overwritten
-            if (lane < runs) {
-                s_run[lane] = (uint16_t)(ord & 0xFFFFu);
-                s_run[kRunLen + lane] = (uint16_t)(ord >> 16);
+        if (!few_classes && ordered) {
+            // Longest runs first, as above, after the workgroup's scan.
+            if (wave == 0) {
+                const uint32_t start = lane < runs ? s_run[lane] : 0u;
+                const uint32_t len = lane < runs ? (uint32_t)s_run[lane + 1] - start : 0u;
+                const uint32_t ord = wave_sort<true>(lane < runs ? (len << 16) | start : 0u, lane);
+                wave_lds_sync();   // every start was read before any is overwritten
+                if (lane < runs) {
+                    s_run[lane] = (uint16_t)(ord & 0xFFFFu);
+                    s_run[kRunLen + lane] = (uint16_t)(ord >> 16);
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
     NMS_MARK(3);
     auto run_len = [&](int r) -> int {

@@ -33,6 +33,14 @@ recorded for the same kernel sources.
 replays) in three campaigns with the workload order rotated, each with a
 direct-launch repeat at the same counts, and times the CPU oracle's
 preprocess and Top-K separately per workload (median of 5 after 1 warm-up).
+
+Completion signals are polled by default (--signals polled puts
+HSA_ENABLE_INTERRUPT=0 in the environment before the HIP runtime starts):
+with the runtime's interrupt-driven default, each hipGraphLaunch spends
+~15-25 us of host time, which is most of a single frame's replay.  The
+default line also carries the C1/C2 lanes in this mode and C2 in the
+interrupt-driven mode (a child process) for comparison.  --launch-cost times
+the launch path alone with empty kernels.
 """
 from __future__ import annotations
 
@@ -805,6 +813,99 @@ def copy_calibration(torch, args) -> int:
     return 0
 
 
+SIGNALS = {"mode": None}
+
+
+def apply_signals(requested: str) -> str:
+    """Put the signal-wait mode in the environment before the HIP runtime
+    starts and return the mode in effect.  With the runtime's default
+    interrupt-driven signals every hipGraphLaunch spent ~15-25 us of host time
+    on this system; polled signals (HSA_ENABLE_INTERRUPT=0) take that to
+    ~2-4 us (`--launch-cost`).  Under a profiler the runtime is already up, so
+    the shell's setting is what holds."""
+    if under_profiler():
+        mode = "polled" if os.environ.get("HSA_ENABLE_INTERRUPT") == "0" else "interrupt"
+        if mode != requested:
+            print(f"bench.py: under a profiler the HIP runtime started before this script; "
+                  f"signals stay {mode} (set HSA_ENABLE_INTERRUPT in the shell)", file=sys.stderr)
+        return mode
+    if requested == "polled":
+        os.environ["HSA_ENABLE_INTERRUPT"] = "0"
+    else:
+        os.environ.pop("HSA_ENABLE_INTERRUPT", None)
+    return requested
+
+
+def single_frame_figures(torch, names=("c1", "c2")) -> dict:
+    """Single-frame lanes beside the default line: 1,000 warm-up and
+    MIN_LATENCY_SAMPLES timed replays each, on this process's signal mode."""
+    out = {}
+    for name in names:
+        w = load_workload(name)
+        lane = make_lane(w, torch)
+        try:
+            res = run_replays(lane, torch, LATENCY["samples"], 1000)
+        finally:
+            lane.destroy()
+        out[workload_name(name, w)] = {
+            "frames_per_s": round(res["frames_per_s"], 1), "p50_us": round(res["p50_us"], 3),
+            "p99_us": round(res["p99_us"], 3), "p99_over_p50": round(res["p99_over_p50"], 4),
+            "latency_samples": res["samples"],
+            "host_p50_us": round(res["host"]["p50_us"], 3),
+            "host_p99_us": round(res["host"]["p99_us"], 3),
+            "host_in_submit_p50_us": round(res["host"]["submit_p50_us"], 3)}
+    return out
+
+
+def interrupt_signal_figures(pinned) -> dict | None:
+    """C2 with the runtime's interrupt-driven signals, in a child process (the
+    mode is fixed when the HIP runtime starts): the comparison for the polled
+    default."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "c2",
+           "--signals", "interrupt", "--steps", str(LATENCY["samples"]), "--warmup", "1000",
+           "--no-cpu-baseline", "--no-extras", "--no-direct"]
+    if pinned is not None:
+        cmd += ["--pin-core", str(pinned)]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=180)
+    except subprocess.TimeoutExpired:
+        return None
+    if r.returncode != 0 or not r.stdout.strip():
+        print(f"[bench] interrupt-signal comparison failed: {r.stderr[-400:]}", file=sys.stderr)
+        return None
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    h = d.get("host_submit_to_return_us") or {}
+    return {"workload": d["config"]["workload"], "signals": d["config"].get("signals"),
+            "p50_us": d["p50_us"], "p99_us": d["p99_us"], "p99_over_p50": d["p99_over_p50"],
+            "latency_samples": d["latency_samples"], "host_p50_us": h.get("p50"),
+            "host_p99_us": h.get("p99"), "host_in_submit_p50_us": h.get("in_submit_p50")}
+
+
+def launch_cost(args) -> int:
+    """The launch path alone: empty kernels, 224 x 256 threads each."""
+    from post_processing_amd import ws
+    forms = {"graph": ws.LAUNCH_GRAPH, "direct": ws.LAUNCH_DIRECT}
+    rows = []
+    for nodes in (1, 2, 4):
+        for fname, form in forms.items():
+            r = ws.launch_cost(nodes, form, replays=3000, warmup=300)
+            row = {"nodes": nodes, "form": fname}
+            for key, arr in r.items():
+                row[key + "_us"] = {q: round(pct(arr, v), 2)
+                                    for q, v in (("p50", 50), ("p90", 90), ("p99", 99))}
+                row[key + "_us"]["min"] = round(float(arr.min()), 2)
+            rows.append(row)
+            print(f"[launch-cost] {nodes} node(s) {fname}: launch {row['launch_us']['p50']} us, "
+                  f"event interval {row['gpu_us']['p50']} us (p99 {row['gpu_us']['p99']})",
+                  file=sys.stderr, flush=True)
+    rec = {"metric": "launch path alone: host time of the launch call(s), host time to "
+                     "completion observed, event interval; empty kernels",
+           "signals": SIGNALS["mode"], "replays": 3000, "warmup": 300, "rows": rows,
+           "versions": versions()}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def load_workload(name: str):
     from post_processing_amd import workloads as wl
     if name == "c5l":
@@ -887,6 +988,7 @@ def campaign(torch, args) -> int:
     rec = {"metric": "campaign: frames/s and p50/p99 us per graph replay, graph vs direct launch",
            "warmup_replays": warm, "timed_replays": reps, "campaigns": 3,
            "order": [CAMPAIGN_ORDER[c:] + CAMPAIGN_ORDER[:c] for c in range(3)],
+           "signals": SIGNALS["mode"],
            "summary": summary, "oracle_ms_1_thread": oracle, "cpu": cpu_model(),
            "host_cpus": os.cpu_count(), "versions": versions(), "gpu_state": gpu_state(),
            "pcie": pcie_link(),
@@ -1029,6 +1131,13 @@ def main(argv=None) -> int:
                          "phase times")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="summarise a rocprofv3 kernel trace of this benchmark and exit (CPU)")
+    ap.add_argument("--signals", default="polled", choices=["polled", "interrupt"],
+                    help="how the HIP runtime waits for completion signals: polled "
+                         "(HSA_ENABLE_INTERRUPT=0, set before HIP starts) or the runtime's "
+                         "interrupt-driven default")
+    ap.add_argument("--launch-cost", action="store_true",
+                    help="time the launch path alone (empty kernels: graph replay against "
+                         "direct launches) and print one JSON record")
     ap.add_argument("--last", type=int, default=0,
                     help="with --trace-summary: also summarise the last N dispatches of each "
                          "kernel and grid")
@@ -1040,6 +1149,7 @@ def main(argv=None) -> int:
     if args.graph_packet_capture == "off":
         # Must be in the environment before torch (or anything else) starts HIP.
         os.environ["DEBUG_CLR_GRAPH_PACKET_CAPTURE"] = "0"
+    SIGNALS["mode"] = apply_signals(args.signals)
     pinned = None
     all_cores = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else []
     ALL_CORES.update(all_cores)
@@ -1073,6 +1183,10 @@ def main(argv=None) -> int:
     if args.input:
         INPUT_OVERRIDE["mode"] = {"device": ws.INPUT_DEVICE, "mapped": ws.INPUT_MAPPED_HOST,
                                   "copy": ws.INPUT_COPY}[args.input]
+    if args.launch_cost:
+        if pinned is not None:
+            os.sched_setaffinity(0, {pinned})
+        return launch_cost(args)
     if args.workload == "copy":
         return copy_calibration(torch, args)
     if args.rotation_probe:
@@ -1142,6 +1256,13 @@ def main(argv=None) -> int:
         if name == "c5t" and not args.no_extras:
             print("[bench] C5L lanes", file=sys.stderr, flush=True)
             extra["c5l"] = c5l_figures(torch)
+            print("[bench] single-frame lanes", file=sys.stderr, flush=True)
+            extra["single_frame"] = single_frame_figures(torch)
+            if SIGNALS["mode"] == "polled" and not under_profiler():
+                print("[bench] C2 with interrupt-driven signals (child process)",
+                      file=sys.stderr, flush=True)
+                torch.cuda.synchronize()
+                extra["single_frame_interrupt_signals"] = interrupt_signal_figures(pinned)
 
     if args.marks and w.k:
         extra["topk_marks_us"] = topk_marks(lane)
@@ -1171,6 +1292,7 @@ def main(argv=None) -> int:
                    "input": input_mode,
                    "graph": True, "lanes": 8 if name == "c5l" else args.lanes,
                    "wait": args.wait,
+                   "signals": SIGNALS["mode"],
                    "graph_packet_capture": args.graph_packet_capture,
                    "host_core": pinned,
                    "parallelism": "single_gpu"},

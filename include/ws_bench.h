@@ -111,6 +111,31 @@ int ws_bench_stage_cold(ws_lane *lane, int32_t stage, void *flush, size_t flush_
 int ws_bench_stage_rotate(ws_lane **lanes, int32_t nlanes, int32_t stage, int32_t warmup,
                           int32_t launches, double *ms_per_launch);
 
+/* Launch forms for ws_bench_launch_cost. */
+#define WS_LAUNCH_GRAPH        0   /* events recorded around one graph replay   */
+#define WS_LAUNCH_DIRECT       1   /* events around direct kernel launches      */
+
+/*
+ * Cost of launching a chain of `nodes` (1..8) kernels that do no work, each
+ * 224 workgroups of 256 threads, on a non-blocking stream of `device` created
+ * for the call: the per-frame launch overhead with the kernels' own work
+ * taken out.  The streams handbook's graph chapter and the WarpStream TRT
+ * article's benchmark passage (graph replay against direct launches) are what
+ * it measures.  `warmup` untimed rounds, then `replays` timed rounds, each
+ * waited for (spinning on the done event, as ws_wait does) before the next:
+ *   launch_us  host time of the launch call(s) of each round;
+ *   total_us   host time from the first call of the round (the start event
+ *              record) to completion observed;
+ *   gpu_us     start->done event interval.
+ * Each array holds `replays` entries.  hip_error (optional) receives the
+ * hipError_t of the call that failed, else 0.  Returns WS_OK,
+ * WS_E_INVALID_ARG (NULL, nodes outside 1..8, replays < 1, warmup < 0,
+ * unknown form) or WS_E_HIP.
+ */
+int ws_bench_launch_cost(int32_t device, int32_t nodes, int32_t form, int32_t warmup,
+                         int32_t replays, float *launch_us, float *total_us, float *gpu_us,
+                         int32_t *hip_error);
+
 #ifdef __cplusplus
 }
 #endif

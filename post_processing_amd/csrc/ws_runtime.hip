@@ -88,6 +88,13 @@ __global__ __launch_bounds__(256) void cache_flush_kernel(uint4* buf, size_t n16
     if (sink != nullptr && acc == 0x9E3779B9u) sink[threadIdx.x] = acc;
 }
 
+// Benchmark aid: a kernel that does no work, for timing the launch path.  It
+// stores only when `tag` is a value no caller passes, which keeps it a real
+// dispatch with an argument.
+__global__ __launch_bounds__(256) void launch_probe_kernel(uint32_t* sink, int32_t tag) {
+    if (tag == INT32_MIN && sink != nullptr) sink[blockIdx.x] = (uint32_t)tag;
+}
+
 int fail(ws_lane* L, hipError_t e, int code) {
     if (L) L->last_err = (int)e;
     return code;
@@ -706,6 +713,81 @@ int ws_bench_stage(ws_lane* L, int32_t stage, int32_t launches, double* ms_per_l
     if (e != hipSuccess) return fail(L, e, WS_E_HIP);
     *ms_per_launch = (double)ms / (double)launches;
     return WS_OK;
+}
+
+int ws_bench_launch_cost(int32_t device, int32_t nodes, int32_t form, int32_t warmup,
+                         int32_t replays, float* launch_us, float* total_us, float* gpu_us,
+                         int32_t* hip_error) {
+    if (hip_error) *hip_error = 0;
+    if (nodes < 1 || nodes > 8 || replays < 1 || warmup < 0 || !launch_us || !total_us ||
+        !gpu_us || (form != WS_LAUNCH_GRAPH && form != WS_LAUNCH_DIRECT))
+        return WS_E_INVALID_ARG;
+    if (hipSetDevice(device) != hipSuccess) return WS_E_HIP;
+    // The launch checks below read the thread's last error, which an earlier
+    // call of this thread (a not-ready event query, say) may have left set.
+    (void)hipGetLastError();
+    constexpr int kGrid = 224;
+    hipStream_t s = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t x = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreate(&e0);
+    if (e == hipSuccess) e = hipEventCreate(&e1);
+    auto chain = [&]() {
+        hipError_t r = hipSuccess;
+        for (int32_t i = 0; i < nodes && r == hipSuccess; ++i) {
+            hipLaunchKernelGGL(launch_probe_kernel, dim3(kGrid), dim3(256), 0, s, nullptr, i);
+            r = hipGetLastError();
+        }
+        return r;
+    };
+    if (e == hipSuccess) e = chain();   // loads the code object outside any capture
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e == hipSuccess && form != WS_LAUNCH_DIRECT) {
+        e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+        if (e == hipSuccess) {
+            const hipError_t le = chain();
+            e = hipStreamEndCapture(s, &g);
+            if (e == hipSuccess) e = le;
+        }
+        if (e == hipSuccess) e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+        if (e == hipSuccess) e = hipGraphUpload(x, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+    }
+    using clk = std::chrono::steady_clock;
+    const auto us = [](clk::time_point a, clk::time_point b) {
+        return (float)std::chrono::duration<double, std::micro>(b - a).count();
+    };
+    for (int32_t it = 0; it < warmup + replays && e == hipSuccess; ++it) {
+        (void)hipGetLastError();   // the previous round's not-ready queries
+        const auto t0 = clk::now();
+        e = hipEventRecord(e0, s);
+        const auto ta = clk::now();
+        if (e == hipSuccess) e = form == WS_LAUNCH_DIRECT ? chain() : hipGraphLaunch(x, s);
+        const auto tb = clk::now();
+        if (e == hipSuccess) e = hipEventRecord(e1, s);
+        if (e != hipSuccess) break;
+        while ((e = hipEventQuery(e1)) == hipErrorNotReady) {
+        }
+        const auto t2 = clk::now();
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        if (e == hipSuccess && it >= warmup) {
+            launch_us[it - warmup] = us(ta, tb);
+            total_us[it - warmup] = us(t0, t2);
+            gpu_us[it - warmup] = ms * 1e3f;
+        }
+    }
+    if (s) hipStreamSynchronize(s);
+    if (x) hipGraphExecDestroy(x);
+    if (g) hipGraphDestroy(g);
+    if (e0) hipEventDestroy(e0);
+    if (e1) hipEventDestroy(e1);
+    if (s) hipStreamDestroy(s);
+    if (hip_error) *hip_error = (int32_t)e;
+    (void)hipGetLastError();   // leave no error behind for the caller's next call
+    return e == hipSuccess ? WS_OK : WS_E_HIP;
 }
 
 }  // extern "C"

@@ -46,6 +46,8 @@ MAX_K = 32
 STAGE_PREPROCESS = 0
 STAGE_TOPK = 1
 STAGE_DETECT = 2
+LAUNCH_GRAPH = 0
+LAUNCH_DIRECT = 1
 DET_MAX_DET = 1024
 
 
@@ -156,6 +158,10 @@ def load(path: str = LIB_PATH):
     lib.ws_bench_stage_rotate.restype = c_int
     lib.ws_run_noalloc.argtypes = [POINTER(LaneConfig), c_void_p, c_void_p]
     lib.ws_run_noalloc.restype = c_int
+    lib.ws_bench_launch_cost.argtypes = [c_int32, c_int32, c_int32, c_int32, c_int32,
+                                         POINTER(c_float), POINTER(c_float), POINTER(c_float),
+                                         POINTER(c_int32)]
+    lib.ws_bench_launch_cost.restype = c_int
     _lib = lib
     return lib
 
@@ -388,6 +394,19 @@ def time_stage_rotate(lanes: list[Lane], stage: int, launches: int, warmup: int 
     if rc != WS_OK:
         raise WsError(rc, "ws_bench_stage_rotate", lanes[0].hip_error())
     return ms.value
+
+
+def launch_cost(nodes: int, form: int, replays: int, warmup: int = 300,
+                device: int = 0) -> dict:
+    """Launch overhead of `nodes` empty kernels in one of the LAUNCH_* forms
+    (native loop): per-round arrays in microseconds, keys launch / total / gpu."""
+    lib = load()
+    arrs = [(c_float * replays)() for _ in range(3)]
+    err = c_int32(0)
+    rc = lib.ws_bench_launch_cost(device, nodes, form, warmup, replays, *arrs, byref(err))
+    if rc != WS_OK:
+        raise WsError(rc, "ws_bench_launch_cost", err.value)
+    return {k: np.ctypeslib.as_array(a).copy() for k, a in zip(("launch", "total", "gpu"), arrs)}
 
 
 def bench_lanes(lanes: list[Lane], replays: int) -> tuple[np.ndarray, float]:

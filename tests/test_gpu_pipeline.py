@@ -572,6 +572,45 @@ def test_library_loaded_before_torch_in_a_fresh_process(gpu_lib):
     assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stderr[-2000:]
 
 
+def test_polled_signals_in_a_fresh_process(gpu_lib):
+    """The deployment setting the benchmark uses: completion signals polled
+    (HSA_ENABLE_INTERRUPT=0 before the HIP runtime starts).  In a fresh
+    process, C2 and C3 lanes (C3's Top-K through the merge kernel) replay 300
+    times and still match the oracle, and the launch-cost harness runs both
+    of its forms."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import os, sys\n"
+        "sys.path.insert(0, 'tests')\n"
+        "assert os.environ.get('HSA_ENABLE_INTERRUPT') == '0'\n"
+        "import torch\n"
+        "from post_processing_amd import ws, workloads as wl\n"
+        "from gpu_util import Run, oracle_outputs, assert_tensor_close, assert_topk_exact\n"
+        "for name in ('c2', 'c3'):\n"
+        "    w = wl.ALL_CONFIGS[name]()\n"
+        "    ref, rtk = oracle_outputs(w)\n"
+        "    r = Run(w, host_input=False)\n"
+        "    try:\n"
+        "        ms = r.lane.bench(300)[0]\n"
+        "        assert (ms > 0).all()\n"
+        "        r.run()\n"
+        "        t, tk = r.outputs()\n"
+        "        assert_tensor_close(t, ref)\n"
+        "        assert_topk_exact(tk, rtk)\n"
+        "    finally:\n"
+        "        r.close()\n"
+        "for form in (ws.LAUNCH_GRAPH, ws.LAUNCH_DIRECT):\n"
+        "    c = ws.launch_cost(2, form, replays=50, warmup=10)\n"
+        "    assert all((a > 0).all() for a in c.values()), (form, c)\n"
+        "print('ok')\n")
+    env = dict(os.environ, HSA_ENABLE_INTERRUPT="0")
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=110, env=env)
+    assert out.returncode == 0 and out.stdout.strip().endswith("ok"), out.stderr[-2000:]
+
+
 @pytest.mark.parametrize("shape", [(16384, 6, 16384, 3, False), (5, 16384, 3, 16384, False),
                                    (16384, 64, 4096, 64, True)])
 def test_maximum_sides(gpu_lib, shape):

@@ -243,23 +243,26 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
 
     int32_t rows = c.rows_per_group;
     if (rows == 0) {
-        // Measured on MI355X: batches (bandwidth work) run best with one row
-        // per workgroup, the most workgroups in flight; single frames with one
-        // row, or two once the tensor has 320+ rows (fewer, fuller groups).
-        // Tiny rows are packed so a workgroup holds at least one full wave.
-        rows = (px == 4 || Dh < 320) ? 1 : 2;
-        while (rows < Dh && (int64_t)(rows + 1) * q <= 64) ++rows;
-        while (staged && rows > 1 && lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes / 2)
-            --rows;
+        // The gather kernel: one row per workgroup, the most workgroups in
+        // flight (its threads walk a workgroup's rows one after another).
+        // The staged kernels, measured on MI355X: one row, or two once the
+        // tensor has 320+ rows (fewer, fuller groups), with tiny rows packed
+        // so a workgroup holds at least one full wave.
+        if (!staged) {
+            rows = 1;
+        } else {
+            rows = (px == 4 || Dh < 320) ? 1 : 2;
+            while (rows < Dh && (int64_t)(rows + 1) * q <= 64) ++rows;
+            while (rows > 1 && lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes / 2) --rows;
+        }
     }
     if (rows > Dh) rows = (int32_t)Dh;
     if (staged && lds_for_rows(rows, p->slot_bytes) > kMaxLdsBytes) return WS_E_INVALID_ARG;
     p->rows_per_group = rows;
-    const int64_t threads = (int64_t)rows * q;
-    // The gather kernel (PX = 1) holds no LDS per thread and takes workgroups
-    // of up to 1024 threads, so a 640-wide row no longer loops over some
-    // threads twice (640x640 letterbox 4.31 -> 4.16 us); the staged kernels
-    // keep 512.
+    // The staged kernels spread a workgroup's rows over its threads (up to
+    // 512).  The gather kernel gives each thread one column of all its rows,
+    // with workgroups of up to 1024 threads, so a 640-wide row takes one pass.
+    const int64_t threads = staged ? (int64_t)rows * q : q;
     const int64_t block_cap = staged ? kMaxPreBlock : kMaxGatherBlock;
     p->pre_block = (int32_t)std::min<int64_t>(block_cap, ceil_div(threads, 64) * 64);
     p->groups_per_frame = (int32_t)ceil_div(Dh, rows);

@@ -250,24 +250,6 @@ __global__ __launch_bounds__(512) void preprocess_kernel(PreParams p) {
     }
 }
 
-// Three dwords of the input from the 4-byte-aligned address at or below byte
-// g (which holds both horizontal taps of a source row: bytes g .. g + 5), or,
-// for the input's last partial window, its bytes below total, zero above.
-__device__ __forceinline__ void load_window(const uint8_t* src, int64_t g, int64_t total,
-                                            uint32_t (&w)[3]) {
-    const int64_t a = g & ~(int64_t)3;
-    if (a + 12 <= total) {
-        const uint32_t* s = reinterpret_cast<const uint32_t*>(src + a);
-        w[0] = s[0];
-        w[1] = s[1];
-        w[2] = s[2];
-    } else {
-        w[0] = w[1] = w[2] = 0u;
-        for (int b = 0; b < 12; ++b)
-            if (a + b < total) w[b >> 2] |= (uint32_t)src[a + b] << (8 * (b & 3));
-    }
-}
-
 // The pixel whose first byte is byte e (0..6) of a window.
 __device__ __forceinline__ uint32_t window_rgb(const uint32_t (&w)[3], uint32_t e) {
     const uint32_t lo = e < 4 ? w[0] : w[1];
@@ -275,60 +257,105 @@ __device__ __forceinline__ uint32_t window_rgb(const uint32_t (&w)[3], uint32_t 
     return __builtin_amdgcn_alignbyte(hi, lo, e & 3u);
 }
 
-// Device-resident single frames with one output column per thread: each
-// thread reads its four taps straight from global memory, one window per
-// source row, so nothing is staged and no barrier precedes the loads.  Same
-// taps and arithmetic as preprocess_kernel<1>.
-template <typename OutT>
+// A source row's window for one output column: the 4-byte-aligned address at
+// or below the column's first tap byte, split into a part common to the
+// workgroup (the row's base, rounded down to 4 bytes, and its remainder) and
+// the lane's 32-bit offset from that base.
+struct RowBase {
+    const uint8_t* ptr;   // source row start rounded down to 4 bytes
+    uint32_t mis;         // row start - ptr (0..3)
+    uint32_t avail;       // bytes of the input from ptr on, capped at 2^32 - 1
+};
+
+__device__ __forceinline__ RowBase row_base(const PreParams& p, int64_t row_start) {
+    RowBase r;
+    const int64_t a = row_start & ~(int64_t)3;
+    r.ptr = p.src + a;
+    r.mis = (uint32_t)(row_start - a);
+    const int64_t rest = p.total_bytes - a;
+    r.avail = rest > (int64_t)0xffffffff ? 0xffffffffu : (uint32_t)rest;
+    return r;
+}
+
+// Three dwords at byte offset `off` (a multiple of 4) from the row base, or,
+// past the end of the input, its bytes below the end and zeros above.
+__device__ __forceinline__ void load_window_at(const RowBase& rb, uint32_t off, uint32_t (&w)[3]) {
+    if (off + 12u <= rb.avail) {
+        const uint32_t* s = reinterpret_cast<const uint32_t*>(rb.ptr + off);
+        w[0] = s[0];
+        w[1] = s[1];
+        w[2] = s[2];
+    } else {
+        w[0] = w[1] = w[2] = 0u;
+        for (uint32_t b = 0; b < 12; ++b)
+            if (off + b < rb.avail) w[b >> 2] |= (uint32_t)rb.ptr[off + b] << (8 * (b & 3));
+    }
+}
+
+// Device-resident frames with one output column per thread: each thread reads
+// its four taps straight from global memory, one window per source row, so
+// nothing is staged and no barrier precedes the loads.  Same taps and
+// arithmetic as preprocess_kernel<PX>.  A workgroup owns rows_per_group
+// consecutive output rows of one frame and walks them in order; a thread owns
+// output columns x = threadIdx.x, + blockDim.x, ...  Everything that depends
+// on the row alone (vertical taps, source and output row addresses) is the
+// same for the whole workgroup, so it is computed once on the scalar unit;
+// a lane keeps its column's horizontal taps across rows and addresses the
+// frame with 32-bit offsets from those row bases.  The channel bytes sit at
+// fixed positions of a pixel word (SH0..SH2), so each unpacks with one
+// conversion.
+template <typename OutT, int SH0, int SH1, int SH2>
 __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
     using Fmt = OutFormat<OutT>;
+    constexpr uint32_t kShift[3] = {SH0, SH1, SH2};
     const int f = blockIdx.x / p.groups_per_frame;
     const int grp = blockIdx.x - f * p.groups_per_frame;
     const int y_base = grp * p.rows_per_group;
     const int nrows = min(p.rows_per_group, p.dst_h - y_base);
     const int64_t fbase = (int64_t)f * p.frame_bytes;
     const int64_t row_bytes = 3 * (int64_t)p.src_w;
-    const int q = p.dst_w;
-    const int work = nrows * q;
     const int64_t plane = (int64_t)p.dst_h * p.dst_w;
     OutT* const frame_out = reinterpret_cast<OutT*>(p.dst) + (int64_t)f * 3 * plane;
-    for (int wi = (int)threadIdx.x; wi < work; wi += (int)blockDim.x) {
-        const int r = wi / q;
-        const int x = wi - r * q;
-        const int y = y_base + r;
-        const int dy = y - p.top;
-        const int dx = x - p.left;
-        float out[3];
-        if (dy >= 0 && dy < p.reg_h && dx >= 0 && dx < p.reg_w) {
-            const AxisTap ty = exact_tap(dy, p.src_h, p.reg_h, p.inv_den_y, p.magic_y);
-            const AxisTap tx = exact_tap(dx, p.src_w, p.reg_w, p.inv_den_x, p.magic_x);
-            const int64_t col = fbase + 3 * (int64_t)tx.i0;
-            const int64_t g0 = col + (int64_t)ty.i0 * row_bytes;
-            const int64_t g1 = col + (int64_t)ty.i1 * row_bytes;
-            uint32_t w0[3], w1[3];
-            load_window(p.src, g0, p.total_bytes, w0);
-            load_window(p.src, g1, p.total_bytes, w1);
-            const uint32_t o0 = (uint32_t)(g0 & 3), o1 = (uint32_t)(g1 & 3);
-            const uint32_t d = 3u * (tx.i1 - tx.i0);   // 0 (edge clamp) or 3
-            const uint32_t t00 = window_rgb(w0, o0), t01 = window_rgb(w0, o0 + d);
-            const uint32_t t10 = window_rgb(w1, o1), t11 = window_rgb(w1, o1 + d);
+    for (uint32_t x = threadIdx.x; x < (uint32_t)p.dst_w; x += blockDim.x) {
+        const int dx = (int)x - p.left;
+        const bool col_in = dx >= 0 && dx < p.reg_w;
+        AxisTap tx{0u, 0u, 0.0f};
+        if (col_in) tx = exact_tap(dx, p.src_w, p.reg_w, p.inv_den_x, p.magic_x);
+        const uint32_t cx = 3u * tx.i0;               // first tap byte within a row
+        const uint32_t d = 3u * (tx.i1 - tx.i0);      // 0 (edge clamp) or 3
+        for (int r = 0; r < nrows; ++r) {
+            const int y = y_base + r;
+            const int dy = y - p.top;
+            float out[3];
+            if (dy >= 0 && dy < p.reg_h && col_in) {
+                const AxisTap ty = exact_tap(dy, p.src_h, p.reg_h, p.inv_den_y, p.magic_y);
+                const RowBase b0 = row_base(p, fbase + (int64_t)ty.i0 * row_bytes);
+                const RowBase b1 = row_base(p, fbase + (int64_t)ty.i1 * row_bytes);
+                const uint32_t e0 = b0.mis + cx, e1 = b1.mis + cx;
+                uint32_t w0[3], w1[3];
+                load_window_at(b0, e0 & ~3u, w0);
+                load_window_at(b1, e1 & ~3u, w1);
+                const uint32_t o0 = e0 & 3u, o1 = e1 & 3u;
+                const uint32_t t00 = window_rgb(w0, o0), t01 = window_rgb(w0, o0 + d);
+                const uint32_t t10 = window_rgb(w1, o1), t11 = window_rgb(w1, o1 + d);
 #pragma unroll
-            for (int c = 0; c < 3; ++c) {
-                const uint32_t sh = p.shift[c];
-                const float p00 = chan(t00, sh), p01 = chan(t01, sh);
-                const float p10 = chan(t10, sh), p11 = chan(t11, sh);
-                const float h0 = fmaf(tx.w, p01 - p00, p00);
-                const float h1 = fmaf(tx.w, p11 - p10, p10);
-                const float v = fmaf(ty.w, h1 - h0, h0);
-                out[c] = fmaf(v, p.a[c], p.b[c]);
+                for (int c = 0; c < 3; ++c) {
+                    const uint32_t sh = kShift[c];
+                    const float p00 = chan(t00, sh), p01 = chan(t01, sh);
+                    const float p10 = chan(t10, sh), p11 = chan(t11, sh);
+                    const float h0 = fmaf(tx.w, p01 - p00, p00);
+                    const float h1 = fmaf(tx.w, p11 - p10, p10);
+                    const float v = fmaf(ty.w, h1 - h0, h0);
+                    out[c] = fmaf(v, p.a[c], p.b[c]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 3; ++c) out[c] = p.padv[c];
             }
-        } else {
+            OutT* const row_out = frame_out + (int64_t)y * p.dst_w;
 #pragma unroll
-            for (int c = 0; c < 3; ++c) out[c] = p.padv[c];
+            for (int c = 0; c < 3; ++c) row_out[c * plane + x] = Fmt::cvt(out[c]);
         }
-        OutT* const px_out = frame_out + (int64_t)y * p.dst_w + x;
-#pragma unroll
-        for (int c = 0; c < 3; ++c) px_out[c * plane] = Fmt::cvt(out[c]);
     }
 }
 
@@ -336,7 +363,13 @@ template <typename OutT>
 hipError_t launch_preprocess_as(const PreParams& p, dim3 g, dim3 b, unsigned lds,
                                 hipStream_t stream) {
     switch (p.pixels_per_thread) {
-        case 1: hipLaunchKernelGGL((preprocess_gather_kernel<OutT>), g, b, 0, stream, p); break;
+        case 1:
+            // Channel byte positions of a pixel word: RGB or BGR producers.
+            if (p.shift[0] == 0)
+                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16>), g, b, 0, stream, p);
+            else
+                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0>), g, b, 0, stream, p);
+            break;
         case 2: hipLaunchKernelGGL((preprocess_kernel<2, OutT>), g, b, lds, stream, p); break;
         case 4: hipLaunchKernelGGL((preprocess_kernel<4, OutT>), g, b, lds, stream, p); break;
         default: return hipErrorInvalidValue;

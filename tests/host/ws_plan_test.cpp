@@ -184,7 +184,8 @@ static int selftest() {
     CHECK(ws::make_plan(c, &p) == WS_E_INVALID_ARG);
     c.pixels_per_thread = 1;
     CHECK(ws::make_plan(c, &p) == WS_OK);
-    CHECK(p.rows_per_group == 7 && p.lds_bytes == 0 && p.pre_block == 1024);
+    // One thread per output column, each walking the workgroup's seven rows.
+    CHECK(p.rows_per_group == 7 && p.lds_bytes == 0 && p.pre_block == 384);
     c = good();
     c.num_scores = 672000;
     c.k = 32;

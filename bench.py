@@ -84,16 +84,16 @@ KERNEL_SOURCES = {
 # counters read for a plain 256 MiB device copy.
 MEASURED = {
     "preprocess": {
-        "sha256_prefix": "df03631e4b730143",
+        "sha256_prefix": "a3510c37b49018d8",
         "profile": "profiles/preprocess_c5t_64x1280x720_to_224.md",
         # cold: the 400 launches rotated over four lanes' batches, start-to-
-        # start period (kernel median 28.557 us); warm: the median of the
+        # start period (kernel median 28.677 us); warm: the median of the
         # other launches of this grid (back-to-back stage launches and graph
-        # replays).  traffic: FETCH_SIZE 53,791 KiB x 2.0 + WRITE_SIZE
-        # 37,632 KiB per launch (median of 47 dispatches), calibrated on a
+        # replays).  traffic: FETCH_SIZE 53,783 KiB x 2.0 + WRITE_SIZE
+        # 37,632 KiB per launch (median of 547 dispatches), calibrated on a
         # 256 MiB device copy (FETCH_SIZE 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
-        "c5t_64x1280x720_to_224": {"cold_us": 28.687, "cold_kernel_us": 28.557,
-                                   "warm_us": 23.077, "traffic": 110_163_968 + 38_535_168},
+        "c5t_64x1280x720_to_224": {"cold_us": 28.815, "cold_kernel_us": 28.677,
+                                   "warm_us": 22.117, "traffic": 110_147_584 + 38_535_168},
     },
 }
 
@@ -1021,6 +1021,8 @@ def trace_summary(path: str) -> int:
         t1 = int(r.get("End_Timestamp") or r.get("EndNs") or 0)
         q = r.get("Queue_Id") or r.get("Stream_Id") or "0"
         grid = r.get("Grid_Size") or r.get("Grid_Size_X") or ""
+        if r.get("Grid_Size_Y") not in (None, "", "1"):
+            grid = f"{grid}x{r['Grid_Size_Y']}"   # frames of a batch in y
         recs.append((q, t0, t1, name, grid))
     recs.sort(key=lambda x: (x[0], x[1]))
     by = {}

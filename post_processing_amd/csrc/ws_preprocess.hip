@@ -277,6 +277,15 @@ __device__ __forceinline__ RowBase row_base(const PreParams& p, int64_t row_star
     return r;
 }
 
+// Three dwords at byte offset `off` (a multiple of 4) from the row base, when
+// the caller has checked that they lie inside the input.
+__device__ __forceinline__ void load_window_fast(const RowBase& rb, uint32_t off, uint32_t (&w)[3]) {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(rb.ptr + off);
+    w[0] = s[0];
+    w[1] = s[1];
+    w[2] = s[2];
+}
+
 // Three dwords at byte offset `off` (a multiple of 4) from the row base, or,
 // past the end of the input, its bytes below the end and zeros above.
 __device__ __forceinline__ void load_window_at(const RowBase& rb, uint32_t off, uint32_t (&w)[3]) {
@@ -292,50 +301,81 @@ __device__ __forceinline__ void load_window_at(const RowBase& rb, uint32_t off, 
     }
 }
 
-// Device-resident frames with one output column per thread: each thread reads
-// its four taps straight from global memory, one window per source row, so
-// nothing is staged and no barrier precedes the loads.  Same taps and
-// arithmetic as preprocess_kernel<PX>.  A workgroup owns rows_per_group
-// consecutive output rows of one frame and walks them in order; a thread owns
-// output columns x = threadIdx.x, + blockDim.x, ...  Everything that depends
-// on the row alone (vertical taps, source and output row addresses) is the
-// same for the whole workgroup, so it is computed once on the scalar unit;
-// a lane keeps its column's horizontal taps across rows and addresses the
-// frame with 32-bit offsets from those row bases.  The channel bytes sit at
-// fixed positions of a pixel word (SH0..SH2), so each unpacks with one
-// conversion.
+// One source-row pair of an output row, as the gather kernel sees it: the
+// same for the whole workgroup, so it lives in scalar registers.
+struct GatherRow {
+    bool inside;          // the output row lies in the resampled region (else pad)
+    bool fast;            // every lane's windows end inside the input
+    float wy;             // vertical weight
+    RowBase b0, b1;       // the two source rows' bases
+};
+
+__device__ __forceinline__ GatherRow gather_row(const PreParams& p, int64_t fbase, int y) {
+    GatherRow g;
+    const int dy = y - p.top;
+    g.inside = dy >= 0 && dy < p.reg_h;
+    // Pad rows read (and ignore) the region's nearest row, so their loads
+    // stay inside the frame.
+    const int dyc = dy < 0 ? 0 : (dy >= p.reg_h ? p.reg_h - 1 : dy);
+    const AxisTap ty = exact_tap(dyc, p.src_h, p.reg_h, p.inv_den_y, p.magic_y);
+    g.wy = ty.w;
+    const int64_t row_bytes = 3 * (int64_t)p.src_w;
+    g.b0 = row_base(p, fbase + (int64_t)ty.i0 * row_bytes);
+    g.b1 = row_base(p, fbase + (int64_t)ty.i1 * row_bytes);
+    // The last window of a row starts at most 3 (src_w - 1) + 3 bytes past
+    // the row base.
+    const uint32_t last = (uint32_t)(3 * (p.src_w - 1) + 3) & ~3u;
+    g.fast = last + 12u <= g.b0.avail && last + 12u <= g.b1.avail;
+    return g;
+}
+
+// Device-resident frames, each thread reading its taps straight from global
+// memory, one window per source row, so nothing is staged and no barrier
+// precedes the loads.  Same taps and arithmetic as preprocess_kernel<PX>.
+// Workgroup (blockIdx.x, blockIdx.y) owns rows_per_group consecutive output
+// rows of frame blockIdx.y; a thread owns output columns threadIdx.x,
+// + blockDim.x, ... of each of those rows.  What depends on the row alone
+// (vertical taps, source and output row addresses) is the same for the whole
+// workgroup and is computed on the scalar unit; a lane keeps its column's
+// horizontal taps across rows and addresses the frame with 32-bit offsets
+// from the row bases.  The channel bytes sit at fixed positions of a pixel
+// word (SH0..SH2), so each unpacks with one conversion.  (Two or four columns
+// per thread, with all their windows requested together, and workgroups that
+// walk many rows with the next row's windows requested ahead, both ran
+// slower on MI355X: the most short-lived waves streamed best.)
 template <typename OutT, int SH0, int SH1, int SH2>
 __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
     using Fmt = OutFormat<OutT>;
     constexpr uint32_t kShift[3] = {SH0, SH1, SH2};
-    const int f = blockIdx.x / p.groups_per_frame;
-    const int grp = blockIdx.x - f * p.groups_per_frame;
-    const int y_base = grp * p.rows_per_group;
+    const int y_base = (int)blockIdx.x * p.rows_per_group;
     const int nrows = min(p.rows_per_group, p.dst_h - y_base);
-    const int64_t fbase = (int64_t)f * p.frame_bytes;
-    const int64_t row_bytes = 3 * (int64_t)p.src_w;
+    const int64_t fbase = (int64_t)blockIdx.y * p.frame_bytes;
     const int64_t plane = (int64_t)p.dst_h * p.dst_w;
-    OutT* const frame_out = reinterpret_cast<OutT*>(p.dst) + (int64_t)f * 3 * plane;
+    OutT* const frame_out = reinterpret_cast<OutT*>(p.dst) + (int64_t)blockIdx.y * 3 * plane;
     for (uint32_t x = threadIdx.x; x < (uint32_t)p.dst_w; x += blockDim.x) {
+        // Pad columns take the region's nearest column's taps, so every load
+        // stays inside the frame.
         const int dx = (int)x - p.left;
         const bool col_in = dx >= 0 && dx < p.reg_w;
-        AxisTap tx{0u, 0u, 0.0f};
-        if (col_in) tx = exact_tap(dx, p.src_w, p.reg_w, p.inv_den_x, p.magic_x);
-        const uint32_t cx = 3u * tx.i0;               // first tap byte within a row
-        const uint32_t d = 3u * (tx.i1 - tx.i0);      // 0 (edge clamp) or 3
+        const int dxc = dx < 0 ? 0 : (dx >= p.reg_w ? p.reg_w - 1 : dx);
+        const AxisTap tx = exact_tap(dxc, p.src_w, p.reg_w, p.inv_den_x, p.magic_x);
+        const uint32_t cx = 3u * tx.i0;                 // first tap byte within a row
+        const uint32_t d = 3u * (tx.i1 - tx.i0);        // 0 (edge clamp) or 3
         for (int r = 0; r < nrows; ++r) {
             const int y = y_base + r;
-            const int dy = y - p.top;
+            const GatherRow g = gather_row(p, fbase, y);
+            uint32_t w0[3], w1[3];
+            if (g.fast) {
+                load_window_fast(g.b0, (g.b0.mis + cx) & ~3u, w0);
+                load_window_fast(g.b1, (g.b1.mis + cx) & ~3u, w1);
+            } else {
+                // The input's last rows: windows near its end read bytewise.
+                load_window_at(g.b0, (g.b0.mis + cx) & ~3u, w0);
+                load_window_at(g.b1, (g.b1.mis + cx) & ~3u, w1);
+            }
             float out[3];
-            if (dy >= 0 && dy < p.reg_h && col_in) {
-                const AxisTap ty = exact_tap(dy, p.src_h, p.reg_h, p.inv_den_y, p.magic_y);
-                const RowBase b0 = row_base(p, fbase + (int64_t)ty.i0 * row_bytes);
-                const RowBase b1 = row_base(p, fbase + (int64_t)ty.i1 * row_bytes);
-                const uint32_t e0 = b0.mis + cx, e1 = b1.mis + cx;
-                uint32_t w0[3], w1[3];
-                load_window_at(b0, e0 & ~3u, w0);
-                load_window_at(b1, e1 & ~3u, w1);
-                const uint32_t o0 = e0 & 3u, o1 = e1 & 3u;
+            if (g.inside && col_in) {
+                const uint32_t o0 = (g.b0.mis + cx) & 3u, o1 = (g.b1.mis + cx) & 3u;
                 const uint32_t t00 = window_rgb(w0, o0), t01 = window_rgb(w0, o0 + d);
                 const uint32_t t10 = window_rgb(w1, o1), t11 = window_rgb(w1, o1 + d);
 #pragma unroll
@@ -345,7 +385,7 @@ __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
                     const float p10 = chan(t10, sh), p11 = chan(t11, sh);
                     const float h0 = fmaf(tx.w, p01 - p00, p00);
                     const float h1 = fmaf(tx.w, p11 - p10, p10);
-                    const float v = fmaf(ty.w, h1 - h0, h0);
+                    const float v = fmaf(g.wy, h1 - h0, h0);
                     out[c] = fmaf(v, p.a[c], p.b[c]);
                 }
             } else {
@@ -363,13 +403,16 @@ template <typename OutT>
 hipError_t launch_preprocess_as(const PreParams& p, dim3 g, dim3 b, unsigned lds,
                                 hipStream_t stream) {
     switch (p.pixels_per_thread) {
-        case 1:
+        case 1: {
+            // Frame in the grid's y dimension, row group in x.
+            const dim3 gg((unsigned)p.groups_per_frame, g.x / (unsigned)p.groups_per_frame);
             // Channel byte positions of a pixel word: RGB or BGR producers.
             if (p.shift[0] == 0)
-                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16>), g, b, 0, stream, p);
+                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16>), gg, b, 0, stream, p);
             else
-                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0>), g, b, 0, stream, p);
+                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0>), gg, b, 0, stream, p);
             break;
+        }
         case 2: hipLaunchKernelGGL((preprocess_kernel<2, OutT>), g, b, lds, stream, p); break;
         case 4: hipLaunchKernelGGL((preprocess_kernel<4, OutT>), g, b, lds, stream, p); break;
         default: return hipErrorInvalidValue;

@@ -84,16 +84,19 @@ KERNEL_SOURCES = {
 # counters read for a plain 256 MiB device copy.
 MEASURED = {
     "preprocess": {
-        "sha256_prefix": "a3510c37b49018d8",
+        "sha256_prefix": "93e68c8ac1ab1abc",
         "profile": "profiles/preprocess_c5t_64x1280x720_to_224.md",
-        # cold: the 400 launches rotated over four lanes' batches, start-to-
-        # start period (kernel median 28.677 us); warm: the median of the
-        # other launches of this grid (back-to-back stage launches and graph
-        # replays).  traffic: FETCH_SIZE 53,783 KiB x 2.0 + WRITE_SIZE
-        # 37,632 KiB per launch (median of 547 dispatches), calibrated on a
-        # 256 MiB device copy (FETCH_SIZE 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
-        "c5t_64x1280x720_to_224": {"cold_us": 28.815, "cold_kernel_us": 28.677,
-                                   "warm_us": 22.117, "traffic": 110_147_584 + 38_535_168},
+        # The 64-frame batch runs the gather kernel with streaming (non-
+        # temporal) frame loads.  cold: the 400 launches rotated over four
+        # lanes' batches, start-to-start period (kernel median 26.276 us);
+        # warm: the median of the other launches of this grid (back-to-back
+        # stage launches and graph replays; streaming loads keep the batch out
+        # of the caches, so these read HBM too).  traffic: FETCH_SIZE
+        # 53,801.5 KiB x 2.0 + WRITE_SIZE 37,632 KiB per launch (median of 547
+        # dispatches), calibrated on a 256 MiB device copy (FETCH_SIZE
+        # 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
+        "c5t_64x1280x720_to_224": {"cold_us": 26.147, "cold_kernel_us": 26.276,
+                                   "warm_us": 26.436, "traffic": 110_185_472 + 38_535_168},
     },
 }
 
@@ -532,6 +535,28 @@ def pinned_h2d_gbs(torch, nbytes: int = 64 << 20, reps: int = 20) -> float:
     gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del h, d
     return gbs
+
+
+def cached_loads_figures(w, torch) -> dict:
+    """The C5T preprocess with cached frame loads (WS_LOADS_CACHED) beside the
+    streaming default: warm (the same batch back to back, so it is read from
+    the last-level cache) and cold (rotated over four lanes' batches), in
+    microseconds per launch."""
+    from post_processing_amd import ws
+    held = KNOBS.get("input_loads")
+    KNOBS["input_loads"] = ws.LOADS_CACHED
+    try:
+        lane = make_lane(w, torch)
+        try:
+            warm = lane.time_stage(ws.STAGE_PREPROCESS, 500) * 1e3
+            cold = rotated_times(w, torch, lane)[f"rotate_{ROTATE_LANES}_lanes"]
+        finally:
+            lane.destroy()
+    finally:
+        KNOBS["input_loads"] = held
+    b = preprocess_bytes(w)["total"]
+    return {"warm_us": round(warm, 3), "warm_frac": round(b / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
+            "cold_us": round(cold, 3), "cold_frac": round(b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
 
 
 def c5l_figures(torch, steps: int = 1000, warmup: int = 100) -> dict:
@@ -1101,6 +1126,8 @@ def main(argv=None) -> int:
                     help="override the workload's input mode")
     ap.add_argument("--pixels-per-thread", type=int, default=0,
                     help="preprocess tuning knob: 1, 2 or 4 (0 = auto)")
+    ap.add_argument("--input-loads", default="auto", choices=["auto", "cached", "streaming"],
+                    help="how the preprocess kernel reads device-resident frames (WS_LOADS_*)")
     ap.add_argument("--autotune", action="store_true",
                     help="let each lane time candidate launch geometries at create")
     ap.add_argument("--wait", default="spin", choices=["spin", "block"],
@@ -1180,6 +1207,8 @@ def main(argv=None) -> int:
 
     KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
                  pixels_per_thread=args.pixels_per_thread, autotune=args.autotune,
+                 input_loads={"auto": ws.LOADS_AUTO, "cached": ws.LOADS_CACHED,
+                              "streaming": ws.LOADS_STREAMING}[args.input_loads],
                  wait_mode=ws.WAIT_BLOCK if args.wait == "block" else ws.WAIT_SPIN)
     TENSOR["dtype"] = args.dtype
     if args.input:
@@ -1258,6 +1287,9 @@ def main(argv=None) -> int:
         if name == "c5t" and not args.no_extras:
             print("[bench] C5L lanes", file=sys.stderr, flush=True)
             extra["c5l"] = c5l_figures(torch)
+            if lane.plan().get("stream_loads"):
+                print("[bench] the same batch with cached frame loads", file=sys.stderr, flush=True)
+                extra["cached_frame_loads"] = cached_loads_figures(w, torch)
             print("[bench] single-frame lanes", file=sys.stderr, flush=True)
             extra["single_frame"] = single_frame_figures(torch)
             if SIGNALS["mode"] == "polled" and not under_profiler():
@@ -1295,6 +1327,7 @@ def main(argv=None) -> int:
                    "graph": True, "lanes": 8 if name == "c5l" else args.lanes,
                    "wait": args.wait,
                    "signals": SIGNALS["mode"],
+                   "frame_loads": "streaming" if res["plan"].get("stream_loads") else "cached",
                    "graph_packet_capture": args.graph_packet_capture,
                    "host_core": pinned,
                    "parallelism": "single_gpu"},

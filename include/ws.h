@@ -129,6 +129,15 @@ typedef struct ws_det_result {
 #define WS_WAIT_SPIN   0        /* ws_wait polls the completion event        */
 #define WS_WAIT_BLOCK  1        /* ws_wait blocks in the runtime             */
 
+#define WS_LOADS_AUTO      0    /* streaming for device-resident batches of
+                                   WS_STREAM_MIN_BATCH frames or more, cached
+                                   otherwise                                 */
+#define WS_LOADS_CACHED    1    /* frame loads allocate in the caches        */
+#define WS_LOADS_STREAMING 2    /* frame loads are non-temporal: a frame read
+                                   once does not displace other data, and a
+                                   batch replayed again is read from HBM     */
+#define WS_STREAM_MIN_BATCH 8
+
 /* Limits checked by ws_create_lane. */
 #define WS_MAX_K       32
 #define WS_MAX_BATCH   64
@@ -191,6 +200,10 @@ typedef struct ws_lane_config {
     int32_t det_reserved;      /* must be 0                                     */
     const float *det_head_dev; /* borrowed head, or NULL: the lane owns one,
                                   zero-filled at create                         */
+    /* How the preprocess kernel reads device-resident frames (a tuning knob:
+     * it changes speed, never results). */
+    int32_t input_loads;       /* WS_LOADS_*                                    */
+    int32_t reserved;          /* must be 0                                     */
 } ws_lane_config;
 
 /* Stable views of a lane's buffers, valid from ws_create_lane to ws_destroy.

@@ -279,11 +279,19 @@ __device__ __forceinline__ RowBase row_base(const PreParams& p, int64_t row_star
 
 // Three dwords at byte offset `off` (a multiple of 4) from the row base, when
 // the caller has checked that they lie inside the input.
+// NT: non-temporal loads (a frame read once does not displace cached data).
+template <bool NT>
 __device__ __forceinline__ void load_window_fast(const RowBase& rb, uint32_t off, uint32_t (&w)[3]) {
     const uint32_t* s = reinterpret_cast<const uint32_t*>(rb.ptr + off);
-    w[0] = s[0];
-    w[1] = s[1];
-    w[2] = s[2];
+    if constexpr (NT) {
+        w[0] = __builtin_nontemporal_load(s);
+        w[1] = __builtin_nontemporal_load(s + 1);
+        w[2] = __builtin_nontemporal_load(s + 2);
+    } else {
+        w[0] = s[0];
+        w[1] = s[1];
+        w[2] = s[2];
+    }
 }
 
 // Three dwords at byte offset `off` (a multiple of 4) from the row base, or,
@@ -339,11 +347,12 @@ __device__ __forceinline__ GatherRow gather_row(const PreParams& p, int64_t fbas
 // workgroup and is computed on the scalar unit; a lane keeps its column's
 // horizontal taps across rows and addresses the frame with 32-bit offsets
 // from the row bases.  The channel bytes sit at fixed positions of a pixel
-// word (SH0..SH2), so each unpacks with one conversion.  (Two or four columns
+// word (SH0..SH2), so each unpacks with one conversion.  NT selects
+// non-temporal frame loads.  (Two or four columns
 // per thread, with all their windows requested together, and workgroups that
 // walk many rows with the next row's windows requested ahead, both ran
 // slower on MI355X: the most short-lived waves streamed best.)
-template <typename OutT, int SH0, int SH1, int SH2>
+template <typename OutT, int SH0, int SH1, int SH2, bool NT>
 __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
     using Fmt = OutFormat<OutT>;
     constexpr uint32_t kShift[3] = {SH0, SH1, SH2};
@@ -366,8 +375,8 @@ __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
             const GatherRow g = gather_row(p, fbase, y);
             uint32_t w0[3], w1[3];
             if (g.fast) {
-                load_window_fast(g.b0, (g.b0.mis + cx) & ~3u, w0);
-                load_window_fast(g.b1, (g.b1.mis + cx) & ~3u, w1);
+                load_window_fast<NT>(g.b0, (g.b0.mis + cx) & ~3u, w0);
+                load_window_fast<NT>(g.b1, (g.b1.mis + cx) & ~3u, w1);
             } else {
                 // The input's last rows: windows near its end read bytewise.
                 load_window_at(g.b0, (g.b0.mis + cx) & ~3u, w0);
@@ -407,10 +416,17 @@ hipError_t launch_preprocess_as(const PreParams& p, dim3 g, dim3 b, unsigned lds
             // Frame in the grid's y dimension, row group in x.
             const dim3 gg((unsigned)p.groups_per_frame, g.x / (unsigned)p.groups_per_frame);
             // Channel byte positions of a pixel word: RGB or BGR producers.
-            if (p.shift[0] == 0)
-                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16>), gg, b, 0, stream, p);
-            else
-                hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0>), gg, b, 0, stream, p);
+            if (p.shift[0] == 0) {
+                if (p.stream_loads)
+                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16, true>), gg, b, 0, stream, p);
+                else
+                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16, false>), gg, b, 0, stream, p);
+            } else {
+                if (p.stream_loads)
+                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0, true>), gg, b, 0, stream, p);
+                else
+                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0, false>), gg, b, 0, stream, p);
+            }
             break;
         }
         case 2: hipLaunchKernelGGL((preprocess_kernel<2, OutT>), g, b, lds, stream, p); break;

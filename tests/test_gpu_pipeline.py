@@ -148,6 +148,32 @@ def test_throughput_batch_parity(gpu_lib, mode):
         r.close()
 
 
+@pytest.mark.parametrize("name,loads", [("c2", "streaming"), ("c3", "streaming"),
+                                         ("c4", "streaming"), ("c5t", "cached")])
+def test_frame_load_modes(gpu_lib, name, loads):
+    """Both frame-load forms of the gather kernel, each on the workloads its
+    automatic choice does not give it (single frames stream here, the
+    64-frame batch reads through the caches), match the oracle and the other
+    form bit for bit; the lane reports the form it runs."""
+    w = wl.c5_throughput(64) if name == "c5t" else wl.ALL_CONFIGS[name]()
+    ref, _ = oracle_outputs(w)
+    mode = ws.LOADS_STREAMING if loads == "streaming" else ws.LOADS_CACHED
+    r = Run(w, host_input=False, input_loads=mode)
+    a = Run(w, host_input=False)
+    try:
+        assert r.lane.plan()["stream_loads"] == (1 if loads == "streaming" else 0)
+        assert a.lane.plan()["stream_loads"] == (1 if name == "c5t" else 0)
+        r.run()
+        a.run()
+        t, _ = r.outputs()
+        u, _ = a.outputs()
+        assert_tensor_close(t, ref)
+        assert np.array_equal(t.view(np.uint32), u.view(np.uint32))
+    finally:
+        r.close()
+        a.close()
+
+
 @pytest.mark.parametrize("seed", range(24))
 @pytest.mark.parametrize("letterbox", [False, True])
 def test_random_small_shapes(gpu_lib, seed, letterbox):

@@ -84,19 +84,18 @@ KERNEL_SOURCES = {
 # counters read for a plain 256 MiB device copy.
 MEASURED = {
     "preprocess": {
-        "sha256_prefix": "93e68c8ac1ab1abc",
+        "sha256_prefix": "dc547138b8977c1f",
         "profile": "profiles/preprocess_c5t_64x1280x720_to_224.md",
-        # The 64-frame batch runs the gather kernel with streaming (non-
-        # temporal) frame loads.  cold: the 400 launches rotated over four
-        # lanes' batches, start-to-start period (kernel median 26.276 us);
-        # warm: the median of the other launches of this grid (back-to-back
-        # stage launches and graph replays; streaming loads keep the batch out
-        # of the caches, so these read HBM too).  traffic: FETCH_SIZE
-        # 53,801.5 KiB x 2.0 + WRITE_SIZE 37,632 KiB per launch (median of 547
-        # dispatches), calibrated on a 256 MiB device copy (FETCH_SIZE
-        # 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
-        "c5t_64x1280x720_to_224": {"cold_us": 26.147, "cold_kernel_us": 26.276,
-                                   "warm_us": 26.436, "traffic": 110_185_472 + 38_535_168},
+        # The 64-frame batch runs the gather kernel with the streaming cache
+        # policy (non-temporal frame loads and tensor stores).  cold: the 400
+        # launches rotated over four lanes' batches, start-to-start period
+        # (kernel median 25.277 us); warm: the median of the other launches
+        # of this grid (back-to-back stage launches and graph replays).
+        # traffic: FETCH_SIZE 53,800.75 KiB x 2.0 + WRITE_SIZE 37,632 KiB per
+        # launch (median of 547 dispatches), calibrated on a 256 MiB device
+        # copy (FETCH_SIZE 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
+        "c5t_64x1280x720_to_224": {"cold_us": 25.432, "cold_kernel_us": 25.277,
+                                   "warm_us": 22.197, "traffic": 110_183_936 + 38_535_168},
     },
 }
 
@@ -537,14 +536,14 @@ def pinned_h2d_gbs(torch, nbytes: int = 64 << 20, reps: int = 20) -> float:
     return gbs
 
 
-def cached_loads_figures(w, torch) -> dict:
-    """The C5T preprocess with cached frame loads (WS_LOADS_CACHED) beside the
-    streaming default: warm (the same batch back to back, so it is read from
-    the last-level cache) and cold (rotated over four lanes' batches), in
-    microseconds per launch."""
+def cache_keep_figures(w, torch) -> dict:
+    """The C5T preprocess with ordinary (cached) frame loads and tensor stores
+    (WS_CACHE_KEEP) beside the streaming default: warm (the same batch back to
+    back, so it is read from the last-level cache) and cold (rotated over four
+    lanes' batches), in microseconds per launch."""
     from post_processing_amd import ws
-    held = KNOBS.get("input_loads")
-    KNOBS["input_loads"] = ws.LOADS_CACHED
+    held = KNOBS.get("cache_policy")
+    KNOBS["cache_policy"] = ws.CACHE_KEEP
     try:
         lane = make_lane(w, torch)
         try:
@@ -553,7 +552,7 @@ def cached_loads_figures(w, torch) -> dict:
         finally:
             lane.destroy()
     finally:
-        KNOBS["input_loads"] = held
+        KNOBS["cache_policy"] = held
     b = preprocess_bytes(w)["total"]
     return {"warm_us": round(warm, 3), "warm_frac": round(b / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
             "cold_us": round(cold, 3), "cold_frac": round(b / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
@@ -1126,8 +1125,8 @@ def main(argv=None) -> int:
                     help="override the workload's input mode")
     ap.add_argument("--pixels-per-thread", type=int, default=0,
                     help="preprocess tuning knob: 1, 2 or 4 (0 = auto)")
-    ap.add_argument("--input-loads", default="auto", choices=["auto", "cached", "streaming"],
-                    help="how the preprocess kernel reads device-resident frames (WS_LOADS_*)")
+    ap.add_argument("--cache-policy", default="auto", choices=["auto", "keep", "stream"],
+                    help="the preprocess kernel's frame loads and tensor stores (WS_CACHE_*)")
     ap.add_argument("--autotune", action="store_true",
                     help="let each lane time candidate launch geometries at create")
     ap.add_argument("--wait", default="spin", choices=["spin", "block"],
@@ -1207,8 +1206,8 @@ def main(argv=None) -> int:
 
     KNOBS.update(rows_per_group=args.rows_per_group, topk_chunk=args.topk_chunk,
                  pixels_per_thread=args.pixels_per_thread, autotune=args.autotune,
-                 input_loads={"auto": ws.LOADS_AUTO, "cached": ws.LOADS_CACHED,
-                              "streaming": ws.LOADS_STREAMING}[args.input_loads],
+                 cache_policy={"auto": ws.CACHE_AUTO, "keep": ws.CACHE_KEEP,
+                               "stream": ws.CACHE_STREAM}[args.cache_policy],
                  wait_mode=ws.WAIT_BLOCK if args.wait == "block" else ws.WAIT_SPIN)
     TENSOR["dtype"] = args.dtype
     if args.input:
@@ -1287,9 +1286,10 @@ def main(argv=None) -> int:
         if name == "c5t" and not args.no_extras:
             print("[bench] C5L lanes", file=sys.stderr, flush=True)
             extra["c5l"] = c5l_figures(torch)
-            if lane.plan().get("stream_loads"):
-                print("[bench] the same batch with cached frame loads", file=sys.stderr, flush=True)
-                extra["cached_frame_loads"] = cached_loads_figures(w, torch)
+            if lane.plan().get("streaming"):
+                print("[bench] the same batch with cached loads and stores", file=sys.stderr,
+                      flush=True)
+                extra["cache_keep"] = cache_keep_figures(w, torch)
             print("[bench] single-frame lanes", file=sys.stderr, flush=True)
             extra["single_frame"] = single_frame_figures(torch)
             if SIGNALS["mode"] == "polled" and not under_profiler():
@@ -1327,7 +1327,7 @@ def main(argv=None) -> int:
                    "graph": True, "lanes": 8 if name == "c5l" else args.lanes,
                    "wait": args.wait,
                    "signals": SIGNALS["mode"],
-                   "frame_loads": "streaming" if res["plan"].get("stream_loads") else "cached",
+                   "cache_policy": "stream" if res["plan"].get("streaming") else "keep",
                    "graph_packet_capture": args.graph_packet_capture,
                    "host_core": pinned,
                    "parallelism": "single_gpu"},

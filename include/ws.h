@@ -129,13 +129,14 @@ typedef struct ws_det_result {
 #define WS_WAIT_SPIN   0        /* ws_wait polls the completion event        */
 #define WS_WAIT_BLOCK  1        /* ws_wait blocks in the runtime             */
 
-#define WS_LOADS_AUTO      0    /* streaming for device-resident batches of
-                                   WS_STREAM_MIN_BATCH frames or more, cached
-                                   otherwise                                 */
-#define WS_LOADS_CACHED    1    /* frame loads allocate in the caches        */
-#define WS_LOADS_STREAMING 2    /* frame loads are non-temporal: a frame read
-                                   once does not displace other data, and a
-                                   batch replayed again is read from HBM     */
+#define WS_CACHE_AUTO   0       /* WS_CACHE_STREAM for device-resident batches
+                                   of WS_STREAM_MIN_BATCH frames or more,
+                                   WS_CACHE_KEEP otherwise                   */
+#define WS_CACHE_KEEP   1       /* frame loads and tensor stores allocate in
+                                   the caches                                */
+#define WS_CACHE_STREAM 2       /* frame loads and tensor stores are
+                                   non-temporal: a batch streamed through
+                                   once does not displace other data         */
 #define WS_STREAM_MIN_BATCH 8
 
 /* Limits checked by ws_create_lane. */
@@ -200,9 +201,9 @@ typedef struct ws_lane_config {
     int32_t det_reserved;      /* must be 0                                     */
     const float *det_head_dev; /* borrowed head, or NULL: the lane owns one,
                                   zero-filled at create                         */
-    /* How the preprocess kernel reads device-resident frames (a tuning knob:
-     * it changes speed, never results). */
-    int32_t input_loads;       /* WS_LOADS_*                                    */
+    /* How the preprocess kernel reads device-resident frames and writes the
+     * tensor (a tuning knob: it changes speed, never results). */
+    int32_t cache_policy;      /* WS_CACHE_*                                    */
     int32_t reserved;          /* must be 0                                     */
 } ws_lane_config;
 

@@ -31,7 +31,8 @@ typedef struct ws_lane_plan {
     int32_t det_anchors;      /* detection anchors (0 = no detection stage)  */
     int32_t det_decode_groups;/* decode workgroups (64 anchors each)         */
     int32_t topk_keys_per_lane;/* Top-K scores per lane per batch: 16 or 32  */
-    int32_t stream_loads;      /* 1 = non-temporal frame loads (WS_LOADS_*)  */
+    int32_t streaming;         /* 1 = non-temporal frame loads and tensor
+                                  stores (WS_CACHE_*)                         */
 } ws_lane_plan;
 
 /* Fill *plan for lane.  Returns WS_OK or WS_E_INVALID_ARG (NULL). */

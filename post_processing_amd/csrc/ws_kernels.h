@@ -30,7 +30,7 @@ struct PreParams {
     int32_t span_lo;        // first staged byte of a source row
     int32_t slot_chunks;    // 16-byte chunks per staged row
     int32_t pixels_per_thread;  // PX: 1, 2 or 4 adjacent output columns
-    int32_t stream_loads;       // gather kernel: non-temporal frame loads
+    int32_t streaming;          // gather kernel: non-temporal frame loads and tensor stores
     int32_t threads_per_row;    // ceil(dst_w / PX)
     int32_t rows_per_group;
     int32_t groups_per_frame;

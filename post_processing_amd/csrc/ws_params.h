@@ -33,7 +33,7 @@ inline void fill_pre_params(const ws_lane_config& c, const Plan& P, const uint8_
     q.span_lo = (int32_t)P.span_lo;
     q.slot_chunks = P.slot_bytes / 16;
     q.pixels_per_thread = P.pixels_per_thread;
-    q.stream_loads = P.stream_loads ? 1 : 0;
+    q.streaming = P.streaming ? 1 : 0;
     q.threads_per_row = P.threads_per_row;
     q.rows_per_group = P.rows_per_group;
     q.groups_per_frame = P.groups_per_frame;

@@ -160,8 +160,8 @@ inline int validate_config(const ws_lane_config* c) {
     if (c->channel_order != WS_CHANNELS_RGB && c->channel_order != WS_CHANNELS_BGR)
         return WS_E_INVALID_ARG;
     if (c->autotune != 0 && c->autotune != 1) return WS_E_INVALID_ARG;
-    if (c->input_loads != WS_LOADS_AUTO && c->input_loads != WS_LOADS_CACHED &&
-        c->input_loads != WS_LOADS_STREAMING)
+    if (c->cache_policy != WS_CACHE_AUTO && c->cache_policy != WS_CACHE_KEEP &&
+        c->cache_policy != WS_CACHE_STREAM)
         return WS_E_INVALID_ARG;
     if (c->reserved != 0) return WS_E_INVALID_ARG;
     return validate_detection(c);
@@ -186,7 +186,7 @@ struct Plan {
     int64_t span_lo = 0, span = 0;
     int32_t slot_bytes = 0;        // LDS bytes per staged source row (16-multiple)
     int32_t pixels_per_thread = 1; // adjacent output columns per thread (1, 2, 4)
-    bool stream_loads = false;     // gather kernel reads frames non-temporally
+    bool streaming = false;        // gather kernel: non-temporal loads and stores
     int32_t threads_per_row = 0;   // ceil(dst_w / pixels_per_thread)
     int32_t rows_per_group = 1;
     int32_t pre_block = 64;
@@ -268,16 +268,16 @@ inline int make_plan(const ws_lane_config& c, Plan* p) {
     // 512).  The gather kernel gives each thread one column of all its rows,
     // with workgroups of up to 1024 threads, so a 640-wide row takes one pass.
     const int64_t threads = staged ? (int64_t)rows * q : q;
-    // A batch of device-resident frames is read once per launch: streaming
-    // loads keep it from displacing the tensor's lines and earlier batches'
-    // write-back from the last-level cache (64 x 1280x720 -> 224: 28.8 ->
-    // 26.4 us per launch with inputs evicted between launches, measured on
-    // MI355X).  The same batch replayed again is then read from HBM each
-    // time (21.9 -> 26.2 us), so single frames, whose producer may have just
-    // written them, keep cached loads.
-    p->stream_loads = !staged && c.input_mode == WS_INPUT_DEVICE &&
-                      (c.input_loads == WS_LOADS_STREAMING ||
-                       (c.input_loads == WS_LOADS_AUTO && c.batch >= WS_STREAM_MIN_BATCH));
+    // A batch of device-resident frames is streamed through once per launch:
+    // non-temporal frame loads and tensor stores keep it from displacing what
+    // the last-level cache holds (64 x 1280x720 -> 224, measured on MI355X:
+    // 28.8 -> 25.4 us per launch with the batches evicted between launches,
+    // 22.0 -> 22.3 us for the same batch replayed).  Single frames, whose
+    // producer may just have written them and whose tensor the next stage
+    // reads, keep ordinary loads and stores.
+    p->streaming = !staged && c.input_mode == WS_INPUT_DEVICE &&
+                      (c.cache_policy == WS_CACHE_STREAM ||
+                       (c.cache_policy == WS_CACHE_AUTO && c.batch >= WS_STREAM_MIN_BATCH));
     const int64_t block_cap = staged ? kMaxPreBlock : kMaxGatherBlock;
     p->pre_block = (int32_t)std::min<int64_t>(block_cap, ceil_div(threads, 64) * 64);
     p->groups_per_frame = (int32_t)ceil_div(Dh, rows);

@@ -79,16 +79,23 @@ __device__ __forceinline__ float chan(uint32_t px, uint32_t shift) {
 template <typename T> struct OutFormat;
 template <> struct OutFormat<float> {
     __device__ static float cvt(float x) { return x; }
+    __device__ static void store_nt(float* d, float x) { __builtin_nontemporal_store(x, d); }
 };
 template <> struct OutFormat<__half> {
     __device__ static uint16_t bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
     __device__ static __half cvt(float x) { return __float2half_rn(x); }
     __device__ static uint32_t pack2(const float* v) { return bits(v[0]) | ((uint32_t)bits(v[1]) << 16); }
+    __device__ static void store_nt(__half* d, float x) {
+        __builtin_nontemporal_store(bits(x), reinterpret_cast<uint16_t*>(d));
+    }
 };
 template <> struct OutFormat<__hip_bfloat16> {
     __device__ static uint16_t bits(float x) { return __bfloat16_as_ushort(__float2bfloat16(x)); }
     __device__ static __hip_bfloat16 cvt(float x) { return __float2bfloat16(x); }
     __device__ static uint32_t pack2(const float* v) { return bits(v[0]) | ((uint32_t)bits(v[1]) << 16); }
+    __device__ static void store_nt(__hip_bfloat16* d, float x) {
+        __builtin_nontemporal_store(bits(x), reinterpret_cast<uint16_t*>(d));
+    }
 };
 
 // Two or four output values as one non-temporal store: the tensor is
@@ -279,7 +286,8 @@ __device__ __forceinline__ RowBase row_base(const PreParams& p, int64_t row_star
 
 // Three dwords at byte offset `off` (a multiple of 4) from the row base, when
 // the caller has checked that they lie inside the input.
-// NT: non-temporal loads (a frame read once does not displace cached data).
+// NT: non-temporal loads (a frame streamed through once does not displace
+// cached data).
 template <bool NT>
 __device__ __forceinline__ void load_window_fast(const RowBase& rb, uint32_t off, uint32_t (&w)[3]) {
     const uint32_t* s = reinterpret_cast<const uint32_t*>(rb.ptr + off);
@@ -348,7 +356,7 @@ __device__ __forceinline__ GatherRow gather_row(const PreParams& p, int64_t fbas
 // horizontal taps across rows and addresses the frame with 32-bit offsets
 // from the row bases.  The channel bytes sit at fixed positions of a pixel
 // word (SH0..SH2), so each unpacks with one conversion.  NT selects
-// non-temporal frame loads.  (Two or four columns
+// non-temporal frame loads and tensor stores.  (Two or four columns
 // per thread, with all their windows requested together, and workgroups that
 // walk many rows with the next row's windows requested ahead, both ran
 // slower on MI355X: the most short-lived waves streamed best.)
@@ -402,8 +410,13 @@ __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
                 for (int c = 0; c < 3; ++c) out[c] = p.padv[c];
             }
             OutT* const row_out = frame_out + (int64_t)y * p.dst_w;
+            if constexpr (NT) {
 #pragma unroll
-            for (int c = 0; c < 3; ++c) row_out[c * plane + x] = Fmt::cvt(out[c]);
+                for (int c = 0; c < 3; ++c) Fmt::store_nt(&row_out[c * plane + x], out[c]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 3; ++c) row_out[c * plane + x] = Fmt::cvt(out[c]);
+            }
         }
     }
 }
@@ -417,12 +430,12 @@ hipError_t launch_preprocess_as(const PreParams& p, dim3 g, dim3 b, unsigned lds
             const dim3 gg((unsigned)p.groups_per_frame, g.x / (unsigned)p.groups_per_frame);
             // Channel byte positions of a pixel word: RGB or BGR producers.
             if (p.shift[0] == 0) {
-                if (p.stream_loads)
+                if (p.streaming)
                     hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16, true>), gg, b, 0, stream, p);
                 else
                     hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16, false>), gg, b, 0, stream, p);
             } else {
-                if (p.stream_loads)
+                if (p.streaming)
                     hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0, true>), gg, b, 0, stream, p);
                 else
                     hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0, false>), gg, b, 0, stream, p);

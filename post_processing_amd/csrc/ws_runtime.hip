@@ -560,7 +560,7 @@ int ws_lane_describe(const ws_lane* L, ws_lane_plan* plan) {
     plan->det_anchors = L->plan.det_anchors;
     plan->det_decode_groups = L->plan.det_decode_groups;
     plan->topk_keys_per_lane = L->plan.topk_keys_per_lane;
-    plan->stream_loads = L->plan.stream_loads ? 1 : 0;
+    plan->streaming = L->plan.streaming ? 1 : 0;
     return WS_OK;
 }
 

@@ -42,9 +42,9 @@ CHANNELS_RGB = 0
 CHANNELS_BGR = 1
 WAIT_SPIN = 0
 WAIT_BLOCK = 1
-LOADS_AUTO = 0
-LOADS_CACHED = 1
-LOADS_STREAMING = 2
+CACHE_AUTO = 0
+CACHE_KEEP = 1
+CACHE_STREAM = 2
 MAX_K = 32
 STAGE_PREPROCESS = 0
 STAGE_TOPK = 1
@@ -83,7 +83,7 @@ class LaneConfig(Structure):
         ("det_classes", c_int32), ("det_max_det", c_int32),
         ("det_conf", c_float), ("det_iou", c_float),
         ("det_agnostic", c_int32), ("det_reserved", c_int32), ("det_head_dev", c_void_p),
-        ("input_loads", c_int32), ("reserved", c_int32),
+        ("cache_policy", c_int32), ("reserved", c_int32),
     ]
 
 
@@ -103,7 +103,7 @@ class LanePlan(Structure):
         ("pre_lds_bytes", c_int32), ("topk_groups", c_int32), ("topk_block", c_int32),
         ("topk_chunk", c_int32), ("graph_nodes", c_int32), ("pixels_per_thread", c_int32),
         ("det_anchors", c_int32), ("det_decode_groups", c_int32), ("topk_keys_per_lane", c_int32),
-        ("stream_loads", c_int32),
+        ("streaming", c_int32),
     ]
 
 
@@ -201,7 +201,7 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
                 topk_chunk=0, pixels_per_thread=0, input_mode=None, tensor_dtype=DTYPE_F32,
                 channel_order=CHANNELS_RGB, autotune=False, det_classes=0, det_max_det=300,
                 det_conf=0.25, det_iou=0.45, det_agnostic=False,
-                det_head_dev=None, input_loads=LOADS_AUTO) -> LaneConfig:
+                det_head_dev=None, cache_policy=CACHE_AUTO) -> LaneConfig:
     c = LaneConfig()
     c.device = device
     c.batch = batch
@@ -226,7 +226,7 @@ def make_config(*, src_w, src_h, dst_w, dst_h, batch=1, letterbox=False, pad=114
     c.tensor_dtype = tensor_dtype
     c.channel_order = channel_order
     c.autotune = 1 if autotune else 0
-    c.input_loads = input_loads
+    c.cache_policy = cache_policy
     c.det_classes = det_classes
     if det_classes:
         c.det_max_det = det_max_det

@@ -73,8 +73,8 @@ static int selftest() {
     BAD(tensor_dtype, 3);
     BAD(channel_order, 2);
     BAD(autotune, 2);
-    BAD(input_loads, 3);
-    BAD(input_loads, -1);
+    BAD(cache_policy, 3);
+    BAD(cache_policy, -1);
     BAD(reserved, 1);
     {
         // detection: a valid 640x640 detection lane, then each field out of range
@@ -189,22 +189,23 @@ static int selftest() {
     CHECK(ws::make_plan(c, &p) == WS_OK);
     // One thread per output column, each walking the workgroup's seven rows.
     CHECK(p.rows_per_group == 7 && p.lds_bytes == 0 && p.pre_block == 384);
-    // Frame loads: streaming for device-resident batches of 8 or more frames
-    // (or when asked), cached otherwise; the staged kernels never stream.
+    // Cache policy: non-temporal frame loads and tensor stores for
+    // device-resident batches of 8 or more frames (or when asked), ordinary
+    // ones otherwise; the staged kernels never stream.
     c = good();
-    CHECK(ws::make_plan(c, &p) == WS_OK && !p.stream_loads);
+    CHECK(ws::make_plan(c, &p) == WS_OK && !p.streaming);
     c.batch = WS_STREAM_MIN_BATCH;
-    CHECK(ws::make_plan(c, &p) == WS_OK && p.stream_loads);
-    c.input_loads = WS_LOADS_CACHED;
-    CHECK(ws::make_plan(c, &p) == WS_OK && !p.stream_loads);
+    CHECK(ws::make_plan(c, &p) == WS_OK && p.streaming);
+    c.cache_policy = WS_CACHE_KEEP;
+    CHECK(ws::make_plan(c, &p) == WS_OK && !p.streaming);
     c.input_mode = WS_INPUT_MAPPED_HOST;
-    c.input_loads = WS_LOADS_STREAMING;
-    CHECK(ws::make_plan(c, &p) == WS_OK && !p.stream_loads);
+    c.cache_policy = WS_CACHE_STREAM;
+    CHECK(ws::make_plan(c, &p) == WS_OK && !p.streaming);
     c = good();
-    c.input_loads = WS_LOADS_STREAMING;
-    CHECK(ws::make_plan(c, &p) == WS_OK && p.stream_loads);
+    c.cache_policy = WS_CACHE_STREAM;
+    CHECK(ws::make_plan(c, &p) == WS_OK && p.streaming);
     c.pixels_per_thread = 2;
-    CHECK(ws::make_plan(c, &p) == WS_OK && !p.stream_loads);
+    CHECK(ws::make_plan(c, &p) == WS_OK && !p.streaming);
     c = good();
     c.num_scores = 672000;
     c.k = 32;
@@ -273,7 +274,7 @@ static int layout() {
     std::printf("ws_lane_config det_agnostic %zu\n", offsetof(ws_lane_config, det_agnostic));
     std::printf("ws_lane_config det_reserved %zu\n", offsetof(ws_lane_config, det_reserved));
     std::printf("ws_lane_config det_head_dev %zu\n", offsetof(ws_lane_config, det_head_dev));
-    std::printf("ws_lane_config input_loads %zu\n", offsetof(ws_lane_config, input_loads));
+    std::printf("ws_lane_config cache_policy %zu\n", offsetof(ws_lane_config, cache_policy));
     std::printf("ws_lane_config reserved %zu\n", offsetof(ws_lane_config, reserved));
     std::printf("ws_lane_view sizeof %zu\n", sizeof(ws_lane_view));
     std::printf("ws_lane_view input_host %zu\n", offsetof(ws_lane_view, input_host));
@@ -301,7 +302,7 @@ static int layout() {
     std::printf("ws_lane_plan det_anchors %zu\n", offsetof(ws_lane_plan, det_anchors));
     std::printf("ws_lane_plan det_decode_groups %zu\n", offsetof(ws_lane_plan, det_decode_groups));
     std::printf("ws_lane_plan topk_keys_per_lane %zu\n", offsetof(ws_lane_plan, topk_keys_per_lane));
-    std::printf("ws_lane_plan stream_loads %zu\n", offsetof(ws_lane_plan, stream_loads));
+    std::printf("ws_lane_plan streaming %zu\n", offsetof(ws_lane_plan, streaming));
     std::printf("ws_det sizeof %zu\n", sizeof(ws_det));
     std::printf("ws_det x1 %zu\n", offsetof(ws_det, x1));
     std::printf("ws_det y1 %zu\n", offsetof(ws_det, y1));

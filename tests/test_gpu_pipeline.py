@@ -148,26 +148,31 @@ def test_throughput_batch_parity(gpu_lib, mode):
         r.close()
 
 
-@pytest.mark.parametrize("name,loads", [("c2", "streaming"), ("c3", "streaming"),
-                                         ("c4", "streaming"), ("c5t", "cached")])
-def test_frame_load_modes(gpu_lib, name, loads):
-    """Both frame-load forms of the gather kernel, each on the workloads its
-    automatic choice does not give it (single frames stream here, the
-    64-frame batch reads through the caches), match the oracle and the other
-    form bit for bit; the lane reports the form it runs."""
+@pytest.mark.parametrize("name,policy,dtype", [
+    ("c2", "stream", ws.DTYPE_F32), ("c3", "stream", ws.DTYPE_F32), ("c4", "stream", ws.DTYPE_F32),
+    ("c2", "stream", ws.DTYPE_F16), ("c3", "stream", ws.DTYPE_BF16), ("c5t", "keep", ws.DTYPE_F32)])
+def test_cache_policies(gpu_lib, name, policy, dtype):
+    """Both cache policies of the gather kernel (ordinary or non-temporal frame
+    loads and tensor stores), each on workloads its automatic choice does not
+    give it (single frames stream here, the 64-frame batch keeps), match the
+    oracle and the other policy bit for bit; the lane reports the policy it
+    runs."""
     w = wl.c5_throughput(64) if name == "c5t" else wl.ALL_CONFIGS[name]()
     ref, _ = oracle_outputs(w)
-    mode = ws.LOADS_STREAMING if loads == "streaming" else ws.LOADS_CACHED
-    r = Run(w, host_input=False, input_loads=mode)
-    a = Run(w, host_input=False)
+    mode = ws.CACHE_STREAM if policy == "stream" else ws.CACHE_KEEP
+    r = Run(w, host_input=False, tensor_dtype=dtype, cache_policy=mode)
+    a = Run(w, host_input=False, tensor_dtype=dtype)
     try:
-        assert r.lane.plan()["stream_loads"] == (1 if loads == "streaming" else 0)
-        assert a.lane.plan()["stream_loads"] == (1 if name == "c5t" else 0)
+        assert r.lane.plan()["streaming"] == (1 if policy == "stream" else 0)
+        assert a.lane.plan()["streaming"] == (1 if name == "c5t" else 0)
         r.run()
         a.run()
         t, _ = r.outputs()
         u, _ = a.outputs()
-        assert_tensor_close(t, ref)
+        if dtype == ws.DTYPE_F32:
+            assert_tensor_close(t, ref)
+        else:
+            assert_rounded_close(t, ref, "f16" if dtype == ws.DTYPE_F16 else "bf16")
         assert np.array_equal(t.view(np.uint32), u.view(np.uint32))
     finally:
         r.close()

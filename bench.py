@@ -84,18 +84,18 @@ KERNEL_SOURCES = {
 # counters read for a plain 256 MiB device copy.
 MEASURED = {
     "preprocess": {
-        "sha256_prefix": "dc547138b8977c1f",
+        "sha256_prefix": "bb32d75899624327",
         "profile": "profiles/preprocess_c5t_64x1280x720_to_224.md",
         # The 64-frame batch runs the gather kernel with the streaming cache
         # policy (non-temporal frame loads and tensor stores).  cold: the 400
         # launches rotated over four lanes' batches, start-to-start period
-        # (kernel median 25.277 us); warm: the median of the other launches
+        # (kernel median 25.237 us); warm: the median of the other launches
         # of this grid (back-to-back stage launches and graph replays).
-        # traffic: FETCH_SIZE 53,800.75 KiB x 2.0 + WRITE_SIZE 37,632 KiB per
+        # traffic: FETCH_SIZE 53,799.5 KiB x 2.0 + WRITE_SIZE 37,632 KiB per
         # launch (median of 547 dispatches), calibrated on a 256 MiB device
         # copy (FETCH_SIZE 131,083.5 KiB, WRITE_SIZE 262,144 KiB).
-        "c5t_64x1280x720_to_224": {"cold_us": 25.432, "cold_kernel_us": 25.277,
-                                   "warm_us": 22.197, "traffic": 110_183_936 + 38_535_168},
+        "c5t_64x1280x720_to_224": {"cold_us": 25.305, "cold_kernel_us": 25.237,
+                                   "warm_us": 22.317, "traffic": 110_181_376 + 38_535_168},
     },
 }
 

@@ -356,11 +356,14 @@ __device__ __forceinline__ GatherRow gather_row(const PreParams& p, int64_t fbas
 // horizontal taps across rows and addresses the frame with 32-bit offsets
 // from the row bases.  The channel bytes sit at fixed positions of a pixel
 // word (SH0..SH2), so each unpacks with one conversion.  NT selects
-// non-temporal frame loads and tensor stores.  (Two or four columns
+// non-temporal frame loads and tensor stores.  PAD_ROWS marks a letterbox
+// with pad rows above or below the region: those rows store the pad value
+// without loading (a separate instance, since the extra scalar test ahead of
+// the loads slowed the plain resize's streaming launch).  (Two or four columns
 // per thread, with all their windows requested together, and workgroups that
 // walk many rows with the next row's windows requested ahead, both ran
 // slower on MI355X: the most short-lived waves streamed best.)
-template <typename OutT, int SH0, int SH1, int SH2, bool NT>
+template <typename OutT, int SH0, int SH1, int SH2, bool NT, bool PAD_ROWS>
 __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
     using Fmt = OutFormat<OutT>;
     constexpr uint32_t kShift[3] = {SH0, SH1, SH2};
@@ -382,13 +385,15 @@ __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
             const int y = y_base + r;
             const GatherRow g = gather_row(p, fbase, y);
             uint32_t w0[3], w1[3];
-            if (g.fast) {
-                load_window_fast<NT>(g.b0, (g.b0.mis + cx) & ~3u, w0);
-                load_window_fast<NT>(g.b1, (g.b1.mis + cx) & ~3u, w1);
-            } else {
-                // The input's last rows: windows near its end read bytewise.
-                load_window_at(g.b0, (g.b0.mis + cx) & ~3u, w0);
-                load_window_at(g.b1, (g.b1.mis + cx) & ~3u, w1);
+            if (!PAD_ROWS || g.inside) {
+                if (g.fast) {
+                    load_window_fast<NT>(g.b0, (g.b0.mis + cx) & ~3u, w0);
+                    load_window_fast<NT>(g.b1, (g.b1.mis + cx) & ~3u, w1);
+                } else {
+                    // The input's last rows: windows near its end read bytewise.
+                    load_window_at(g.b0, (g.b0.mis + cx) & ~3u, w0);
+                    load_window_at(g.b1, (g.b1.mis + cx) & ~3u, w1);
+                }
             }
             float out[3];
             if (g.inside && col_in) {
@@ -421,6 +426,22 @@ __global__ __launch_bounds__(1024) void preprocess_gather_kernel(PreParams p) {
     }
 }
 
+template <typename OutT, int SH0, int SH1, int SH2>
+void launch_gather(const PreParams& p, dim3 g, dim3 b, hipStream_t stream) {
+    const bool pad_rows = p.reg_h < p.dst_h;
+    if (p.streaming) {
+        if (pad_rows)
+            hipLaunchKernelGGL((preprocess_gather_kernel<OutT, SH0, SH1, SH2, true, true>), g, b, 0, stream, p);
+        else
+            hipLaunchKernelGGL((preprocess_gather_kernel<OutT, SH0, SH1, SH2, true, false>), g, b, 0, stream, p);
+    } else {
+        if (pad_rows)
+            hipLaunchKernelGGL((preprocess_gather_kernel<OutT, SH0, SH1, SH2, false, true>), g, b, 0, stream, p);
+        else
+            hipLaunchKernelGGL((preprocess_gather_kernel<OutT, SH0, SH1, SH2, false, false>), g, b, 0, stream, p);
+    }
+}
+
 template <typename OutT>
 hipError_t launch_preprocess_as(const PreParams& p, dim3 g, dim3 b, unsigned lds,
                                 hipStream_t stream) {
@@ -429,17 +450,10 @@ hipError_t launch_preprocess_as(const PreParams& p, dim3 g, dim3 b, unsigned lds
             // Frame in the grid's y dimension, row group in x.
             const dim3 gg((unsigned)p.groups_per_frame, g.x / (unsigned)p.groups_per_frame);
             // Channel byte positions of a pixel word: RGB or BGR producers.
-            if (p.shift[0] == 0) {
-                if (p.streaming)
-                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16, true>), gg, b, 0, stream, p);
-                else
-                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 0, 8, 16, false>), gg, b, 0, stream, p);
-            } else {
-                if (p.streaming)
-                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0, true>), gg, b, 0, stream, p);
-                else
-                    hipLaunchKernelGGL((preprocess_gather_kernel<OutT, 16, 8, 0, false>), gg, b, 0, stream, p);
-            }
+            if (p.shift[0] == 0)
+                launch_gather<OutT, 0, 8, 16>(p, gg, b, stream);
+            else
+                launch_gather<OutT, 16, 8, 0>(p, gg, b, stream);
             break;
         }
         case 2: hipLaunchKernelGGL((preprocess_kernel<2, OutT>), g, b, lds, stream, p); break;

@@ -78,13 +78,13 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Bitonic network stages for block size B with distances J, J/2, ..., 1.
-// Lanes in a block whose bit B is clear run ascending, the others descending;
-// DESC flips the whole network.  B = 64 with J = 32 is the final merge.  One
-// compare per stage: a lane keeps its own key when "mine is larger" agrees
-// with the side of the pair it must end on.
+// One bitonic network stage for block size B at lane distance J.  Lanes in a
+// block whose bit B is clear run ascending, the others descending; DESC flips
+// the whole network.  B = 64 with J = 32 is the final merge.  One compare per
+// stage: a lane keeps its own key when "mine is larger" agrees with the side
+// of the pair it must end on.
 template <int B, int J, bool DESC, typename T>
-__device__ __forceinline__ T bitonic_stages(T x, int lane) {
+__device__ __forceinline__ T bitonic_stage(T x, int lane) {
     T y;
     if constexpr (sizeof(T) == 8) y = xor_lane64<J>(x, lane);
     else y = xor_lane32<J>(x, lane);
@@ -100,6 +100,12 @@ __device__ __forceinline__ T bitonic_stages(T x, int lane) {
     } else {
         x = ((x > y) == keep_large) ? x : y;
     }
+    return x;
+}
+
+template <int B, int J, bool DESC, typename T>
+__device__ __forceinline__ T bitonic_stages(T x, int lane) {
+    x = bitonic_stage<B, J, DESC>(x, lane);
     if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC>(x, lane);
     return x;
 }

@@ -461,7 +461,7 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(
 // bitonic sequence, and a clean-up over distances 16 .. 1 sorts it either
 // way.  Keys are distinct (the index is in the low word), so each fold is
 // exact.  Each wave loads R registers (list pairs wave, wave + 4, ...), each
-// in the order its place in a binary fold tree asks for, and folds them; the
+// in the order its place in the fold asks for, and folds them; the
 // root leaves the lower half descending and the upper ascending, so the
 // upper half, swapped down, folds into the lower.  The four waves merge
 // through LDS.  Nothing depends on the data: no bound, no survivor count, no
@@ -470,46 +470,70 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_kernel(
 // ascending leaf is reversed in registers.
 constexpr int kFoldMaxLists = 128;
 
-// Order of leaf r under a tree node over [lo, hi) whose output is descending
-// (true) or ascending: left subtrees produce descending, right ones ascending.
-constexpr bool fold_leaf_desc(int r, int lo, int hi, bool desc) {
-    return hi - lo == 1 ? desc
-                        : (r < lo + (hi - lo + 1) / 2
-                               ? fold_leaf_desc(r, lo, lo + (hi - lo + 1) / 2, true)
-                               : fold_leaf_desc(r, lo + (hi - lo + 1) / 2, hi, false));
+// The fold runs level by level: nodes 2q and 2q + 1 of a level fold into node
+// q of the next, and an odd level's last node passes through to the next
+// level's last.  The pairs of a level are independent, so each clean-up
+// distance is issued for all of them before the next: their dependent
+// compare-exchange chains interleave instead of running one after another.
+// A pair folds a descending node (even index) with an ascending one (odd), so
+// a leaf's order is fixed by its index at the first level where it is paired.
+constexpr bool fold_node_desc(int i, int n) {
+    return n <= 1 ? true
+                  : ((n & 1) && i == n - 1 ? fold_node_desc((n + 1) / 2 - 1, (n + 1) / 2)
+                                           : (i & 1) == 0);
 }
 
-// Bit r set: leaf r of the tree over [0, R) is loaded descending.
+// Bit r set: leaf r of R is loaded descending.
 template <int R>
 constexpr uint32_t fold_leaf_mask() {
     uint32_t m = 0;
-    for (int r = 0; r < R; ++r) m |= fold_leaf_desc(r, 0, R, true) ? 1u << r : 0u;
+    for (int r = 0; r < R; ++r) m |= fold_node_desc(r, R) ? 1u << r : 0u;
     return m;
 }
 
-template <int LO, int HI, bool DESC, int R>
-__device__ __forceinline__ uint64_t fold_tree(const uint64_t (&x)[R], int lane) {
-    if constexpr (HI - LO == 1) {
-        return x[LO];
-    } else {
-        constexpr int MID = LO + (HI - LO + 1) / 2;
-        const uint64_t a = fold_tree<LO, MID, true>(x, lane);
-        const uint64_t b = fold_tree<MID, HI, false>(x, lane);
-        return bitonic_stages<64, 16, DESC>(umax64(a, b), lane);
-    }
+// Bit q set: node q of a level of NN nodes ends descending.
+template <int NN>
+constexpr uint32_t fold_desc_mask() {
+    uint32_t m = 0;
+    for (int q = 0; q < NN; ++q) m |= fold_node_desc(q, NN) ? 1u << q : 0u;
+    return m;
 }
 
-// The root: lower half descending, upper half ascending.  One register is
-// loaded that way; otherwise the last fold runs its two halves opposite ways.
-template <int R>
-__device__ __forceinline__ uint64_t fold_root(const uint64_t (&x)[R], int lane) {
-    if constexpr (R == 1) {
+// Clean-up distances J .. 1 for the first M nodes of a level of NN: each ends
+// in the order the next level needs of it, both halves of a register alike.
+// Each step is written for all M registers at once (exchanges, then compares
+// and picks), so the registers' chains interleave in the issued code.
+template <int J, int M, int NN>
+__device__ __forceinline__ void fold_stage(uint64_t (&y)[NN], int lane) {
+    constexpr uint32_t kDesc = fold_desc_mask<NN>();
+    const bool lower = (lane & J) == 0;
+    uint64_t o[M];
+#pragma unroll
+    for (int q = 0; q < M; ++q) o[q] = xor_lane64<J>(y[q], lane);
+    bool keep[M];
+#pragma unroll
+    for (int q = 0; q < M; ++q) keep[q] = (y[q] > o[q]) == (lower == (((kDesc >> q) & 1u) != 0));
+#pragma unroll
+    for (int q = 0; q < M; ++q) y[q] = keep[q] ? y[q] : o[q];
+    if constexpr (J > 1) fold_stage<J / 2, M>(y, lane);
+}
+
+// Folds N registers into one whose lower half is descending and upper half
+// ascending (the root pairs the last two nodes half by half that way).
+template <int N>
+__device__ __forceinline__ uint64_t fold_levels(const uint64_t (&x)[N], int lane) {
+    if constexpr (N == 1) {
         return x[0];
+    } else if constexpr (N == 2) {
+        return bitonic_stages<32, 16, true>(umax64(x[0], x[1]), lane);
     } else {
-        constexpr int MID = (R + 1) / 2;
-        const uint64_t a = fold_tree<0, MID, true>(x, lane);
-        const uint64_t b = fold_tree<MID, R, false>(x, lane);
-        return bitonic_stages<32, 16, true>(umax64(a, b), lane);
+        constexpr int M = N / 2, NN = (N + 1) / 2;
+        uint64_t y[NN];
+#pragma unroll
+        for (int q = 0; q < M; ++q) y[q] = umax64(x[2 * q], x[2 * q + 1]);
+        fold_stage<16, M>(y, lane);
+        if constexpr (N & 1) y[NN - 1] = x[N - 1];
+        return fold_levels<NN>(y, lane);
     }
 }
 
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(kTopkMaxThreads) void topk_fold_kernel(
             x[r] = ((kLeafDesc >> r) & 1u) ? v : reverse_half64(v, lane);
         }
     }
-    uint64_t w = fold_root<R>(x, lane);
+    uint64_t w = fold_levels<R>(x, lane);
     w = bitonic_stages<64, 16, true>(umax64(w, xor_lane64<32>(w, lane)), lane);
     WS_MARK(mark + 2);
     WaveTopK<16> st;

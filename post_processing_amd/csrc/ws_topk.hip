@@ -289,19 +289,11 @@ struct WaveTopK {
     }
 };
 
-// Two lists of up to 32 keys per register, one per 32-lane half, each
-// sorted descending within its half.  Folding a list read reversed into each
-// half (ascending) is an elementwise maximum -- the 32 largest of each union
-// as a bitonic sequence -- and a clean-up over distances 16 .. 1, which never
-// crosses the halves.
-__device__ __forceinline__ uint64_t fold_halves(uint64_t desc2, uint64_t asc2, int lane) {
-    return bitonic_stages<64, 16, true>(umax64(desc2, asc2), lane);
-}
-
 // Into wave 0: lanes < k of st.best hold the workgroup's k best, descending,
 // other lanes 0.  Each wave's k best go to its LDS row; wave 0 folds rows 1
-// and 3 into rows 0 and 2 side by side (one per half), then the upper half
-// into the lower.
+// and 3, read reversed, into rows 0 and 2 side by side (one per half), the
+// lower half ending descending and the upper ascending, then the upper half,
+// swapped down, into the lower: one LDS round trip.
 template <int E>
 __device__ __forceinline__ void block_merge(WaveTopK<E>& st, uint64_t (*s_list)[64], int wave,
                                             int waves) {
@@ -314,12 +306,9 @@ __device__ __forceinline__ void block_merge(WaveTopK<E>& st, uint64_t (*s_list)[
     const int dw = lane < 32 ? 0 : 2, aw = dw + 1;
     const uint64_t d = (dw < waves && h < k) ? s_list[dw][h] : 0;
     const uint64_t a = (aw < waves && r < k) ? s_list[aw][r] : 0;
-    const uint64_t x = fold_halves(d, a, lane);
-    wave_lds_sync();
-    s_list[0][lane] = x;
-    wave_lds_sync();
-    const uint64_t up = (lane < 32 && r < k) ? s_list[0][32 + r] : 0;
-    st.best = fold_halves(lane < 32 ? x : 0, up, lane);
+    const uint64_t x = bitonic_stages<32, 16, true>(umax64(d, a), lane);
+    const uint64_t y = bitonic_stages<64, 16, true>(umax64(x, xor_lane64<32>(x, lane)), lane);
+    st.best = lane < 32 ? y : 0;
     st.thr = readlane64(st.best, k - 1);
 }
 

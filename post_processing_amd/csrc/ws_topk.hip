@@ -62,7 +62,7 @@ __device__ __forceinline__ uint32_t order_image(float v) {
 
 // Sort a bitonic sequence (one key per lane) into descending lane order.
 __device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
-    return bitonic_stages<64, 32, true>(x, lane);
+    return bitonic_stages<64, 32, true, true>(x, lane);
 }
 
 constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
@@ -73,7 +73,7 @@ constexpr int kInsertMax = 4;                      // fewer survivors: insert on
 // from the top instead takes 32 rounds of compare, ballot and count, each
 // waiting on the last.
 __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k, int lane) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(m, lane), k - 1);
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true, true>(m, lane), k - 1);
 }
 
 // Number of the n keys of v (LDS) greater than x; sixteen loads are issued
@@ -158,16 +158,16 @@ struct WaveTopK {
             for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
         } else if (empty && cnt <= 64) {
             // The first keys: sorted, they are the list.
-            best = wave_sort_desc_first(lane < cnt ? scratch[lane] : 0, lane, cnt);
+            best = wave_sort_desc_first<true>(lane < cnt ? scratch[lane] : 0, lane, cnt);
             thr = readlane64(best, k - 1);
         } else if (k + cnt <= 64) {
             const uint64_t x = lane < k ? best : (lane < k + cnt ? scratch[lane - k] : 0);
-            best = wave_sort_desc_first(x, lane, k + cnt);
+            best = wave_sort_desc_first<true>(x, lane, k + cnt);
             thr = readlane64(best, k - 1);
         } else {
             for (int t = 0; t < cnt; t += 64) {
                 const uint64_t tile = t + lane < cnt ? scratch[t + lane] : 0;
-                best = wave_clean_desc(umax64(best, wave_sort<false>(tile, lane)), lane);
+                best = wave_clean_desc(umax64(best, wave_sort<false, true>(tile, lane)), lane);
             }
             thr = readlane64(best, k - 1);
         }
@@ -306,8 +306,9 @@ __device__ __forceinline__ void block_merge(WaveTopK<E>& st, uint64_t (*s_list)[
     const int dw = lane < 32 ? 0 : 2, aw = dw + 1;
     const uint64_t d = (dw < waves && h < k) ? s_list[dw][h] : 0;
     const uint64_t a = (aw < waves && r < k) ? s_list[aw][r] : 0;
-    const uint64_t x = bitonic_stages<32, 16, true>(umax64(d, a), lane);
-    const uint64_t y = bitonic_stages<64, 16, true>(umax64(x, xor_lane64<32>(x, lane)), lane);
+    const uint64_t x = bitonic_stages<32, 16, true, true>(umax64(d, a), lane);
+    const uint64_t y =
+        bitonic_stages<64, 16, true, true>(umax64(x, xor_lane64<32>(x, lane)), lane);
     st.best = lane < 32 ? y : 0;
     st.thr = readlane64(st.best, k - 1);
 }

@@ -306,9 +306,8 @@ __device__ __forceinline__ void block_merge(WaveTopK<E>& st, uint64_t (*s_list)[
     const int dw = lane < 32 ? 0 : 2, aw = dw + 1;
     const uint64_t d = (dw < waves && h < k) ? s_list[dw][h] : 0;
     const uint64_t a = (aw < waves && r < k) ? s_list[aw][r] : 0;
-    const uint64_t x = bitonic_stages<32, 16, true, true>(umax64(d, a), lane);
-    const uint64_t y =
-        bitonic_stages<64, 16, true, true>(umax64(x, xor_lane64<32>(x, lane)), lane);
+    const uint64_t x = bitonic_stages<32, 16, true>(umax64(d, a), lane);
+    const uint64_t y = bitonic_stages<64, 16, true>(umax64(x, xor_lane64<32>(x, lane)), lane);
     st.best = lane < 32 ? y : 0;
     st.thr = readlane64(st.best, k - 1);
 }

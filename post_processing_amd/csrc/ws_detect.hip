@@ -1014,22 +1014,6 @@ __device__ __forceinline__ void gather(const DetParams& p, const uint64_t* __res
 // Up to this many kept boxes are placed by counting, not sorted.
 constexpr int kRankByCountMax = 256;
 
-// Number of the n keys of v (LDS) above x; sixteen loads are issued before
-// their compares.
-__device__ __forceinline__ int count_above(const uint64_t* v, int n, uint64_t x) {
-    int r = 0;
-    int j = 0;
-    for (; j + 16 <= n; j += 16) {
-        uint64_t t[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) t[u] = v[j + u];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) r += t[u] > x ? 1 : 0;
-    }
-    for (; j < n; ++j) r += v[j] > x ? 1 : 0;
-    return r;
-}
-
 // Bytes of the suppression kernel's shared region after the keys, run
 // starts and prefix sums: per-wave kept-position lists, or (at other times)
 // the class counters (two 16-bit counters per word) or the kept boxes, areas
@@ -1418,12 +1402,34 @@ __global__ __launch_bounds__(NT) void det_nms_kernel(
     if (any_class) {
         for (int q = tid; q < count; q += NT) emit(s[k_pos[q]] & ~1ull, k_box[q], q);
     } else if (kept_total <= kRankByCountMax) {
-        for (int t = tid; t < kept_total; t += NT) {
-            const uint64_t x = s[t];
-            const int r = count_above(s, kept_total, x);
-            if (r < count) {
-                if (staged) emit(x, staged_box(x), r);
-                else emit(x, global_box(x), r);
+        // Eight lanes rank each kept key: lane j of the group counts the keys
+        // above it among keys j, j + 8, ... (eight reads in flight), and the
+        // eight counts are summed across the group (lane distances 1, 2, 4).
+        // A group's lanes are all below `pairs` or all at or above it.
+        const int pairs = kept_total * 8;
+        for (int base = 0; base < pairs; base += NT) {   // uniform
+            const int e = base + tid;
+            if (e < pairs) {
+                const int t = e >> 3, j = e & 7;
+                const uint64_t x = s[t];
+                uint32_t r = 0;
+                for (int i0 = j; i0 < kept_total; i0 += 64) {
+                    uint64_t v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int i = i0 + 8 * u;
+                        v[u] = i < kept_total ? s[i] : 0;   // 0 is above no key
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) r += v[u] > x ? 1u : 0u;
+                }
+                r += xor_lane32<1>(r, lane);
+                r += xor_lane32<2>(r, lane);
+                r += xor_lane32<4>(r, lane);
+                if (j == 0 && (int)r < count) {
+                    if (staged) emit(x, staged_box(x), (int)r);
+                    else emit(x, global_box(x), (int)r);
+                }
             }
         }
     } else if (staged) {

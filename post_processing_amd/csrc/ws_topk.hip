@@ -65,6 +65,14 @@ __device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
     return bitonic_stages<64, 32, true, true>(x, lane);
 }
 
+// The lane number through an empty asm: the lane masks of a network given
+// this value are shared within that network only, not hoisted to the
+// kernel's start with every other network's.
+__device__ __forceinline__ int fresh_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
 constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
 
 // K-th largest of one 32-bit value per lane, with multiplicity: lane k - 1 of
@@ -158,11 +166,11 @@ struct WaveTopK {
             for (int i = 0; i < cnt; ++i) insert(readlane64(cand, i));
         } else if (empty && cnt <= 64) {
             // The first keys: sorted, they are the list.
-            best = wave_sort_desc_first<true>(lane < cnt ? scratch[lane] : 0, lane, cnt);
+            best = wave_sort_desc_first(lane < cnt ? scratch[lane] : 0, fresh_lane(lane), cnt);
             thr = readlane64(best, k - 1);
         } else if (k + cnt <= 64) {
             const uint64_t x = lane < k ? best : (lane < k + cnt ? scratch[lane - k] : 0);
-            best = wave_sort_desc_first<true>(x, lane, k + cnt);
+            best = wave_sort_desc_first(x, fresh_lane(lane), k + cnt);
             thr = readlane64(best, k - 1);
         } else {
             for (int t = 0; t < cnt; t += 64) {

@@ -81,7 +81,7 @@ constexpr int kInsertMax = 4;                      // fewer survivors: insert on
 // from the top instead takes 32 rounds of compare, ballot and count, each
 // waiting on the last.
 __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t m, int k, int lane) {
-    return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true, true>(m, lane), k - 1);
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(m, fresh_lane(lane)), k - 1);
 }
 
 // Number of the n keys of v (LDS) greater than x; sixteen loads are issued

@@ -83,21 +83,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 // the whole network.  B = 64 with J = 32 is the final merge.  One compare per
 // stage: a lane keeps its own key when "mine is larger" agrees with the side
 // of the pair it must end on.
-//
-// FRESH passes the lane number through an empty asm first, so the stage's
-// lane masks are computed where the stage runs.  Otherwise the compiler
-// computes every mask of a kernel once, at its start; in a kernel with many
-// networks they outgrow the scalar registers and are spilled to vector-
-// register lanes and read back one by one inside the networks.
-template <int B, int J, bool DESC, bool FRESH = false, typename T>
+template <int B, int J, bool DESC, typename T>
 __device__ __forceinline__ T bitonic_stage(T x, int lane) {
-    int l = lane;
-    if constexpr (FRESH) asm volatile("" : "+v"(l));
     T y;
-    if constexpr (sizeof(T) == 8) y = xor_lane64<J>(x, l);
-    else y = xor_lane32<J>(x, l);
-    const bool lower = (l & J) == 0;
-    const bool ascending_block = (l & B) == 0;
+    if constexpr (sizeof(T) == 8) y = xor_lane64<J>(x, lane);
+    else y = xor_lane32<J>(x, lane);
+    const bool lower = (lane & J) == 0;
+    const bool ascending_block = (lane & B) == 0;
     const bool keep_large = (lower != ascending_block) != DESC;
     if constexpr (sizeof(T) == 4) {
         // 32-bit keys: maximum and minimum are single instructions, and the
@@ -111,26 +103,26 @@ __device__ __forceinline__ T bitonic_stage(T x, int lane) {
     return x;
 }
 
-template <int B, int J, bool DESC, bool FRESH = false, typename T>
+template <int B, int J, bool DESC, typename T>
 __device__ __forceinline__ T bitonic_stages(T x, int lane) {
-    x = bitonic_stage<B, J, DESC, FRESH>(x, lane);
-    if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC, FRESH>(x, lane);
+    x = bitonic_stage<B, J, DESC>(x, lane);
+    if constexpr (J > 1) return bitonic_stages<B, J / 2, DESC>(x, lane);
     return x;
 }
 
 // Sort one key per lane within each block of S lanes (S a power of two up to
 // 64): block 0 ends in DESC order, the next block in the other order, and so
 // on.  S = 64 sorts the whole wave.
-template <int S, bool DESC, bool FRESH = false, typename T>
+template <int S, bool DESC, typename T>
 __device__ __forceinline__ T sort_lanes(T x, int lane) {
-    if constexpr (S > 2) x = sort_lanes<S / 2, DESC, FRESH>(x, lane);
-    return bitonic_stages<S, S / 2, DESC, FRESH>(x, lane);
+    if constexpr (S > 2) x = sort_lanes<S / 2, DESC>(x, lane);
+    return bitonic_stages<S, S / 2, DESC>(x, lane);
 }
 
 // Sort one key per lane across the wave.
-template <bool DESC, bool FRESH = false, typename T>
+template <bool DESC, typename T>
 __device__ __forceinline__ T wave_sort(T x, int lane) {
-    return sort_lanes<64, DESC, FRESH>(x, lane);
+    return sort_lanes<64, DESC>(x, lane);
 }
 
 // Sort one key per lane across the wave when only lanes below n (n <= 64,
@@ -139,11 +131,11 @@ __device__ __forceinline__ T wave_sort(T x, int lane) {
 // covers n leaves block 0 sorted and the rest all-smallest, which is the whole
 // wave sorted descending.  Fewer stages for few keys: 6 up to 8, 10 up to 16,
 // 21 beyond.
-template <bool FRESH = false, typename T>
+template <typename T>
 __device__ __forceinline__ T wave_sort_desc_first(T x, int lane, int n) {
-    if (n <= 8) return sort_lanes<8, true, FRESH>(x, lane);
-    if (n <= 16) return sort_lanes<16, true, FRESH>(x, lane);
-    return sort_lanes<64, true, FRESH>(x, lane);
+    if (n <= 8) return sort_lanes<8, true>(x, lane);
+    if (n <= 16) return sort_lanes<16, true>(x, lane);
+    return sort_lanes<64, true>(x, lane);
 }
 
 // Bitonic network over a block of 64*K keys held K per lane -- key r*64 +

@@ -60,17 +60,17 @@ __device__ __forceinline__ uint32_t order_image(float v) {
     return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 
-// Sort a bitonic sequence (one key per lane) into descending lane order.
-__device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
-    return bitonic_stages<64, 32, true, true>(x, lane);
-}
-
 // The lane number through an empty asm: the lane masks of a network given
 // this value are shared within that network only, not hoisted to the
 // kernel's start with every other network's.
 __device__ __forceinline__ int fresh_lane(int lane) {
     asm volatile("" : "+v"(lane));
     return lane;
+}
+
+// Sort a bitonic sequence (one key per lane) into descending lane order.
+__device__ __forceinline__ uint64_t wave_clean_desc(uint64_t x, int lane) {
+    return bitonic_stages<64, 32, true>(x, fresh_lane(lane));
 }
 
 constexpr int kInsertMax = 4;                      // fewer survivors: insert one by one
@@ -175,7 +175,7 @@ struct WaveTopK {
         } else {
             for (int t = 0; t < cnt; t += 64) {
                 const uint64_t tile = t + lane < cnt ? scratch[t + lane] : 0;
-                best = wave_clean_desc(umax64(best, wave_sort<false, true>(tile, lane)), lane);
+                best = wave_clean_desc(umax64(best, wave_sort<false>(tile, fresh_lane(lane))), lane);
             }
             thr = readlane64(best, k - 1);
         }
